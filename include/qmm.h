@@ -1,0 +1,190 @@
+/*
+ * qmm.h -- C ABI of libqmm: fused-dequant matmul of Q4_K / Q6_K weights with
+ * Q8_1-quantized activations on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, then section):
+ *   [8e]  minfer ch. 06, "06 · 8e/8e② — decode MMVQ: dp4a integer dot
+ *         products + the llama.cpp launch table"
+ *   [MMQ] ZINC, "ZINC MMQ v2 — Fused Q4_K×Q8_1 Tensor-Core GEMM (beat
+ *         llama.cpp)"
+ *   [GAP] ZINC, "Prefill Gap Closure Plan — ZINC CUDA vs llama.cpp"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every buffer argument is a DEVICE pointer owned by the caller
+ *   (e.g. torch tensor storage) and must be 16-byte aligned; the library never
+ *   allocates, frees or keeps a pointer past the call.  Outputs must not alias
+ *   inputs.
+ * Stream.  `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *   only enqueues work on that stream and returns; none synchronises.
+ * Status.  Every entry point returns QMM_OK (0) or a negative qmm_status.
+ *   Argument errors are detected on the host before anything is enqueued, so
+ *   a failing call has no effect.  QMM_ERR_HIP reports a launch error from the
+ *   HIP runtime.  Device-side data (e.g. expert ids) cannot be checked without
+ *   a synchronisation; their ranges are documented preconditions.
+ *
+ * Layouts
+ * -------
+ * Q4_K weights: rows of K/256 super-blocks of 144 bytes (f16 d at 0, f16
+ *   dmin at 2, 12 bytes of packed 6-bit sub-block scales/mins at 4, 128 bytes
+ *   of 4-bit values at 16); weight = d*sc*q - dmin*m per 32-weight sub-block
+ *   ([8e] §2 and §3.2).  Row-major [M][K/256][144].
+ * Q6_K weights: rows of K/256 super-blocks of 210 bytes (ql[128] at 0,
+ *   qh[64] at 128, int8 sc[16] at 192, f16 d at 208); weight = d*sc*(q6-32)
+ *   per 16-weight sub-block ([8e] §3.1 and §3.3).  Row-major [M][K/256][210].
+ * Q8_1 activations ("pad40"): rows of K/32 blocks of 40 bytes (f16 d at 0,
+ *   two zero pad bytes, int8 q[32] at 4, int32 sum of q at 36) ([8e] §2;
+ *   [MMQ] "What they do right").  Row-major [rows][K/32][40].
+ * Outputs: fp32, token-major y[t*M + i] ([8e] §3.2).
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qmm_status {
+    QMM_OK = 0,
+    QMM_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    QMM_ERR_SHAPE = -2,       /* a size is out of range or not a block multiple  */
+    QMM_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned                */
+    QMM_ERR_WORKSPACE = -4,   /* workspace smaller than qmm_workspace_bytes()    */
+    QMM_ERR_HIP = -5,         /* the HIP runtime reported an error               */
+    QMM_ERR_UNSUPPORTED = -6  /* unknown format / operation code                 */
+} qmm_status;
+
+/* Weight formats for moe_grouped_mmq / qmm_debug_subdots. */
+#define QMM_Q4_K 12
+#define QMM_Q6_K 14
+
+/* Operation codes for qmm_workspace_bytes. */
+#define QMM_OP_MMQ 1
+#define QMM_OP_MOE 2
+
+/* Largest token count accepted by the matvec entry points. */
+#define QMM_MMVQ_MAX_T 8
+
+/*
+ * q8_1_quantize -- fp32 activations x[T][K] (row-major) -> Q8_1 xq[T][K/32].
+ * Per 32-block: am = max|x|, d = am/127, di = 1/d (0 if d == 0),
+ * q = clamp(rint(x*di), -128, 127) rounding half to even, stored with
+ * f16(d) (round to nearest even), zero pad and the int32 sum of q
+ * ([8e] §2 and the quantizer of §3.2).  IEEE fp32 division, no contraction:
+ * the bytes are bit-identical to the IEEE emulation of these steps.
+ * Requires T >= 0, K > 0, K % 32 == 0.  T == 0 is a no-op.
+ */
+int q8_1_quantize(const float* x, void* xq, int64_t T, int64_t K, void* stream);
+
+/*
+ * mmvq_q4k / mmvq_q6k -- decode matvec y[T][M] = xq[T][K] . W[M][K]^T for
+ * 1 <= T <= QMM_MMVQ_MAX_T ([8e] §2-§3.2: integer 4-way dot products of
+ * unpacked 4-bit (6-bit) weights with int8 activations; the Q4_K min term
+ * uses the activation sum from a dot product against ones).  One wave64 per
+ * weight row streams the row's blocks.  Requires M >= 1, K % 256 == 0.
+ * Output fp32, y[t*M + i].  Deterministic: identical inputs give identical
+ * bits.
+ */
+int mmvq_q4k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
+             void* stream);
+int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
+             void* stream);
+
+/*
+ * mmq_q4k / mmq_q6k -- prefill GEMM y[T][M] = xq[T][K] . W[M][K]^T for any
+ * T >= 1 ([MMQ] "Kernel architecture": fused dequant inside the matrix
+ * inner loop, Q8_1 activations; "Persistent kernel + atomic work queue").
+ * Weights are unpacked to int8 and multiplied on int8 MFMA with int32
+ * accumulation per sub-block, then scaled in fp32.  Output tiles are claimed
+ * from per-XCD atomic counters in `ws`; each tile runs its whole K loop in one
+ * workgroup (no split-K, no fixup), so results are deterministic.
+ * `ws` must hold qmm_workspace_bytes(QMM_OP_MMQ, ...) bytes and be zero-filled
+ * before its first use (qmm_workspace_init); every call leaves it zeroed.
+ * Calls sharing one workspace must be ordered on one stream.
+ * Requires M >= 1, T >= 1, K % 256 == 0.
+ */
+int mmq_q4k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
+            void* ws, size_t ws_bytes, void* stream);
+int mmq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
+            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_mmq -- routed-expert grouped GEMM ([GAP] lever T2 and its
+ * de-risk paragraph: histogram of expert ids, prefix-sum offsets, per-expert
+ * slot buckets, one product per expert, scatter back; [MMQ] "MoE routing
+ * (fused gather)": work entries (expert, m_tile, n_tile)).
+ *   fmt                  QMM_Q4_K or QMM_Q6_K
+ *   w                    E experts, each M rows of K weights, expert e at
+ *                        (const char*)w + e*expert_stride_bytes
+ *   xq                   Q8_1 activations, rows of K/32 blocks: T rows when
+ *                        x_rows_per_token == 1 (row t), else T*top_k rows
+ *                        (row t*top_k + k), x_rows_per_token == top_k
+ *   ids                  int32 [T][top_k], every id in [0, E) (precondition)
+ *   expert_weights       NULL: y is per-slot, y[(t*top_k + k)*M + i] =
+ *                        W[ids[t][k]] . x_row; otherwise fp32 [T][top_k] and
+ *                        y[t*M + i] = sum_k p[t][k] * (W[ids[t][k]] . x_row)
+ *                        summed in increasing k (deterministic, no atomics)
+ *   ws                   qmm_workspace_bytes(QMM_OP_MOE, M, K, T, E, top_k)
+ *                        bytes; holds the buckets, the queue counters and, in
+ *                        weighted mode, the per-slot fp32 results
+ * Work is tiled as 128 weight rows x 32 routed slots of one expert, so an
+ * expert's weights are read once per 32 tokens routed to it.  Requires
+ * 1 <= E <= 512, M >= 1, K % 256 == 0, 1 <= top_k <= min(E, 64), T >= 1,
+ * x_rows_per_token in {1, top_k}, expert_stride_bytes >= M*K/256*block bytes
+ * and a multiple of 16.
+ */
+int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
+                    int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,
+                    const int32_t* ids, const float* expert_weights, int64_t T, int64_t top_k,
+                    float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * swiglu_q8_1 -- glue between the grouped gate/up and down calls: reads the
+ * per-slot gate||up rows g_u[R][2*F] (fp32; gate in columns 0..F-1, up in
+ * F..2F-1), computes h = silu(gate) * up in fp32 and writes Q8_1 hq[R][F/32]
+ * with the quantizer of q8_1_quantize.  The pages name fused SwiGLU producers
+ * of the quantized activation ([8e] §3.2) but give no formula; silu(g)*u is
+ * the reading taken.  Requires R >= 0, F % 32 == 0.
+ */
+int swiglu_q8_1(const float* g_u, void* hq, int64_t R, int64_t F, void* stream);
+
+/* Bytes of workspace needed by `op` (QMM_OP_MMQ or QMM_OP_MOE) for the given
+ * sizes; unused sizes may be 0.  Returns 0 for an unknown op. */
+size_t qmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k);
+
+/* Zero-fills a workspace on `stream` with a fill kernel (no memset node). */
+int qmm_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a qmm_status value. */
+const char* qmm_status_str(int status);
+
+/*
+ * qmm_debug_subdots -- test hook: the integer stage of the MMVQ
+ * (path == 0) or MMQ (path == 1) kernel of format `fmt`, built from the same
+ * source as the product kernels, writing the exact integer sub-block sums
+ * instead of the scaled result.  Q4_K: D[T][M][K/32] = sum nib*q and
+ * S[T][K/32] = sum q (the ones-dot on path 0, the stored sum on path 1).
+ * Q6_K: D[T][M][K/16] = sum (q6-32)*q and S is not written.  T <= 8 for
+ * path 0.  Path 1 needs an MMQ workspace (ws, ws_bytes) like mmq_q4k; path 0
+ * ignores it.  D and S are zero-filled by the call.  For tests on small
+ * shapes only.
+ */
+int qmm_debug_subdots(int fmt, int path, const void* w, const void* xq, int32_t* D, int32_t* S,
+                      int64_t M, int64_t K, int64_t T, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qmm_probe_read -- measurement hook, not part of the method: a read-only
+ * streaming kernel over `bytes` bytes of `buf` (a multiple of 16) that
+ * reduces them to one word written to sink[0].  Gives the HBM read ceiling
+ * at a given byte count ([8e] §3.3 and §6: measure a read-only ceiling before
+ * calling a bandwidth figure a limit).
+ */
+int qmm_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMM_H */

@@ -41,4 +41,4 @@ from .quantize import quantize_q8_1  # noqa: F401
 from .matmul import (  # noqa: F401
     dense, abs_bound, q4k_subdots, q6k_subdots, q4k_factored, q6k_factored,
 )
-from .moe import route_buckets, grouped, combine, swiglu  # noqa: F401
+from .moe import route_buckets, grouped, grouped_blocks, combine, swiglu  # noqa: F401

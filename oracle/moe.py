@@ -77,3 +77,30 @@ def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     """``silu(gate) * up = gate / (1 + exp(-gate)) * up`` in float64 (glue reading)."""
     g = np.asarray(gate, np.float64)
     return g / (1.0 + np.exp(-g)) * np.asarray(up, np.float64)
+
+
+def grouped_blocks(dequant, blocks: np.ndarray, X: np.ndarray, ids: np.ndarray,
+                   rows_per_token: int, experts=None):
+    """``grouped`` for quantized expert weights, one expert dequantised at a time.
+
+    ``dequant`` maps one expert's blocks to float64 [M, K] (``q4k_dequant`` or
+    ``q6k_dequant``).  Returns ``(y_slot, bound)`` with
+    ``bound[s] = sum_k |W[e]| |x_row|`` (the per-element error scale); only
+    the slots of ``experts`` (all by default) are filled.
+    """
+    T, top_k = ids.shape
+    E = blocks.shape[0]
+    M = blocks.shape[1]
+    y = np.zeros((T * top_k, M), dtype=np.float64)
+    bound = np.zeros((T * top_k, M), dtype=np.float64)
+    _, offsets, bucket = route_buckets(ids, E)
+    Xf = np.asarray(X, np.float64)
+    for e in (range(E) if experts is None else experts):
+        slots = bucket[offsets[e]:offsets[e + 1]]
+        if slots.size == 0:
+            continue
+        W = dequant(blocks[e])
+        rows = slots // top_k if rows_per_token == 1 else slots
+        y[slots] = Xf[rows] @ W.T
+        bound[slots] = np.abs(Xf[rows]) @ np.abs(W).T
+    return y, bound

@@ -1,0 +1,220 @@
+"""Python binding of libqmm: fused-dequant Q4_K / Q6_K x Q8_1 matmul on MI355X.
+
+Thin marshalling over the C ABI of ``include/qmm.h``: each function checks
+tensor dtypes, devices and shapes, allocates outputs with torch, and passes
+raw device pointers and the current HIP stream.  Every step of the
+computation runs in the HIP kernels of ``libqmm.so``.
+
+Tensor layouts (uint8 unless stated):
+  Q4_K weights  [M, K/256, 144]      Q6_K weights  [M, K/256, 210]
+  Q8_1 blocks   [rows, K/32, 40]     outputs       float32 [T, M]
+  MoE experts   [E, M, K/256, bytes] (contiguous; the expert stride is taken
+                from the tensor)
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    QMM_MMVQ_MAX_T, QMM_OP_MMQ, QMM_OP_MOE, QMM_Q4_K, QMM_Q6_K, QmmError, LIB_PATH,
+)
+
+__all__ = [
+    "q8_1_quantize", "mmvq_q4k", "mmvq_q6k", "mmq_q4k", "mmq_q6k", "moe_grouped_mmq",
+    "swiglu_q8_1", "workspace", "workspace_bytes", "debug_subdots", "probe_read", "QmmError",
+    "QMM_Q4_K", "QMM_Q6_K", "LIB_PATH",
+]
+
+_BLOCK_BYTES = {QMM_Q4_K: 144, QMM_Q6_K: 210}
+
+
+def _p(t: torch.Tensor | None):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int | None = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _weights(w: torch.Tensor, fmt: int, name: str = "w"):
+    _need(w, torch.uint8, name, 3)
+    if w.shape[2] != _BLOCK_BYTES[fmt]:
+        raise ValueError(f"{name}: blocks of {_BLOCK_BYTES[fmt]} bytes expected")
+    return w.shape[0], w.shape[1] * 256
+
+
+def _acts(xq: torch.Tensor, K: int, name: str = "xq"):
+    _need(xq, torch.uint8, name, 3)
+    if xq.shape[2] != 40 or xq.shape[1] * 32 != K:
+        raise ValueError(f"{name}: expected [rows, {K // 32}, 40], got {tuple(xq.shape)}")
+    return xq.shape[0]
+
+
+def workspace_bytes(op: int, M: int = 0, K: int = 0, T: int = 0, E: int = 0, top_k: int = 0) -> int:
+    return int(_lib.LIB.qmm_workspace_bytes(op, M, K, T, E, top_k))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace of ``nbytes`` bytes (16-byte multiple) on ``device``."""
+    return torch.zeros((max(16, (nbytes + 15) // 16 * 16),), dtype=torch.uint8, device=device)
+
+
+_MMQ_WS: dict = {}
+
+
+def _mmq_ws(device: torch.device) -> torch.Tensor:
+    key = (device.index if device.index is not None else torch.cuda.current_device())
+    ws = _MMQ_WS.get(key)
+    if ws is None:
+        ws = workspace(workspace_bytes(QMM_OP_MMQ), device)
+        _MMQ_WS[key] = ws
+    return ws
+
+
+def q8_1_quantize(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 ``x[T, K]`` -> Q8_1 blocks ``[T, K/32, 40]``."""
+    _need(x, torch.float32, "x", 2)
+    T, K = x.shape
+    if out is None:
+        out = torch.empty((T, K // 32, 40), dtype=torch.uint8, device=x.device)
+    _acts(out, K, "out")
+    _lib.call("q8_1_quantize", _p(x), _p(out), T, K, _stream(x.device))
+    return out
+
+
+def _mmvq(name: str, fmt: int, w, xq, out):
+    M, K = _weights(w, fmt)
+    T = _acts(xq, K)
+    if out is None:
+        out = torch.empty((T, M), dtype=torch.float32, device=w.device)
+    _need(out, torch.float32, "out", 2)
+    _lib.call(name, _p(w), _p(xq), _p(out), M, K, T, _stream(w.device))
+    return out
+
+
+def mmvq_q4k(w: torch.Tensor, xq: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode matvec, Q4_K weights x Q8_1 activations (T <= 8) -> fp32 [T, M]."""
+    return _mmvq("mmvq_q4k", QMM_Q4_K, w, xq, out)
+
+
+def mmvq_q6k(w: torch.Tensor, xq: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode matvec, Q6_K weights x Q8_1 activations (T <= 8) -> fp32 [T, M]."""
+    return _mmvq("mmvq_q6k", QMM_Q6_K, w, xq, out)
+
+
+def _mmq(name: str, fmt: int, w, xq, out, ws):
+    M, K = _weights(w, fmt)
+    T = _acts(xq, K)
+    if out is None:
+        out = torch.empty((T, M), dtype=torch.float32, device=w.device)
+    _need(out, torch.float32, "out", 2)
+    ws = _mmq_ws(w.device) if ws is None else ws
+    _need(ws, torch.uint8, "ws", 1)
+    _lib.call(name, _p(w), _p(xq), _p(out), M, K, T, _p(ws), ws.numel(), _stream(w.device))
+    return out
+
+
+def mmq_q4k(w, xq, out=None, ws=None) -> torch.Tensor:
+    """Prefill GEMM, Q4_K weights x Q8_1 activations -> fp32 [T, M] (int8 MFMA)."""
+    return _mmq("mmq_q4k", QMM_Q4_K, w, xq, out, ws)
+
+
+def mmq_q6k(w, xq, out=None, ws=None) -> torch.Tensor:
+    """Prefill GEMM, Q6_K weights x Q8_1 activations -> fp32 [T, M] (int8 MFMA)."""
+    return _mmq("mmq_q6k", QMM_Q6_K, w, xq, out, ws)
+
+
+def moe_grouped_mmq(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.Tensor,
+                    expert_weights: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Grouped expert GEMM.
+
+    ``w`` [E, M, K/256, bytes]; ``ids`` int32 [T, top_k]; ``xq`` has T rows
+    (one per token) or T*top_k rows (one per slot).  Without
+    ``expert_weights`` the result is per slot, [T*top_k, M]; with fp32
+    ``expert_weights`` [T, top_k] it is the weighted sum over k, [T, M].
+    """
+    _need(w, torch.uint8, "w", 4)
+    if w.shape[3] != _BLOCK_BYTES[fmt]:
+        raise ValueError("w: wrong block size for fmt")
+    E, M, K = w.shape[0], w.shape[1], w.shape[2] * 256
+    _need(ids, torch.int32, "ids", 2)
+    T, top_k = ids.shape
+    rows = _acts(xq, K)
+    if rows == T:
+        rows_per_token = 1
+    elif rows == T * top_k:
+        rows_per_token = top_k
+    else:
+        raise ValueError("xq must have T or T*top_k rows")
+    if expert_weights is not None:
+        _need(expert_weights, torch.float32, "expert_weights", 2)
+        if tuple(expert_weights.shape) != (T, top_k):
+            raise ValueError("expert_weights must be [T, top_k]")
+    out_rows = T if expert_weights is not None else T * top_k
+    if out is None:
+        out = torch.empty((out_rows, M), dtype=torch.float32, device=w.device)
+    _need(out, torch.float32, "out", 2)
+    need = workspace_bytes(QMM_OP_MOE, M, K, T, E, top_k)
+    if ws is None:
+        ws = workspace(need, w.device)
+    _need(ws, torch.uint8, "ws", 1)
+    stride = w.stride(0)
+    _lib.call("moe_grouped_mmq", fmt, _p(w), E, M, K, stride, _p(xq), rows_per_token, _p(ids),
+              _p(expert_weights), T, top_k, _p(out), _p(ws), ws.numel(), _stream(w.device))
+    return out
+
+
+def swiglu_q8_1(g_u: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows ``g_u[R, 2F]`` (gate | up) -> Q8_1 of silu(gate) * up, ``[R, F/32, 40]``."""
+    _need(g_u, torch.float32, "g_u", 2)
+    R, F2 = g_u.shape
+    F = F2 // 2
+    if out is None:
+        out = torch.empty((R, F // 32, 40), dtype=torch.uint8, device=g_u.device)
+    _acts(out, F, "out")
+    _lib.call("swiglu_q8_1", _p(g_u), _p(out), R, F, _stream(g_u.device))
+    return out
+
+
+def debug_subdots(fmt: int, path: int, w: torch.Tensor, xq: torch.Tensor):
+    """Integer stage of the MMVQ (path 0) or MMQ (path 1) kernel: (D, S) int32.
+
+    Q4_K: D [T, M, K/32], S [T, K/32]; Q6_K: D [T, M, K/16], S None.
+    """
+    M, K = _weights(w, fmt)
+    T = _acts(xq, K)
+    nsub = K // 32 if fmt == QMM_Q4_K else K // 16
+    D = torch.empty((T, M, nsub), dtype=torch.int32, device=w.device)
+    S = torch.empty((T, K // 32), dtype=torch.int32, device=w.device) if fmt == QMM_Q4_K else None
+    ws = _mmq_ws(w.device)
+    _lib.call("qmm_debug_subdots", fmt, path, _p(w), _p(xq), _p(D), _p(S), M, K, T, _p(ws),
+              ws.numel(), _stream(w.device))
+    return D, S
+
+
+def probe_read(buf: torch.Tensor, nbytes: int | None = None, sink: torch.Tensor | None = None):
+    """Enqueue the read-only ceiling probe over the first ``nbytes`` of ``buf``."""
+    if buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    if sink is None:
+        sink = torch.zeros((4,), dtype=torch.int32, device=buf.device)
+    _lib.call("qmm_probe_read", _p(buf), nbytes, _p(sink), _stream(buf.device))
+    return sink

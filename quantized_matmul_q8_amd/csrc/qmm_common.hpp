@@ -1,0 +1,151 @@
+// Internal helpers shared by the libqmm translation units (device and host).
+//
+// Pages cited (title, then section):
+//   [8e]  minfer ch. 06, "06 · 8e/8e② — decode MMVQ: dp4a integer dot products
+//         + the llama.cpp launch table"
+//   [MMQ] ZINC, "ZINC MMQ v2 — Fused Q4_K×Q8_1 Tensor-Core GEMM (beat llama.cpp)"
+//   [GAP] ZINC, "Prefill Gap Closure Plan — ZINC CUDA vs llama.cpp"
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "qmm.h"
+
+namespace qmm {
+
+constexpr int kQK = 256;       // weights per K-quant super-block
+constexpr int kQB = 32;        // activations per Q8_1 block
+constexpr int kQ4Bytes = 144;  // Q4_K super-block bytes
+constexpr int kQ6Bytes = 210;  // Q6_K super-block bytes
+constexpr int kQ8Bytes = 40;   // Q8_1 block bytes
+constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, each with its own L2
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline hipStream_t to_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Map the runtime's last error (after an enqueue) to a status.
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? QMM_OK : QMM_ERR_HIP;
+}
+
+// Compute units of the current device, cached per device id.
+int device_cu_count();
+
+// ----------------------------------------------------------------------------
+// Device side
+// ----------------------------------------------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// 16-byte load from a 4-byte aligned address (one dwordx4 load).
+struct __attribute__((aligned(4))) u32x4_a4 { uint32_t v[4]; };
+
+__device__ __forceinline__ uint4 ld16_a4(const void* p) {
+  const u32x4_a4 t = *reinterpret_cast<const u32x4_a4*>(p);
+  return make_uint4(t.v[0], t.v[1], t.v[2], t.v[3]);
+}
+
+__device__ __forceinline__ uint4 ld16_a16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// 16-byte aligned load marked non-temporal (streamed once; keeps L2 for data
+// that is reused).
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 16 bytes from a 2-byte aligned address: aligned dword loads joined with a
+// byte funnel shift.  Q6_K blocks are 210 bytes, so every other block starts
+// at 2 mod 4.  The fifth dword is read only when the address is misaligned,
+// so nothing past p + 16 is touched for aligned addresses.
+__device__ __forceinline__ uint4 ld16_a2(const uint8_t* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(a & ~static_cast<uintptr_t>(3));
+  const uint32_t sh = static_cast<uint32_t>(a & 3u);
+  const uint32_t w0 = base[0], w1 = base[1], w2 = base[2], w3 = base[3];
+  const uint32_t w4 = sh ? base[4] : 0u;
+  return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
+                    __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh));
+}
+
+__device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+
+// IEEE binary16 bits <-> float (exact widening; round-to-nearest-even narrowing).
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+__device__ __forceinline__ uint32_t f2h_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// Four int8 x int8 products summed into c ([8e] §2: the 4-way integer dot).
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
+}
+
+// Q4_K packed 6-bit scale and min of sub-block j (0..7).  s0, s1, s2 are the
+// 12 packed bytes as little-endian dwords (bytes 0-3, 4-7, 8-11).  Packing as
+// read for the Q4_K format (GGUF K-quant layout):
+//   j < 4:  sc = S[j] & 63,                 m = S[j+4] & 63
+//   j >= 4: sc = S[j+4] & 15 | (S[j-4]>>6)<<4, m = S[j+4]>>4 | (S[j]>>6)<<4
+__device__ __forceinline__ void q4k_scale_min(int j, uint32_t s0, uint32_t s1, uint32_t s2,
+                                              int& sc, int& m) {
+  const int k = (j & 3) * 8;
+  const int sc_lo = (s0 >> k) & 63, m_lo = (s1 >> k) & 63;
+  const int sc_hi = ((s2 >> k) & 15) | (((s0 >> (k + 6)) & 3) << 4);
+  const int m_hi = ((s2 >> (k + 4)) & 15) | (((s1 >> (k + 6)) & 3) << 4);
+  sc = j < 4 ? sc_lo : sc_hi;
+  m = j < 4 ? m_lo : m_hi;
+}
+
+// Wave64 reductions.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Quantize one 32-activation block to Q8_1 with eight consecutive lanes.
+// Lane `part` (0..7) holds x[4*part .. 4*part+3]; all eight lanes must be
+// active (they exchange values).  dst is the block's 40 bytes (4-byte
+// aligned); nothing is stored when `store` is false.  Steps of [8e] §3.2
+// (max |x|, d = am/127, reciprocal, round to nearest even, clamp, pack,
+// sum), in IEEE fp32 with no contraction so the bytes are reproducible.
+__device__ __forceinline__ void q8_1_block_8lanes(float4 v, int part, uint8_t* dst, bool store) {
+#pragma clang fp contract(off)
+  float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  am = fmaxf(am, __shfl_xor(am, 4));
+  const float d = am / 127.0f;
+  const float di = d != 0.0f ? 1.0f / d : 0.0f;
+  const int q0 = max(-128, min(127, static_cast<int>(rintf(v.x * di))));
+  const int q1 = max(-128, min(127, static_cast<int>(rintf(v.y * di))));
+  const int q2 = max(-128, min(127, static_cast<int>(rintf(v.z * di))));
+  const int q3 = max(-128, min(127, static_cast<int>(rintf(v.w * di))));
+  const uint32_t packed = (static_cast<uint32_t>(q0) & 255u) | ((static_cast<uint32_t>(q1) & 255u) << 8) |
+                          ((static_cast<uint32_t>(q2) & 255u) << 16) | (static_cast<uint32_t>(q3) << 24);
+  int s = q0 + q1 + q2 + q3;
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  if (!store) return;
+  reinterpret_cast<uint32_t*>(dst + 4)[part] = packed;
+  if (part == 0) {
+    reinterpret_cast<uint32_t*>(dst)[0] = f2h_bits(d);  // f16 d, zero pad
+    reinterpret_cast<int32_t*>(dst + 36)[0] = s;
+  }
+}
+
+}  // namespace qmm

@@ -1,0 +1,123 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/qmm.h declares, and rejects bad arguments on the host with the
+documented status codes before anything is enqueued.
+
+Every call below fails host validation, so no kernel is launched and the
+fake (aligned, non-null) device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+qmm = pytest.importorskip("quantized_matmul_q8_amd")
+from quantized_matmul_q8_amd import _lib  # noqa: E402
+
+L = _lib.LIB
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced
+MISAL = ctypes.c_void_p(0x10004)     # 4-byte aligned only
+NUL = ctypes.c_void_p(0)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared()
+    for n in ("q8_1_quantize", "mmvq_q4k", "mmvq_q6k", "mmq_q4k", "mmq_q6k", "moe_grouped_mmq"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = _declared()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_library_is_in_tree():
+    assert os.path.dirname(os.path.abspath(_lib.LIB_PATH)) == os.path.join(ROOT, "quantized_matmul_q8_amd")
+
+
+def test_status_strings():
+    assert L.qmm_status_str(0) == b"ok"
+    for st in range(-6, 0):
+        assert L.qmm_status_str(st) not in (b"ok", b"unknown status")
+    assert L.qmm_status_str(-99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    assert L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 4096, 4096, 512, 0, 0) >= 36
+    moe = L.qmm_workspace_bytes(_lib.QMM_OP_MOE, 2048, 768, 512, 128, 8)
+    # per-slot fp32 scratch dominates: T*top_k*M*4
+    assert moe >= 512 * 8 * 2048 * 4
+    assert L.qmm_workspace_bytes(99, 1, 1, 1, 1, 1) == 0
+
+
+def test_quantize_errors():
+    assert L.q8_1_quantize(FAKE, FAKE, 1, 33, NUL) == _lib.QMM_ERR_SHAPE
+    assert L.q8_1_quantize(FAKE, FAKE, -1, 32, NUL) == _lib.QMM_ERR_SHAPE
+    assert L.q8_1_quantize(NUL, FAKE, 1, 32, NUL) == _lib.QMM_ERR_NULL
+    assert L.q8_1_quantize(MISAL, FAKE, 1, 32, NUL) == _lib.QMM_ERR_ALIGN
+    assert L.q8_1_quantize(NUL, NUL, 0, 32, NUL) == _lib.QMM_OK      # T = 0 is a no-op
+
+
+@pytest.mark.parametrize("fn", ["mmvq_q4k", "mmvq_q6k"])
+def test_mmvq_errors(fn):
+    f = getattr(L, fn)
+    assert f(FAKE, FAKE, FAKE, 4, 300, 1, NUL) == _lib.QMM_ERR_SHAPE     # K % 256
+    assert f(FAKE, FAKE, FAKE, 4, 256, 9, NUL) == _lib.QMM_ERR_SHAPE     # T > 8
+    assert f(FAKE, FAKE, FAKE, 0, 256, 1, NUL) == _lib.QMM_ERR_SHAPE     # M < 1
+    assert f(FAKE, NUL, FAKE, 4, 256, 1, NUL) == _lib.QMM_ERR_NULL
+    assert f(FAKE, FAKE, MISAL, 4, 256, 1, NUL) == _lib.QMM_ERR_ALIGN
+
+
+@pytest.mark.parametrize("fn", ["mmq_q4k", "mmq_q6k"])
+def test_mmq_errors(fn):
+    f = getattr(L, fn)
+    assert f(FAKE, FAKE, FAKE, 4, 256, 0, FAKE, 256, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 255, 1, FAKE, 256, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 256, 1, NUL, 256, NUL) == _lib.QMM_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 4, 256, 1, MISAL, 256, NUL) == _lib.QMM_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, 4, 256, 1, FAKE, 8, NUL) == _lib.QMM_ERR_WORKSPACE
+
+
+def test_moe_errors():
+    f = L.moe_grouped_mmq
+    ok = dict(fmt=_lib.QMM_Q4_K, w=FAKE, E=8, M=64, K=256, stride=64 * 144, xq=FAKE, rpt=1,
+              ids=FAKE, p=NUL, T=4, top_k=2, y=FAKE, ws=FAKE, wsb=16, st=NUL)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["fmt"], a["w"], a["E"], a["M"], a["K"], a["stride"], a["xq"], a["rpt"], a["ids"],
+                 a["p"], a["T"], a["top_k"], a["y"], a["ws"], a["wsb"], a["st"])
+
+    assert call(fmt=7) == _lib.QMM_ERR_UNSUPPORTED
+    assert call(top_k=9) == _lib.QMM_ERR_SHAPE           # top_k > E
+    assert call(rpt=3) == _lib.QMM_ERR_SHAPE             # rows per token not 1 or top_k
+    assert call(stride=64 * 144 - 16) == _lib.QMM_ERR_SHAPE
+    assert call(E=0) == _lib.QMM_ERR_SHAPE
+    assert call(E=513, top_k=2) == _lib.QMM_ERR_SHAPE
+    assert call(ids=NUL) == _lib.QMM_ERR_NULL
+    assert call(p=MISAL) == _lib.QMM_ERR_ALIGN
+    assert call() == _lib.QMM_ERR_WORKSPACE              # 16 bytes is too small
+
+
+def test_debug_and_probe_errors():
+    f = L.qmm_debug_subdots
+    assert f(3, 0, FAKE, FAKE, FAKE, FAKE, 4, 256, 1, FAKE, 256, NUL) == _lib.QMM_ERR_UNSUPPORTED
+    assert f(_lib.QMM_Q4_K, 2, FAKE, FAKE, FAKE, FAKE, 4, 256, 1, FAKE, 256, NUL) == _lib.QMM_ERR_UNSUPPORTED
+    assert f(_lib.QMM_Q4_K, 0, FAKE, FAKE, FAKE, FAKE, 4, 256, 9, FAKE, 256, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(_lib.QMM_Q4_K, 0, FAKE, FAKE, FAKE, NUL, 4, 256, 1, FAKE, 256, NUL) == _lib.QMM_ERR_NULL
+    assert f(_lib.QMM_Q4_K, 1, FAKE, FAKE, FAKE, FAKE, 4, 256, 1, FAKE, 8, NUL) == _lib.QMM_ERR_WORKSPACE
+    assert L.qmm_probe_read(FAKE, 20, FAKE, NUL) == _lib.QMM_ERR_SHAPE
+    assert L.qmm_probe_read(NUL, 16, FAKE, NUL) == _lib.QMM_ERR_NULL
+    assert L.swiglu_q8_1(FAKE, FAKE, 1, 48, NUL) == _lib.QMM_ERR_SHAPE
+    assert L.qmm_workspace_init(MISAL, 16, NUL) == _lib.QMM_ERR_ALIGN

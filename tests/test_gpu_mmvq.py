@@ -1,0 +1,85 @@
+"""GPU parity for the decode matvec (MMVQ) kernels against the fp64 oracle.
+
+fp32 outputs must satisfy |y - y_ref| <= 1e-4 * sum_k |w_ik| |x_tk| element
+by element; the integer sub-block sums of the kernels' own integer stage must
+match the oracle's exactly.  The full 4096 x 11008 decode shape is checked at
+T = 1 and T = 4, in the launch configuration the bench uses.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import qmm_synth
+from _gpu import assert_parity, dev, host, say
+
+import quantized_matmul_q8_amd as qmm
+
+pytestmark = pytest.mark.gpu
+
+FMTS = {
+    "q4k": (qmm_synth.q4k_weights, oracle.q4k_dequant, qmm.mmvq_q4k, qmm.QMM_Q4_K),
+    "q6k": (qmm_synth.q6k_weights, oracle.q6k_dequant, qmm.mmvq_q6k, qmm.QMM_Q6_K),
+}
+CASES = [(1, 256, 1), (7, 512, 3), (37, 1280, 8), (64, 2304, 4), (5, 256, 2), (1024, 1024, 1),
+         (4096, 11008, 1), (4096, 11008, 4)]
+
+
+def _inputs(fmt, M, K, T, seed):
+    gen = FMTS[fmt][0]
+    g = qmm_synth.rng(seed)
+    w = gen(g, M, K)
+    x = qmm_synth.activations(g, T, K)
+    return w, x, oracle.quantize_q8_1(x)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M,K,T", CASES)
+def test_parity(fmt, M, K, T):
+    w, x, xq = _inputs(fmt, M, K, T, seed=M + K + T)
+    say(f"mmvq_{fmt}", f"M={M} K={K} T={T}")
+    y = host(FMTS[fmt][2](dev(w), dev(xq)))
+    W, X = FMTS[fmt][1](w), oracle.q8_1_dequant(xq)
+    assert_parity(y, oracle.dense(W, X), oracle.abs_bound(W, X), f"mmvq_{fmt} {M}x{K} T={T}")
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_end_to_end_from_fp32(fmt):
+    # GPU quantizer feeding the GPU matvec, as in the decode step
+    w, x, xq = _inputs(fmt, 300, 2048, 2, seed=5)
+    say(f"q8_1_quantize + mmvq_{fmt}", "M=300 K=2048 T=2")
+    y = host(FMTS[fmt][2](dev(w), qmm.q8_1_quantize(dev(x))))
+    W, X = FMTS[fmt][1](w), oracle.q8_1_dequant(xq)
+    assert_parity(y, oracle.dense(W, X), oracle.abs_bound(W, X), fmt)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M,K,T", [(3, 256, 1), (9, 768, 4), (33, 1024, 8)])
+def test_integer_stage_bit_exact(fmt, M, K, T):
+    w, x, xq = _inputs(fmt, M, K, T, seed=7 * M + T)
+    say(f"debug_subdots path=0 {fmt}", f"M={M} K={K} T={T}")
+    D, S = qmm.debug_subdots(FMTS[fmt][3], 0, dev(w), dev(xq))
+    if fmt == "q4k":
+        Dr, Sr = oracle.q4k_subdots(w, xq)
+        assert np.array_equal(host(S), Sr)
+    else:
+        Dr = oracle.q6k_subdots(w, xq)
+    assert np.array_equal(host(D), Dr)
+
+
+def test_zero_scales_give_exact_zero():
+    g = qmm_synth.rng(3)
+    w = qmm_synth.q4k_weights(g, 16, 512)
+    w[:, :, 4:16] = 0            # all sc = m = 0
+    xq = oracle.quantize_q8_1(qmm_synth.activations(g, 2, 512))
+    say("mmvq_q4k zero scales")
+    y = host(qmm.mmvq_q4k(dev(w), dev(xq)))
+    assert not y.any()
+
+
+def test_deterministic():
+    w, x, xq = _inputs("q4k", 4096, 11008, 4, seed=11)
+    wd, xd = dev(w), dev(xq)
+    say("mmvq_q4k determinism 4096x11008 T=4")
+    a = host(qmm.mmvq_q4k(wd, xd))
+    b = host(qmm.mmvq_q4k(wd, xd))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
