@@ -134,7 +134,7 @@ int mmq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64
  * expert's weights are read once per 32 tokens routed to it.  Requires
  * 1 <= E <= 512, M >= 1, K % 256 == 0, 1 <= top_k <= min(E, 64), T >= 1,
  * x_rows_per_token in {1, top_k}, expert_stride_bytes >= M*K/256*block bytes
- * and a multiple of 16.
+ * and a multiple of 16 (Q4_K) or 2 (Q6_K).
  */
 int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
                     int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,

@@ -76,7 +76,8 @@ def combine(y_slot: np.ndarray, probs: np.ndarray) -> np.ndarray:
 def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     """``silu(gate) * up = gate / (1 + exp(-gate)) * up`` in float64 (glue reading)."""
     g = np.asarray(gate, np.float64)
-    return g / (1.0 + np.exp(-g)) * np.asarray(up, np.float64)
+    with np.errstate(over="ignore"):      # exp(-g) -> inf gives the exact limit -0
+        return g / (1.0 + np.exp(-g)) * np.asarray(up, np.float64)
 
 
 def grouped_blocks(dequant, blocks: np.ndarray, X: np.ndarray, ids: np.ndarray,

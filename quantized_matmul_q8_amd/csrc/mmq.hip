@@ -257,9 +257,11 @@ __device__ __forceinline__ void mmq_tile(const MmqParams& P, uint8_t* smem, cons
               }
             } else {
               const float2 bp = xb[s * BN + jcol];
+              // reinterpret the whole vector: X holds 1.5*2^23 + D as fp32 bits
+              const v16f Xf = __builtin_bit_cast(v16f, X);
 #pragma unroll
               for (int v = 0; v < 16; ++v) {
-                const float t = __builtin_fmaf(bp.x, __builtin_bit_cast(float, X[v]), bp.y);
+                const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
                 acc[ct][v] = __builtin_fmaf(al[v], t, acc[ct][v]);
               }
             }
@@ -344,9 +346,11 @@ __device__ __forceinline__ void mmq_tile(const MmqParams& P, uint8_t* smem, cons
               }
             } else {
               const float2 bp = xb[s * BN + jcol];
+              // reinterpret the whole vector: X holds 1.5*2^23 + D as fp32 bits
+              const v16f Xf = __builtin_bit_cast(v16f, X);
 #pragma unroll
               for (int v = 0; v < 16; ++v) {
-                const float t = __builtin_fmaf(bp.x, __builtin_bit_cast(float, X[v]), bp.y);
+                const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
                 acc[ct][v] = __builtin_fmaf(al[v], t, acc[ct][v]);
               }
             }

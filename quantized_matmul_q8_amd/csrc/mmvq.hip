@@ -10,90 +10,191 @@
 // Q6_K uses the signed values q6 - 32, so no min term is needed; its dot is
 // sum(q6*q) - 32*sum(q), again with the ones dot.
 //
-// Geometry (re-derived for MI355X; [8e] §2 "the MMVQ geometry" is the
-// 256-thread-per-row prior art for a 48-SM LPDDR part): one wave64 per weight
-// row, four rows per 256-thread workgroup.  The row's (super-block, part)
-// units are dealt round-robin to the 64 lanes; a Q4_K unit is 16 bytes of
-// packed values (32 weights: 16 of sub-block 2p, 16 of 2p+1), so consecutive
-// lanes read consecutive 16-byte chunks of a block and every dwordx4 load of
-// the wave covers ~1 KB of the row.  At M = 4096 the grid holds 4096 waves
-// (16 per CU), enough loads in flight to cover HBM latency.  The row sum is a
-// wave reduction; lane 0 writes y[t*M + row].  Loads of weights are
-// non-temporal: each byte is used once and must not evict the activations.
+// Geometry for MI355X.  [8e] §2 describes the MMVQ geometry of a 48-SM
+// LPDDR part (256 threads per row, one row per block) and its lesson: the
+// kernel is latency-bound until enough loads are in flight.  Here:
+// * one wave64 per weight row, eight rows per 512-thread workgroup; the
+//   row's units of 64 weights (Q4_K: the 32 value bytes of sub-blocks 2p and
+//   2p+1 plus the block header; Q6_K: one half-block quarter) are dealt
+//   round-robin to the 64 lanes, so a wave's loads cover consecutive row
+//   bytes;
+// * every lane issues ALL its weight loads of a chunk (up to kUnits units)
+//   before using any of them, so a wave has its whole row in flight at once;
+//   weight loads are non-temporal (each byte is used once);
+// * the activations of all T tokens are staged once per workgroup into LDS
+//   as int8 payload plus, per 32-block, the fp32 scale and the activation
+//   sums of the block and of its two 16-halves (the ones dots, computed once
+//   per workgroup instead of once per row), so the eight rows share one read
+//   of them and per-unit activation reads are LDS reads.  Staging loads are
+//   issued before the weight loads, so waiting for them does not wait for the
+//   weights (loads complete in issue order).  The weight and activation
+//   pointers are deliberately not __restrict__: loads through restrict
+//   pointers count as invariant and the compiler then moves them past the
+//   barrier to their first use, serialising one HBM round trip per unit.
+// When T*K is too large for the LDS budget the row is processed in K chunks.
+// The row sum is a wave reduction; lane 0 writes y[t*M + row].
 #include "qmm_common.hpp"
 
 namespace qmm {
 
-constexpr int kMmvqRowsPerBlock = 4;
+constexpr int kMmvqWaves = 8;             // rows per workgroup
+constexpr int kMmvqThreads = 64 * kMmvqWaves;
+constexpr int kMmvqLdsBudget = 64 * 1024; // bytes of staged activations per workgroup
+constexpr int kQ6Units = 3;               // max Q6_K units (64 weights) per lane per chunk
+
+// Super-blocks per K chunk so that T tokens of staged activations fit the
+// LDS budget (1.5 bytes per activation) and the lane unit limit.
+static int mmvq_chunk_blocks(int nb, int T, int units_per_block, int max_units) {
+  int by_lds = kMmvqLdsBudget / (T * kQK * 3 / 2);
+  int by_units = 64 * max_units / units_per_block;
+  int c = by_lds < by_units ? by_lds : by_units;
+  if (c < 1) c = 1;
+  return c < nb ? c : nb;
+}
+
+// Stage Q8_1 blocks [blk0, blk0 + nblk) of T tokens into LDS:
+// xs_q[t][32*j .. 32*j+31] int8 payload and xs_s[t][j] = (d, S, S_lo, S_hi):
+// fp32 scale, sum of the 32 values and of each 16-half.  The load is
+// unconditional (out-of-range threads re-read block 0) so that no branch
+// separates the staging loads from the weight loads that follow them.
+__device__ __forceinline__ void stage_acts_load(const uint8_t* xq, size_t xstride, int T, int blk0,
+                                                int nblk, int r, uint2 (&u)[5], int& t, int& j) {
+  const int bi = threadIdx.x + kMmvqThreads * r;
+  const int bc = bi < T * nblk ? bi : 0;
+  t = bc / nblk;
+  j = bc % nblk;
+  const uint2* src = reinterpret_cast<const uint2*>(xq + t * xstride + static_cast<size_t>(blk0 + j) * kQ8Bytes);
+#pragma unroll
+  for (int k = 0; k < 5; ++k) u[k] = src[k];
+}
+
+// Unconditional as well: threads past the end re-write block 0 of token 0
+// with the same bytes the owning thread writes.
+__device__ __forceinline__ void stage_acts_store(uint8_t* xs_q, float4* xs_s, int nblk, const uint2 (&u)[5],
+                                                 int t, int j) {
+  uint4* dq = reinterpret_cast<uint4*>(xs_q + (static_cast<size_t>(t) * nblk + j) * 32);
+  dq[0] = make_uint4(u[0].y, u[1].x, u[1].y, u[2].x);
+  dq[1] = make_uint4(u[2].y, u[3].x, u[3].y, u[4].x);
+  // activation sums as integer dots against ones ([8e] §2)
+  int lo = dot4(0x01010101u, u[0].y, 0);
+  lo = dot4(0x01010101u, u[1].x, lo);
+  lo = dot4(0x01010101u, u[1].y, lo);
+  lo = dot4(0x01010101u, u[2].x, lo);
+  int hi = dot4(0x01010101u, u[2].y, 0);
+  hi = dot4(0x01010101u, u[3].x, hi);
+  hi = dot4(0x01010101u, u[3].y, hi);
+  hi = dot4(0x01010101u, u[4].x, hi);
+  xs_s[t * nblk + j] = make_float4(h2f(u[0].x & 0xffffu), static_cast<float>(lo + hi),
+                                   static_cast<float>(lo), static_cast<float>(hi));
+}
+
+// Q4_K rows are read as plain consecutive 16-byte chunks: lane l loads
+// chunks l, l + 64, l + 128, ... of its row, so each wave load instruction
+// covers 1 KB of contiguous bytes (the access pattern of the read-ceiling
+// probe; loads of 16 bytes at a 32-byte stride or per-lane header loads cost
+// 25-40% more time for the same bytes).  A 144-byte block is exactly nine
+// chunks: chunk 0 is the header (d, dmin, packed scales), chunk 1 + 2p + h
+// holds value bytes 16 + 32p + 16h .. +15, i.e. 16 weights of sub-block 2p
+// (low nibbles) and 16 of sub-block 2p + 1 (high nibbles).  Rounds are
+// consumed in load order; in each round the header chunks are written to a
+// per-wave LDS slot and the value chunks read their block's header from it
+// (headers precede their values, and one wave's LDS accesses are ordered).
+constexpr int kQ4Rounds = 7;  // chunks per lane per segment (7 x 64 = 448 >= 43 blocks x 9)
 
 // DEBUG == true: write the integer sub-block sums (D per (t, row, sub-block),
-// S per (t, sub-block) from row 0) with integer atomics into zeroed buffers,
-// instead of the scaled result.  Same loads, unpacking and dot products.
+// S per (t, sub-block) from row 0) instead of the scaled result.  Same
+// loads, unpacking and dot products; the two 16-weight halves of D are
+// added with integer atomics into zeroed buffers.
 template <int T, bool DEBUG>
-__global__ __launch_bounds__(256) void mmvq_q4k_kernel(const uint8_t* __restrict__ w,
-                                                       const uint8_t* __restrict__ xq,
-                                                       float* __restrict__ y, int M, int nb,
-                                                       int32_t* __restrict__ dbgD,
-                                                       int32_t* __restrict__ dbgS) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kMmvqRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= M) return;  // uniform per wave
+__global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w, const uint8_t* xq,
+                                                                float* __restrict__ y, int M, int nb,
+                                                                int cb, int32_t* __restrict__ dbgD,
+                                                                int32_t* __restrict__ dbgS) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row_raw = blockIdx.x * kMmvqWaves + wave;
+  const bool row_ok = row_raw < M;
+  const int row = row_ok ? row_raw : M - 1;  // out-of-range waves load a valid row, store nothing
   const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ4Bytes;
-  const int nunits = nb * 8;
   const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
+  uint8_t* xs_q = lds;
+  float4* xs_s = reinterpret_cast<float4*>(lds + static_cast<size_t>(T) * cb * 8 * 32);
+  uint4* hdr_s = reinterpret_cast<uint4*>(lds + static_cast<size_t>(T) * cb * 8 * 48) + wave * cb;
+  constexpr int RS = (T * 64 * 8 + kMmvqThreads - 1) / kMmvqThreads;  // staging rounds bound
   float acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = 0.0f;
 
-  for (int u = lane; u < nunits; u += 64) {
-    const int b = u >> 3, c = u & 7, p = c >> 1, h = c & 1;
-    const uint8_t* blk = wrow + b * kQ4Bytes;
-    const uint4 hdr = ld16_nt(blk);
-    const uint4 qv = ld16_nt(blk + 16 + 32 * p + 16 * h);
-    int sc0, m0, sc1, m1;
-    q4k_scale_min(2 * p, hdr.y, hdr.z, hdr.w, sc0, m0);
-    q4k_scale_min(2 * p + 1, hdr.y, hdr.z, hdr.w, sc1, m1);
-    const float d = h2f(hdr.x & 0xffffu), dmin = h2f(hdr.x >> 16);
-    const float ds0 = d * static_cast<float>(sc0), dm0 = dmin * static_cast<float>(m0);
-    const float ds1 = d * static_cast<float>(sc1), dm1 = dmin * static_cast<float>(m1);
-    const uint32_t lo0 = qv.x & 0x0f0f0f0fu, lo1 = qv.y & 0x0f0f0f0fu;
-    const uint32_t lo2 = qv.z & 0x0f0f0f0fu, lo3 = qv.w & 0x0f0f0f0fu;
-    const uint32_t hi0 = (qv.x >> 4) & 0x0f0f0f0fu, hi1 = (qv.y >> 4) & 0x0f0f0f0fu;
-    const uint32_t hi2 = (qv.z >> 4) & 0x0f0f0f0fu, hi3 = (qv.w >> 4) & 0x0f0f0f0fu;
-    const int sb0 = b * 8 + 2 * p;  // Q8_1 block of sub-block 2p (2p+1 follows)
+  for (int b0 = 0; b0 < nb; b0 += cb) {
+    const int nbc = min(cb, nb - b0);
+    const int nblk = nbc * 8;   // Q8_1 blocks in this segment
+    const int nch = nbc * 9;    // 16-byte chunks of the row in this segment
+    // 1. activation staging loads (issued first)
+    uint2 su[RS][5];
+    int st[RS], sj[RS];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const uint8_t* xb = xq + t * xstride + static_cast<size_t>(sb0) * kQ8Bytes;
-      const uint4 x0 = ld16_a4(xb + 4 + 16 * h);
-      const uint4 x1 = ld16_a4(xb + kQ8Bytes + 4 + 16 * h);
-      const float dx0 = h2f(ld_u16(xb)), dx1 = h2f(ld_u16(xb + kQ8Bytes));
-      int D0 = dot4(lo0, x0.x, 0);
-      D0 = dot4(lo1, x0.y, D0);
-      D0 = dot4(lo2, x0.z, D0);
-      D0 = dot4(lo3, x0.w, D0);
-      int S0 = dot4(0x01010101u, x0.x, 0);
-      S0 = dot4(0x01010101u, x0.y, S0);
-      S0 = dot4(0x01010101u, x0.z, S0);
-      S0 = dot4(0x01010101u, x0.w, S0);
-      int D1 = dot4(hi0, x1.x, 0);
-      D1 = dot4(hi1, x1.y, D1);
-      D1 = dot4(hi2, x1.z, D1);
-      D1 = dot4(hi3, x1.w, D1);
-      int S1 = dot4(0x01010101u, x1.x, 0);
-      S1 = dot4(0x01010101u, x1.y, S1);
-      S1 = dot4(0x01010101u, x1.z, S1);
-      S1 = dot4(0x01010101u, x1.w, S1);
-      if constexpr (DEBUG) {
-        int32_t* Dt = dbgD + (static_cast<size_t>(t) * M + row) * (nb * 8);
-        atomicAdd(Dt + sb0, D0);
-        atomicAdd(Dt + sb0 + 1, D1);
-        if (row == 0) {
-          atomicAdd(dbgS + static_cast<size_t>(t) * nb * 8 + sb0, S0);
-          atomicAdd(dbgS + static_cast<size_t>(t) * nb * 8 + sb0 + 1, S1);
+    for (int r = 0; r < RS; ++r) stage_acts_load(xq, xstride, T, b0 * 8, nblk, r, su[r], st[r], sj[r]);
+    // 2. every chunk of this lane (unconditional loads; extra lanes re-read the last chunk)
+    const uint8_t* seg = wrow + static_cast<size_t>(b0) * kQ4Bytes;
+    uint4 v[kQ4Rounds];
+#pragma unroll
+    for (int r = 0; r < kQ4Rounds; ++r) v[r] = ld16_nt(seg + 16 * min(lane + 64 * r, nch - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. publish the activations
+    __syncthreads();  // previous segment's LDS reads are done
+#pragma unroll
+    for (int r = 0; r < RS; ++r) stage_acts_store(xs_q, xs_s, nblk, su[r], st[r], sj[r]);
+    __syncthreads();
+    // 4. consume the rounds in load order
+#pragma unroll
+    for (int r = 0; r < kQ4Rounds; ++r) {
+      const int c = lane + 64 * r;
+      if (64 * r >= nch) break;                 // uniform: round entirely past the segment
+      const int bl = c / 9, k = c - 9 * bl;     // block within segment, chunk within block
+      if (c < nch && k == 0) hdr_s[bl] = v[r];  // header chunk
+      if (c < nch && k != 0) {
+        const uint4 hdr = hdr_s[bl];
+        const int p = (k - 1) >> 1, h = (k - 1) & 1;
+        int sc0, m0, sc1, m1;
+        q4k_scale_min(2 * p, hdr.y, hdr.z, hdr.w, sc0, m0);
+        q4k_scale_min(2 * p + 1, hdr.y, hdr.z, hdr.w, sc1, m1);
+        const float d = h2f(hdr.x & 0xffffu), dmin = h2f(hdr.x >> 16);
+        const float ds0 = d * static_cast<float>(sc0), dm0 = dmin * static_cast<float>(m0);
+        const float ds1 = d * static_cast<float>(sc1), dm1 = dmin * static_cast<float>(m1);
+        const uint32_t qw[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+        const int j0 = bl * 8 + 2 * p;  // segment-local Q8_1 block of sub-block 2p (2p+1 follows)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint8_t* xb = xs_q + (static_cast<size_t>(t) * nblk + j0) * 32 + 16 * h;
+          const uint4 xa = *reinterpret_cast<const uint4*>(xb);       // 16 activations of 2p
+          const uint4 xc = *reinterpret_cast<const uint4*>(xb + 32);  // 16 activations of 2p+1
+          const uint32_t x0[4] = {xa.x, xa.y, xa.z, xa.w};
+          const uint32_t x1[4] = {xc.x, xc.y, xc.z, xc.w};
+          const float4 s0 = xs_s[t * nblk + j0], s1 = xs_s[t * nblk + j0 + 1];  // (d, S, S_lo, S_hi)
+          int D0 = 0, D1 = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            D0 = dot4(qw[i] & 0x0f0f0f0fu, x0[i], D0);         // sub-block 2p: low nibbles
+            D1 = dot4((qw[i] >> 4) & 0x0f0f0f0fu, x1[i], D1);  // sub-block 2p+1: high nibbles
+          }
+          // activation sum of the 16 weights' half, from the staged ones dots
+          const float S0 = h ? s0.w : s0.z, S1 = h ? s1.w : s1.z;
+          if constexpr (DEBUG) {
+            if (row_ok) {
+              const int sb0 = b0 * 8 + j0;
+              int32_t* Dt = dbgD + (static_cast<size_t>(t) * M + row) * (nb * 8);
+              atomicAdd(Dt + sb0, D0);
+              atomicAdd(Dt + sb0 + 1, D1);
+              if (row == 0 && h == 0) {
+                dbgS[static_cast<size_t>(t) * nb * 8 + sb0] = static_cast<int>(s0.y);
+                dbgS[static_cast<size_t>(t) * nb * 8 + sb0 + 1] = static_cast<int>(s1.y);
+              }
+            }
+          } else {
+            acc[t] += s0.x * (ds0 * static_cast<float>(D0) - dm0 * S0) +
+                      s1.x * (ds1 * static_cast<float>(D1) - dm1 * S1);
+          }
         }
-      } else {
-        acc[t] += dx0 * (ds0 * static_cast<float>(D0) - dm0 * static_cast<float>(S0)) +
-                  dx1 * (ds1 * static_cast<float>(D1) - dm1 * static_cast<float>(S1));
       }
     }
   }
@@ -101,76 +202,117 @@ __global__ __launch_bounds__(256) void mmvq_q4k_kernel(const uint8_t* __restrict
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float s = wave_sum(acc[t]);
-      if (lane == 0) y[static_cast<size_t>(t) * M + row] = s;
+      if (lane == 0 && row_ok) y[static_cast<size_t>(t) * M + row] = s;
     }
   }
+}
+
+// 8 bytes from a 2-byte aligned address inside a block (third dword read only
+// when misaligned, so nothing past p + 8 is touched otherwise).
+__device__ __forceinline__ uint2 ld8_a2(const uint8_t* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(a & ~static_cast<uintptr_t>(3));
+  const uint32_t sh = static_cast<uint32_t>(a & 3u);
+  const uint32_t w0 = base[0], w1 = base[1];
+  const uint32_t w2 = sh ? base[2] : 0u;
+  return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));
 }
 
 // Q6_K unit: one half h of the super-block and 16 lanes l0..l0+15 of it, i.e.
 // 64 weights in four 16-weight sub-blocks (g = 0..3 at positions
 // 128h + 32g + l).  Bytes used: ql[64h + l0 ..+16], ql[64h + 32 + l0 ..+16],
-// qh[32h + l0 ..+16], four scales and d.  Blocks are 2-byte aligned.
+// qh[32h + l0 ..+16], sc[8h .. 8h+7] (four of them), d.  Blocks are 2-byte
+// aligned.
 template <int T, bool DEBUG>
-__global__ __launch_bounds__(256) void mmvq_q6k_kernel(const uint8_t* __restrict__ w,
-                                                       const uint8_t* __restrict__ xq,
-                                                       float* __restrict__ y, int M, int nb,
-                                                       int32_t* __restrict__ dbgD) {
+__global__ __launch_bounds__(kMmvqThreads) void mmvq_q6k_kernel(const uint8_t* w, const uint8_t* xq,
+                                                                float* __restrict__ y, int M, int nb,
+                                                                int cb, int32_t* __restrict__ dbgD) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kMmvqRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= M) return;
+  const int row_raw = blockIdx.x * kMmvqWaves + (threadIdx.x >> 6);
+  const bool row_ok = row_raw < M;
+  const int row = row_ok ? row_raw : M - 1;
   const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ6Bytes;
-  const int nunits = nb * 4;
   const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
+  uint8_t* xs_q = lds;
+  float4* xs_s = reinterpret_cast<float4*>(lds + static_cast<size_t>(T) * cb * 8 * 32);
+  constexpr int RS = (T * 64 * 8 + kMmvqThreads - 1) / kMmvqThreads;
   float acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = 0.0f;
 
-  for (int u = lane; u < nunits; u += 64) {
-    const int b = u >> 2, c = u & 3, h = c >> 1, half16 = c & 1, l0 = half16 * 16;
-    const uint8_t* blk = wrow + static_cast<size_t>(b) * kQ6Bytes;
-    const uint4 qa = ld16_a2(blk + 64 * h + l0);        // g = 0 (low nibbles), g = 2 (high)
-    const uint4 qb = ld16_a2(blk + 64 * h + 32 + l0);   // g = 1 (low nibbles), g = 3 (high)
-    const uint4 qh = ld16_a2(blk + 128 + 32 * h + l0);  // bit pairs of g = 0..3
-    const float d = h2f(ld_u16(blk + 208));
-    float dsc[4];
+  for (int b0 = 0; b0 < nb; b0 += cb) {
+    const int nbc = min(cb, nb - b0);
+    const int nblk = nbc * 8;
+    const int nunits = nbc * 4;
+    uint2 su[RS][5];
+    int st[RS], sj[RS];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t two = ld_u16(blk + 192 + 8 * h + 2 * g);  // sc[8h+2g], sc[8h+2g+1]
-      const int sc = static_cast<int8_t>((two >> (8 * half16)) & 0xffu);
-      dsc[g] = d * static_cast<float>(sc);
+    for (int r = 0; r < RS; ++r) stage_acts_load(xq, xstride, T, b0 * 8, nblk, r, su[r], st[r], sj[r]);
+    uint4 qa[kQ6Units], qb[kQ6Units], qh[kQ6Units];
+    uint2 scs[kQ6Units];
+    uint32_t dd[kQ6Units];
+#pragma unroll
+    for (int i = 0; i < kQ6Units; ++i) {
+      const int u = min(lane + 64 * i, nunits - 1);  // unconditional: extra units re-read the last one
+      const int b = b0 + (u >> 2), c = u & 3, h = c >> 1, l0 = (c & 1) * 16;
+      const uint8_t* blk = wrow + static_cast<size_t>(b) * kQ6Bytes;
+      qa[i] = ld16_a2(blk + 64 * h + l0);        // g = 0 (low nibbles), g = 2 (high)
+      qb[i] = ld16_a2(blk + 64 * h + 32 + l0);   // g = 1 (low nibbles), g = 3 (high)
+      qh[i] = ld16_a2(blk + 128 + 32 * h + l0);  // bit pairs of g = 0..3
+      scs[i] = ld8_a2(blk + 192 + 8 * h);        // sc[8h .. 8h+7]
+      dd[i] = ld_u16(blk + 208);
     }
-    const uint32_t qa_[4] = {qa.x, qa.y, qa.z, qa.w};
-    const uint32_t qb_[4] = {qb.x, qb.y, qb.z, qb.w};
-    const uint32_t qh_[4] = {qh.x, qh.y, qh.z, qh.w};
-    uint32_t q6[4][4];
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      q6[0][k] = (qa_[k] & 0x0f0f0f0fu) | ((qh_[k] << 4) & 0x30303030u);
-      q6[1][k] = (qb_[k] & 0x0f0f0f0fu) | ((qh_[k] << 2) & 0x30303030u);
-      q6[2][k] = ((qa_[k] >> 4) & 0x0f0f0f0fu) | (qh_[k] & 0x30303030u);
-      q6[3][k] = ((qb_[k] >> 4) & 0x0f0f0f0fu) | ((qh_[k] >> 2) & 0x30303030u);
-    }
+    for (int r = 0; r < RS; ++r) stage_acts_store(xs_q, xs_s, nblk, su[r], st[r], sj[r]);
+    __syncthreads();
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
+    for (int i = 0; i < kQ6Units; ++i) {
+      const int u = lane + 64 * i;
+      if (u >= nunits) break;
+      const int bl = u >> 2, c = u & 3, h = c >> 1, half16 = c & 1, l0 = half16 * 16;
+      const float d = h2f(dd[i]);
+      float dsc[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int sblk = b * 8 + 4 * h + g;  // Q8_1 block holding these weights
-        const uint8_t* xb = xq + t * xstride + static_cast<size_t>(sblk) * kQ8Bytes;
-        const uint4 xv = ld16_a4(xb + 4 + l0);
-        const float dx = h2f(ld_u16(xb));
-        int D = dot4(q6[g][0], xv.x, 0);
-        D = dot4(q6[g][1], xv.y, D);
-        D = dot4(q6[g][2], xv.z, D);
-        D = dot4(q6[g][3], xv.w, D);
-        int S = dot4(0x01010101u, xv.x, 0);
-        S = dot4(0x01010101u, xv.y, S);
-        S = dot4(0x01010101u, xv.z, S);
-        S = dot4(0x01010101u, xv.w, S);
-        const int D6 = D - 32 * S;  // sum (q6 - 32) * q, exact
-        if constexpr (DEBUG) {
-          dbgD[(static_cast<size_t>(t) * M + row) * (nb * 16) + sblk * 2 + half16] = D6;
-        } else {
-          acc[t] += dx * dsc[g] * static_cast<float>(D6);
+        // sc[8h + 2g + half16]: byte (2g + half16) of the 8 loaded bytes
+        const uint32_t word = g < 2 ? scs[i].x : scs[i].y;
+        const int sc = static_cast<int8_t>((word >> (8 * (2 * (g & 1) + half16))) & 0xffu);
+        dsc[g] = d * static_cast<float>(sc);
+      }
+      const uint32_t qa_[4] = {qa[i].x, qa[i].y, qa[i].z, qa[i].w};
+      const uint32_t qb_[4] = {qb[i].x, qb[i].y, qb[i].z, qb[i].w};
+      const uint32_t qh_[4] = {qh[i].x, qh[i].y, qh[i].z, qh[i].w};
+      uint32_t q6[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        q6[0][k] = (qa_[k] & 0x0f0f0f0fu) | ((qh_[k] << 4) & 0x30303030u);
+        q6[1][k] = (qb_[k] & 0x0f0f0f0fu) | ((qh_[k] << 2) & 0x30303030u);
+        q6[2][k] = ((qa_[k] >> 4) & 0x0f0f0f0fu) | (qh_[k] & 0x30303030u);
+        q6[3][k] = ((qb_[k] >> 4) & 0x0f0f0f0fu) | ((qh_[k] >> 2) & 0x30303030u);
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int jl = bl * 8 + 4 * h + g;  // chunk-local Q8_1 block holding these weights
+          const uint4 xv = *reinterpret_cast<const uint4*>(xs_q + (static_cast<size_t>(t) * nblk + jl) * 32 + l0);
+          const float4 sv = xs_s[t * nblk + jl];  // (d, S, S_lo, S_hi)
+          int D = dot4(q6[g][0], xv.x, 0);
+          D = dot4(q6[g][1], xv.y, D);
+          D = dot4(q6[g][2], xv.z, D);
+          D = dot4(q6[g][3], xv.w, D);
+          // sum (q6 - 32) * q = D - 32 * S_half, exact in fp32 (|.| < 2^24)
+          const float D6 = static_cast<float>(D) - 32.0f * (half16 ? sv.w : sv.z);
+          if constexpr (DEBUG) {
+            if (row_ok)
+              dbgD[(static_cast<size_t>(t) * M + row) * (nb * 16) + (b0 * 8 + jl) * 2 + half16] =
+                  static_cast<int>(D6);
+          } else {
+            acc[t] += sv.x * dsc[g] * D6;
+          }
         }
       }
     }
@@ -179,20 +321,25 @@ __global__ __launch_bounds__(256) void mmvq_q6k_kernel(const uint8_t* __restrict
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float s = wave_sum(acc[t]);
-      if (lane == 0) y[static_cast<size_t>(t) * M + row] = s;
+      if (lane == 0 && row_ok) y[static_cast<size_t>(t) * M + row] = s;
     }
   }
 }
 
+static size_t mmvq_lds_bytes(int T, int cb) { return static_cast<size_t>(T) * cb * 8 * 48; }
+
 template <bool DEBUG>
 static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int nb, int T,
                            int32_t* D, int32_t* S, hipStream_t st) {
-  const dim3 grid((M + kMmvqRowsPerBlock - 1) / kMmvqRowsPerBlock), block(256);
+  // segment: whole blocks whose 9 chunks fit kQ4Rounds rounds, within the LDS budget
+  const int cb = mmvq_chunk_blocks(nb, T, 9, kQ4Rounds);
+  const dim3 grid((M + kMmvqWaves - 1) / kMmvqWaves), block(kMmvqThreads);
+  const size_t lds = mmvq_lds_bytes(T, cb) + static_cast<size_t>(kMmvqWaves) * cb * 16;
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const uint8_t* xp = static_cast<const uint8_t*>(xq);
   switch (T) {
 #define QMM_CASE(TT) \
-  case TT: hipLaunchKernelGGL((mmvq_q4k_kernel<TT, DEBUG>), grid, block, 0, st, wp, xp, y, M, nb, D, S); break;
+  case TT: hipLaunchKernelGGL((mmvq_q4k_kernel<TT, DEBUG>), grid, block, lds, st, wp, xp, y, M, nb, cb, D, S); break;
     QMM_CASE(1) QMM_CASE(2) QMM_CASE(3) QMM_CASE(4) QMM_CASE(5) QMM_CASE(6) QMM_CASE(7) QMM_CASE(8)
 #undef QMM_CASE
     default: return QMM_ERR_SHAPE;
@@ -203,12 +350,14 @@ static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int n
 template <bool DEBUG>
 static int launch_mmvq_q6k(const void* w, const void* xq, float* y, int M, int nb, int T,
                            int32_t* D, hipStream_t st) {
-  const dim3 grid((M + kMmvqRowsPerBlock - 1) / kMmvqRowsPerBlock), block(256);
+  const int cb = mmvq_chunk_blocks(nb, T, 4, kQ6Units);
+  const dim3 grid((M + kMmvqWaves - 1) / kMmvqWaves), block(kMmvqThreads);
+  const size_t lds = mmvq_lds_bytes(T, cb);
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const uint8_t* xp = static_cast<const uint8_t*>(xq);
   switch (T) {
 #define QMM_CASE(TT) \
-  case TT: hipLaunchKernelGGL((mmvq_q6k_kernel<TT, DEBUG>), grid, block, 0, st, wp, xp, y, M, nb, D); break;
+  case TT: hipLaunchKernelGGL((mmvq_q6k_kernel<TT, DEBUG>), grid, block, lds, st, wp, xp, y, M, nb, cb, D); break;
     QMM_CASE(1) QMM_CASE(2) QMM_CASE(3) QMM_CASE(4) QMM_CASE(5) QMM_CASE(6) QMM_CASE(7) QMM_CASE(8)
 #undef QMM_CASE
     default: return QMM_ERR_SHAPE;

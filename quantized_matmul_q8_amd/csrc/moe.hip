@@ -177,7 +177,9 @@ extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int
     return QMM_ERR_SHAPE;
   if (x_rows_per_token != 1 && x_rows_per_token != top_k) return QMM_ERR_SHAPE;
   const int64_t row_bytes = (K / kQK) * (fmt == QMM_Q4_K ? kQ4Bytes : kQ6Bytes);
-  if (expert_stride_bytes < M * row_bytes || (expert_stride_bytes % 16) != 0) return QMM_ERR_SHAPE;
+  // Q4_K blocks are read with 16-byte loads, Q6_K blocks with 2-byte aligned ones
+  const int64_t stride_align = fmt == QMM_Q4_K ? 16 : 2;
+  if (expert_stride_bytes < M * row_bytes || (expert_stride_bytes % stride_align) != 0) return QMM_ERR_SHAPE;
   if (!w || !xq || !ids || !y || !ws) return QMM_ERR_NULL;
   if (!aligned16(w) || !aligned16(xq) || !aligned16(ids) || !aligned16(y) || !aligned16(ws) ||
       (expert_weights && !aligned16(expert_weights)))

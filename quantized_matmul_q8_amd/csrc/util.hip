@@ -41,25 +41,26 @@ static int zero_fill(void* p, size_t bytes, hipStream_t st) {
   return launch_status();
 }
 
-// Read-only streaming: each thread folds 16-byte words with xor; the store
-// is taken only for an improbable value so the kernel writes (almost)
-// nothing while the compiler must still perform every load.
+// Read-only streaming: every thread first issues all of its kProbeUnroll
+// 16-byte loads (lane-contiguous, one grid stride apart), then folds them
+// with xor, so each wave has kProbeUnroll loads in flight instead of one.
+// The store is taken only for an improbable value, so the kernel writes
+// (almost) nothing while the compiler must still perform every load.
+constexpr int kProbeUnroll = 8;
+
 __global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ p, int64_t n,
                                                          uint32_t* __restrict__ sink) {
-  uint32_t acc = 0;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const uint4 a = ld16_nt(p + i);
-    const uint4 b = ld16_nt(p + i + stride);
-    const uint4 c = ld16_nt(p + i + 2 * stride);
-    const uint4 d = ld16_nt(p + i + 3 * stride);
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  uint4 v[kProbeUnroll];
+#pragma unroll
+  for (int u = 0; u < kProbeUnroll; ++u) {
+    const int64_t i = i0 + u * stride;
+    v[u] = i < n ? ld16_nt(p + i) : make_uint4(0u, 0u, 0u, 0u);
   }
-  for (; i < n; i += stride) {
-    const uint4 a = ld16_nt(p + i);
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
-  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
@@ -122,8 +123,8 @@ extern "C" int qmm_probe_read(const void* buf, size_t bytes, uint32_t* sink, voi
   if (!aligned16(buf) || !aligned16(sink)) return QMM_ERR_ALIGN;
   if (bytes == 0 || (bytes % 16) != 0) return QMM_ERR_SHAPE;
   const int64_t n = static_cast<int64_t>(bytes / 16);
-  int64_t grid = device_cu_count() * 8;
-  if (grid * 256 > n) grid = (n + 255) / 256;
+  const int64_t grid = (n + 256 * kProbeUnroll - 1) / (256 * kProbeUnroll);
+  if (grid > 0x7fffffff) return QMM_ERR_SHAPE;
   hipLaunchKernelGGL(probe_read_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, to_stream(stream),
                      static_cast<const uint4*>(buf), n, sink);
   return launch_status();

@@ -103,6 +103,8 @@ def test_moe_errors():
     assert call(top_k=9) == _lib.QMM_ERR_SHAPE           # top_k > E
     assert call(rpt=3) == _lib.QMM_ERR_SHAPE             # rows per token not 1 or top_k
     assert call(stride=64 * 144 - 16) == _lib.QMM_ERR_SHAPE
+    assert call(stride=64 * 144 + 8) == _lib.QMM_ERR_SHAPE      # Q4_K stride % 16
+    assert call(fmt=_lib.QMM_Q6_K, stride=64 * 210 + 1) == _lib.QMM_ERR_SHAPE   # Q6_K stride % 2
     assert call(E=0) == _lib.QMM_ERR_SHAPE
     assert call(E=513, top_k=2) == _lib.QMM_ERR_SHAPE
     assert call(ids=NUL) == _lib.QMM_ERR_NULL
