@@ -1,8 +1,8 @@
 """Build libqmm.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
 Runs hipcc once over every source in ``csrc/``.  Flags: ``-O3``, no fast
-math (the Q8_1 quantizer must match IEEE fp32 bit for bit), and packed fp32
-VALU instructions disabled for the device code.
+math (the Q8_1 quantizer must match IEEE fp32 bit for bit), packed fp32 VALU
+instructions disabled for the device code, and MFMA results kept in VGPRs.
 """
 from __future__ import annotations
 
@@ -33,6 +33,9 @@ def build(verbose: bool = False) -> str:
     cmd = [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results in VGPRs: the AGPR form made the epilogue copy every
+        # int8-MFMA result back with accvgpr reads (one VALU op per element)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-function",
         f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp, *srcs,
     ]

@@ -61,16 +61,29 @@ struct MmqParams {
   int32_t* dbgS;
 };
 
+// LDS of one pipeline stage (two stages are used, double-buffered).
+// Activation payload: for each Q8_1 block s of the super-block, the 32 int8
+// values of every column are cut into pieces (Q4_K 2 x 16 bytes: one MFMA
+// k-group each; Q6_K 4 x 8 bytes) and piece k of all columns is one
+// contiguous run, so the MFMA operand reads of 32 consecutive columns are
+// consecutive.  Rows of s are padded so that the commit stores (8 lanes =
+// the 8 blocks of one token) fall on different banks; reads stay a per-lane
+// base plus immediate offsets.
 template <int FMT, int NT>
 struct MmqSmem {
   static constexpr int BN = 32 * NT;
   static constexpr int NS16 = FMT == QMM_Q4_K ? 8 : 16;     // scale groups per super-block
-  static constexpr int kXq = 0;                              // [8][BN][32] int8 payload
-  static constexpr int kXb = kXq + 8 * BN * 32;              // [8][BN] (beta, -beta*C)
-  static constexpr int kXs = kXb + 8 * BN * 8;               // [NS][BN] beta*S (Q4_K: 8 per 32, Q6_K: 16 per 16)
-  static constexpr int kWa = kXs + NS16 * BN * 4;            // [4 waves][NS16][32] alpha
+  static constexpr int kPiece = FMT == QMM_Q4_K ? 16 : 8;    // payload bytes per piece
+  static constexpr int kXqRow = 32 * BN + 8 * kPiece;       // bytes per block row s
+  static constexpr int kXbRow = BN + 8;                      // float2 per block row
+  static constexpr int kXsRow = FMT == QMM_Q4_K ? BN + 8 : BN + 4;  // floats per scale row
+  static constexpr int kXq = 0;                              // [8][32/kPiece][BN][kPiece] int8 payload
+  static constexpr int kXb = kXq + 8 * kXqRow;               // [8][kXbRow] (beta, -beta*C)
+  static constexpr int kXs = kXb + 8 * kXbRow * 8;           // [NS16][kXsRow] beta*S (Q4_K: per 32, Q6_K: per 16)
+  static constexpr int kWa = kXs + NS16 * kXsRow * 4;        // [4 waves][NS16][32] alpha = d*sc
   static constexpr int kWm = kWa + 4 * NS16 * 32 * 4;        // Q4_K: [4][8][32] -dmin*m
-  static constexpr int kBytes = kWm + (FMT == QMM_Q4_K ? 4 * 8 * 32 * 4 : 0);
+  static constexpr int kStage = (kWm + (FMT == QMM_Q4_K ? 4 * 8 * 32 * 4 : 0) + 15) & ~15;
+  static constexpr int kBytes = 2 * kStage;
 };
 
 // Token (activation row, output row) of column j of a tile.  Dense: token
@@ -95,43 +108,130 @@ __device__ __forceinline__ void col_rows(const MmqParams& P, const TileCols& tc,
   }
 }
 
-// Stage the activations of super-block sb for the tile's BN columns:
-// payload bytes, (beta, -beta*C) and beta * (block or half-block) sums.
+// Registers holding one super-block's global data between its loads and
+// its commit to LDS (the software pipeline's in-flight stage).
+template <int FMT, int NT>
+struct MmqPrefetch {
+  static constexpr int RX = 32 * NT * 8 / kMmqThreads;  // Q8_1 blocks staged per thread
+  uint2 xu[RX][5];                                      // raw 40-byte activation blocks
+  // Q4_K: header and the 4 x 16 value bytes of this lane's row and k-group
+  uint4 hdr;
+  uint4 q[4];
+  // Q6_K: per (half h, 16-group hf): qh bytes; per (h, parity, hf): ql bytes
+  // (8 bytes each as raw aligned dwords + shift), scales of this k-group, d
+  uint32_t qh_raw[2][2][3], ql_raw[2][2][2][3], sc_raw[3], d_raw, sh;
+};
+
+// 8 bytes at p (2-byte aligned) from three raw aligned dwords and the shift.
+__device__ __forceinline__ void raw8_load(const uint8_t* p, uint32_t (&r)[3], uint32_t& sh) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(a & ~static_cast<uintptr_t>(3));
+  sh = static_cast<uint32_t>(a & 3u);
+  r[0] = base[0];
+  r[1] = base[1];
+  r[2] = sh ? base[2] : 0u;  // only when misaligned: never reads past p + 8 otherwise
+}
+__device__ __forceinline__ uint2 raw8_join(const uint32_t (&r)[3], uint32_t sh) {
+  return make_uint2(__builtin_amdgcn_alignbyte(r[1], r[0], sh), __builtin_amdgcn_alignbyte(r[2], r[1], sh));
+}
+
+// Issue the global loads of super-block sb (activations of the tile's
+// columns, this lane's weight bytes) into registers.
+template <int FMT, int NT>
+__device__ __forceinline__ void mmq_load(const MmqParams& P, MmqPrefetch<FMT, NT>& F, const int* xrow,
+                                         size_t xstride, const uint8_t* wr, int sb, int g) {
+#pragma unroll
+  for (int r = 0; r < MmqPrefetch<FMT, NT>::RX; ++r) {
+    const int s = (threadIdx.x + kMmqThreads * r) & 7;
+    const uint2* src = reinterpret_cast<const uint2*>(P.xq + static_cast<size_t>(xrow[r]) * xstride +
+                                                      static_cast<size_t>(sb * 8 + s) * kQ8Bytes);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) F.xu[r][k] = src[k];
+  }
+  if constexpr (FMT == QMM_Q4_K) {
+    const uint8_t* blk = wr + static_cast<size_t>(sb) * kQ4Bytes;
+    F.hdr = ld16_a16(blk);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) F.q[p] = ld16_a16(blk + 16 + 32 * p + 16 * g);
+  } else {
+    const uint8_t* blk = wr + static_cast<size_t>(sb) * kQ6Bytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        raw8_load(blk + 128 + 32 * h + 16 * hf + 8 * g, F.qh_raw[h][hf], F.sh);
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+          raw8_load(blk + 64 * h + 32 * par + 16 * hf + 8 * g, F.ql_raw[h][par][hf], F.sh);
+      }
+    raw8_load(blk + 192 + 8 * g, F.sc_raw, F.sh);
+    F.d_raw = ld_u16(blk + 208);
+  }
+}
+
+// Write super-block sb's prefetched data to LDS stage `st`: activation
+// payload, (beta, -beta*C), beta*S, and this wave's decoded weight scales.
 template <int FMT, int NT, int MODE>
-__device__ __forceinline__ void stage_x(const MmqParams& P, uint8_t* smem, const int* xrow,
-                                        int sb, size_t xstride, const int* orow,
-                                        const bool* cvalid, bool write_dbg_s) {
+__device__ __forceinline__ void mmq_commit(const MmqParams& P, uint8_t* st, const MmqPrefetch<FMT, NT>& F,
+                                           const int* orow, const bool* cvalid, int sb, int wave, int col,
+                                           int g, bool write_dbg_s) {
   using L = MmqSmem<FMT, NT>;
   constexpr int BN = L::BN;
 #pragma unroll
-  for (int r = 0; r < BN * 8 / kMmqThreads; ++r) {
+  for (int r = 0; r < MmqPrefetch<FMT, NT>::RX; ++r) {
     const int bi = threadIdx.x + kMmqThreads * r;
     const int j = bi >> 3, s = bi & 7;
-    const uint2* src = reinterpret_cast<const uint2*>(P.xq + static_cast<size_t>(xrow[r]) * xstride +
-                                                      static_cast<size_t>(sb * 8 + s) * kQ8Bytes);
-    const uint2 u0 = src[0], u1 = src[1], u2 = src[2], u3 = src[3], u4 = src[4];
-    uint4* dq = reinterpret_cast<uint4*>(smem + L::kXq + (s * BN + j) * 32);
-    dq[0] = make_uint4(u0.y, u1.x, u1.y, u2.x);
-    dq[1] = make_uint4(u2.y, u3.x, u3.y, u4.x);
-    const float beta = h2f(u0.x & 0xffffu);
-    reinterpret_cast<float2*>(smem + L::kXb)[s * BN + j] = make_float2(beta, -beta * kMagic);
+    const uint2* u = F.xu[r];  // u[0].x = d and pad, u[0].y .. u[4].x = q[0..31], u[4].y = S
+    uint8_t* dq = st + L::kXq + s * L::kXqRow;
     if constexpr (FMT == QMM_Q4_K) {
-      const int S = static_cast<int>(u4.y);
-      reinterpret_cast<float*>(smem + L::kXs)[s * BN + j] = beta * static_cast<float>(S);
+      reinterpret_cast<uint4*>(dq)[j] = make_uint4(u[0].y, u[1].x, u[1].y, u[2].x);
+      reinterpret_cast<uint4*>(dq + 16 * BN)[j] = make_uint4(u[2].y, u[3].x, u[3].y, u[4].x);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        reinterpret_cast<uint2*>(dq + 8 * BN * k)[j] = make_uint2(u[k].y, u[k + 1].x);  // q[8k .. 8k+7]
+    }
+    const float beta = h2f(u[0].x & 0xffffu);
+    reinterpret_cast<float2*>(st + L::kXb)[s * L::kXbRow + j] = make_float2(beta, -beta * kMagic);
+    if constexpr (FMT == QMM_Q4_K) {
+      const int S = static_cast<int>(u[4].y);
+      reinterpret_cast<float*>(st + L::kXs)[s * L::kXsRow + j] = beta * static_cast<float>(S);
       if (MODE == kDebug && write_dbg_s && cvalid[r])
         P.dbgS[static_cast<size_t>(orow[r]) * P.nb * 8 + sb * 8 + s] = S;
     } else {
-      int S0 = dot4(0x01010101u, u0.y, 0);
-      S0 = dot4(0x01010101u, u1.x, S0);
-      S0 = dot4(0x01010101u, u1.y, S0);
-      S0 = dot4(0x01010101u, u2.x, S0);
-      int S1 = dot4(0x01010101u, u2.y, 0);
-      S1 = dot4(0x01010101u, u3.x, S1);
-      S1 = dot4(0x01010101u, u3.y, S1);
-      S1 = dot4(0x01010101u, u4.x, S1);
-      float* xs = reinterpret_cast<float*>(smem + L::kXs);
-      xs[(2 * s) * BN + j] = beta * static_cast<float>(S0);
-      xs[(2 * s + 1) * BN + j] = beta * static_cast<float>(S1);
+      int S0 = dot4(0x01010101u, u[0].y, 0);
+      S0 = dot4(0x01010101u, u[1].x, S0);
+      S0 = dot4(0x01010101u, u[1].y, S0);
+      S0 = dot4(0x01010101u, u[2].x, S0);
+      int S1 = dot4(0x01010101u, u[2].y, 0);
+      S1 = dot4(0x01010101u, u[3].x, S1);
+      S1 = dot4(0x01010101u, u[3].y, S1);
+      S1 = dot4(0x01010101u, u[4].x, S1);
+      float* xs = reinterpret_cast<float*>(st + L::kXs);
+      xs[(2 * s) * L::kXsRow + j] = beta * static_cast<float>(S0);
+      xs[(2 * s + 1) * L::kXsRow + j] = beta * static_cast<float>(S1);
+    }
+  }
+  float* wa_w = reinterpret_cast<float*>(st + L::kWa) + wave * L::NS16 * 32;
+  if constexpr (FMT == QMM_Q4_K) {
+    // lane (row col, half g) decodes sub-blocks 4g .. 4g+3 of its row
+    const float d = h2f(F.hdr.x & 0xffffu), dmin = h2f(F.hdr.x >> 16);
+    float* wm_w = reinterpret_cast<float*>(st + L::kWm) + wave * 8 * 32;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      int sc, m;
+      q4k_scale_min(4 * g + jj, F.hdr.y, F.hdr.z, F.hdr.w, sc, m);
+      wa_w[(4 * g + jj) * 32 + col] = d * static_cast<float>(sc);
+      wm_w[(4 * g + jj) * 32 + col] = -(dmin * static_cast<float>(m));
+    }
+  } else {
+    // lane (row col, half g) holds scales 8g .. 8g+7 of its row
+    const float d = h2f(F.d_raw);
+    const uint2 sc8 = raw8_join(F.sc_raw, F.sh);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t word = q < 4 ? sc8.x : sc8.y;
+      wa_w[(8 * g + q) * 32 + col] = d * static_cast<float>(static_cast<int8_t>((word >> (8 * (q & 3))) & 0xffu));
     }
   }
 }
@@ -165,12 +265,19 @@ __device__ __forceinline__ void store_tile(const MmqParams& P, const TileCols& t
 }
 
 // One output tile: rows [m0, m0+128) of weight matrix wbase, columns tc.
+// Software pipeline over super-blocks: while super-block sb is multiplied
+// from LDS stage sb&1, the loads of sb+1 are in flight; one barrier per
+// super-block (the double buffer makes the write of stage (sb+1)&1 safe:
+// every wave has passed the barrier of sb, hence finished reading sb-1).
+// Within a super-block the MFMAs of one sub-block are issued together, then
+// their epilogues; scheduling barriers between sub-blocks keep later MFMAs
+// from being hoisted (their results would not fit in registers).
 template <int FMT, int NT, int MODE>
 __device__ __forceinline__ void mmq_tile(const MmqParams& P, uint8_t* smem, const uint8_t* wbase,
                                          int m0, const TileCols& tc, bool write_dbg_s) {
   using L = MmqSmem<FMT, NT>;
   constexpr int BN = L::BN;
-  constexpr int RX = BN * 8 / kMmqThreads;  // staged activation blocks per thread
+  constexpr int RX = MmqPrefetch<FMT, NT>::RX;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
   const int r0 = m0 + wave * 32;
   const int wrow = min(r0 + col, P.M - 1);  // A-operand row of this lane
@@ -193,130 +300,109 @@ __device__ __forceinline__ void mmq_tile(const MmqParams& P, uint8_t* smem, cons
 #pragma unroll
   for (int v = 0; v < 16; ++v) magic[v] = static_cast<int>(kMagicBits);
 
-  const float* wa = reinterpret_cast<const float*>(smem + L::kWa) + wave * L::NS16 * 32;
-  const uint8_t* xqs = smem + L::kXq;
-  const float2* xb = reinterpret_cast<const float2*>(smem + L::kXb);
-  const float* xs = reinterpret_cast<const float*>(smem + L::kXs);
-
+  MmqPrefetch<FMT, NT> F;
+  mmq_load<FMT, NT>(P, F, xrow, xstride, wr, 0, g);
   for (int sb = 0; sb < P.nb; ++sb) {
-    __syncthreads();  // previous super-block's LDS reads are done
-    stage_x<FMT, NT, MODE>(P, smem, xrow, sb, xstride, orow, cvalid, write_dbg_s);
-
+    uint8_t* st = smem + (sb & 1) * L::kStage;
+    mmq_commit<FMT, NT, MODE>(P, st, F, orow, cvalid, sb, wave, col, g, write_dbg_s);
+    // this super-block's A operand bytes leave the prefetch registers
+    uint4 qcur[4];
+    uint2 qlc[2][2][2], qhc[2][2];
     if constexpr (FMT == QMM_Q4_K) {
-      const uint8_t* blk = wr + static_cast<size_t>(sb) * kQ4Bytes;
-      const uint4 hdr = ld16_a16(blk);
-      uint4 qv[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) qv[p] = ld16_a16(blk + 16 + 32 * p + 16 * g);
-      // lane (row col, half g) decodes sub-blocks 4g .. 4g+3 of its row
-      const float d = h2f(hdr.x & 0xffffu), dmin = h2f(hdr.x >> 16);
-      float* wa_w = reinterpret_cast<float*>(smem + L::kWa) + wave * 8 * 32;
-      float* wm_w = reinterpret_cast<float*>(smem + L::kWm) + wave * 8 * 32;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        int sc, m;
-        q4k_scale_min(4 * g + jj, hdr.y, hdr.z, hdr.w, sc, m);
-        wa_w[(4 * g + jj) * 32 + col] = d * static_cast<float>(sc);
-        wm_w[(4 * g + jj) * 32 + col] = -(dmin * static_cast<float>(m));
-      }
-      __syncthreads();
-
-      const float* wm = reinterpret_cast<const float*>(smem + L::kWm) + wave * 8 * 32;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const v4i a_lo = {static_cast<int>(qv[p].x & 0x0f0f0f0fu), static_cast<int>(qv[p].y & 0x0f0f0f0fu),
-                          static_cast<int>(qv[p].z & 0x0f0f0f0fu), static_cast<int>(qv[p].w & 0x0f0f0f0fu)};
-        const v4i a_hi = {static_cast<int>((qv[p].x >> 4) & 0x0f0f0f0fu),
-                          static_cast<int>((qv[p].y >> 4) & 0x0f0f0f0fu),
-                          static_cast<int>((qv[p].z >> 4) & 0x0f0f0f0fu),
-                          static_cast<int>((qv[p].w >> 4) & 0x0f0f0f0fu)};
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int s = 2 * p + hh;
-          const v4i a = hh ? a_hi : a_lo;
-          float al[16];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float4 t4 = *reinterpret_cast<const float4*>(wa + s * 32 + 8 * k + 4 * g);
-            al[4 * k] = t4.x; al[4 * k + 1] = t4.y; al[4 * k + 2] = t4.z; al[4 * k + 3] = t4.w;
-          }
-#pragma unroll
-          for (int ct = 0; ct < NT; ++ct) {
-            const int jcol = ct * 32 + col;
-            const v4i bq = *reinterpret_cast<const v4i*>(xqs + (s * BN + jcol) * 32 + 16 * g);
-            const v16i X = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq, magic, 0, 0, 0);
-            if constexpr (MODE == kDebug) {
-              int xr, orr; bool ok;
-              col_rows<MODE>(P, tc, jcol, xr, orr, ok);
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int row = r0 + 8 * (v >> 2) + 4 * g + (v & 3);
-                if (ok && row < P.M)
-                  P.dbgD[(static_cast<size_t>(orr) * P.M + row) * (P.nb * 8) + sb * 8 + s] =
-                      X[v] - static_cast<int>(kMagicBits);
-              }
-            } else {
-              const float2 bp = xb[s * BN + jcol];
-              // reinterpret the whole vector: X holds 1.5*2^23 + D as fp32 bits
-              const v16f Xf = __builtin_bit_cast(v16f, X);
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
-                acc[ct][v] = __builtin_fmaf(al[v], t, acc[ct][v]);
-              }
-            }
-          }
-        }
-        // min term of sub-blocks 2p, 2p+1: A[i][k] = -dmin*m, B[k][j] = beta*S
-        const float am = wm[(2 * p + g) * 32 + col];
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-          const float bm = xs[(2 * p + g) * BN + ct * 32 + col];
-          acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, bm, acc[ct], 0, 0, 0);
-        }
-      }
+      for (int p = 0; p < 4; ++p) qcur[p] = F.q[p];
     } else {
-      // Q6_K: lane (row col, k-group g) reads, for each 16-weight sub-block,
-      // the 8 weights at positions 8g..8g+7 of the sub-block.
-      const uint8_t* blk = wr + static_cast<size_t>(sb) * kQ6Bytes;
-      const float d = h2f(ld_u16(blk + 208));
-      float* wa_w = reinterpret_cast<float*>(smem + L::kWa) + wave * 16 * 32;
-      // lane half g decodes scales 8g .. 8g+7
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t two = ld_u16(blk + 192 + 8 * g + 2 * q);
-        wa_w[(8 * g + 2 * q) * 32 + col] = d * static_cast<float>(static_cast<int8_t>(two & 0xffu));
-        wa_w[(8 * g + 2 * q + 1) * 32 + col] = d * static_cast<float>(static_cast<int8_t>(two >> 8));
-      }
-      // q6 values: for half h, parity (g&1 of the 32-group), 16-sub-block
-      // half hf: ql bytes 64h + 32*par + 16hf + 8g .. +8; qh bytes
-      // 32h + 16hf + 8g .. +8.
-      uint2 ql[2][2][2], qh[2][2];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const uint4 hq = ld16_a2(blk + 128 + 32 * h + 16 * hf);  // 16 bytes, lanes pick 8
-          qh[h][hf] = g ? make_uint2(hq.z, hq.w) : make_uint2(hq.x, hq.y);
+          qhc[h][hf] = raw8_join(F.qh_raw[h][hf], F.sh);
 #pragma unroll
-          for (int par = 0; par < 2; ++par) {
-            const uint4 lq = ld16_a2(blk + 64 * h + 32 * par + 16 * hf);
-            ql[h][par][hf] = g ? make_uint2(lq.z, lq.w) : make_uint2(lq.x, lq.y);
+          for (int par = 0; par < 2; ++par) qlc[h][par][hf] = raw8_join(F.ql_raw[h][par][hf], F.sh);
+        }
+    }
+    __syncthreads();
+    if (sb + 1 < P.nb) mmq_load<FMT, NT>(P, F, xrow, xstride, wr, sb + 1, g);
+
+    const float* wa = reinterpret_cast<const float*>(st + L::kWa) + wave * L::NS16 * 32;
+    const uint8_t* xqs = st + L::kXq;
+    const float2* xb = reinterpret_cast<const float2*>(st + L::kXb);
+    const float* xs = reinterpret_cast<const float*>(st + L::kXs);
+
+    if constexpr (FMT == QMM_Q4_K) {
+      const float* wm = reinterpret_cast<const float*>(st + L::kWm) + wave * 8 * 32;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int p = s >> 1;
+        const uint4 qv = qcur[p];
+        const int sh = (s & 1) * 4;
+        const v4i a = {static_cast<int>((qv.x >> sh) & 0x0f0f0f0fu), static_cast<int>((qv.y >> sh) & 0x0f0f0f0fu),
+                       static_cast<int>((qv.z >> sh) & 0x0f0f0f0fu), static_cast<int>((qv.w >> sh) & 0x0f0f0f0fu)};
+        v16i X[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const v4i bq = *reinterpret_cast<const v4i*>(xqs + s * L::kXqRow + 16 * BN * g + 16 * (ct * 32 + col));
+          X[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq, magic, 0, 0, 0);
+        }
+        float al[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 t4 = *reinterpret_cast<const float4*>(wa + s * 32 + 8 * k + 4 * g);
+          al[4 * k] = t4.x; al[4 * k + 1] = t4.y; al[4 * k + 2] = t4.z; al[4 * k + 3] = t4.w;
+        }
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const int jcol = ct * 32 + col;
+          if constexpr (MODE == kDebug) {
+            int xr, orr; bool ok;
+            col_rows<MODE>(P, tc, jcol, xr, orr, ok);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int row = r0 + 8 * (v >> 2) + 4 * g + (v & 3);
+              if (ok && row < P.M)
+                P.dbgD[(static_cast<size_t>(orr) * P.M + row) * (P.nb * 8) + sb * 8 + s] =
+                    X[ct][v] - static_cast<int>(kMagicBits);
+            }
+          } else {
+            const float2 bp = xb[s * L::kXbRow + jcol];
+            // the whole vector is reinterpreted: X holds 1.5*2^23 + D as fp32 bits
+            const v16f Xf = __builtin_bit_cast(v16f, X[ct]);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
+              acc[ct][v] = __builtin_fmaf(al[v], t, acc[ct][v]);
+            }
           }
         }
-      __syncthreads();
-
+        if (s & 1) {
+          // min term of sub-blocks s-1, s: A[i][k] = -dmin*m, B[k][j] = beta*S
+          const float am = wm[(s - 1 + g) * 32 + col];
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            const float bm = xs[(s - 1 + g) * L::kXsRow + ct * 32 + col];
+            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, bm, acc[ct], 0, 0, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {  // Q8_1 block = 32-group (h = s/4, gg = s%4)
         const int h = s >> 2, gg = s & 3, par = gg & 1, shl = 4 * (gg >> 1), shh = 2 * gg;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const uint2 lq = ql[h][par][hf];
-          const uint2 hq = qh[h][hf];
+          const uint2 lq = qlc[h][par][hf];
+          const uint2 hq = qhc[h][hf];
           const uint32_t q0 = ((lq.x >> shl) & 0x0f0f0f0fu) | (((hq.x >> shh) & 0x03030303u) << 4);
           const uint32_t q1 = ((lq.y >> shl) & 0x0f0f0f0fu) | (((hq.y >> shh) & 0x03030303u) << 4);
           const long a = static_cast<long>((static_cast<unsigned long>(q1) << 32) | q0);
           const int s16 = 2 * s + hf;
+          v16i X[NT];
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            const long bq = *reinterpret_cast<const long*>(xqs + s * L::kXqRow + 8 * BN * (2 * hf + g) + 8 * (ct * 32 + col));
+            X[ct] = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq, magic, 0, 0, 0);
+          }
           float al[16];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -326,28 +412,26 @@ __device__ __forceinline__ void mmq_tile(const MmqParams& P, uint8_t* smem, cons
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) {
             const int jcol = ct * 32 + col;
-            const long bq = *reinterpret_cast<const long*>(xqs + (s * BN + jcol) * 32 + 16 * hf + 8 * g);
-            const v16i X = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq, magic, 0, 0, 0);
             if constexpr (MODE == kDebug) {
               int xr, orr; bool ok;
               col_rows<MODE>(P, tc, jcol, xr, orr, ok);
               // D6 = sum (q6 - 32) q = D - 32 * S16, S16 = sum of the 16 int8 activations
-              const uint4 pq = *reinterpret_cast<const uint4*>(xqs + (s * BN + jcol) * 32 + 16 * hf);
-              int S16 = dot4(0x01010101u, pq.x, 0);
-              S16 = dot4(0x01010101u, pq.y, S16);
-              S16 = dot4(0x01010101u, pq.z, S16);
-              S16 = dot4(0x01010101u, pq.w, S16);
+              const uint2 p0 = *reinterpret_cast<const uint2*>(xqs + s * L::kXqRow + 8 * BN * (2 * hf) + 8 * jcol);
+              const uint2 p1 = *reinterpret_cast<const uint2*>(xqs + s * L::kXqRow + 8 * BN * (2 * hf + 1) + 8 * jcol);
+              int S16 = dot4(0x01010101u, p0.x, 0);
+              S16 = dot4(0x01010101u, p0.y, S16);
+              S16 = dot4(0x01010101u, p1.x, S16);
+              S16 = dot4(0x01010101u, p1.y, S16);
 #pragma unroll
               for (int v = 0; v < 16; ++v) {
                 const int row = r0 + 8 * (v >> 2) + 4 * g + (v & 3);
                 if (ok && row < P.M)
                   P.dbgD[(static_cast<size_t>(orr) * P.M + row) * (P.nb * 16) + sb * 16 + s16] =
-                      X[v] - static_cast<int>(kMagicBits) - 32 * S16;
+                      X[ct][v] - static_cast<int>(kMagicBits) - 32 * S16;
               }
             } else {
-              const float2 bp = xb[s * BN + jcol];
-              // reinterpret the whole vector: X holds 1.5*2^23 + D as fp32 bits
-              const v16f Xf = __builtin_bit_cast(v16f, X);
+              const float2 bp = xb[s * L::kXbRow + jcol];
+              const v16f Xf = __builtin_bit_cast(v16f, X[ct]);
 #pragma unroll
               for (int v = 0; v < 16; ++v) {
                 const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
@@ -355,18 +439,18 @@ __device__ __forceinline__ void mmq_tile(const MmqParams& P, uint8_t* smem, cons
               }
             }
           }
-        }
-      }
-      // offset term: sum_s16 (-32 * d * sc) * (beta * S16), 8 MFMAs of K = 2
-      if constexpr (MODE != kDebug) {
+          if constexpr (MODE != kDebug) {
+            if (hf) {
+              // offset term of the two 16-halves of block s: A = -32 * d * sc, B = beta * S16
+              const float am = -32.0f * wa[(2 * s + g) * 32 + col];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float am = -32.0f * wa[(2 * q + g) * 32 + col];
-#pragma unroll
-          for (int ct = 0; ct < NT; ++ct) {
-            const float bm = xs[(2 * q + g) * BN + ct * 32 + col];
-            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, bm, acc[ct], 0, 0, 0);
+              for (int ct = 0; ct < NT; ++ct) {
+                const float bm = xs[(2 * s + g) * L::kXsRow + ct * 32 + col];
+                acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, bm, acc[ct], 0, 0, 0);
+              }
+            }
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -374,9 +458,12 @@ __device__ __forceinline__ void mmq_tile(const MmqParams& P, uint8_t* smem, cons
   if constexpr (MODE != kDebug) store_tile<NT, MODE>(P, tc, r0, acc, P.y);
 }
 
-// Persistent loop over the tiles of the call.
+// Persistent loop over the tiles of the call.  Two waves per SIMD are
+// required: with one, nothing hides the MFMA and LDS latencies of the
+// epilogue.  (Q6_K with 64-column tiles then spills a few registers to
+// scratch, which costs less than one resident wave or 32-column tiles.)
 template <int FMT, int NT, int MODE>
-__global__ __launch_bounds__(kMmqThreads) void mmq_kernel(MmqParams P) {
+__global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mmq_kernel(MmqParams P) {
   using L = MmqSmem<FMT, NT>;
   constexpr int BN = L::BN;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
@@ -467,7 +554,9 @@ static int launch_mmq(const MmqParams& P, int total_tiles_hint, hipStream_t st) 
   return launch_status();
 }
 
-constexpr int kDenseNT = 2;  // dense tiles: 128 rows x 64 tokens
+// Dense tiles: 128 rows x 64 tokens for both formats.
+template <int FMT>
+constexpr int kDenseNT = 2;
 constexpr int kMoeNT = 1;    // MoE tiles: 128 rows x 32 routed tokens
 constexpr size_t kCounterBytes = 256;
 
@@ -483,14 +572,16 @@ int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64
   P.counters = static_cast<unsigned*>(ws);
   P.dbgD = dbgD;
   P.dbgS = dbgS;
-  constexpr int BN = 32 * kDenseNT;
-  const int tiles = static_cast<int>(((M + kMmqBM - 1) / kMmqBM) * ((T + BN - 1) / BN));
   const bool dbg = dbgD != nullptr;
-  if (fmt == QMM_Q4_K)
-    return dbg ? launch_mmq<QMM_Q4_K, kDenseNT, kDebug>(P, tiles, st)
-               : launch_mmq<QMM_Q4_K, kDenseNT, kDense>(P, tiles, st);
-  return dbg ? launch_mmq<QMM_Q6_K, kDenseNT, kDebug>(P, tiles, st)
-             : launch_mmq<QMM_Q6_K, kDenseNT, kDense>(P, tiles, st);
+  const int64_t mt = (M + kMmqBM - 1) / kMmqBM;
+  if (fmt == QMM_Q4_K) {
+    constexpr int NT = kDenseNT<QMM_Q4_K>;
+    const int tiles = static_cast<int>(mt * ((T + 32 * NT - 1) / (32 * NT)));
+    return dbg ? launch_mmq<QMM_Q4_K, NT, kDebug>(P, tiles, st) : launch_mmq<QMM_Q4_K, NT, kDense>(P, tiles, st);
+  }
+  constexpr int NT = kDenseNT<QMM_Q6_K>;
+  const int tiles = static_cast<int>(mt * ((T + 32 * NT - 1) / (32 * NT)));
+  return dbg ? launch_mmq<QMM_Q6_K, NT, kDebug>(P, tiles, st) : launch_mmq<QMM_Q6_K, NT, kDense>(P, tiles, st);
 }
 
 // Grouped launch used by moe_grouped_mmq (after route preparation on the
