@@ -34,6 +34,8 @@
 //   for the next call without a memset.
 #include "qmm_common.hpp"
 
+#include <type_traits>
+
 namespace qmm {
 
 constexpr int kMmqThreads = 256;       // 4 waves
@@ -66,21 +68,22 @@ struct MmqParams {
 // values of every column are cut into pieces (Q4_K 2 x 16 bytes: one MFMA
 // k-group each; Q6_K 4 x 8 bytes) and piece k of all columns is one
 // contiguous run, so the MFMA operand reads of 32 consecutive columns are
-// consecutive.  Rows of s are padded so that the commit stores (8 lanes =
-// the 8 blocks of one token) fall on different banks; reads stay a per-lane
-// base plus immediate offsets.
+// consecutive.  Rows of s are padded by 32 bytes so that the commit stores
+// (8 lanes = the 8 blocks of one token, next 8 lanes = next token) of any
+// 16 lanes (16-byte pieces) or 32 lanes (8-byte pieces) fall on distinct
+// banks; reads stay a per-lane base plus immediate offsets.
 template <int FMT, int NT>
 struct MmqSmem {
   static constexpr int BN = 32 * NT;
   static constexpr int NS16 = FMT == QMM_Q4_K ? 8 : 16;     // scale groups per super-block
   static constexpr int kPiece = FMT == QMM_Q4_K ? 16 : 8;    // payload bytes per piece
-  static constexpr int kXqRow = 32 * BN + 8 * kPiece;       // bytes per block row s
-  static constexpr int kXbRow = BN + 8;                      // float2 per block row
-  static constexpr int kXsRow = FMT == QMM_Q4_K ? BN + 8 : BN + 4;  // floats per scale row
+  static constexpr int kXqRow = 32 * BN + 32;               // bytes per block row s
+  static constexpr int kXbRow = BN + 4;                      // float2 per block row
+  static constexpr int kXsRow = BN + 8;                      // floats per beta*S row
   static constexpr int kXq = 0;                              // [8][32/kPiece][BN][kPiece] int8 payload
   static constexpr int kXb = kXq + 8 * kXqRow;               // [8][kXbRow] (beta, -beta*C)
-  static constexpr int kXs = kXb + 8 * kXbRow * 8;           // [NS16][kXsRow] beta*S (Q4_K: per 32, Q6_K: per 16)
-  static constexpr int kWa = kXs + NS16 * kXsRow * 4;        // [4 waves][NS16][32] alpha = d*sc
+  static constexpr int kXs = kXb + 8 * kXbRow * 8;           // Q4_K: [8][kXsRow] beta*S
+  static constexpr int kWa = kXs + (FMT == QMM_Q4_K ? 8 * kXsRow * 4 : 0);  // [4 waves][NS16][32] alpha = d*sc
   static constexpr int kWm = kWa + 4 * NS16 * 32 * 4;        // Q4_K: [4][8][32] -dmin*m
   static constexpr int kStage = (kWm + (FMT == QMM_Q4_K ? 4 * 8 * 32 * 4 : 0) + 15) & ~15;
   static constexpr int kBytes = 2 * kStage;
@@ -198,18 +201,6 @@ __device__ __forceinline__ void mmq_commit(const MmqParams& P, uint8_t* st, cons
       reinterpret_cast<float*>(st + L::kXs)[s * L::kXsRow + j] = beta * static_cast<float>(S);
       if (MODE == kDebug && write_dbg_s && cvalid[r])
         P.dbgS[static_cast<size_t>(orow[r]) * P.nb * 8 + sb * 8 + s] = S;
-    } else {
-      int S0 = dot4(0x01010101u, u[0].y, 0);
-      S0 = dot4(0x01010101u, u[1].x, S0);
-      S0 = dot4(0x01010101u, u[1].y, S0);
-      S0 = dot4(0x01010101u, u[2].x, S0);
-      int S1 = dot4(0x01010101u, u[2].y, 0);
-      S1 = dot4(0x01010101u, u[3].x, S1);
-      S1 = dot4(0x01010101u, u[3].y, S1);
-      S1 = dot4(0x01010101u, u[4].x, S1);
-      float* xs = reinterpret_cast<float*>(st + L::kXs);
-      xs[(2 * s) * L::kXsRow + j] = beta * static_cast<float>(S0);
-      xs[(2 * s + 1) * L::kXsRow + j] = beta * static_cast<float>(S1);
     }
   }
   float* wa_w = reinterpret_cast<float*>(st + L::kWa) + wave * L::NS16 * 32;
@@ -264,258 +255,318 @@ __device__ __forceinline__ void store_tile(const MmqParams& P, const TileCols& t
   }
 }
 
-// One output tile: rows [m0, m0+128) of weight matrix wbase, columns tc.
-// Software pipeline over super-blocks: while super-block sb is multiplied
-// from LDS stage sb&1, the loads of sb+1 are in flight; one barrier per
-// super-block (the double buffer makes the write of stage (sb+1)&1 safe:
-// every wave has passed the barrier of sb, hence finished reading sb-1).
-// Within a super-block the MFMAs of one sub-block are issued together, then
-// their epilogues; scheduling barriers between sub-blocks keep later MFMAs
-// from being hoisted (their results would not fit in registers).
-template <int FMT, int NT, int MODE>
-__device__ __forceinline__ void mmq_tile(const MmqParams& P, uint8_t* smem, const uint8_t* wbase,
-                                         int m0, const TileCols& tc, bool write_dbg_s) {
-  using L = MmqSmem<FMT, NT>;
-  constexpr int BN = L::BN;
-  constexpr int RX = MmqPrefetch<FMT, NT>::RX;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
-  const int r0 = m0 + wave * 32;
-  const int wrow = min(r0 + col, P.M - 1);  // A-operand row of this lane
-  const size_t xstride = static_cast<size_t>(P.nb) * 8 * kQ8Bytes;
-  constexpr int kRowBytes = FMT == QMM_Q4_K ? kQ4Bytes : kQ6Bytes;
-  const uint8_t* wr = wbase + static_cast<size_t>(wrow) * P.nb * kRowBytes;
+// A operand bytes of one super-block for this lane (row col of the wave's
+// 32 rows, k-group g), taken out of the prefetch registers before the loads
+// of the next super-block reuse them.
+template <int FMT>
+struct MmqOperand;
+template <>
+struct MmqOperand<QMM_Q4_K> {
+  uint4 q[4];  // bytes 16 + 32p + 16g .. +15 of the block: nibbles of sub-blocks 2p, 2p+1
+};
+template <>
+struct MmqOperand<QMM_Q6_K> {
+  uint2 ql[2][2][2], qh[2][2];  // [h][parity][16-half] low-nibble bytes, [h][16-half] high-bit bytes
+};
 
-  int xrow[RX], orow[RX];
-  bool cvalid[RX];
+template <int FMT, int NT>
+__device__ __forceinline__ void take_operand(const MmqPrefetch<FMT, NT>& F, MmqOperand<FMT>& A) {
+  if constexpr (FMT == QMM_Q4_K) {
 #pragma unroll
-  for (int r = 0; r < RX; ++r)
-    col_rows<MODE>(P, tc, (threadIdx.x + kMmqThreads * r) >> 3, xrow[r], orow[r], cvalid[r]);
-
-  v16f acc[NT];
+    for (int p = 0; p < 4; ++p) A.q[p] = F.q[p];
+  } else {
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[ct][v] = 0.0f;
-  v16i magic;
+      for (int hf = 0; hf < 2; ++hf) {
+        A.qh[h][hf] = raw8_join(F.qh_raw[h][hf], F.sh);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) magic[v] = static_cast<int>(kMagicBits);
-
-  MmqPrefetch<FMT, NT> F;
-  mmq_load<FMT, NT>(P, F, xrow, xstride, wr, 0, g);
-  for (int sb = 0; sb < P.nb; ++sb) {
-    uint8_t* st = smem + (sb & 1) * L::kStage;
-    mmq_commit<FMT, NT, MODE>(P, st, F, orow, cvalid, sb, wave, col, g, write_dbg_s);
-    // this super-block's A operand bytes leave the prefetch registers
-    uint4 qcur[4];
-    uint2 qlc[2][2][2], qhc[2][2];
-    if constexpr (FMT == QMM_Q4_K) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) qcur[p] = F.q[p];
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          qhc[h][hf] = raw8_join(F.qh_raw[h][hf], F.sh);
-#pragma unroll
-          for (int par = 0; par < 2; ++par) qlc[h][par][hf] = raw8_join(F.ql_raw[h][par][hf], F.sh);
-        }
-    }
-    __syncthreads();
-    if (sb + 1 < P.nb) mmq_load<FMT, NT>(P, F, xrow, xstride, wr, sb + 1, g);
-
-    const float* wa = reinterpret_cast<const float*>(st + L::kWa) + wave * L::NS16 * 32;
-    const uint8_t* xqs = st + L::kXq;
-    const float2* xb = reinterpret_cast<const float2*>(st + L::kXb);
-    const float* xs = reinterpret_cast<const float*>(st + L::kXs);
-
-    if constexpr (FMT == QMM_Q4_K) {
-      const float* wm = reinterpret_cast<const float*>(st + L::kWm) + wave * 8 * 32;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int p = s >> 1;
-        const uint4 qv = qcur[p];
-        const int sh = (s & 1) * 4;
-        const v4i a = {static_cast<int>((qv.x >> sh) & 0x0f0f0f0fu), static_cast<int>((qv.y >> sh) & 0x0f0f0f0fu),
-                       static_cast<int>((qv.z >> sh) & 0x0f0f0f0fu), static_cast<int>((qv.w >> sh) & 0x0f0f0f0fu)};
-        v16i X[NT];
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-          const v4i bq = *reinterpret_cast<const v4i*>(xqs + s * L::kXqRow + 16 * BN * g + 16 * (ct * 32 + col));
-          X[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq, magic, 0, 0, 0);
-        }
-        float al[16];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float4 t4 = *reinterpret_cast<const float4*>(wa + s * 32 + 8 * k + 4 * g);
-          al[4 * k] = t4.x; al[4 * k + 1] = t4.y; al[4 * k + 2] = t4.z; al[4 * k + 3] = t4.w;
-        }
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-          const int jcol = ct * 32 + col;
-          if constexpr (MODE == kDebug) {
-            int xr, orr; bool ok;
-            col_rows<MODE>(P, tc, jcol, xr, orr, ok);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int row = r0 + 8 * (v >> 2) + 4 * g + (v & 3);
-              if (ok && row < P.M)
-                P.dbgD[(static_cast<size_t>(orr) * P.M + row) * (P.nb * 8) + sb * 8 + s] =
-                    X[ct][v] - static_cast<int>(kMagicBits);
-            }
-          } else {
-            const float2 bp = xb[s * L::kXbRow + jcol];
-            // the whole vector is reinterpreted: X holds 1.5*2^23 + D as fp32 bits
-            const v16f Xf = __builtin_bit_cast(v16f, X[ct]);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
-              acc[ct][v] = __builtin_fmaf(al[v], t, acc[ct][v]);
-            }
-          }
-        }
-        if (s & 1) {
-          // min term of sub-blocks s-1, s: A[i][k] = -dmin*m, B[k][j] = beta*S
-          const float am = wm[(s - 1 + g) * 32 + col];
-#pragma unroll
-          for (int ct = 0; ct < NT; ++ct) {
-            const float bm = xs[(s - 1 + g) * L::kXsRow + ct * 32 + col];
-            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, bm, acc[ct], 0, 0, 0);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int par = 0; par < 2; ++par) A.ql[h][par][hf] = raw8_join(F.ql_raw[h][par][hf], F.sh);
       }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {  // Q8_1 block = 32-group (h = s/4, gg = s%4)
-        const int h = s >> 2, gg = s & 3, par = gg & 1, shl = 4 * (gg >> 1), shh = 2 * gg;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const uint2 lq = qlc[h][par][hf];
-          const uint2 hq = qhc[h][hf];
-          const uint32_t q0 = ((lq.x >> shl) & 0x0f0f0f0fu) | (((hq.x >> shh) & 0x03030303u) << 4);
-          const uint32_t q1 = ((lq.y >> shl) & 0x0f0f0f0fu) | (((hq.y >> shh) & 0x03030303u) << 4);
-          const long a = static_cast<long>((static_cast<unsigned long>(q1) << 32) | q0);
-          const int s16 = 2 * s + hf;
-          v16i X[NT];
-#pragma unroll
-          for (int ct = 0; ct < NT; ++ct) {
-            const long bq = *reinterpret_cast<const long*>(xqs + s * L::kXqRow + 8 * BN * (2 * hf + g) + 8 * (ct * 32 + col));
-            X[ct] = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq, magic, 0, 0, 0);
-          }
-          float al[16];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float4 t4 = *reinterpret_cast<const float4*>(wa + s16 * 32 + 8 * k + 4 * g);
-            al[4 * k] = t4.x; al[4 * k + 1] = t4.y; al[4 * k + 2] = t4.z; al[4 * k + 3] = t4.w;
-          }
-#pragma unroll
-          for (int ct = 0; ct < NT; ++ct) {
-            const int jcol = ct * 32 + col;
-            if constexpr (MODE == kDebug) {
-              int xr, orr; bool ok;
-              col_rows<MODE>(P, tc, jcol, xr, orr, ok);
-              // D6 = sum (q6 - 32) q = D - 32 * S16, S16 = sum of the 16 int8 activations
-              const uint2 p0 = *reinterpret_cast<const uint2*>(xqs + s * L::kXqRow + 8 * BN * (2 * hf) + 8 * jcol);
-              const uint2 p1 = *reinterpret_cast<const uint2*>(xqs + s * L::kXqRow + 8 * BN * (2 * hf + 1) + 8 * jcol);
-              int S16 = dot4(0x01010101u, p0.x, 0);
-              S16 = dot4(0x01010101u, p0.y, S16);
-              S16 = dot4(0x01010101u, p1.x, S16);
-              S16 = dot4(0x01010101u, p1.y, S16);
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int row = r0 + 8 * (v >> 2) + 4 * g + (v & 3);
-                if (ok && row < P.M)
-                  P.dbgD[(static_cast<size_t>(orr) * P.M + row) * (P.nb * 16) + sb * 16 + s16] =
-                      X[ct][v] - static_cast<int>(kMagicBits) - 32 * S16;
-              }
-            } else {
-              const float2 bp = xb[s * L::kXbRow + jcol];
-              const v16f Xf = __builtin_bit_cast(v16f, X[ct]);
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
-                acc[ct][v] = __builtin_fmaf(al[v], t, acc[ct][v]);
-              }
-            }
-          }
-          if constexpr (MODE != kDebug) {
-            if (hf) {
-              // offset term of the two 16-halves of block s: A = -32 * d * sc, B = beta * S16
-              const float am = -32.0f * wa[(2 * s + g) * 32 + col];
-#pragma unroll
-              for (int ct = 0; ct < NT; ++ct) {
-                const float bm = xs[(2 * s + g) * L::kXsRow + ct * 32 + col];
-                acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, bm, acc[ct], 0, 0, 0);
-              }
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
   }
-  if constexpr (MODE != kDebug) store_tile<NT, MODE>(P, tc, r0, acc, P.y);
 }
 
-// Persistent loop over the tiles of the call.  Two waves per SIMD are
-// required: with one, nothing hides the MFMA and LDS latencies of the
-// epilogue.  (Q6_K with 64-column tiles then spills a few registers to
-// scratch, which costs less than one resident wave or 32-column tiles.)
+// LDS operands of one MFMA sub-block u for this lane: the 16 row scales
+// alpha of its rows, (beta, -beta*C) and the B operand of each column tile,
+// and for Q4_K at odd u the min-term operands of sub-blocks u-1, u.
+template <int FMT, int NT>
+struct SubOps {
+  using BQ = std::conditional_t<FMT == QMM_Q4_K, v4i, long>;
+  float al[16];
+  float2 bp[NT];
+  BQ bq[NT];
+  float am, bm[NT];
+};
+
+// u indexes MFMA sub-blocks: Q4_K u = the 32-weight sub-block (= Q8_1 block);
+// Q6_K u = 2*s + hf, 16-weight group hf of Q8_1 block s.
+template <int FMT, int NT>
+__device__ __forceinline__ void load_sub(const uint8_t* st, int u, SubOps<FMT, NT>& O) {
+  using L = MmqSmem<FMT, NT>;
+  constexpr int BN = L::BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
+  const int s = FMT == QMM_Q4_K ? u : u >> 1;
+  // B operand: piece g (Q4_K: k-group g of the 32 values) or quarter 2*hf+g (Q6_K)
+  const uint8_t* xq = st + L::kXq + s * L::kXqRow + L::kPiece * col;
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    if constexpr (FMT == QMM_Q4_K)
+      O.bq[ct] = *reinterpret_cast<const v4i*>(xq + 16 * BN * g + 16 * 32 * ct);
+    else
+      O.bq[ct] = *reinterpret_cast<const long*>(xq + 8 * BN * (2 * (u & 1) + g) + 8 * 32 * ct);
+  }
+  const float* wa = reinterpret_cast<const float*>(st + L::kWa) + wave * L::NS16 * 32 + u * 32 + 4 * g;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 t4 = *reinterpret_cast<const float4*>(wa + 8 * k);
+    O.al[4 * k] = t4.x; O.al[4 * k + 1] = t4.y; O.al[4 * k + 2] = t4.z; O.al[4 * k + 3] = t4.w;
+  }
+  const float2* xb = reinterpret_cast<const float2*>(st + L::kXb) + s * L::kXbRow + col;
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) O.bp[ct] = xb[32 * ct];
+  if constexpr (FMT == QMM_Q4_K) {
+    if (u & 1) {
+      O.am = reinterpret_cast<const float*>(st + L::kWm)[wave * 8 * 32 + (u - 1 + g) * 32 + col];
+      const float* xs = reinterpret_cast<const float*>(st + L::kXs) + (u - 1 + g) * L::kXsRow + col;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) O.bm[ct] = xs[32 * ct];
+    }
+  }
+}
+
+// A operand of MFMA sub-block u from this lane's weight bytes.
+//   Q4_K: the 4-bit values (0..15) of sub-block u, 16 per lane.
+//   Q6_K: the signed values q - 32, 8 per lane: the low nibble from ql and
+//   the two high bits from qh; a byte-table lookup (v_perm) maps the high
+//   bits hi to the int8 16*(hi-2), which has a zero low nibble.
+__device__ __forceinline__ v4i build_a(const MmqOperand<QMM_Q4_K>& A, int u) {
+  const uint4 qv = A.q[u >> 1];
+  const int sh = (u & 1) * 4;
+  return v4i{static_cast<int>((qv.x >> sh) & 0x0f0f0f0fu), static_cast<int>((qv.y >> sh) & 0x0f0f0f0fu),
+             static_cast<int>((qv.z >> sh) & 0x0f0f0f0fu), static_cast<int>((qv.w >> sh) & 0x0f0f0f0fu)};
+}
+constexpr uint32_t kQ6HiTable = 0x1000F0E0u;  // bytes -32, -16, 0, 16 as int8
+__device__ __forceinline__ long build_a(const MmqOperand<QMM_Q6_K>& A, int u) {
+  const int s = u >> 1, hf = u & 1;
+  const int h = s >> 2, gg = s & 3, par = gg & 1, shl = 4 * (gg >> 1), shh = 2 * gg;
+  const uint2 lq = A.ql[h][par][hf];
+  const uint2 hq = A.qh[h][hf];
+  const uint32_t q0 = ((lq.x >> shl) & 0x0f0f0f0fu) |
+                      __builtin_amdgcn_perm(kQ6HiTable, kQ6HiTable, (hq.x >> shh) & 0x03030303u);
+  const uint32_t q1 = ((lq.y >> shl) & 0x0f0f0f0fu) |
+                      __builtin_amdgcn_perm(kQ6HiTable, kQ6HiTable, (hq.y >> shh) & 0x03030303u);
+  return static_cast<long>((static_cast<unsigned long>(q1) << 32) | q0);
+}
+
+__device__ __forceinline__ v16i mfma_sub(const v4i& a, const v4i& b, const v16i& c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16i mfma_sub(long a, long b, const v16i& c) {
+  return __builtin_amdgcn_mfma_i32_32x32x16_i8(a, b, c, 0, 0, 0);
+}
+
+// Multiply-accumulate super-block sb from LDS stage st.  Software pipeline
+// over sub-blocks: the LDS operands of sub-block u+1 are read while u is
+// rescaled, and the MFMA of (u+1, column tile ct) is issued right after the
+// epilogue of (u, ct) has consumed its registers, so the matrix core runs
+// under the epilogue of the next column tile.  The epilogue adds
+// alpha * beta * D into acc (2 VALU ops per element); the Q4_K min term
+// goes through fp32 MFMAs into the same accumulator.  Q6_K has no separate
+// term: its A operand is already signed.
+template <int FMT, int NT, int MODE>
+__device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* st, const MmqOperand<FMT>& A,
+                                            v16f (&acc)[NT], const v16i& magic,
+                                            const TileCols& tc, int r0, int sb) {
+  constexpr int NU = FMT == QMM_Q4_K ? 8 : 16;  // MFMA sub-blocks per super-block
+  const int g = (threadIdx.x & 63) >> 5, col = threadIdx.x & 31;
+  SubOps<FMT, NT> O[2];
+  v16i X[NT];
+  load_sub<FMT, NT>(st, 0, O[0]);
+  {
+    const auto a0 = build_a(A, 0);
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) X[ct] = mfma_sub(a0, O[0].bq[ct], magic);
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int b = u & 1;
+    const bool more = u + 1 < NU;
+    if (more) load_sub<FMT, NT>(st, u + 1, O[b ^ 1]);
+    const auto an = build_a(A, more ? u + 1 : u);
+    // scheduling barriers pin the order: operand reads of u+1 first, then
+    // per column tile its epilogue followed by its next MFMA (left to
+    // itself the compiler sinks the reads behind the epilogue and exposes
+    // the LDS latency)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      if constexpr (MODE == kDebug) {
+        int xr, orr; bool ok;
+        col_rows<MODE>(P, tc, ct * 32 + col, xr, orr, ok);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = r0 + 8 * (v >> 2) + 4 * g + (v & 3);
+          if (ok && row < P.M)
+            P.dbgD[(static_cast<size_t>(orr) * P.M + row) * (P.nb * NU) + sb * NU + u] =
+                X[ct][v] - static_cast<int>(kMagicBits);
+        }
+      } else {
+        // the whole vector is reinterpreted: X holds 1.5*2^23 + D as fp32 bits
+        const v16f Xf = __builtin_bit_cast(v16f, X[ct]);
+        const float2 bp = O[b].bp[ct];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
+          acc[ct][v] = __builtin_fmaf(O[b].al[v], t, acc[ct][v]);
+        }
+      }
+      if constexpr (FMT == QMM_Q4_K && MODE != kDebug) {
+        // min term, K = 2 fp32 MFMA over sub-blocks u-1, u (lane half g
+        // takes u-1+g): A[i][k] = -dmin*m, B[k][j] = beta*S.  The next VALU
+        // write of acc[ct] comes one column tile later, under which it runs.
+        if (u & 1) acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(O[b].am, O[b].bm[ct], acc[ct], 0, 0, 0);
+      }
+      if (more) X[ct] = mfma_sub(an, O[b ^ 1].bq[ct], magic);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Per-thread addressing of one tile: the activation rows this thread stages
+// (columns (threadIdx.x + 256 r) / 8) and the weight row of its A operand.
+template <int FMT, int NT, int MODE>
+struct TileRef {
+  static constexpr int RX = MmqPrefetch<FMT, NT>::RX;
+  TileCols tc;
+  int r0;                 // first row of this wave
+  const uint8_t* wr;      // weight row of this lane
+  int xrow[RX], orow[RX];
+  bool cvalid[RX];
+  bool dbg_s;             // debug: this tile writes the activation sums
+};
+
+// Tile idx of the call: rows, routed columns and weight matrix.
+template <int FMT, int NT, int MODE>
+__device__ __forceinline__ void tile_ref(const MmqParams& P, int idx, TileRef<FMT, NT, MODE>& R) {
+  constexpr int BN = 32 * NT;
+  int m_tile;
+  const uint8_t* wbase = P.w;
+  if constexpr (MODE == kMoe) {
+    int lo = 0, hi = P.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (P.work_off[mid] <= idx) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int cnt = P.counts[e];
+    const int ntile = (cnt + BN - 1) / BN;
+    const int local = idx - P.work_off[e];
+    m_tile = local / ntile;
+    const int n_tile = local % ntile;
+    R.tc.n0 = n_tile * BN;
+    R.tc.ncols = min(BN, cnt - R.tc.n0);
+    R.tc.slot_base = P.offsets[e];
+    wbase = P.w + static_cast<size_t>(e) * static_cast<size_t>(P.expert_stride);
+  } else {
+    const int ntile = (P.T + BN - 1) / BN;
+    m_tile = idx / ntile;
+    const int n_tile = idx % ntile;
+    R.tc.n0 = n_tile * BN;
+    R.tc.ncols = min(BN, P.T - R.tc.n0);
+    R.tc.slot_base = 0;
+  }
+  R.dbg_s = MODE == kDebug && m_tile == 0;
+  R.r0 = m_tile * kMmqBM + (threadIdx.x >> 6) * 32;
+  const int wrow = min(R.r0 + (threadIdx.x & 31), P.M - 1);
+  constexpr int kRowBytes = FMT == QMM_Q4_K ? kQ4Bytes : kQ6Bytes;
+  R.wr = wbase + static_cast<size_t>(wrow) * P.nb * kRowBytes;
+#pragma unroll
+  for (int r = 0; r < R.RX; ++r)
+    col_rows<MODE>(P, R.tc, (threadIdx.x + kMmqThreads * r) >> 3, R.xrow[r], R.orow[r], R.cvalid[r]);
+}
+
+// Next tile for this workgroup, or -1 (thread 0 only).  The tiles are split
+// into kXcds contiguous ranges with one counter each; a workgroup starts on
+// the range of its XCD (blockIdx % kXcds) and moves on when it is drained.
+__device__ __forceinline__ int claim_tile(const MmqParams& P, int total, int home, int& qi) {
+  for (; qi < kXcds; ++qi) {
+    const int q = (home + qi) % kXcds;
+    const int start = static_cast<int>((static_cast<int64_t>(total) * q) / kXcds);
+    const int size = static_cast<int>((static_cast<int64_t>(total) * (q + 1)) / kXcds) - start;
+    const unsigned c = atomicAdd(&P.counters[q], 1u);
+    if (c < static_cast<unsigned>(size)) return start + static_cast<int>(c);
+  }
+  return -1;
+}
+
+// Persistent loop over the tiles of the call, software-pipelined over
+// super-blocks: while super-block k is multiplied from LDS stage k&1, the
+// loads of super-block k+1 are in flight, across tile boundaries too (the
+// next tile is claimed one tile ahead).  One barrier per super-block: the
+// write of stage (k+1)&1 comes after the barrier of k, which every wave
+// passes only after finishing super-block k-1 from that stage.  Two waves
+// per SIMD are required: with one, nothing hides the MFMA and LDS latencies
+// of the epilogue.  (Q6_K with 64-column tiles then spills a few registers
+// to scratch, which costs less than one resident wave or 32-column tiles.)
 template <int FMT, int NT, int MODE>
 __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mmq_kernel(MmqParams P) {
   using L = MmqSmem<FMT, NT>;
   constexpr int BN = L::BN;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
-  __shared__ unsigned s_claim;
+  __shared__ int s_tile[2];
 
-  const int mt = (P.M + kMmqBM - 1) / kMmqBM;
   int total;
   if constexpr (MODE == kMoe) {
     total = P.work_off[P.E];
   } else {
-    total = mt * ((P.T + BN - 1) / BN);
+    total = ((P.M + kMmqBM - 1) / kMmqBM) * ((P.T + BN - 1) / BN);
   }
   const int home = static_cast<int>(blockIdx.x % kXcds);
-  for (int qi = 0; qi < kXcds; ++qi) {
-    const int q = (home + qi) % kXcds;
-    const int start = static_cast<int>((static_cast<int64_t>(total) * q) / kXcds);
-    const int size = static_cast<int>((static_cast<int64_t>(total) * (q + 1)) / kXcds) - start;
-    while (true) {
-      if (threadIdx.x == 0) s_claim = atomicAdd(&P.counters[q], 1u);
-      __syncthreads();
-      const unsigned c = s_claim;
-      __syncthreads();
-      if (c >= static_cast<unsigned>(size)) break;
-      const int idx = start + static_cast<int>(c);
-      TileCols tc;
-      int m_tile;
-      const uint8_t* wbase = P.w;
-      if constexpr (MODE == kMoe) {
-        int lo = 0, hi = P.E;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (P.work_off[mid] <= idx) lo = mid; else hi = mid;
+  int qi = 0;  // queue cursor, used by thread 0 only
+  if (threadIdx.x == 0) s_tile[0] = claim_tile(P, total, home, qi);
+  __syncthreads();
+  int cur = s_tile[0];
+  if (cur >= 0) {
+    if (threadIdx.x == 0) s_tile[1] = claim_tile(P, total, home, qi);  // read after the next barrier
+    const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31, wave = threadIdx.x >> 6;
+    const size_t xstride = static_cast<size_t>(P.nb) * 8 * kQ8Bytes;
+    v16i magic;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) magic[v] = static_cast<int>(kMagicBits);
+    TileRef<FMT, NT, MODE> R, Rn;
+    tile_ref<FMT, NT, MODE>(P, cur, R);
+    MmqPrefetch<FMT, NT> F;
+    mmq_load<FMT, NT>(P, F, R.xrow, xstride, R.wr, 0, g);
+    int k = 0;  // super-blocks done by this workgroup (selects the LDS stage)
+    for (int it = 0;; ++it) {
+      v16f acc[NT];
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[ct][v] = 0.0f;
+      int next = -1;
+      for (int sb = 0; sb < P.nb; ++sb, ++k) {
+        uint8_t* st = smem + (k & 1) * L::kStage;
+        mmq_commit<FMT, NT, MODE>(P, st, F, R.orow, R.cvalid, sb, wave, col, g, R.dbg_s);
+        MmqOperand<FMT> A;
+        take_operand<FMT, NT>(F, A);
+        __syncthreads();
+        if (sb + 1 < P.nb) {
+          mmq_load<FMT, NT>(P, F, R.xrow, xstride, R.wr, sb + 1, g);
+        } else {
+          next = s_tile[(it + 1) & 1];
+          if (next >= 0) {
+            tile_ref<FMT, NT, MODE>(P, next, Rn);
+            mmq_load<FMT, NT>(P, F, Rn.xrow, xstride, Rn.wr, 0, g);
+          }
         }
-        const int e = lo;
-        const int cnt = P.counts[e];
-        const int ntile = (cnt + BN - 1) / BN;
-        const int local = idx - P.work_off[e];
-        m_tile = local / ntile;
-        const int n_tile = local % ntile;
-        tc.n0 = n_tile * BN;
-        tc.ncols = min(BN, cnt - tc.n0);
-        tc.slot_base = P.offsets[e];
-        wbase = P.w + static_cast<size_t>(e) * static_cast<size_t>(P.expert_stride);
-      } else {
-        const int ntile = (P.T + BN - 1) / BN;
-        m_tile = idx / ntile;
-        const int n_tile = idx % ntile;
-        tc.n0 = n_tile * BN;
-        tc.ncols = min(BN, P.T - tc.n0);
-        tc.slot_base = 0;
+        mmq_compute<FMT, NT, MODE>(P, st, A, acc, magic, R.tc, R.r0, sb);
       }
-      mmq_tile<FMT, NT, MODE>(P, smem, wbase, m_tile * kMmqBM, tc, MODE == kDebug && m_tile == 0);
+      if constexpr (MODE != kDebug) store_tile<NT, MODE>(P, R.tc, R.r0, acc, P.y);
+      if (next < 0) break;
+      R = Rn;
+      // the slot written here was last read before the barriers of this tile
+      if (threadIdx.x == 0) s_tile[it & 1] = claim_tile(P, total, home, qi);
     }
   }
   // exit: the last workgroup out resets the queue counters for the next call
@@ -554,11 +605,24 @@ static int launch_mmq(const MmqParams& P, int total_tiles_hint, hipStream_t st) 
   return launch_status();
 }
 
-// Dense tiles: 128 rows x 64 tokens for both formats.
-template <int FMT>
-constexpr int kDenseNT = 2;
 constexpr int kMoeNT = 1;    // MoE tiles: 128 rows x 32 routed tokens
 constexpr size_t kCounterBytes = 256;
+
+// Dense tiles are 128 rows x 64 tokens, or 128 x 32 when there are very few
+// 64-token tiles.  (A 64-token tile per CU outruns two 32-token tiles per
+// CU: the A operand, row scales and epilogue set-up are shared by twice the
+// MFMAs.)
+constexpr int64_t kDenseMinTiles2 = 64;
+template <int FMT>
+static int mmq_dense_fmt(const MmqParams& P, bool dbg, hipStream_t st) {
+  const int64_t mt = (P.M + kMmqBM - 1) / kMmqBM;
+  const int64_t tiles2 = mt * ((P.T + 63) / 64);
+  if (tiles2 >= kDenseMinTiles2)
+    return dbg ? launch_mmq<FMT, 2, kDebug>(P, static_cast<int>(tiles2), st)
+               : launch_mmq<FMT, 2, kDense>(P, static_cast<int>(tiles2), st);
+  const int tiles1 = static_cast<int>(mt * ((P.T + 31) / 32));
+  return dbg ? launch_mmq<FMT, 1, kDebug>(P, tiles1, st) : launch_mmq<FMT, 1, kDense>(P, tiles1, st);
+}
 
 int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
               void* ws, hipStream_t st, int32_t* dbgD, int32_t* dbgS) {
@@ -573,15 +637,7 @@ int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64
   P.dbgD = dbgD;
   P.dbgS = dbgS;
   const bool dbg = dbgD != nullptr;
-  const int64_t mt = (M + kMmqBM - 1) / kMmqBM;
-  if (fmt == QMM_Q4_K) {
-    constexpr int NT = kDenseNT<QMM_Q4_K>;
-    const int tiles = static_cast<int>(mt * ((T + 32 * NT - 1) / (32 * NT)));
-    return dbg ? launch_mmq<QMM_Q4_K, NT, kDebug>(P, tiles, st) : launch_mmq<QMM_Q4_K, NT, kDense>(P, tiles, st);
-  }
-  constexpr int NT = kDenseNT<QMM_Q6_K>;
-  const int tiles = static_cast<int>(mt * ((T + 32 * NT - 1) / (32 * NT)));
-  return dbg ? launch_mmq<QMM_Q6_K, NT, kDebug>(P, tiles, st) : launch_mmq<QMM_Q6_K, NT, kDense>(P, tiles, st);
+  return fmt == QMM_Q4_K ? mmq_dense_fmt<QMM_Q4_K>(P, dbg, st) : mmq_dense_fmt<QMM_Q6_K>(P, dbg, st);
 }
 
 // Grouped launch used by moe_grouped_mmq (after route preparation on the
