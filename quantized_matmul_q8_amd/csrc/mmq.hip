@@ -445,9 +445,18 @@ struct TileRef {
   bool dbg_s;             // debug: this tile writes the activation sums
 };
 
+// MoE tables copied to LDS at kernel start: the tile search runs in LDS
+// instead of as a chain of dependent global loads.
+struct MoeTables {
+  const int* work_off;  // [E+1]
+  const int* counts;    // [E]
+  const int* offsets;   // [E]
+};
+
 // Tile idx of the call: rows, routed columns and weight matrix.
 template <int FMT, int NT, int MODE>
-__device__ __forceinline__ void tile_ref(const MmqParams& P, int idx, TileRef<FMT, NT, MODE>& R) {
+__device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb, int idx,
+                                         TileRef<FMT, NT, MODE>& R) {
   constexpr int BN = 32 * NT;
   int m_tile;
   const uint8_t* wbase = P.w;
@@ -455,17 +464,17 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, int idx, TileRef<FM
     int lo = 0, hi = P.E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (P.work_off[mid] <= idx) lo = mid; else hi = mid;
+      if (Tb.work_off[mid] <= idx) lo = mid; else hi = mid;
     }
     const int e = lo;
-    const int cnt = P.counts[e];
+    const int cnt = Tb.counts[e];
     const int ntile = (cnt + BN - 1) / BN;
-    const int local = idx - P.work_off[e];
+    const int local = idx - Tb.work_off[e];
     m_tile = local / ntile;
     const int n_tile = local % ntile;
     R.tc.n0 = n_tile * BN;
     R.tc.ncols = min(BN, cnt - R.tc.n0);
-    R.tc.slot_base = P.offsets[e];
+    R.tc.slot_base = Tb.offsets[e];
     wbase = P.w + static_cast<size_t>(e) * static_cast<size_t>(P.expert_stride);
   } else {
     const int ntile = (P.T + BN - 1) / BN;
@@ -501,43 +510,58 @@ __device__ __forceinline__ int claim_tile(const MmqParams& P, int total, int hom
 
 // Persistent loop over the tiles of the call, software-pipelined over
 // super-blocks: while super-block k is multiplied from LDS stage k&1, the
-// loads of super-block k+1 are in flight, across tile boundaries too (the
-// next tile is claimed one tile ahead).  One barrier per super-block: the
-// write of stage (k+1)&1 comes after the barrier of k, which every wave
-// passes only after finishing super-block k-1 from that stage.  Two waves
-// per SIMD are required: with one, nothing hides the MFMA and LDS latencies
-// of the epilogue.  (Q6_K with 64-column tiles then spills a few registers
-// to scratch, which costs less than one resident wave or 32-column tiles.)
+// loads of super-block k+1 are in flight, across tile boundaries too.  One
+// barrier per super-block: the write of stage (k+1)&1 comes after the
+// barrier of k, which every wave passes only after finishing super-block
+// k-1 from that stage.  Tiles are claimed two ahead: thread 0 issues the
+// claim of tile i+2 at the first super-block of tile i and publishes it in
+// a 3-slot ring at the end of tile i, so neither the atomic's latency nor
+// the next tile's set-up waits in front of a barrier.  Two waves per SIMD
+// are required: with one, nothing hides the MFMA and LDS latencies of the
+// epilogue.
 template <int FMT, int NT, int MODE>
 __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mmq_kernel(MmqParams P) {
   using L = MmqSmem<FMT, NT>;
   constexpr int BN = L::BN;
+  constexpr int kTab = MODE == kMoe ? kMoeMaxE + 1 : 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
-  __shared__ int s_tile[2];
+  __shared__ int s_tile[3];
+  __shared__ int s_work_off[kTab], s_counts[kTab], s_offsets[kTab];
 
+  MoeTables Tb{s_work_off, s_counts, s_offsets};
   int total;
   if constexpr (MODE == kMoe) {
+    for (int i = threadIdx.x; i <= P.E; i += kMmqThreads) {
+      s_work_off[i] = P.work_off[i];
+      if (i < P.E) {
+        s_counts[i] = P.counts[i];
+        s_offsets[i] = P.offsets[i];
+      }
+    }
     total = P.work_off[P.E];
   } else {
     total = ((P.M + kMmqBM - 1) / kMmqBM) * ((P.T + BN - 1) / BN);
   }
   const int home = static_cast<int>(blockIdx.x % kXcds);
   int qi = 0;  // queue cursor, used by thread 0 only
-  if (threadIdx.x == 0) s_tile[0] = claim_tile(P, total, home, qi);
+  if (threadIdx.x == 0) {
+    s_tile[0] = claim_tile(P, total, home, qi);
+    s_tile[1] = s_tile[0] >= 0 ? claim_tile(P, total, home, qi) : -1;
+  }
   __syncthreads();
   int cur = s_tile[0];
   if (cur >= 0) {
-    if (threadIdx.x == 0) s_tile[1] = claim_tile(P, total, home, qi);  // read after the next barrier
     const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31, wave = threadIdx.x >> 6;
     const size_t xstride = static_cast<size_t>(P.nb) * 8 * kQ8Bytes;
     v16i magic;
 #pragma unroll
     for (int v = 0; v < 16; ++v) magic[v] = static_cast<int>(kMagicBits);
     TileRef<FMT, NT, MODE> R, Rn;
-    tile_ref<FMT, NT, MODE>(P, cur, R);
+    tile_ref<FMT, NT, MODE>(P, Tb, cur, R);
     MmqPrefetch<FMT, NT> F;
     mmq_load<FMT, NT>(P, F, R.xrow, xstride, R.wr, 0, g);
-    int k = 0;  // super-blocks done by this workgroup (selects the LDS stage)
+    int k = 0;        // super-blocks done by this workgroup (selects the LDS stage)
+    int pending = -1;  // thread 0: claim in flight for tile it+2
     for (int it = 0;; ++it) {
       v16f acc[NT];
 #pragma unroll
@@ -551,22 +575,25 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 
         MmqOperand<FMT> A;
         take_operand<FMT, NT>(F, A);
         __syncthreads();
+        if (sb == 0) {
+          // tile it+1 was published before this barrier; its rows resolve
+          // under this tile's super-blocks
+          next = s_tile[(it + 1) % 3];
+          if (next >= 0) tile_ref<FMT, NT, MODE>(P, Tb, next, Rn);
+          if (threadIdx.x == 0) pending = next >= 0 ? claim_tile(P, total, home, qi) : -1;
+        }
         if (sb + 1 < P.nb) {
           mmq_load<FMT, NT>(P, F, R.xrow, xstride, R.wr, sb + 1, g);
-        } else {
-          next = s_tile[(it + 1) & 1];
-          if (next >= 0) {
-            tile_ref<FMT, NT, MODE>(P, next, Rn);
-            mmq_load<FMT, NT>(P, F, Rn.xrow, xstride, Rn.wr, 0, g);
-          }
+        } else if (next >= 0) {
+          mmq_load<FMT, NT>(P, F, Rn.xrow, xstride, Rn.wr, 0, g);
         }
         mmq_compute<FMT, NT, MODE>(P, st, A, acc, magic, R.tc, R.r0, sb);
       }
       if constexpr (MODE != kDebug) store_tile<NT, MODE>(P, R.tc, R.r0, acc, P.y);
       if (next < 0) break;
       R = Rn;
-      // the slot written here was last read before the barriers of this tile
-      if (threadIdx.x == 0) s_tile[it & 1] = claim_tile(P, total, home, qi);
+      // slot (it+2)%3 was last read at the first barrier of tile it-1
+      if (threadIdx.x == 0) s_tile[(it + 2) % 3] = pending;
     }
   }
   // exit: the last workgroup out resets the queue counters for the next call

@@ -12,10 +12,10 @@
 // Route preparation runs in one 1024-thread workgroup (4096 slots at
 // T = 512, top-8).  Buckets are stable (slots of an expert in increasing
 // order) without sorting: each of the 16 waves owns a contiguous slot range;
-// for 64 slots at a time, lanes with the same expert find each other with one
-// ballot per id bit, so a lane's rank among equal ids is a popcount.  Pass 1
-// counts per (wave, expert), a scan turns counts into offsets, pass 2 repeats
-// the ranking and writes every slot to its place.  It also writes the work
+// among 64 slots, lanes with the same expert find each other with one ballot
+// per id bit, so a lane's rank among equal ids is a popcount.  Pass 1 counts
+// per (wave, expert), wave scans turn counts into offsets, pass 2 repeats the
+// ranking and writes every slot to its place.  It also writes the work
 // prefix (m_tiles * ceil(count / 32) per expert) and zeroes the queue
 // counters that the grouped kernel claims tiles from.
 //
@@ -23,9 +23,10 @@
 // k with no atomics, so results are bit-reproducible.
 #include "qmm_common.hpp"
 
+#include <algorithm>
+
 namespace qmm {
 
-constexpr int kMoeMaxE = 512;
 constexpr int kMoeMaxTopK = 64;
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
@@ -81,12 +82,18 @@ __device__ __forceinline__ uint64_t peers_of(int e, bool v, int nbits) {
   return peers;
 }
 
+// Slots are ranked kRouteBatch x 64 at a time per wave; the ids of a batch
+// are loaded together, so a pass costs one memory round trip per batch
+// instead of one per 64 slots.
+constexpr int kRouteBatch = 8;
+
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     const int32_t* __restrict__ ids, int n, int E, int mt, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ work_off, int32_t* __restrict__ bucket,
     unsigned* __restrict__ counters) {
   __shared__ int cnt[kRouteWaves][kMoeMaxE];
-  __shared__ int s_off[kMoeMaxE];
+  __shared__ int s_off[kMoeMaxE + 1];
+  __shared__ int s_wsum[kMoeMaxE + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int i = tid; i < kRouteWaves * kMoeMaxE; i += kRouteThreads) (&cnt[0][0])[i] = 0;
   __syncthreads();
@@ -97,12 +104,20 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   // pass 1: per-(wave, expert) counts
-  for (int base = beg; base < end; base += 64) {
-    const int s = base + lane;
-    const int e = s < end ? ids[s] : -1;
-    const bool v = e >= 0 && e < E;
-    const uint64_t peers = peers_of(e, v, nbits);
-    if (v && __popcll(peers & below) == 0) cnt[wave][e] += __popcll(peers);
+  for (int base = beg; base < end; base += 64 * kRouteBatch) {
+    int ev[kRouteBatch];
+#pragma unroll
+    for (int r = 0; r < kRouteBatch; ++r) {
+      const int s = base + 64 * r + lane;
+      ev[r] = s < end ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kRouteBatch; ++r) {
+      const int e = ev[r];
+      const bool v = e >= 0 && e < E;
+      const uint64_t peers = peers_of(e, v, nbits);
+      if (v && __popcll(peers & below) == 0) cnt[wave][e] += __popcll(peers);
+    }
   }
   __syncthreads();
   // exclusive prefix over waves for each expert, per-expert totals
@@ -114,53 +129,94 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
       run += c;
     }
     counts[e] = run;
-    s_off[e] = run;  // total, turned into the offset below
+    s_off[e] = run;
+    s_wsum[e] = ((run + kMoeBN - 1) / kMoeBN) * mt;
   }
   __syncthreads();
-  if (tid == 0) {
+  // exclusive scans over experts (E <= 512 fits one wave's 8 passes)
+  if (wave == 0) {
     int off = 0, woff = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = s_off[e];
-      s_off[e] = off;
-      offsets[e] = off;
-      work_off[e] = woff;
-      off += c;
-      woff += ((c + kMoeBN - 1) / kMoeBN) * mt;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      int c = e < E ? s_off[e] : 0, wv = e < E ? s_wsum[e] : 0;
+      // inclusive wave scans
+      for (int d = 1; d < 64; d <<= 1) {
+        const int cu = __shfl_up(c, d), wu = __shfl_up(wv, d);
+        if (lane >= d) { c += cu; wv += wu; }
+      }
+      const int cx = __shfl_up(c, 1), wx = __shfl_up(wv, 1);
+      const int ce = lane == 0 ? 0 : cx, we = lane == 0 ? 0 : wx;
+      if (e < E) {
+        s_off[e] = off + ce;
+        offsets[e] = off + ce;
+        work_off[e] = woff + we;
+      }
+      off += __shfl(c, 63);
+      woff += __shfl(wv, 63);
     }
-    offsets[E] = off;
-    work_off[E] = woff;
+    if (lane == 0) {
+      offsets[E] = off;
+      work_off[E] = woff;
+    }
   }
   __syncthreads();
   // pass 2: stable scatter of slot ids
-  for (int base = beg; base < end; base += 64) {
-    const int s = base + lane;
-    const int e = s < end ? ids[s] : -1;
-    const bool v = e >= 0 && e < E;
-    const uint64_t peers = peers_of(e, v, nbits);
-    const int rank = __popcll(peers & below);
-    int prior = 0;
-    if (v) prior = cnt[wave][e];
-    if (v) bucket[s_off[e] + prior + rank] = s;
-    if (v && rank == 0) cnt[wave][e] = prior + __popcll(peers);
+  for (int base = beg; base < end; base += 64 * kRouteBatch) {
+    int ev[kRouteBatch];
+#pragma unroll
+    for (int r = 0; r < kRouteBatch; ++r) {
+      const int s = base + 64 * r + lane;
+      ev[r] = s < end ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kRouteBatch; ++r) {
+      const int s = base + 64 * r + lane;
+      const int e = ev[r];
+      const bool v = e >= 0 && e < E;
+      const uint64_t peers = peers_of(e, v, nbits);
+      const int rank = __popcll(peers & below);
+      int prior = 0;
+      if (v) prior = cnt[wave][e];
+      if (v) bucket[s_off[e] + prior + rank] = s;
+      if (v && rank == 0) cnt[wave][e] = prior + __popcll(peers);
+    }
   }
   if (tid <= kXcds) counters[tid] = 0u;
 }
 
+// One workgroup per (token, 1024-column chunk); each thread one float4 of
+// the output row (M % 4 == 0) or one float.  The slot weights of the token
+// are uniform over the workgroup.
+template <bool VEC>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ ys,
                                                           const float* __restrict__ p,
                                                           const int32_t* __restrict__ ids, int E,
-                                                          float* __restrict__ y, int T, int top_k,
-                                                          int M) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= static_cast<int64_t>(T) * M) return;
-  const int t = static_cast<int>(i / M), c = static_cast<int>(i % M);
-  float acc = 0.0f;
-  for (int k = 0; k < top_k; ++k) {
-    const int s = t * top_k + k;
-    const int e = ids[s];
-    if (e >= 0 && e < E) acc = __builtin_fmaf(p[s], ys[static_cast<int64_t>(s) * M + c], acc);
+                                                          float* __restrict__ y, int top_k, int M, int t0) {
+  const int t = t0 + static_cast<int>(blockIdx.y);
+  const int c = (blockIdx.x * 256 + threadIdx.x) * (VEC ? 4 : 1);
+  if (c >= M) return;
+  const size_t slot0 = static_cast<size_t>(t) * top_k;
+  if constexpr (VEC) {
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int k = 0; k < top_k; ++k) {
+      const int e = ids[slot0 + k];
+      if (e < 0 || e >= E) continue;
+      const float w = p[slot0 + k];
+      const float4 v = *reinterpret_cast<const float4*>(ys + (slot0 + k) * M + c);
+      acc.x = __builtin_fmaf(w, v.x, acc.x);
+      acc.y = __builtin_fmaf(w, v.y, acc.y);
+      acc.z = __builtin_fmaf(w, v.z, acc.z);
+      acc.w = __builtin_fmaf(w, v.w, acc.w);
+    }
+    *reinterpret_cast<float4*>(y + static_cast<size_t>(t) * M + c) = acc;
+  } else {
+    float acc = 0.0f;
+    for (int k = 0; k < top_k; ++k) {
+      const int e = ids[slot0 + k];
+      if (e >= 0 && e < E) acc = __builtin_fmaf(p[slot0 + k], ys[(slot0 + k) * M + c], acc);
+    }
+    y[static_cast<size_t>(t) * M + c] = acc;
   }
-  y[i] = acc;
 }
 
 }  // namespace qmm
@@ -199,9 +255,20 @@ extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int
                       L.counts, L.offsets, L.bucket, L.work_off, static_cast<int>(E),
                       static_cast<int>(top_k), static_cast<int>(x_rows_per_token), st);
   if (rc != QMM_OK || !expert_weights) return rc;
-  const int64_t total = T * M;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
-                     L.scratch, expert_weights, ids, static_cast<int>(E), y, static_cast<int>(T),
-                     static_cast<int>(top_k), static_cast<int>(M));
+  const bool vec = (M % 4) == 0;
+  const int per_block = vec ? 1024 : 256;
+  constexpr int64_t kMaxGridY = 65535;
+  for (int64_t t0 = 0; t0 < T; t0 += kMaxGridY) {
+    const dim3 grid(static_cast<unsigned>((M + per_block - 1) / per_block),
+                    static_cast<unsigned>(std::min(kMaxGridY, T - t0)));
+    if (vec)
+      hipLaunchKernelGGL(moe_combine_kernel<true>, grid, dim3(256), 0, st, L.scratch, expert_weights, ids,
+                         static_cast<int>(E), y, static_cast<int>(top_k), static_cast<int>(M), static_cast<int>(t0));
+    else
+      hipLaunchKernelGGL(moe_combine_kernel<false>, grid, dim3(256), 0, st, L.scratch, expert_weights, ids,
+                         static_cast<int>(E), y, static_cast<int>(top_k), static_cast<int>(M), static_cast<int>(t0));
+    rc = launch_status();
+    if (rc != QMM_OK) return rc;
+  }
   return launch_status();
 }

@@ -21,6 +21,7 @@ constexpr int kQ4Bytes = 144;  // Q4_K super-block bytes
 constexpr int kQ6Bytes = 210;  // Q6_K super-block bytes
 constexpr int kQ8Bytes = 40;   // Q8_1 block bytes
 constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, each with its own L2
+constexpr int kMoeMaxE = 512;  // experts per grouped MoE call
 
 // ----------------------------------------------------------------------------
 // Host side
