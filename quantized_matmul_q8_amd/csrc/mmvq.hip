@@ -18,9 +18,9 @@
 //   2p+1 plus the block header; Q6_K: one half-block quarter) are dealt
 //   round-robin to the 64 lanes, so a wave's loads cover consecutive row
 //   bytes;
-// * every lane issues ALL its weight loads of a chunk (up to kUnits units)
-//   before using any of them, so a wave has its whole row in flight at once;
-//   weight loads are non-temporal (each byte is used once);
+// * weight loads run a fixed number of rounds ahead of their use (Q4_K) or
+//   are all issued before use (Q6_K); weight loads are non-temporal (each
+//   byte is used once);
 // * the activations of all T tokens are staged once per workgroup into LDS
 //   as int8 payload plus, per 32-block, the fp32 scale and the activation
 //   sums of the block and of its two 16-halves (the ones dots, computed once
@@ -52,11 +52,29 @@ static int mmvq_chunk_blocks(int nb, int T, int units_per_block, int max_units) 
   return c < nb ? c : nb;
 }
 
-// Stage Q8_1 blocks [blk0, blk0 + nblk) of T tokens into LDS:
-// xs_q[t][32*j .. 32*j+31] int8 payload and xs_s[t][j] = (d, S, S_lo, S_hi):
-// fp32 scale, sum of the 32 values and of each 16-half.  The load is
-// unconditional (out-of-range threads re-read block 0) so that no branch
-// separates the staging loads from the weight loads that follow them.
+// Staged activations, in the order the lanes consume them (consecutive
+// lanes read consecutive 16-byte slots, so the reads are free of bank
+// conflicts).  Per token t and segment-local super-block bl, 384 bytes:
+// * Q4_K, value chunk v = 0..7 (pair p = v/2, half h = v%2), index
+//   i = (t*cb + bl)*8 + v in three arrays of 16-byte entries:
+//     A[i]  activations 16h .. 16h+15 of Q8_1 block 2p   (low-nibble sub-block)
+//     B[i]  the same of block 2p+1                        (high-nibble sub-block)
+//     Z[i]  (d, S_h) of block 2p, (d, S_h) of block 2p+1 (fp32; S_h the sum of
+//           the 16 activations, an integer dot against ones)
+// * Q6_K, unit u = 0..3 (half h = u/2 of the super-block, 16-half l = u%2),
+//   index i = (t*cb + bl)*4 + u in six arrays: P_g[i] (g = 0..3) the
+//   activations 16l .. 16l+15 of Q8_1 block 4h + g, Z01[i] and Z23[i] the
+//   (d, S_l) pairs of blocks 4h, 4h+1 and 4h+2, 4h+3.
+// Each array holds T*cb*8 (Q4_K) or T*cb*4 (Q6_K) entries.
+template <int FMT>
+__device__ __forceinline__ uint4* stage_array(uint8_t* lds, int T, int cb, int a) {
+  return reinterpret_cast<uint4*>(lds + static_cast<size_t>(a) * T * cb * (FMT == QMM_Q4_K ? 128 : 64));
+}
+
+// Load Q8_1 blocks [blk0, blk0 + nblk) of T tokens: this thread's r-th
+// block.  The load is unconditional (out-of-range threads re-read block 0)
+// so that no branch separates the staging loads from the weight loads that
+// follow them.
 __device__ __forceinline__ void stage_acts_load(const uint8_t* xq, size_t xstride, int T, int blk0,
                                                 int nblk, int r, uint2 (&u)[5], int& t, int& j) {
   const int bi = threadIdx.x + kMmvqThreads * r;
@@ -68,14 +86,14 @@ __device__ __forceinline__ void stage_acts_load(const uint8_t* xq, size_t xstrid
   for (int k = 0; k < 5; ++k) u[k] = src[k];
 }
 
-// Unconditional as well: threads past the end re-write block 0 of token 0
-// with the same bytes the owning thread writes.
-__device__ __forceinline__ void stage_acts_store(uint8_t* xs_q, float4* xs_s, int nblk, const uint2 (&u)[5],
-                                                 int t, int j) {
-  uint4* dq = reinterpret_cast<uint4*>(xs_q + (static_cast<size_t>(t) * nblk + j) * 32);
-  dq[0] = make_uint4(u[0].y, u[1].x, u[1].y, u[2].x);
-  dq[1] = make_uint4(u[2].y, u[3].x, u[3].y, u[4].x);
-  // activation sums as integer dots against ones ([8e] §2)
+// Store one loaded block into the staged layout.  Unconditional as well:
+// threads past the end re-write block 0 of token 0 with the same bytes the
+// owning thread writes.
+template <int FMT>
+__device__ __forceinline__ void stage_acts_store(uint8_t* lds, int T, int cb, const uint2 (&u)[5], int t, int j) {
+  const uint4 half0 = make_uint4(u[0].y, u[1].x, u[1].y, u[2].x);
+  const uint4 half1 = make_uint4(u[2].y, u[3].x, u[3].y, u[4].x);
+  // activation sums of the two 16-halves as integer dots against ones ([8e] §2)
   int lo = dot4(0x01010101u, u[0].y, 0);
   lo = dot4(0x01010101u, u[1].x, lo);
   lo = dot4(0x01010101u, u[1].y, lo);
@@ -84,8 +102,27 @@ __device__ __forceinline__ void stage_acts_store(uint8_t* xs_q, float4* xs_s, in
   hi = dot4(0x01010101u, u[3].x, hi);
   hi = dot4(0x01010101u, u[3].y, hi);
   hi = dot4(0x01010101u, u[4].x, hi);
-  xs_s[t * nblk + j] = make_float4(h2f(u[0].x & 0xffffu), static_cast<float>(lo + hi),
-                                   static_cast<float>(lo), static_cast<float>(hi));
+  const float d = h2f(u[0].x & 0xffffu);
+  const int bl = j >> 3, s = j & 7;
+  if constexpr (FMT == QMM_Q4_K) {
+    const int p = s >> 1, par = s & 1;
+    const size_t i0 = (static_cast<size_t>(t) * cb + bl) * 8 + 2 * p;  // value chunk v = 2p + h
+    uint4* X = stage_array<FMT>(lds, T, cb, par);
+    X[i0] = half0;
+    X[i0 + 1] = half1;
+    float2* Z = reinterpret_cast<float2*>(stage_array<FMT>(lds, T, cb, 2));
+    Z[2 * i0 + par] = make_float2(d, static_cast<float>(lo));
+    Z[2 * (i0 + 1) + par] = make_float2(d, static_cast<float>(hi));
+  } else {
+    const int h = s >> 2, g = s & 3;
+    const size_t i0 = (static_cast<size_t>(t) * cb + bl) * 4 + 2 * h;  // unit u = 2h + l
+    uint4* X = stage_array<FMT>(lds, T, cb, g);
+    X[i0] = half0;
+    X[i0 + 1] = half1;
+    float2* Z = reinterpret_cast<float2*>(stage_array<FMT>(lds, T, cb, 4 + (g >> 1)));
+    Z[2 * i0 + (g & 1)] = make_float2(d, static_cast<float>(lo));
+    Z[2 * (i0 + 1) + (g & 1)] = make_float2(d, static_cast<float>(hi));
+  }
 }
 
 // Q4_K rows are read as plain consecutive 16-byte chunks: lane l loads
@@ -95,11 +132,25 @@ __device__ __forceinline__ void stage_acts_store(uint8_t* xs_q, float4* xs_s, in
 // 25-40% more time for the same bytes).  A 144-byte block is exactly nine
 // chunks: chunk 0 is the header (d, dmin, packed scales), chunk 1 + 2p + h
 // holds value bytes 16 + 32p + 16h .. +15, i.e. 16 weights of sub-block 2p
-// (low nibbles) and 16 of sub-block 2p + 1 (high nibbles).  Rounds are
-// consumed in load order; in each round the header chunks are written to a
-// per-wave LDS slot and the value chunks read their block's header from it
-// (headers precede their values, and one wave's LDS accesses are ordered).
+// (low nibbles) and 16 of sub-block 2p + 1 (high nibbles).
+//
+// Rounds are consumed in load order.  In a round, header chunks are copied
+// to a per-wave ring of 16 block slots in LDS; then the (at most eight)
+// headers that arrived in this round are decoded by all 64 lanes at once,
+// lane l taking sub-block l % 8 of the (l / 8)-th of them, into a ring of
+// (d*sc, dmin*m) pairs; then each value chunk reads its two pairs with one
+// 16-byte LDS read.  Every scale is thus decoded once per row instead of
+// once per chunk, with no divergent decode path.  A block's header precedes
+// its values and a value chunk's header lies in the same or the previous
+// round (64 chunks > 9), so at most 15 blocks are live and 16 slots never
+// collide; one wave's LDS accesses execute in program order.
 constexpr int kQ4Rounds = 7;  // chunks per lane per segment (7 x 64 = 448 >= 43 blocks x 9)
+constexpr int kQ4Ring = 16;   // block slots per wave in the header and scale rings
+// Rounds in flight ahead of the one being consumed.  Issuing every round up
+// front buys no memory parallelism (a CU's miss queue fills and the issue
+// stalls) and delays the activation staging, which waits for all waves of
+// the workgroup; two rounds ahead keep the queue full while computing.
+constexpr int kQ4Ahead = 2;
 
 // DEBUG == true: write the integer sub-block sums (D per (t, row, sub-block),
 // S per (t, sub-block) from row 0) instead of the scaled result.  Same
@@ -117,9 +168,12 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w
   const int row = row_ok ? row_raw : M - 1;  // out-of-range waves load a valid row, store nothing
   const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ4Bytes;
   const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
-  uint8_t* xs_q = lds;
-  float4* xs_s = reinterpret_cast<float4*>(lds + static_cast<size_t>(T) * cb * 8 * 32);
-  uint4* hdr_s = reinterpret_cast<uint4*>(lds + static_cast<size_t>(T) * cb * 8 * 48) + wave * cb;
+  const uint4* stA = stage_array<QMM_Q4_K>(lds, T, cb, 0);
+  const uint4* stB = stage_array<QMM_Q4_K>(lds, T, cb, 1);
+  const float4* stZ = reinterpret_cast<const float4*>(stage_array<QMM_Q4_K>(lds, T, cb, 2));
+  uint8_t* rings = lds + static_cast<size_t>(T) * cb * 8 * 48 + static_cast<size_t>(wave) * kQ4Ring * 80;
+  uint4* hdr_ring = reinterpret_cast<uint4*>(rings);                  // [16] raw headers
+  float2* sc_ring = reinterpret_cast<float2*>(rings + kQ4Ring * 16);  // [16][8] (d*sc, dmin*m)
   constexpr int RS = (T * 64 * 8 + kMmvqThreads - 1) / kMmvqThreads;  // staging rounds bound
   float acc[T];
 #pragma unroll
@@ -138,64 +192,77 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w
     const uint8_t* seg = wrow + static_cast<size_t>(b0) * kQ4Bytes;
     uint4 v[kQ4Rounds];
 #pragma unroll
-    for (int r = 0; r < kQ4Rounds; ++r) v[r] = ld16_nt(seg + 16 * min(lane + 64 * r, nch - 1));
+    for (int r = 0; r < kQ4Ahead; ++r) v[r] = ld16_nt(seg + 16 * min(lane + 64 * r, nch - 1));
     __builtin_amdgcn_sched_barrier(0);
     // 3. publish the activations
     __syncthreads();  // previous segment's LDS reads are done
 #pragma unroll
-    for (int r = 0; r < RS; ++r) stage_acts_store(xs_q, xs_s, nblk, su[r], st[r], sj[r]);
+    for (int r = 0; r < RS; ++r) stage_acts_store<QMM_Q4_K>(lds, T, cb, su[r], st[r], sj[r]);
+    if constexpr (DEBUG) {
+      if (blockIdx.x == 0) {
+#pragma unroll
+        for (int r = 0; r < RS; ++r)
+          dbgS[static_cast<size_t>(st[r]) * nb * 8 + b0 * 8 + sj[r]] = static_cast<int>(su[r][4].y);
+      }
+    }
     __syncthreads();
     // 4. consume the rounds in load order
+    int bl = lane / 9, k = lane - 9 * (lane / 9);  // block and chunk-in-block of chunk lane + 64 r
 #pragma unroll
     for (int r = 0; r < kQ4Rounds; ++r) {
-      const int c = lane + 64 * r;
+      if (r + kQ4Ahead < kQ4Rounds) {
+        v[r + kQ4Ahead] = ld16_nt(seg + 16 * min(lane + 64 * (r + kQ4Ahead), nch - 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (64 * r >= nch) break;                 // uniform: round entirely past the segment
-      const int bl = c / 9, k = c - 9 * bl;     // block within segment, chunk within block
-      if (c < nch && k == 0) hdr_s[bl] = v[r];  // header chunk
-      if (c < nch && k != 0) {
-        const uint4 hdr = hdr_s[bl];
+      const bool ok = lane + 64 * r < nch;
+      if (ok && k == 0) hdr_ring[bl % kQ4Ring] = v[r];  // header chunk
+      {
+        // headers of blocks (64r + 8) / 9 .. (64r + 63) / 9 arrived in this round
+        const int bd = (64 * r + 8) / 9 + (lane >> 3), jd = lane & 7;
+        if (bd <= (64 * r + 63) / 9 && bd < nbc) {
+          const uint4 hdr = hdr_ring[bd % kQ4Ring];
+          int sc, m;
+          q4k_scale_min(jd, hdr.y, hdr.z, hdr.w, sc, m);
+          sc_ring[(bd % kQ4Ring) * 8 + jd] =
+              make_float2(h2f(hdr.x & 0xffffu) * static_cast<float>(sc), h2f(hdr.x >> 16) * static_cast<float>(m));
+        }
+      }
+      if (ok && k != 0) {
         const int p = (k - 1) >> 1, h = (k - 1) & 1;
-        int sc0, m0, sc1, m1;
-        q4k_scale_min(2 * p, hdr.y, hdr.z, hdr.w, sc0, m0);
-        q4k_scale_min(2 * p + 1, hdr.y, hdr.z, hdr.w, sc1, m1);
-        const float d = h2f(hdr.x & 0xffffu), dmin = h2f(hdr.x >> 16);
-        const float ds0 = d * static_cast<float>(sc0), dm0 = dmin * static_cast<float>(m0);
-        const float ds1 = d * static_cast<float>(sc1), dm1 = dmin * static_cast<float>(m1);
+        const float4 dsm = *reinterpret_cast<const float4*>(sc_ring + (bl % kQ4Ring) * 8 + 2 * p);
+        const float ds0 = dsm.x, dm0 = dsm.y, ds1 = dsm.z, dm1 = dsm.w;
         const uint32_t qw[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-        const int j0 = bl * 8 + 2 * p;  // segment-local Q8_1 block of sub-block 2p (2p+1 follows)
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          const uint8_t* xb = xs_q + (static_cast<size_t>(t) * nblk + j0) * 32 + 16 * h;
-          const uint4 xa = *reinterpret_cast<const uint4*>(xb);       // 16 activations of 2p
-          const uint4 xc = *reinterpret_cast<const uint4*>(xb + 32);  // 16 activations of 2p+1
+          const size_t i = (static_cast<size_t>(t) * cb + bl) * 8 + (k - 1);
+          const uint4 xa = stA[i];  // 16 activations of sub-block 2p
+          const uint4 xc = stB[i];  // 16 activations of sub-block 2p+1
+          const float4 z = stZ[i];  // (d, S_h) of 2p, (d, S_h) of 2p+1
           const uint32_t x0[4] = {xa.x, xa.y, xa.z, xa.w};
           const uint32_t x1[4] = {xc.x, xc.y, xc.z, xc.w};
-          const float4 s0 = xs_s[t * nblk + j0], s1 = xs_s[t * nblk + j0 + 1];  // (d, S, S_lo, S_hi)
           int D0 = 0, D1 = 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            D0 = dot4(qw[i] & 0x0f0f0f0fu, x0[i], D0);         // sub-block 2p: low nibbles
-            D1 = dot4((qw[i] >> 4) & 0x0f0f0f0fu, x1[i], D1);  // sub-block 2p+1: high nibbles
+          for (int i4 = 0; i4 < 4; ++i4) {
+            D0 = dot4(qw[i4] & 0x0f0f0f0fu, x0[i4], D0);         // sub-block 2p: low nibbles
+            D1 = dot4((qw[i4] >> 4) & 0x0f0f0f0fu, x1[i4], D1);  // sub-block 2p+1: high nibbles
           }
-          // activation sum of the 16 weights' half, from the staged ones dots
-          const float S0 = h ? s0.w : s0.z, S1 = h ? s1.w : s1.z;
           if constexpr (DEBUG) {
             if (row_ok) {
-              const int sb0 = b0 * 8 + j0;
+              const int sb0 = b0 * 8 + bl * 8 + 2 * p;
               int32_t* Dt = dbgD + (static_cast<size_t>(t) * M + row) * (nb * 8);
               atomicAdd(Dt + sb0, D0);
               atomicAdd(Dt + sb0 + 1, D1);
-              if (row == 0 && h == 0) {
-                dbgS[static_cast<size_t>(t) * nb * 8 + sb0] = static_cast<int>(s0.y);
-                dbgS[static_cast<size_t>(t) * nb * 8 + sb0 + 1] = static_cast<int>(s1.y);
-              }
             }
           } else {
-            acc[t] += s0.x * (ds0 * static_cast<float>(D0) - dm0 * S0) +
-                      s1.x * (ds1 * static_cast<float>(D1) - dm1 * S1);
+            acc[t] += z.x * (ds0 * static_cast<float>(D0) - dm0 * z.y) +
+                      z.z * (ds1 * static_cast<float>(D1) - dm1 * z.w);
           }
         }
       }
+      // chunk lane + 64 (r + 1): 64 = 7 * 9 + 1
+      bl += 7;
+      if (++k == 9) { k = 0; ++bl; }
     }
   }
   if constexpr (!DEBUG) {
@@ -234,8 +301,6 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q6k_kernel(const uint8_t* w
   const int row = row_ok ? row_raw : M - 1;
   const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ6Bytes;
   const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
-  uint8_t* xs_q = lds;
-  float4* xs_s = reinterpret_cast<float4*>(lds + static_cast<size_t>(T) * cb * 8 * 32);
   constexpr int RS = (T * 64 * 8 + kMmvqThreads - 1) / kMmvqThreads;
   float acc[T];
 #pragma unroll
@@ -266,7 +331,7 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q6k_kernel(const uint8_t* w
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < RS; ++r) stage_acts_store(xs_q, xs_s, nblk, su[r], st[r], sj[r]);
+    for (int r = 0; r < RS; ++r) stage_acts_store<QMM_Q6_K>(lds, T, cb, su[r], st[r], sj[r]);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kQ6Units; ++i) {
@@ -295,23 +360,25 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q6k_kernel(const uint8_t* w
       }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
+        const size_t ix = (static_cast<size_t>(t) * cb + bl) * 4 + c;
+        const float4 z01 = reinterpret_cast<const float4*>(stage_array<QMM_Q6_K>(lds, T, cb, 4))[ix];
+        const float4 z23 = reinterpret_cast<const float4*>(stage_array<QMM_Q6_K>(lds, T, cb, 5))[ix];
+        const float zd[4] = {z01.x, z01.z, z23.x, z23.z}, zs[4] = {z01.y, z01.w, z23.y, z23.w};
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int jl = bl * 8 + 4 * h + g;  // chunk-local Q8_1 block holding these weights
-          const uint4 xv = *reinterpret_cast<const uint4*>(xs_q + (static_cast<size_t>(t) * nblk + jl) * 32 + l0);
-          const float4 sv = xs_s[t * nblk + jl];  // (d, S, S_lo, S_hi)
+          const uint4 xv = stage_array<QMM_Q6_K>(lds, T, cb, g)[ix];  // activations of block 4h+g, half l
           int D = dot4(q6[g][0], xv.x, 0);
           D = dot4(q6[g][1], xv.y, D);
           D = dot4(q6[g][2], xv.z, D);
           D = dot4(q6[g][3], xv.w, D);
           // sum (q6 - 32) * q = D - 32 * S_half, exact in fp32 (|.| < 2^24)
-          const float D6 = static_cast<float>(D) - 32.0f * (half16 ? sv.w : sv.z);
+          const float D6 = static_cast<float>(D) - 32.0f * zs[g];
           if constexpr (DEBUG) {
             if (row_ok)
-              dbgD[(static_cast<size_t>(t) * M + row) * (nb * 16) + (b0 * 8 + jl) * 2 + half16] =
+              dbgD[(static_cast<size_t>(t) * M + row) * (nb * 16) + (b0 * 8 + bl * 8 + 4 * h + g) * 2 + half16] =
                   static_cast<int>(D6);
           } else {
-            acc[t] += sv.x * dsc[g] * D6;
+            acc[t] += zd[g] * dsc[g] * D6;
           }
         }
       }
@@ -334,7 +401,7 @@ static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int n
   // segment: whole blocks whose 9 chunks fit kQ4Rounds rounds, within the LDS budget
   const int cb = mmvq_chunk_blocks(nb, T, 9, kQ4Rounds);
   const dim3 grid((M + kMmvqWaves - 1) / kMmvqWaves), block(kMmvqThreads);
-  const size_t lds = mmvq_lds_bytes(T, cb) + static_cast<size_t>(kMmvqWaves) * cb * 16;
+  const size_t lds = mmvq_lds_bytes(T, cb) + static_cast<size_t>(kMmvqWaves) * kQ4Ring * 80;
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const uint8_t* xp = static_cast<const uint8_t*>(xq);
   switch (T) {
