@@ -127,9 +127,8 @@ struct MmqPrefetch {
 
 // 8 bytes at p (2-byte aligned) from three raw aligned dwords and the shift.
 __device__ __forceinline__ void raw8_load(const uint8_t* p, uint32_t (&r)[3], uint32_t& sh) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const uint32_t* base = reinterpret_cast<const uint32_t*>(a & ~static_cast<uintptr_t>(3));
-  sh = static_cast<uint32_t>(a & 3u);
+  sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(p - sh);  // stays a global pointer
   r[0] = base[0];
   r[1] = base[1];
   r[2] = sh ? base[2] : 0u;  // only when misaligned: never reads past p + 8 otherwise

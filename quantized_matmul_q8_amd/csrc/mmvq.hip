@@ -277,9 +277,8 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w
 // 8 bytes from a 2-byte aligned address inside a block (third dword read only
 // when misaligned, so nothing past p + 8 is touched otherwise).
 __device__ __forceinline__ uint2 ld8_a2(const uint8_t* p) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const uint32_t* base = reinterpret_cast<const uint32_t*>(a & ~static_cast<uintptr_t>(3));
-  const uint32_t sh = static_cast<uint32_t>(a & 3u);
+  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(p - sh);
   const uint32_t w0 = base[0], w1 = base[1];
   const uint32_t w2 = sh ? base[2] : 0u;
   return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));

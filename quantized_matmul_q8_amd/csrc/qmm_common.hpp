@@ -68,10 +68,12 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
 // byte funnel shift.  Q6_K blocks are 210 bytes, so every other block starts
 // at 2 mod 4.  The fifth dword is read only when the address is misaligned,
 // so nothing past p + 16 is touched for aligned addresses.
+// The aligned base is formed by pointer arithmetic on p (not through an
+// integer), so the loads keep p's global address space instead of becoming
+// flat loads (which also count against the LDS wait counter).
 __device__ __forceinline__ uint4 ld16_a2(const uint8_t* p) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const uint32_t* base = reinterpret_cast<const uint32_t*>(a & ~static_cast<uintptr_t>(3));
-  const uint32_t sh = static_cast<uint32_t>(a & 3u);
+  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(p - sh);
   const uint32_t w0 = base[0], w1 = base[1], w2 = base[2], w3 = base[3];
   const uint32_t w4 = sh ? base[4] : 0u;
   return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
