@@ -98,13 +98,16 @@ int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int6
  * T >= 1 ([MMQ] "Kernel architecture": fused dequant inside the matrix
  * inner loop, Q8_1 activations; "Persistent kernel + atomic work queue").
  * Weights are unpacked to int8 and multiplied on int8 MFMA with int32
- * accumulation per sub-block, then scaled in fp32.  Output tiles are claimed
- * from per-XCD atomic counters in `ws`; each tile runs its whole K loop in one
- * workgroup (no split-K, no fixup), so results are deterministic.
- * `ws` must hold qmm_workspace_bytes(QMM_OP_MMQ, ...) bytes and be zero-filled
- * before its first use (qmm_workspace_init); every call leaves it zeroed.
+ * accumulation per sub-block, then scaled in fp32.  A first kernel repacks
+ * the Q8_1 activations into `ws` (MFMA operand order plus per-block fp32
+ * factors); output tiles are then claimed from per-XCD atomic counters in
+ * `ws`; each tile runs its whole K loop in one workgroup (its two K halves
+ * summed in a fixed order, no split across workgroups, no fixup), so results
+ * are deterministic.  `ws` must hold
+ * qmm_workspace_bytes(QMM_OP_MMQ, M, K, T, 0, 0) bytes; its contents are
+ * scratch (the call initialises what it uses, no zero-fill is needed).
  * Calls sharing one workspace must be ordered on one stream.
- * Requires M >= 1, T >= 1, K % 256 == 0.
+ * Requires M >= 1, 1 <= T <= 2^24, K % 256 == 0, K/256 <= 65536.
  */
 int mmq_q4k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
             void* ws, size_t ws_bytes, void* stream);
@@ -128,8 +131,10 @@ int mmq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64
  *                        y[t*M + i] = sum_k p[t][k] * (W[ids[t][k]] . x_row)
  *                        summed in increasing k (deterministic, no atomics)
  *   ws                   qmm_workspace_bytes(QMM_OP_MOE, M, K, T, E, top_k)
- *                        bytes; holds the buckets, the queue counters and, in
- *                        weighted mode, the per-slot fp32 results
+ *                        bytes of scratch (no initialisation needed); holds
+ *                        the buckets, the queue counters, the routed rows
+ *                        repacked per expert and, in weighted mode, the
+ *                        per-slot fp32 results
  * Work is tiled as 128 weight rows x 32 routed slots of one expert, so an
  * expert's weights are read once per 32 tokens routed to it.  Requires
  * 1 <= E <= 512, M >= 1, K % 256 == 0, 1 <= top_k <= min(E, 64), T >= 1,
@@ -155,7 +160,9 @@ int swiglu_q8_1(const float* g_u, void* hq, int64_t R, int64_t F, void* stream);
  * sizes; unused sizes may be 0.  Returns 0 for an unknown op. */
 size_t qmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k);
 
-/* Zero-fills a workspace on `stream` with a fill kernel (no memset node). */
+/* Zero-fills a workspace on `stream` with a fill kernel (no memset node).
+ * Not required by any entry point (each initialises the workspace state it
+ * uses); kept for callers that want deterministic workspace contents. */
 int qmm_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a qmm_status value. */

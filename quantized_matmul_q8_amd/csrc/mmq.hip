@@ -2,256 +2,251 @@
 // for many tokens, Q4_K or Q6_K weights against Q8_1 activations, on int8
 // MFMA with int32 accumulation per sub-block and an fp32 epilogue.
 //
-// Prior art: [MMQ] "Kernel architecture" (128x128 tiles of weights x tokens,
-// dequant fused into the matrix inner loop, Q8_1 activations, persistent
-// workgroups claiming tiles from an atomic counter instead of Stream-K plus a
-// fixup pass, MoE work entries (expert, m_tile, n_tile)); [GAP] root cause 1
-// and lever T1; [8e] §2 for the min-term factorisation.  Re-designed for
-// gfx950 as follows.
+// Prior art: [MMQ] "Kernel architecture" (tiles of weights x tokens, dequant
+// fused into the matrix inner loop, Q8_1 activations, persistent workgroups
+// claiming tiles from an atomic counter instead of Stream-K plus a fixup
+// pass, MoE work entries (expert, m_tile, n_tile)); [GAP] root cause 1 and
+// lever T1; [8e] §2 for the min-term factorisation.  Re-designed for gfx950:
 //
-// * Matrix core.  One v_mfma_i32_32x32x32_i8 covers exactly one 32-weight
-//   Q4_K sub-block of 32 rows x 32 tokens: A = unpacked 4-bit values (0..15),
-//   B = the Q8_1 int8 values, int32 result D per (row, token, sub-block).  Q6_K
-//   has 16-weight sub-blocks and uses v_mfma_i32_32x32x16_i8 per sub-block,
-//   with the unsigned 6-bit values as A.
-// * Epilogue.  Every (row i, token j, sub-block s) has its own factor
-//   alpha_is * beta_js (weight scale d*sc, activation scale d_x), so each
-//   MFMA result is rescaled before the next sub-block.  The MFMA accumulator
-//   starts at the bit pattern of 1.5*2^23; since |D| < 2^22 the int32 result
-//   read as fp32 is exactly 1.5*2^23 + D.  Then
+// * Activation repack.  A pre-pass turns the Q8_1 rows of every 32-column
+//   tile (tokens; for MoE the routed slots of one expert, gathered through
+//   the bucket) into one chunk per super-block: the int8 values in MFMA
+//   B-operand order (sub-block s, 16-value half h, column), then per (s,
+//   column) the fp32 pair (beta, -beta*C) of the epilogue and beta*S of the
+//   min term.  The main kernel then copies whole chunks from global memory
+//   straight into LDS (global_load_lds_dwordx4: no registers, no VALU), so
+//   staging costs a few instructions per super-block.
+// * Matrix core.  One v_mfma_i32_32x32x32_i8 covers one 32-weight Q4_K
+//   sub-block of 32 rows x 32 columns: A = unpacked 4-bit values (0..15),
+//   B = the Q8_1 int8 values, int32 result D per (row, column, sub-block).
+//   Q6_K has 16-weight sub-blocks and uses v_mfma_i32_32x32x16_i8 with the
+//   signed values q6 - 32 as A.
+// * Epilogue.  Every (row i, column j, sub-block s) has its own factor
+//   alpha_is * beta_js, so each MFMA result is rescaled before the next
+//   sub-block.  The MFMA accumulator starts at the bits of 1.5*2^23; since
+//   |D| < 2^22 the int32 result read as fp32 is exactly 1.5*2^23 + D, and
 //     t   = fma(beta, X, -beta*1.5*2^23)   = beta*D, rounded once
 //     acc = fma(alpha, t, acc)
-//   i.e. two fp32 VALU ops per output element per sub-block, no conversion.
-// * Min term.  sum_s (-dmin*m_is) * (beta_js*S_js) is a small GEMM over the
-//   sub-block index; it runs on v_mfma_f32_32x32x2_f32 straight into the fp32
-//   accumulator (Q6_K: the -32 offset of the signed values, the same way).
-// * Work queue.  Persistent grid; tiles are split into 8 contiguous ranges,
-//   one per XCD (workgroup b runs on XCD b % 8), each with its own atomic
-//   counter, so the weight rows of a range stay in one XCD's L2.  A workgroup
-//   that drains its range helps the others.  Tiles run their whole K loop in
-//   one workgroup: no split-K, no fixup, deterministic results.  The last
-//   workgroup to leave resets the counters, so the workspace is zero again
-//   for the next call without a memset.
+//   is two fp32 VALU ops per output element per sub-block.  The Q4_K min
+//   term sum_s (-dmin*m_is) * (beta_js*S_js) runs on v_mfma_f32_32x32x2_f32
+//   straight into the accumulator.
+// * Workgroup.  Eight waves (two per SIMD, which the VALU-bound epilogue
+//   needs to reach the issue rate): a tile of 128 rows x 32*NT columns, row
+//   group rw = wave % 4 (32 rows), K half kh = wave / 4 taking the
+//   super-blocks of parity kh.  The two halves are summed through LDS at the
+//   end of the tile, in a fixed order.  One barrier per step of two
+//   super-blocks; the next step's chunks and weight bytes are in flight
+//   during the current step (double-buffered LDS, register prefetch).
+// * Work queue.  Persistent grid, one workgroup per CU; tiles are split into
+//   8 contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), each
+//   with its own atomic counter, so a range's weight rows stay in one XCD's
+//   L2.  A workgroup's first tile is fixed by its index; later tiles are
+//   claimed one ahead, with the atomic's latency hidden under the current
+//   tile.  Tiles run their whole K loop in one workgroup: no split across
+//   workgroups, no fixup, deterministic results.  The kernel that runs just
+//   before on the stream (activation repack, route preparation) zeroes the
+//   counters, so the workspace needs no initialisation and no memset.
 #include "qmm_common.hpp"
 
 #include <type_traits>
 
 namespace qmm {
 
-constexpr int kMmqThreads = 256;       // 4 waves
-constexpr int kMmqBM = 128;            // weight rows per tile (32 per wave)
+constexpr int kMmqWaves = 8;
+constexpr int kMmqThreads = 64 * kMmqWaves;
+constexpr int kMmqBM = 128;            // weight rows per tile (32 per row group)
 constexpr uint32_t kMagicBits = 0x4B400000u;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+
+// Repacked activation chunk: 32 columns x one super-block (8 Q8_1 blocks).
+constexpr int kChunkCols = 32;
+constexpr int kChunkPay = 0;       // [8 s][2 h][32 col] x 16 bytes: values 16h .. 16h+15 of block s
+constexpr int kChunkFac = 8192;    // [8 s][32 col] float2 (beta, -beta*C)
+constexpr int kChunkSig = 10240;   // [8 s][32 col] float beta*S
+constexpr int kChunkBytes = 11264; // 11 x 1 KB
+constexpr int kChunkKB = kChunkBytes / 1024;
 
 enum MmqMode { kDense = 0, kMoe = 1, kDebug = 2 };
 
 struct MmqParams {
   const uint8_t* w;
-  const uint8_t* xq;
+  const uint8_t* xr;            // repacked chunks: (ctile, sb) at (ctile * nb + sb) * kChunkBytes
   float* y;
-  int M, nb, T;                 // rows, super-blocks per row, tokens (dense)
-  unsigned* counters;           // kXcds queue counters, then the exit counter
+  int M, nb, T;                 // rows, super-blocks per row, columns (dense)
+  unsigned* counters;           // kXcds work-queue counters (zero at kernel start)
   // MoE (mode kMoe)
   const int32_t* counts;        // [E] routed slots per expert
   const int32_t* offsets;       // [E+1] slot offsets into bucket
   const int32_t* bucket;        // [T*top_k] slots grouped by expert
-  const int32_t* work_off;      // [E+1] prefix of (m_tiles * n_tiles(e))
-  int E, top_k, rows_per_token;
+  const int32_t* work_off;      // [E+1] prefix of m_tiles * column tiles
+  const int32_t* ct_off;        // [E+1] prefix of column tiles (chunk rows)
+  int E;
   int64_t expert_stride;
   // debug (mode kDebug)
   int32_t* dbgD;
-  int32_t* dbgS;
 };
 
-// LDS of one pipeline stage (two stages are used, double-buffered).
-// Activation payload: for each Q8_1 block s of the super-block, the 32 int8
-// values of every column are cut into pieces (Q4_K 2 x 16 bytes: one MFMA
-// k-group each; Q6_K 4 x 8 bytes) and piece k of all columns is one
-// contiguous run, so the MFMA operand reads of 32 consecutive columns are
-// consecutive.  Rows of s are padded by 32 bytes so that the commit stores
-// (8 lanes = the 8 blocks of one token, next 8 lanes = next token) of any
-// 16 lanes (16-byte pieces) or 32 lanes (8-byte pieces) fall on distinct
-// banks; reads stay a per-lane base plus immediate offsets.
-template <int FMT, int NT>
-struct MmqSmem {
-  static constexpr int BN = 32 * NT;
-  static constexpr int NS16 = FMT == QMM_Q4_K ? 8 : 16;     // scale groups per super-block
-  static constexpr int kPiece = FMT == QMM_Q4_K ? 16 : 8;    // payload bytes per piece
-  static constexpr int kXqRow = 32 * BN + 32;               // bytes per block row s
-  static constexpr int kXbRow = BN + 4;                      // float2 per block row
-  static constexpr int kXsRow = BN + 8;                      // floats per beta*S row
-  static constexpr int kXq = 0;                              // [8][32/kPiece][BN][kPiece] int8 payload
-  static constexpr int kXb = kXq + 8 * kXqRow;               // [8][kXbRow] (beta, -beta*C)
-  static constexpr int kXs = kXb + 8 * kXbRow * 8;           // Q4_K: [8][kXsRow] beta*S
-  static constexpr int kWa = kXs + (FMT == QMM_Q4_K ? 8 * kXsRow * 4 : 0);  // [4 waves][NS16][32] alpha = d*sc
-  static constexpr int kWm = kWa + 4 * NS16 * 32 * 4;        // Q4_K: [4][8][32] -dmin*m
-  static constexpr int kStage = (kWm + (FMT == QMM_Q4_K ? 4 * 8 * 32 * 4 : 0) + 15) & ~15;
-  static constexpr int kBytes = 2 * kStage;
-};
-
-// Token (activation row, output row) of column j of a tile.  Dense: token
-// n0 + j (clamped for loads).  MoE: the j-th routed slot of the tile.
-struct TileCols {
-  int n0, ncols;      // first column, valid columns
-  int slot_base;      // MoE: offset of the expert's slots in bucket
+// ----------------------------------------------------------------------------
+// Activation repack: one workgroup per (super-block sb, column tile); thread
+// (s = tid / 32, col = tid % 32) converts block (row of col, 8 sb + s).
+// ----------------------------------------------------------------------------
+struct RepackParams {
+  const uint8_t* xq;
+  uint8_t* xr;
+  int nb;                       // super-blocks per row
+  int T;                        // dense: rows
+  // MoE: column tile -> (expert, slots)
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* bucket;
+  const int32_t* ct_off;
+  int E, top_k, rows_per_token;
+  int32_t* dbgS;                // dense debug: S[row][K/32]
+  unsigned* counters;           // dense: work-queue counters, zeroed here for the GEMM that follows
 };
 
 template <int MODE>
-__device__ __forceinline__ void col_rows(const MmqParams& P, const TileCols& tc, int j, int& xrow,
-                                         int& orow, bool& valid) {
-  const int jj = min(j, tc.ncols - 1);
-  valid = j < tc.ncols;
+__global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
+  const int sb = blockIdx.x, ctile = blockIdx.y;
+  const int s = threadIdx.x >> 5, col = threadIdx.x & 31;
+  if (P.counters != nullptr && sb == 0 && ctile == 0 && threadIdx.x < kXcds) P.counters[threadIdx.x] = 0u;
+  int xrow = 0, ncols;
   if constexpr (MODE == kMoe) {
-    const int slot = P.bucket[tc.slot_base + tc.n0 + jj];
-    xrow = P.rows_per_token == 1 ? slot / P.top_k : slot;
-    orow = slot;
+    if (ctile >= P.ct_off[P.E]) return;
+    int lo = 0, hi = P.E;  // expert e with ct_off[e] <= ctile < ct_off[e+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (P.ct_off[mid] <= ctile) lo = mid; else hi = mid;
+    }
+    const int n0 = (ctile - P.ct_off[lo]) * kChunkCols;
+    ncols = min(kChunkCols, P.counts[lo] - n0);
+    if (col < ncols) {
+      const int slot = P.bucket[P.offsets[lo] + n0 + col];
+      xrow = P.rows_per_token == 1 ? slot / P.top_k : slot;
+    }
   } else {
-    xrow = tc.n0 + jj;
-    orow = xrow;
+    ncols = min(kChunkCols, P.T - ctile * kChunkCols);
+    xrow = ctile * kChunkCols + col;
   }
+  uint2 u[5];
+  if (col < ncols) {
+    const uint2* src = reinterpret_cast<const uint2*>(
+        P.xq + static_cast<size_t>(xrow) * P.nb * 8 * kQ8Bytes + static_cast<size_t>(sb * 8 + s) * kQ8Bytes);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) u[k] = src[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 5; ++k) u[k] = make_uint2(0u, 0u);
+  }
+  uint8_t* ch = P.xr + (static_cast<size_t>(ctile) * P.nb + sb) * kChunkBytes;
+  uint4* pay = reinterpret_cast<uint4*>(ch + kChunkPay);
+  pay[(2 * s) * 32 + col] = make_uint4(u[0].y, u[1].x, u[1].y, u[2].x);      // q[0..15]
+  pay[(2 * s + 1) * 32 + col] = make_uint4(u[2].y, u[3].x, u[3].y, u[4].x);  // q[16..31]
+  const float beta = h2f(u[0].x & 0xffffu);
+  const int S = static_cast<int>(u[4].y);
+  reinterpret_cast<float2*>(ch + kChunkFac)[s * 32 + col] = make_float2(beta, -beta * kMagic);
+  reinterpret_cast<float*>(ch + kChunkSig)[s * 32 + col] = beta * static_cast<float>(S);
+  // debug: the stored sums, Q4_K only (the Q6_K hook passes no S buffer)
+  if (MODE == kDebug && P.dbgS != nullptr && col < ncols)
+    P.dbgS[static_cast<size_t>(xrow) * P.nb * 8 + sb * 8 + s] = S;
 }
 
-// Registers holding one super-block's global data between its loads and
-// its commit to LDS (the software pipeline's in-flight stage).
+// ----------------------------------------------------------------------------
+// Main kernel
+// ----------------------------------------------------------------------------
+// How a step is split between the two K halves (wave groups) of a
+// workgroup.  Q4_K: a step is two super-blocks; half kh takes super-block
+// 2*step + kh (its 8 sub-blocks).  Q6_K: a step is one super-block; half kh
+// takes its elements 128kh .. 128kh+127, i.e. MFMA sub-blocks 8kh .. 8kh+7
+// (half the weight bytes per wave, so the 64-column tile fits the register
+// budget).  Either way a wave multiplies 8 MFMA sub-blocks per step.
+template <int FMT>
+struct StepSplit {
+  static constexpr int kSbPerStep = FMT == QMM_Q4_K ? 2 : 1;
+  static constexpr int kNU = 8;                        // MFMA sub-blocks per wave per step
+  static constexpr int kSubsPerSb = FMT == QMM_Q4_K ? 8 : 16;
+  __device__ __forceinline__ static int sb(int step, int kh) { return FMT == QMM_Q4_K ? 2 * step + kh : step; }
+  __device__ __forceinline__ static int u0(int kh) { return FMT == QMM_Q4_K ? 0 : 8 * kh; }   // first sub-block
+  __device__ __forceinline__ static int chunk_half(int kh) { return FMT == QMM_Q4_K ? kh : 0; }
+  static int nsteps(int nb) { return FMT == QMM_Q4_K ? (nb + 1) / 2 : nb; }
+};
+
 template <int FMT, int NT>
-struct MmqPrefetch {
-  static constexpr int RX = 32 * NT * 8 / kMmqThreads;  // Q8_1 blocks staged per thread
-  uint2 xu[RX][5];                                      // raw 40-byte activation blocks
-  // Q4_K: header and the 4 x 16 value bytes of this lane's row and k-group
-  uint4 hdr;
-  uint4 q[4];
-  // Q6_K: per (half h, 16-group hf): qh bytes; per (h, parity, hf): ql bytes
-  // (8 bytes each as raw aligned dwords + shift), scales of this k-group, d
-  uint32_t qh_raw[2][2][3], ql_raw[2][2][2][3], sc_raw[3], d_raw, sh;
+struct MmqSmem {
+  static constexpr int kChunks = StepSplit<FMT>::kSbPerStep * NT * kChunkBytes;  // [half][ct] chunks
+  static constexpr int kRed = 4 * NT * 16 * 64 * 4;                             // split-K reduction
+  static constexpr int kStage = kChunks > kRed ? kChunks : kRed;
+  static constexpr int kWave = (8 * 32 + (FMT == QMM_Q4_K ? 8 * 32 : 0)) * 4;  // alpha (+ -dmin*m), 8 sub-blocks
+  static constexpr int kWaveOff = 2 * kStage;
+  static constexpr int kBytes = kWaveOff + kMmqWaves * kWave;
+};
+
+// Registers holding one super-block's weight bytes between their loads and
+// their use (the software pipeline's in-flight stage).
+template <int FMT>
+struct MmqPrefetch;
+template <>
+struct MmqPrefetch<QMM_Q4_K> {
+  uint4 hdr;   // d, dmin, packed scales
+  uint4 q[4];  // bytes 16 + 32p + 16g .. +15: nibbles of sub-blocks 2p, 2p+1 for this lane's k-group
+};
+template <>
+struct MmqPrefetch<QMM_Q6_K> {
+  // this wave's half of the super-block: per 16-group hf its qh bytes, per
+  // (parity, hf) its ql bytes (8 bytes each as raw aligned dwords + shift),
+  // the 4 scales this lane decodes (two 2-byte loads), d
+  uint32_t qh_raw[2][3], ql_raw[2][2][3], sc_lo, sc_hi, d_raw, sh;
 };
 
 // 8 bytes at p (2-byte aligned) from three raw aligned dwords and the shift.
+// The third dword is always read (no divergent branch): callers only use it
+// for pieces that end at least 4 bytes before the end of their block.
 __device__ __forceinline__ void raw8_load(const uint8_t* p, uint32_t (&r)[3], uint32_t& sh) {
   sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
   const uint32_t* base = reinterpret_cast<const uint32_t*>(p - sh);  // stays a global pointer
   r[0] = base[0];
   r[1] = base[1];
-  r[2] = sh ? base[2] : 0u;  // only when misaligned: never reads past p + 8 otherwise
+  r[2] = base[2];
 }
 __device__ __forceinline__ uint2 raw8_join(const uint32_t (&r)[3], uint32_t sh) {
   return make_uint2(__builtin_amdgcn_alignbyte(r[1], r[0], sh), __builtin_amdgcn_alignbyte(r[2], r[1], sh));
 }
 
-// Issue the global loads of super-block sb (activations of the tile's
-// columns, this lane's weight bytes) into registers.
-template <int FMT, int NT>
-__device__ __forceinline__ void mmq_load(const MmqParams& P, MmqPrefetch<FMT, NT>& F, const int* xrow,
-                                         size_t xstride, const uint8_t* wr, int sb, int g) {
-#pragma unroll
-  for (int r = 0; r < MmqPrefetch<FMT, NT>::RX; ++r) {
-    const int s = (threadIdx.x + kMmqThreads * r) & 7;
-    const uint2* src = reinterpret_cast<const uint2*>(P.xq + static_cast<size_t>(xrow[r]) * xstride +
-                                                      static_cast<size_t>(sb * 8 + s) * kQ8Bytes);
-#pragma unroll
-    for (int k = 0; k < 5; ++k) F.xu[r][k] = src[k];
-  }
-  if constexpr (FMT == QMM_Q4_K) {
-    const uint8_t* blk = wr + static_cast<size_t>(sb) * kQ4Bytes;
-    F.hdr = ld16_a16(blk);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) F.q[p] = ld16_a16(blk + 16 + 32 * p + 16 * g);
-  } else {
-    const uint8_t* blk = wr + static_cast<size_t>(sb) * kQ6Bytes;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        raw8_load(blk + 128 + 32 * h + 16 * hf + 8 * g, F.qh_raw[h][hf], F.sh);
-#pragma unroll
-        for (int par = 0; par < 2; ++par)
-          raw8_load(blk + 64 * h + 32 * par + 16 * hf + 8 * g, F.ql_raw[h][par][hf], F.sh);
-      }
-    raw8_load(blk + 192 + 8 * g, F.sc_raw, F.sh);
-    F.d_raw = ld_u16(blk + 208);
-  }
-}
 
-// Write super-block sb's prefetched data to LDS stage `st`: activation
-// payload, (beta, -beta*C), beta*S, and this wave's decoded weight scales.
-template <int FMT, int NT, int MODE>
-__device__ __forceinline__ void mmq_commit(const MmqParams& P, uint8_t* st, const MmqPrefetch<FMT, NT>& F,
-                                           const int* orow, const bool* cvalid, int sb, int wave, int col,
-                                           int g, bool write_dbg_s) {
-  using L = MmqSmem<FMT, NT>;
-  constexpr int BN = L::BN;
+// Weight bytes of super-block sb for this lane (row wr, k-group g), one
+// load slot at a time.
+//   Q4_K: slot 0 the header (d, dmin, packed scales), slots 1..4 the 16
+//   value bytes 16 + 32p + 16g of pair p = u - 1.
+//   Q6_K (half kh of the block): slots 0..5 the 8-byte pieces of 16-group hf:
+//   qh, then ql of parity 0 and 1; slot 6 the 4 scales this lane decodes;
+//   slot 7 d.
+__device__ __forceinline__ void load_weight_slot(MmqPrefetch<QMM_Q4_K>& F, const uint8_t* wr, int sb, int g,
+                                                 int u, int /*kh: whole block*/) {
+  const uint8_t* blk = wr + static_cast<size_t>(sb) * kQ4Bytes;
+  if (u == 0) F.hdr = ld16_a16(blk);
 #pragma unroll
-  for (int r = 0; r < MmqPrefetch<FMT, NT>::RX; ++r) {
-    const int bi = threadIdx.x + kMmqThreads * r;
-    const int j = bi >> 3, s = bi & 7;
-    const uint2* u = F.xu[r];  // u[0].x = d and pad, u[0].y .. u[4].x = q[0..31], u[4].y = S
-    uint8_t* dq = st + L::kXq + s * L::kXqRow;
-    if constexpr (FMT == QMM_Q4_K) {
-      reinterpret_cast<uint4*>(dq)[j] = make_uint4(u[0].y, u[1].x, u[1].y, u[2].x);
-      reinterpret_cast<uint4*>(dq + 16 * BN)[j] = make_uint4(u[2].y, u[3].x, u[3].y, u[4].x);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        reinterpret_cast<uint2*>(dq + 8 * BN * k)[j] = make_uint2(u[k].y, u[k + 1].x);  // q[8k .. 8k+7]
-    }
-    const float beta = h2f(u[0].x & 0xffffu);
-    reinterpret_cast<float2*>(st + L::kXb)[s * L::kXbRow + j] = make_float2(beta, -beta * kMagic);
-    if constexpr (FMT == QMM_Q4_K) {
-      const int S = static_cast<int>(u[4].y);
-      reinterpret_cast<float*>(st + L::kXs)[s * L::kXsRow + j] = beta * static_cast<float>(S);
-      if (MODE == kDebug && write_dbg_s && cvalid[r])
-        P.dbgS[static_cast<size_t>(orow[r]) * P.nb * 8 + sb * 8 + s] = S;
-    }
-  }
-  float* wa_w = reinterpret_cast<float*>(st + L::kWa) + wave * L::NS16 * 32;
-  if constexpr (FMT == QMM_Q4_K) {
-    // lane (row col, half g) decodes sub-blocks 4g .. 4g+3 of its row
-    const float d = h2f(F.hdr.x & 0xffffu), dmin = h2f(F.hdr.x >> 16);
-    float* wm_w = reinterpret_cast<float*>(st + L::kWm) + wave * 8 * 32;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      int sc, m;
-      q4k_scale_min(4 * g + jj, F.hdr.y, F.hdr.z, F.hdr.w, sc, m);
-      wa_w[(4 * g + jj) * 32 + col] = d * static_cast<float>(sc);
-      wm_w[(4 * g + jj) * 32 + col] = -(dmin * static_cast<float>(m));
-    }
-  } else {
-    // lane (row col, half g) holds scales 8g .. 8g+7 of its row
-    const float d = h2f(F.d_raw);
-    const uint2 sc8 = raw8_join(F.sc_raw, F.sh);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t word = q < 4 ? sc8.x : sc8.y;
-      wa_w[(8 * g + q) * 32 + col] = d * static_cast<float>(static_cast<int8_t>((word >> (8 * (q & 3))) & 0xffu));
-    }
-  }
+  for (int p = 0; p < 4; ++p)
+    if (u == p + 1) F.q[p] = ld16_a16(blk + 16 + 32 * p + 16 * g);
 }
-
-// Store a wave's 32 x (32*NT) fp32 tile.  acc[ct][v] holds row
-// 8*(v/4) + 4*(lane/32) + v%4 of the wave's rows and column ct*32 + lane%32.
-template <int NT, int MODE>
-__device__ __forceinline__ void store_tile(const MmqParams& P, const TileCols& tc, int r0,
-                                           const v16f (&acc)[NT], float* out) {
-  const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
+__device__ __forceinline__ void load_weight_slot(MmqPrefetch<QMM_Q6_K>& F, const uint8_t* wr, int sb, int g,
+                                                 int u, int kh) {
+  // half kh of the block: qh bytes 128 + 32kh + 16hf + 8g, ql bytes
+  // 64kh + 32par + 16hf + 8g (each piece ends by byte 192, so the raw loads'
+  // extra dword stays inside the 210-byte block), scales 192 + 8kh + 4g
+  // (4 of them), d at 208
+  const uint8_t* blk = wr + static_cast<size_t>(sb) * kQ6Bytes;
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct) {
-    int xrow, orow;
-    bool valid;
-    col_rows<MODE>(P, tc, ct * 32 + col, xrow, orow, valid);
-    if (!valid) continue;
-    float* yr = out + static_cast<size_t>(orow) * P.M;
+  for (int hf = 0; hf < 2; ++hf) {
+    if (u == 3 * hf) raw8_load(blk + 128 + 32 * kh + 16 * hf + 8 * g, F.qh_raw[hf], F.sh);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int row = r0 + 8 * k + 4 * g;
-      if ((P.M & 3) == 0 && row + 3 < P.M) {
-        *reinterpret_cast<float4*>(yr + row) =
-            make_float4(acc[ct][4 * k], acc[ct][4 * k + 1], acc[ct][4 * k + 2], acc[ct][4 * k + 3]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (row + r < P.M) yr[row + r] = acc[ct][4 * k + r];
-      }
-    }
+    for (int par = 0; par < 2; ++par)
+      if (u == 3 * hf + 1 + par) raw8_load(blk + 64 * kh + 32 * par + 16 * hf + 8 * g, F.ql_raw[par][hf], F.sh);
   }
+  if (u == 6) {
+    F.sc_lo = ld_u16(blk + 192 + 8 * kh + 4 * g);
+    F.sc_hi = ld_u16(blk + 194 + 8 * kh + 4 * g);
+  }
+  if (u == 7) F.d_raw = ld_u16(blk + 208);
 }
 
 // A operand bytes of one super-block for this lane (row col of the wave's
@@ -261,28 +256,48 @@ template <int FMT>
 struct MmqOperand;
 template <>
 struct MmqOperand<QMM_Q4_K> {
-  uint4 q[4];  // bytes 16 + 32p + 16g .. +15 of the block: nibbles of sub-blocks 2p, 2p+1
+  uint4 q[4];
 };
 template <>
 struct MmqOperand<QMM_Q6_K> {
-  uint2 ql[2][2][2], qh[2][2];  // [h][parity][16-half] low-nibble bytes, [h][16-half] high-bit bytes
+  uint2 ql[2][2], qh[2];  // this half's [parity][16-half] low-nibble bytes, [16-half] high-bit bytes
 };
 
-template <int FMT, int NT>
-__device__ __forceinline__ void take_operand(const MmqPrefetch<FMT, NT>& F, MmqOperand<FMT>& A) {
-  if constexpr (FMT == QMM_Q4_K) {
+__device__ __forceinline__ void take_operand(const MmqPrefetch<QMM_Q4_K>& F, MmqOperand<QMM_Q4_K>& A) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) A.q[p] = F.q[p];
-  } else {
+  for (int p = 0; p < 4; ++p) A.q[p] = F.q[p];
+}
+__device__ __forceinline__ void take_operand(const MmqPrefetch<QMM_Q6_K>& F, MmqOperand<QMM_Q6_K>& A) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+  for (int hf = 0; hf < 2; ++hf) {
+    A.qh[hf] = raw8_join(F.qh_raw[hf], F.sh);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        A.qh[h][hf] = raw8_join(F.qh_raw[h][hf], F.sh);
-#pragma unroll
-        for (int par = 0; par < 2; ++par) A.ql[h][par][hf] = raw8_join(F.ql_raw[h][par][hf], F.sh);
-      }
+    for (int par = 0; par < 2; ++par) A.ql[par][hf] = raw8_join(F.ql_raw[par][hf], F.sh);
   }
+}
+
+// Decoded weight scales of this wave's rows to the wave's LDS region:
+// alpha[u][row] = d*sc and, for Q4_K, mu[j][row] = -dmin*m.
+__device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q4_K>& F, float* wave_lds, int col, int g) {
+  // lane (row col, half g) decodes sub-blocks 4g .. 4g+3 of its row
+  const float d = h2f(F.hdr.x & 0xffffu), dmin = h2f(F.hdr.x >> 16);
+  float* wa = wave_lds;
+  float* wm = wave_lds + 8 * 32;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    int sc, m;
+    q4k_scale_min(4 * g + jj, F.hdr.y, F.hdr.z, F.hdr.w, sc, m);
+    wa[(4 * g + jj) * 32 + col] = d * static_cast<float>(sc);
+    wm[(4 * g + jj) * 32 + col] = -(dmin * static_cast<float>(m));
+  }
+}
+__device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q6_K>& F, float* wave_lds, int col, int g) {
+  // lane (row col, k-group g) holds scales 8kh + 4g .. +3 of its row: local sub-blocks 4g .. 4g+3
+  const float d = h2f(F.d_raw);
+  const uint32_t word = F.sc_lo | (F.sc_hi << 16);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    wave_lds[(4 * g + q) * 32 + col] = d * static_cast<float>(static_cast<int8_t>((word >> (8 * q)) & 0xffu));
 }
 
 // LDS operands of one MFMA sub-block u for this lane: the 16 row scales
@@ -297,38 +312,35 @@ struct SubOps {
   float am, bm[NT];
 };
 
-// u indexes MFMA sub-blocks: Q4_K u = the 32-weight sub-block (= Q8_1 block);
-// Q6_K u = 2*s + hf, 16-weight group hf of Q8_1 block s.
+// u indexes MFMA sub-blocks of the super-block: Q4_K u = the 32-weight
+// sub-block (= Q8_1 block); Q6_K u = 2*s + hf, 16-weight group hf of Q8_1
+// block s.  ul = u - (first sub-block of this wave's half) indexes the
+// wave's scale region wl; st = this half's chunks ([ct] x kChunkBytes).
 template <int FMT, int NT>
-__device__ __forceinline__ void load_sub(const uint8_t* st, int u, SubOps<FMT, NT>& O) {
-  using L = MmqSmem<FMT, NT>;
-  constexpr int BN = L::BN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
+__device__ __forceinline__ void load_sub(const uint8_t* st, const float* wl, int u, int ul, SubOps<FMT, NT>& O) {
+  const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
   const int s = FMT == QMM_Q4_K ? u : u >> 1;
-  // B operand: piece g (Q4_K: k-group g of the 32 values) or quarter 2*hf+g (Q6_K)
-  const uint8_t* xq = st + L::kXq + s * L::kXqRow + L::kPiece * col;
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
+    const uint8_t* ch = st + ct * kChunkBytes;
     if constexpr (FMT == QMM_Q4_K)
-      O.bq[ct] = *reinterpret_cast<const v4i*>(xq + 16 * BN * g + 16 * 32 * ct);
+      O.bq[ct] = *reinterpret_cast<const v4i*>(ch + kChunkPay + ((2 * s + g) * 32 + col) * 16);
     else
-      O.bq[ct] = *reinterpret_cast<const long*>(xq + 8 * BN * (2 * (u & 1) + g) + 8 * 32 * ct);
+      O.bq[ct] = *reinterpret_cast<const long*>(ch + kChunkPay + ((2 * s + (u & 1)) * 32 + col) * 16 + 8 * g);
+    O.bp[ct] = reinterpret_cast<const float2*>(ch + kChunkFac)[s * 32 + col];
   }
-  const float* wa = reinterpret_cast<const float*>(st + L::kWa) + wave * L::NS16 * 32 + u * 32 + 4 * g;
+  const float* wa = wl + ul * 32 + 4 * g;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const float4 t4 = *reinterpret_cast<const float4*>(wa + 8 * k);
     O.al[4 * k] = t4.x; O.al[4 * k + 1] = t4.y; O.al[4 * k + 2] = t4.z; O.al[4 * k + 3] = t4.w;
   }
-  const float2* xb = reinterpret_cast<const float2*>(st + L::kXb) + s * L::kXbRow + col;
-#pragma unroll
-  for (int ct = 0; ct < NT; ++ct) O.bp[ct] = xb[32 * ct];
   if constexpr (FMT == QMM_Q4_K) {
     if (u & 1) {
-      O.am = reinterpret_cast<const float*>(st + L::kWm)[wave * 8 * 32 + (u - 1 + g) * 32 + col];
-      const float* xs = reinterpret_cast<const float*>(st + L::kXs) + (u - 1 + g) * L::kXsRow + col;
+      O.am = wl[8 * 32 + (u - 1 + g) * 32 + col];
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) O.bm[ct] = xs[32 * ct];
+      for (int ct = 0; ct < NT; ++ct)
+        O.bm[ct] = reinterpret_cast<const float*>(st + ct * kChunkBytes + kChunkSig)[(u - 1 + g) * 32 + col];
     }
   }
 }
@@ -346,10 +358,11 @@ __device__ __forceinline__ v4i build_a(const MmqOperand<QMM_Q4_K>& A, int u) {
 }
 constexpr uint32_t kQ6HiTable = 0x1000F0E0u;  // bytes -32, -16, 0, 16 as int8
 __device__ __forceinline__ long build_a(const MmqOperand<QMM_Q6_K>& A, int u) {
+  // u in this wave's half: its half h is implied by the operand bytes taken
   const int s = u >> 1, hf = u & 1;
-  const int h = s >> 2, gg = s & 3, par = gg & 1, shl = 4 * (gg >> 1), shh = 2 * gg;
-  const uint2 lq = A.ql[h][par][hf];
-  const uint2 hq = A.qh[h][hf];
+  const int gg = s & 3, par = gg & 1, shl = 4 * (gg >> 1), shh = 2 * gg;
+  const uint2 lq = A.ql[par][hf];
+  const uint2 hq = A.qh[hf];
   const uint32_t q0 = ((lq.x >> shl) & 0x0f0f0f0fu) |
                       __builtin_amdgcn_perm(kQ6HiTable, kQ6HiTable, (hq.x >> shh) & 0x03030303u);
   const uint32_t q1 = ((lq.y >> shl) & 0x0f0f0f0fu) |
@@ -364,84 +377,131 @@ __device__ __forceinline__ v16i mfma_sub(long a, long b, const v16i& c) {
   return __builtin_amdgcn_mfma_i32_32x32x16_i8(a, b, c, 0, 0, 0);
 }
 
-// Multiply-accumulate super-block sb from LDS stage st.  Software pipeline
-// over sub-blocks: the LDS operands of sub-block u+1 are read while u is
-// rescaled, and the MFMA of (u+1, column tile ct) is issued right after the
-// epilogue of (u, ct) has consumed its registers, so the matrix core runs
-// under the epilogue of the next column tile.  The epilogue adds
-// alpha * beta * D into acc (2 VALU ops per element); the Q4_K min term
-// goes through fp32 MFMAs into the same accumulator.  Q6_K has no separate
-// term: its A operand is already signed.
-template <int FMT, int NT, int MODE>
-__device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* st, const MmqOperand<FMT>& A,
-                                            v16f (&acc)[NT], const v16i& magic,
-                                            const TileCols& tc, int r0, int sb) {
-  constexpr int NU = FMT == QMM_Q4_K ? 8 : 16;  // MFMA sub-blocks per super-block
-  const int g = (threadIdx.x & 63) >> 5, col = threadIdx.x & 31;
-  SubOps<FMT, NT> O[2];
-  v16i X[NT];
-  load_sub<FMT, NT>(st, 0, O[0]);
-  {
-    const auto a0 = build_a(A, 0);
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) X[ct] = mfma_sub(a0, O[0].bq[ct], magic);
+// Token (output row) of column j of a tile, and whether it is valid.
+struct TileCols {
+  int n0, ncols;      // first column (dense) or first routed slot index (MoE), valid columns
+  int slot_base;      // MoE: offset of the expert's slots in bucket
+};
+
+template <int MODE>
+__device__ __forceinline__ int col_out_row(const MmqParams& P, const TileCols& tc, int j, bool& valid) {
+  valid = j < tc.ncols;
+  if constexpr (MODE == kMoe) {
+    return valid ? P.bucket[tc.slot_base + tc.n0 + j] : 0;
+  } else {
+    return tc.n0 + j;
   }
+}
+
+// Epilogue of (sub-block u of the step, column tile ct): acc += alpha *
+// beta * D, and for Q4_K every second sub-block the min term.  Debug mode
+// writes the integer sums D instead.
+template <int FMT, int NT, int MODE>
+__device__ __forceinline__ void mmq_epilogue(const MmqParams& P, const TileCols& tc, int r0, int sb, int ub, int u,
+                                             int ct, const v16i& Xc, const SubOps<FMT, NT>& Ou, v16f (&acc)[NT]) {
+  if constexpr (MODE == kDebug) {
+    constexpr int NSB = StepSplit<FMT>::kSubsPerSb;
+    const int g = (threadIdx.x & 63) >> 5, col = threadIdx.x & 31;
+    bool ok;
+    const int orr = col_out_row<MODE>(P, tc, ct * 32 + col, ok);
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int b = u & 1;
-    const bool more = u + 1 < NU;
-    if (more) load_sub<FMT, NT>(st, u + 1, O[b ^ 1]);
-    const auto an = build_a(A, more ? u + 1 : u);
-    // scheduling barriers pin the order: operand reads of u+1 first, then
-    // per column tile its epilogue followed by its next MFMA (left to
-    // itself the compiler sinks the reads behind the epilogue and exposes
-    // the LDS latency)
-    __builtin_amdgcn_sched_barrier(0);
+    for (int v = 0; v < 16; ++v) {
+      const int row = r0 + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (ok && row < P.M)
+        P.dbgD[(static_cast<size_t>(orr) * P.M + row) * (P.nb * NSB) + sb * NSB + ub + u] =
+            Xc[v] - static_cast<int>(kMagicBits);
+    }
+  } else {
+    // the whole vector is reinterpreted: X holds 1.5*2^23 + D as fp32 bits
+    const v16f Xf = __builtin_bit_cast(v16f, Xc);
+    const float2 bp = Ou.bp[ct];
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      if constexpr (MODE == kDebug) {
-        int xr, orr; bool ok;
-        col_rows<MODE>(P, tc, ct * 32 + col, xr, orr, ok);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = r0 + 8 * (v >> 2) + 4 * g + (v & 3);
-          if (ok && row < P.M)
-            P.dbgD[(static_cast<size_t>(orr) * P.M + row) * (P.nb * NU) + sb * NU + u] =
-                X[ct][v] - static_cast<int>(kMagicBits);
-        }
-      } else {
-        // the whole vector is reinterpreted: X holds 1.5*2^23 + D as fp32 bits
-        const v16f Xf = __builtin_bit_cast(v16f, X[ct]);
-        const float2 bp = O[b].bp[ct];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
-          acc[ct][v] = __builtin_fmaf(O[b].al[v], t, acc[ct][v]);
-        }
-      }
-      if constexpr (FMT == QMM_Q4_K && MODE != kDebug) {
-        // min term, K = 2 fp32 MFMA over sub-blocks u-1, u (lane half g
-        // takes u-1+g): A[i][k] = -dmin*m, B[k][j] = beta*S.  The next VALU
-        // write of acc[ct] comes one column tile later, under which it runs.
-        if (u & 1) acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(O[b].am, O[b].bm[ct], acc[ct], 0, 0, 0);
-      }
-      if (more) X[ct] = mfma_sub(an, O[b ^ 1].bq[ct], magic);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int v = 0; v < 16; ++v) {
+      const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
+      acc[ct][v] = __builtin_fmaf(Ou.al[v], t, acc[ct][v]);
+    }
+    if constexpr (FMT == QMM_Q4_K) {
+      // min term, K = 2 fp32 MFMA over sub-blocks u-1, u (lane half g
+      // takes u-1+g): A[i][k] = -dmin*m, B[k][j] = beta*S
+      if (u & 1) acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ou.am, Ou.bm[ct], acc[ct], 0, 0, 0);
     }
   }
 }
 
-// Per-thread addressing of one tile: the activation rows this thread stages
-// (columns (threadIdx.x + 256 r) / 8) and the weight row of its A operand.
+template <int FMT, int NT>
+struct StepLoads;
+
+// Multiply-accumulate this wave's 8 MFMA sub-blocks of a step (its rows, its
+// half's chunks; ub = first sub-block of the half within the super-block),
+// issuing slot u of the next step's loads at sub-block u.  Software
+// pipelined over sub-blocks so that the matrix core and the LDS reads run
+// under the epilogue (see the two cases below).
 template <int FMT, int NT, int MODE>
+__device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* st, const float* wl,
+                                            const MmqOperand<FMT>& A, v16f (&acc)[NT], const v16i& magic,
+                                            const TileCols& tc, int r0, int sb, int ub,
+                                            const StepLoads<FMT, NT>& pre, MmqPrefetch<FMT>& F) {
+  constexpr int NU = StepSplit<FMT>::kNU;         // MFMA sub-blocks of this wave per step
+  constexpr int NSB = StepSplit<FMT>::kSubsPerSb; // MFMA sub-blocks per super-block
+  const int g = (threadIdx.x & 63) >> 5, col = threadIdx.x & 31;
+  if constexpr (NT == 1) {
+    // One column tile: the MFMA of sub-block u+1 is issued before the
+    // epilogue of u (two result buffers), so it runs under that epilogue;
+    // LDS operands are read two sub-blocks ahead (three buffers).
+    SubOps<FMT, NT> O[3];
+    v16i X[2];
+    load_sub<FMT, NT>(st, wl, ub, 0, O[0]);
+    load_sub<FMT, NT>(st, wl, ub + 1, 1, O[1]);
+    X[0] = mfma_sub(build_a(A, 0), O[0].bq[0], magic);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if constexpr (StepLoads<FMT, NT>::kInLoop) pre.issue(u, F);  // one slot of the next step's loads
+      if (u + 2 < NU) load_sub<FMT, NT>(st, wl, ub + u + 2, u + 2, O[(u + 2) % 3]);
+      if (u + 1 < NU) X[(u + 1) & 1] = mfma_sub(build_a(A, u + 1), O[(u + 1) % 3].bq[0], magic);
+      __builtin_amdgcn_sched_barrier(0);
+      mmq_epilogue<FMT, NT, MODE>(P, tc, r0, sb, ub, u, 0, X[u & 1], O[u % 3], acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // Several column tiles: the MFMA of (u+1, ct) is issued right after the
+    // epilogue of (u, ct) has consumed its result registers, so it runs under
+    // the epilogue of the next column tile; LDS operands of u+1 are read
+    // while u is rescaled.
+    SubOps<FMT, NT> O[2];
+    v16i X[NT];
+    load_sub<FMT, NT>(st, wl, ub, 0, O[0]);
+    {
+      const auto a0 = build_a(A, 0);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) X[ct] = mfma_sub(a0, O[0].bq[ct], magic);
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int b = u & 1;
+      const bool more = u + 1 < NU;
+      if constexpr (StepLoads<FMT, NT>::kInLoop) pre.issue(u, F);  // one slot of the next step's loads
+      if (more) load_sub<FMT, NT>(st, wl, ub + u + 1, u + 1, O[b ^ 1]);
+      const auto an = build_a(A, more ? u + 1 : u);
+      // scheduling barriers pin the order: operand reads of u+1 first, then
+      // per column tile its epilogue followed by its next MFMA
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        mmq_epilogue<FMT, NT, MODE>(P, tc, r0, sb, ub, u, ct, X[ct], O[b], acc);
+        if (more) X[ct] = mfma_sub(an, O[b ^ 1].bq[ct], magic);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+// Per-thread addressing of one tile.
 struct TileRef {
-  static constexpr int RX = MmqPrefetch<FMT, NT>::RX;
   TileCols tc;
+  int ctile0;             // first chunk row (column tile) of the tile
+  int nct;                // valid column tiles (chunks) in the tile
   int r0;                 // first row of this wave
   const uint8_t* wr;      // weight row of this lane
-  int xrow[RX], orow[RX];
-  bool cvalid[RX];
-  bool dbg_s;             // debug: this tile writes the activation sums
 };
 
 // MoE tables copied to LDS at kernel start: the tile search runs in LDS
@@ -450,12 +510,11 @@ struct MoeTables {
   const int* work_off;  // [E+1]
   const int* counts;    // [E]
   const int* offsets;   // [E]
+  const int* ct_off;    // [E]
 };
 
-// Tile idx of the call: rows, routed columns and weight matrix.
 template <int FMT, int NT, int MODE>
-__device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb, int idx,
-                                         TileRef<FMT, NT, MODE>& R) {
+__device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb, int idx, TileRef& R) {
   constexpr int BN = 32 * NT;
   int m_tile;
   const uint8_t* wbase = P.w;
@@ -465,15 +524,16 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
       const int mid = (lo + hi) >> 1;
       if (Tb.work_off[mid] <= idx) lo = mid; else hi = mid;
     }
-    const int e = lo;
-    const int cnt = Tb.counts[e];
+    const int e = __builtin_amdgcn_readfirstlane(lo);
+    const int cnt = __builtin_amdgcn_readfirstlane(Tb.counts[e]);
     const int ntile = (cnt + BN - 1) / BN;
-    const int local = idx - Tb.work_off[e];
+    const int local = idx - __builtin_amdgcn_readfirstlane(Tb.work_off[e]);
     m_tile = local / ntile;
     const int n_tile = local % ntile;
     R.tc.n0 = n_tile * BN;
     R.tc.ncols = min(BN, cnt - R.tc.n0);
     R.tc.slot_base = Tb.offsets[e];
+    R.ctile0 = Tb.ct_off[e] + n_tile * NT;
     wbase = P.w + static_cast<size_t>(e) * static_cast<size_t>(P.expert_stride);
   } else {
     const int ntile = (P.T + BN - 1) / BN;
@@ -482,143 +542,310 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
     R.tc.n0 = n_tile * BN;
     R.tc.ncols = min(BN, P.T - R.tc.n0);
     R.tc.slot_base = 0;
+    R.ctile0 = n_tile * NT;
   }
-  R.dbg_s = MODE == kDebug && m_tile == 0;
-  R.r0 = m_tile * kMmqBM + (threadIdx.x >> 6) * 32;
+  // every value above is the same in all lanes (the tile index is): keep
+  // them in scalar registers so the tile's control flow is scalar
+  R.tc.n0 = __builtin_amdgcn_readfirstlane(R.tc.n0);
+  R.tc.ncols = __builtin_amdgcn_readfirstlane(R.tc.ncols);
+  R.tc.slot_base = __builtin_amdgcn_readfirstlane(R.tc.slot_base);
+  R.ctile0 = __builtin_amdgcn_readfirstlane(R.ctile0);
+  R.nct = (R.tc.ncols + kChunkCols - 1) / kChunkCols;
+  m_tile = __builtin_amdgcn_readfirstlane(m_tile);
+  const int rw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
+  R.r0 = m_tile * kMmqBM + rw * 32;
   const int wrow = min(R.r0 + (threadIdx.x & 31), P.M - 1);
   constexpr int kRowBytes = FMT == QMM_Q4_K ? kQ4Bytes : kQ6Bytes;
   R.wr = wbase + static_cast<size_t>(wrow) * P.nb * kRowBytes;
-#pragma unroll
-  for (int r = 0; r < R.RX; ++r)
-    col_rows<MODE>(P, R.tc, (threadIdx.x + kMmqThreads * r) >> 3, R.xrow[r], R.orow[r], R.cvalid[r]);
 }
 
-// Next tile for this workgroup, or -1 (thread 0 only).  The tiles are split
-// into kXcds contiguous ranges with one counter each; a workgroup starts on
-// the range of its XCD (blockIdx % kXcds) and moves on when it is drained.
-__device__ __forceinline__ int claim_tile(const MmqParams& P, int total, int home, int& qi) {
-  for (; qi < kXcds; ++qi) {
-    const int q = (home + qi) % kXcds;
-    const int start = static_cast<int>((static_cast<int64_t>(total) * q) / kXcds);
-    const int size = static_cast<int>((static_cast<int64_t>(total) * (q + 1)) / kXcds) - start;
-    const unsigned c = atomicAdd(&P.counters[q], 1u);
-    if (c < static_cast<unsigned>(size)) return start + static_cast<int>(c);
+// LDS byte address of a (generic) pointer into shared memory: a flat
+// address in the LDS aperture carries the LDS offset in its low 32 bits.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4; the LDS base goes through M0).  Written as
+// inline assembly so the compiler does not track it: its own tracking treats
+// every later LDS read as a possible alias and waits for all loads in flight,
+// which would serialise the prefetch of the next step into this one.  The
+// kernel waits for these copies explicitly (vmcnt(0), then a barrier).
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "s"(m0v)
+                   : "memory", "m0");
+}
+
+// The loads of one step -- the chunks of its two super-blocks (copied into
+// LDS stage dst, [kh][ct] chunks) and this wave's weight bytes -- issued one
+// slot at a time by issue(u), so they spread over the sub-block loop of the
+// previous step instead of queueing all at once in the address unit.  Chunk
+// copies: each wave instruction moves 1 KB (lane l the 16 bytes at 16*l);
+// wave w takes instructions w, w + 8, ...
+template <int FMT, int NT>
+struct StepLoads {
+  using SP = StepSplit<FMT>;
+  static constexpr int NU = SP::kNU;                          // slots per step
+  static constexpr int kInstr = SP::kSbPerStep * NT * kChunkKB;
+  static constexpr int kDma = (kInstr + kMmqWaves - 1) / kMmqWaves;  // chunk copies per wave
+  static constexpr int kW = FMT == QMM_Q4_K ? 5 : 8;           // weight loads per wave
+  // Q4_K spreads its loads over the sub-block loop of the previous step;
+  // Q6_K issues them all before it (spread out, they keep enough address
+  // registers live to overflow its register budget)
+  static constexpr bool kInLoop = FMT == QMM_Q4_K;
+  static constexpr int kWs = FMT == QMM_Q4_K ? kW : 0;  // weight loads spread over the slots
+  static constexpr int kL = kDma + kWs;                  // loads spread over the slots
+  const uint8_t* xr;       // chunk (ctile0, 0) of the loaded tile
+  const uint8_t* wr;       // this lane's weight row of the loaded tile
+  uint32_t dst;            // LDS address of the stage
+  int nb, nct, step;       // super-blocks per row, valid column tiles, step to load
+  bool any;                // false: nothing to load
+  int wave, kh, g;
+
+  __device__ __forceinline__ void dma(int i) const {
+    const int j = wave + kMmqWaves * i;
+    if (j >= kInstr) return;
+    const int hj = j / (NT * kChunkKB), ct = (j / kChunkKB) % NT, q = j % kChunkKB;
+    const int sbj = SP::kSbPerStep * step + hj;
+    if (sbj < nb && ct < nct)
+      dma16(xr + (static_cast<size_t>(ct) * nb + sbj) * kChunkBytes + q * 1024 + (threadIdx.x & 63) * 16,
+            dst + (hj * NT + ct) * kChunkBytes + q * 1024);
   }
-  return -1;
+
+  // Load i of kL is issued at slot (i * NU) / kL, alternating chunk copies
+  // and weight loads while both remain; Q6_K's weight loads all at slot 0.
+  __device__ __forceinline__ void issue(int u, MmqPrefetch<FMT>& F) const {
+    if (!any) return;
+    const int sbw = SP::sb(step, kh);
+    if constexpr (FMT == QMM_Q6_K) {
+      if (u == 0 && sbw < nb)
+#pragma unroll
+        for (int w = 0; w < kW; ++w) load_weight_slot(F, wr, sbw, g, w, kh);
+    }
+#pragma unroll
+    for (int i = 0; i < kL; ++i) {
+      if ((i * NU) / kL != u) continue;
+      constexpr int kPair = kDma < kWs ? kDma : kWs;
+      int di = -1, wi = -1;
+      if (i < 2 * kPair) {
+        if (i & 1) wi = i >> 1; else di = i >> 1;
+      } else if (kDma > kWs) {
+        di = kPair + (i - 2 * kPair);
+      } else {
+        wi = kPair + (i - 2 * kPair);
+      }
+      if (di >= 0) dma(di);
+      if constexpr (FMT == QMM_Q4_K) {
+        if (wi >= 0 && sbw < nb) load_weight_slot(F, wr, sbw, g, wi, kh);
+      }
+    }
+  }
+
+  // everything at once (a wave with no compute in this step)
+  __device__ __forceinline__ void issue_all(MmqPrefetch<FMT>& F) const {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) issue(u, F);
+  }
+};
+
+template <int FMT, int NT>
+__device__ __forceinline__ StepLoads<FMT, NT> step_loads(const MmqParams& P, const TileRef& R, int step,
+                                                         uint32_t dst, bool any, int wave, int kh, int g) {
+  StepLoads<FMT, NT> L;
+  L.xr = P.xr + static_cast<size_t>(R.ctile0) * P.nb * kChunkBytes;
+  L.wr = R.wr;
+  L.dst = dst;
+  L.nb = P.nb;
+  L.nct = R.nct;
+  L.step = step;
+  L.any = any;
+  L.wave = wave;
+  L.kh = kh;
+  L.g = g;
+  return L;
 }
 
-// Persistent loop over the tiles of the call, software-pipelined over
-// super-blocks: while super-block k is multiplied from LDS stage k&1, the
-// loads of super-block k+1 are in flight, across tile boundaries too.  One
-// barrier per super-block: the write of stage (k+1)&1 comes after the
-// barrier of k, which every wave passes only after finishing super-block
-// k-1 from that stage.  Tiles are claimed two ahead: thread 0 issues the
-// claim of tile i+2 at the first super-block of tile i and publishes it in
-// a 3-slot ring at the end of tile i, so neither the atomic's latency nor
-// the next tile's set-up waits in front of a barrier.  Two waves per SIMD
-// are required: with one, nothing hides the MFMA and LDS latencies of the
-// epilogue.
+// Store a wave's 32 x (32*NT) fp32 tile.  acc[ct][v] holds row
+// 8*(v/4) + 4*(lane/32) + v%4 of the wave's rows and column ct*32 + lane%32.
+template <int NT, int MODE>
+__device__ __forceinline__ void store_tile(const MmqParams& P, const TileCols& tc, int r0,
+                                           const v16f (&acc)[NT]) {
+  const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    bool valid;
+    const int orow = col_out_row<MODE>(P, tc, ct * 32 + col, valid);
+    if (!valid) continue;
+    float* yr = P.y + static_cast<size_t>(orow) * P.M;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int row = r0 + 8 * k + 4 * g;
+      if ((P.M & 3) == 0 && row + 3 < P.M) {
+        *reinterpret_cast<float4*>(yr + row) =
+            make_float4(acc[ct][4 * k], acc[ct][4 * k + 1], acc[ct][4 * k + 2], acc[ct][4 * k + 3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (row + r < P.M) yr[row + r] = acc[ct][4 * k + r];
+      }
+    }
+  }
+}
+
+// Work queues.  The tiles are split into kXcds contiguous ranges, one per
+// XCD (workgroup b runs on XCD b % kXcds), so a range's weight rows stay in
+// one XCD's L2.  Workgroup b takes tile b / kXcds of its range as its first
+// tile (no atomic on the critical path at start-up); every further tile
+// comes from the range's atomic counter: ticket c is tile nw + c of the range,
+// nw being the number of workgroups on that XCD.  A failed claim ends the
+// workgroup.  The counters are zeroed by the kernel that runs before this one
+// on the stream (activation repack or route preparation).
+struct Queue {
+  int start, size;  // tile range of this workgroup's XCD
+  int nw;           // workgroups on this XCD
+  int home;
+};
+
+__device__ __forceinline__ Queue make_queue(int total) {
+  Queue Q;
+  Q.home = static_cast<int>(blockIdx.x % kXcds);
+  Q.start = static_cast<int>((static_cast<int64_t>(total) * Q.home) / kXcds);
+  Q.size = static_cast<int>((static_cast<int64_t>(total) * (Q.home + 1)) / kXcds) - Q.start;
+  Q.nw = static_cast<int>((gridDim.x - Q.home + kXcds - 1) / kXcds);
+  return Q;
+}
+
+__device__ __forceinline__ void wait_vm_all() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Persistent loop over the tiles of the call.  Steps of two super-blocks
+// (one per K half); at the top of a step every wave waits for its own loads
+// of the step (issued during the previous step), then one barrier publishes
+// the copied chunks and frees the other LDS stage, into which the next step's
+// chunks are copied, slot by slot, while this step is computed.  Loads of a
+// tile's first step are issued during the previous tile's last step.  The
+// next tile is claimed one ahead: thread 0 issues the atomic at the top of a
+// tile's first step and reads its value at the top of the tile's last step
+// (after the full wait there, so with two or more steps it costs no stall),
+// then publishes it before that step's barrier.
 template <int FMT, int NT, int MODE>
 __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mmq_kernel(MmqParams P) {
   using L = MmqSmem<FMT, NT>;
-  constexpr int BN = L::BN;
   constexpr int kTab = MODE == kMoe ? kMoeMaxE + 1 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
-  __shared__ int s_tile[3];
-  __shared__ int s_work_off[kTab], s_counts[kTab], s_offsets[kTab];
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  __shared__ int s_next[2];
+  __shared__ int s_work_off[kTab], s_counts[kTab], s_offsets[kTab], s_ct_off[kTab];
 
-  MoeTables Tb{s_work_off, s_counts, s_offsets};
+  MoeTables Tb{s_work_off, s_counts, s_offsets, s_ct_off};
   int total;
   if constexpr (MODE == kMoe) {
     for (int i = threadIdx.x; i <= P.E; i += kMmqThreads) {
       s_work_off[i] = P.work_off[i];
+      s_ct_off[i] = P.ct_off[i];
       if (i < P.E) {
         s_counts[i] = P.counts[i];
         s_offsets[i] = P.offsets[i];
       }
     }
-    total = P.work_off[P.E];
+    total = __builtin_amdgcn_readfirstlane(P.work_off[P.E]);
+    __syncthreads();
   } else {
-    total = ((P.M + kMmqBM - 1) / kMmqBM) * ((P.T + BN - 1) / BN);
+    total = ((P.M + kMmqBM - 1) / kMmqBM) * ((P.T + 32 * NT - 1) / (32 * NT));
   }
-  const int home = static_cast<int>(blockIdx.x % kXcds);
-  int qi = 0;  // queue cursor, used by thread 0 only
-  if (threadIdx.x == 0) {
-    s_tile[0] = claim_tile(P, total, home, qi);
-    s_tile[1] = s_tile[0] >= 0 ? claim_tile(P, total, home, qi) : -1;
+  const Queue Q = make_queue(total);
+  const int b8 = static_cast<int>(blockIdx.x / kXcds);
+  if (b8 >= Q.size) return;  // no tile for this workgroup (uniform)
+  const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kh = wave >> 2;
+  float* wl = reinterpret_cast<float*>(smem + L::kWaveOff + wave * L::kWave);
+  const int nsteps = FMT == QMM_Q4_K ? (P.nb + 1) >> 1 : P.nb;
+  v16i magic;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) magic[v] = static_cast<int>(kMagicBits);
+  // opaque to the compiler, so it stays in registers instead of being
+  // rebuilt (16 moves) in front of every MFMA
+  __asm__ volatile("" : "+v"(magic));
+  TileRef R, Rn;
+  tile_ref<FMT, NT, MODE>(P, Tb, Q.start + b8, R);
+  MmqPrefetch<FMT> F;
+  const uint32_t lds0 = lds_addr(smem);
+  {
+    const StepLoads<FMT, NT> first = step_loads<FMT, NT>(P, R, 0, lds0, true, wave, kh, g);
+    first.issue_all(F);
   }
-  __syncthreads();
-  int cur = s_tile[0];
-  if (cur >= 0) {
-    const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31, wave = threadIdx.x >> 6;
-    const size_t xstride = static_cast<size_t>(P.nb) * 8 * kQ8Bytes;
-    v16i magic;
+  int k = 0;            // steps done by this workgroup (selects the LDS stage)
+  unsigned ticket = 0;  // thread 0: counter value of the claim of the next tile
+  for (int it = 0;; ++it) {
+    v16f acc[NT];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) magic[v] = static_cast<int>(kMagicBits);
-    TileRef<FMT, NT, MODE> R, Rn;
-    tile_ref<FMT, NT, MODE>(P, Tb, cur, R);
-    MmqPrefetch<FMT, NT> F;
-    mmq_load<FMT, NT>(P, F, R.xrow, xstride, R.wr, 0, g);
-    int k = 0;        // super-blocks done by this workgroup (selects the LDS stage)
-    int pending = -1;  // thread 0: claim in flight for tile it+2
-    for (int it = 0;; ++it) {
-      v16f acc[NT];
+    for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[ct][v] = 0.0f;
-      int next = -1;
-      for (int sb = 0; sb < P.nb; ++sb, ++k) {
-        uint8_t* st = smem + (k & 1) * L::kStage;
-        mmq_commit<FMT, NT, MODE>(P, st, F, R.orow, R.cvalid, sb, wave, col, g, R.dbg_s);
-        MmqOperand<FMT> A;
-        take_operand<FMT, NT>(F, A);
-        __syncthreads();
-        if (sb == 0) {
-          // tile it+1 was published before this barrier; its rows resolve
-          // under this tile's super-blocks
-          next = s_tile[(it + 1) % 3];
-          if (next >= 0) tile_ref<FMT, NT, MODE>(P, Tb, next, Rn);
-          if (threadIdx.x == 0) pending = next >= 0 ? claim_tile(P, total, home, qi) : -1;
-        }
-        if (sb + 1 < P.nb) {
-          mmq_load<FMT, NT>(P, F, R.xrow, xstride, R.wr, sb + 1, g);
-        } else if (next >= 0) {
-          mmq_load<FMT, NT>(P, F, Rn.xrow, xstride, Rn.wr, 0, g);
-        }
-        mmq_compute<FMT, NT, MODE>(P, st, A, acc, magic, R.tc, R.r0, sb);
+      for (int v = 0; v < 16; ++v) acc[ct][v] = 0.0f;
+    int next = -1;
+    for (int step = 0; step < nsteps; ++step, ++k) {
+      uint8_t* st = smem + (k & 1) * L::kStage;
+      const int sb = StepSplit<FMT>::sb(step, kh);
+      const bool active = sb < P.nb;
+      const bool last = step + 1 == nsteps;
+      MmqOperand<FMT> A;
+      if (active) {
+        take_operand(F, A);
+        write_scales(F, wl, col, g);
       }
-      if constexpr (MODE != kDebug) store_tile<NT, MODE>(P, R.tc, R.r0, acc, P.y);
-      if (next < 0) break;
-      R = Rn;
-      // slot (it+2)%3 was last read at the first barrier of tile it-1
-      if (threadIdx.x == 0) s_tile[(it + 2) % 3] = pending;
+      wait_vm_all();
+      if (threadIdx.x == 0) {
+        if (step == 0) ticket = atomicAdd(&P.counters[Q.home], 1u);
+        if (last) {
+          const int j = Q.nw + static_cast<int>(ticket);
+          s_next[it & 1] = j < Q.size ? Q.start + j : -1;
+        }
+      }
+      __syncthreads();
+      if (last) {
+        next = __builtin_amdgcn_readfirstlane(s_next[it & 1]);
+        if (next >= 0) tile_ref<FMT, NT, MODE>(P, Tb, next, Rn);
+      }
+      const uint32_t dst = lds0 + ((k + 1) & 1) * L::kStage;
+      const StepLoads<FMT, NT> pre = last ? step_loads<FMT, NT>(P, Rn, 0, dst, next >= 0, wave, kh, g)
+                                          : step_loads<FMT, NT>(P, R, step + 1, dst, true, wave, kh, g);
+      if (!StepLoads<FMT, NT>::kInLoop || !active) pre.issue_all(F);
+      if (active) {
+        mmq_compute<FMT, NT, MODE>(P, st + StepSplit<FMT>::chunk_half(kh) * NT * kChunkBytes, wl, A, acc, magic,
+                                   R.tc, R.r0, sb, StepSplit<FMT>::u0(kh), pre, F);
+      }
     }
-  }
-  // exit: the last workgroup out resets the queue counters for the next call
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const unsigned done = atomicAdd(&P.counters[kXcds], 1u);
-    if (done == gridDim.x - 1) {
-      for (int q = 0; q < kXcds; ++q) atomicExch(&P.counters[q], 0u);
-      atomicExch(&P.counters[kXcds], 0u);
+    if constexpr (MODE != kDebug) {
+      // sum the two K halves through the stage just computed from
+      __syncthreads();
+      float* red = reinterpret_cast<float*>(smem + ((k - 1) & 1) * L::kStage);
+      const int rw = wave & 3;
+      if (kh == 1) {
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) red[((rw * NT + ct) * 16 + v) * 64 + lane] = acc[ct][v];
+      }
+      __syncthreads();
+      if (kh == 0) {
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[ct][v] += red[((rw * NT + ct) * 16 + v) * 64 + lane];
+        store_tile<NT, MODE>(P, R.tc, R.r0, acc);
+      }
     }
+    if (next < 0) break;
+    R = Rn;
   }
 }
 
-// Grid size: enough resident workgroups to fill the device, a multiple of
-// the XCD count so every XCD range has workers.
-template <int FMT, int NT, int MODE>
+// Grid size: one workgroup per CU (eight waves, two per SIMD), a multiple
+// of the XCD count so every XCD range has workers.
 static int mmq_grid(int total_tiles_hint) {
-  static int per_cu = -1;
-  if (per_cu < 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mmq_kernel<FMT, NT, MODE>, kMmqThreads, 0) !=
-            hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
-  }
-  int g = device_cu_count() * per_cu;
+  int g = device_cu_count();
   if (total_tiles_hint > 0 && total_tiles_hint < g) g = total_tiles_hint;
   g = ((g + kXcds - 1) / kXcds) * kXcds;
   return g < kXcds ? kXcds : g;
@@ -626,56 +853,104 @@ static int mmq_grid(int total_tiles_hint) {
 
 template <int FMT, int NT, int MODE>
 static int launch_mmq(const MmqParams& P, int total_tiles_hint, hipStream_t st) {
-  const int grid = mmq_grid<FMT, NT, MODE>(total_tiles_hint);
-  hipLaunchKernelGGL((mmq_kernel<FMT, NT, MODE>), dim3(grid), dim3(kMmqThreads), 0, st, P);
+  using L = MmqSmem<FMT, NT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmq_kernel<FMT, NT, MODE>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, L::kBytes) != hipSuccess)
+      return QMM_ERR_HIP;
+    attr_set = true;
+  }
+  const int grid = mmq_grid(total_tiles_hint);
+  hipLaunchKernelGGL((mmq_kernel<FMT, NT, MODE>), dim3(grid), dim3(kMmqThreads), L::kBytes, st, P);
   return launch_status();
 }
 
-constexpr int kMoeNT = 1;    // MoE tiles: 128 rows x 32 routed tokens
 constexpr size_t kCounterBytes = 256;
 
-// Dense tiles are 128 rows x 64 tokens, or 128 x 32 when there are very few
-// 64-token tiles.  (A 64-token tile per CU outruns two 32-token tiles per
-// CU: the A operand, row scales and epilogue set-up are shared by twice the
-// MFMAs.)
-constexpr int64_t kDenseMinTiles2 = 64;
+static size_t mmq_chunk_bytes(int64_t ctiles, int64_t nb) {
+  return static_cast<size_t>(ctiles) * static_cast<size_t>(nb) * kChunkBytes;
+}
+
+size_t mmq_workspace_bytes(int64_t K, int64_t T) {
+  const int64_t ctiles = (T + kChunkCols - 1) / kChunkCols;
+  return kCounterBytes + mmq_chunk_bytes(ctiles, K / kQK);
+}
+
+// Upper bound of the column tiles of a grouped call: sum over experts of
+// ceil(count / 32) <= (slots + 31 * E) / 32.
+int64_t moe_max_ctiles(int64_t slots, int64_t E) { return (slots + 31 * E) / 32; }
+size_t moe_chunk_bytes(int64_t slots, int64_t E, int64_t K) {
+  return mmq_chunk_bytes(moe_max_ctiles(slots, E), K / kQK);
+}
+
+// Dense tiles are 128 rows x 64 tokens (128 x 32 for calls with few tokens).
 template <int FMT>
 static int mmq_dense_fmt(const MmqParams& P, bool dbg, hipStream_t st) {
   const int64_t mt = (P.M + kMmqBM - 1) / kMmqBM;
-  const int64_t tiles2 = mt * ((P.T + 63) / 64);
-  if (tiles2 >= kDenseMinTiles2)
-    return dbg ? launch_mmq<FMT, 2, kDebug>(P, static_cast<int>(tiles2), st)
-               : launch_mmq<FMT, 2, kDense>(P, static_cast<int>(tiles2), st);
-  const int tiles1 = static_cast<int>(mt * ((P.T + 31) / 32));
-  return dbg ? launch_mmq<FMT, 1, kDebug>(P, tiles1, st) : launch_mmq<FMT, 1, kDense>(P, tiles1, st);
+  if (P.T > 32) {
+    const int tiles = static_cast<int>(mt * ((P.T + 63) / 64));
+    return dbg ? launch_mmq<FMT, 2, kDebug>(P, tiles, st) : launch_mmq<FMT, 2, kDense>(P, tiles, st);
+  }
+  const int tiles = static_cast<int>(mt * ((P.T + 31) / 32));
+  return dbg ? launch_mmq<FMT, 1, kDebug>(P, tiles, st) : launch_mmq<FMT, 1, kDense>(P, tiles, st);
 }
 
 int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
               void* ws, hipStream_t st, int32_t* dbgD, int32_t* dbgS) {
+  const bool dbg = dbgD != nullptr;
+  uint8_t* xr = static_cast<uint8_t*>(ws) + kCounterBytes;
+  const int nb = static_cast<int>(K / kQK);
+  const int ctiles = static_cast<int>((T + kChunkCols - 1) / kChunkCols);
+  RepackParams R{};
+  R.xq = static_cast<const uint8_t*>(xq);
+  R.xr = xr;
+  R.nb = nb;
+  R.T = static_cast<int>(T);
+  R.dbgS = dbgS;
+  R.counters = static_cast<unsigned*>(ws);
+  if (dbg)
+    hipLaunchKernelGGL(mmq_repack_kernel<kDebug>, dim3(nb, ctiles), dim3(256), 0, st, R);
+  else
+    hipLaunchKernelGGL(mmq_repack_kernel<kDense>, dim3(nb, ctiles), dim3(256), 0, st, R);
+  int rc = launch_status();
+  if (rc != QMM_OK) return rc;
   MmqParams P{};
   P.w = static_cast<const uint8_t*>(w);
-  P.xq = static_cast<const uint8_t*>(xq);
+  P.xr = xr;
   P.y = y;
   P.M = static_cast<int>(M);
-  P.nb = static_cast<int>(K / kQK);
+  P.nb = nb;
   P.T = static_cast<int>(T);
   P.counters = static_cast<unsigned*>(ws);
   P.dbgD = dbgD;
-  P.dbgS = dbgS;
-  const bool dbg = dbgD != nullptr;
   return fmt == QMM_Q4_K ? mmq_dense_fmt<QMM_Q4_K>(P, dbg, st) : mmq_dense_fmt<QMM_Q6_K>(P, dbg, st);
 }
 
 // Grouped launch used by moe_grouped_mmq (after route preparation on the
-// same stream): tiles of 128 rows x 32 routed slots.
+// same stream): repack of the routed rows per expert, then tiles of 128 rows
+// x 32 routed slots.
 int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, const uint8_t* xq,
                    float* out, unsigned* counters, const int32_t* counts, const int32_t* offsets,
-                   const int32_t* bucket, const int32_t* work_off, int E, int top_k,
-                   int rows_per_token, hipStream_t st) {
-  static_assert(32 * kMoeNT == 32 && kMmqBM == 128, "route preparation assumes 128 x 32 tiles");
+                   const int32_t* bucket, const int32_t* work_off, const int32_t* ct_off, uint8_t* xr,
+                   int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st) {
+  RepackParams R{};
+  R.xq = xq;
+  R.xr = xr;
+  R.nb = nb;
+  R.counts = counts;
+  R.offsets = offsets;
+  R.bucket = bucket;
+  R.ct_off = ct_off;
+  R.E = E;
+  R.top_k = top_k;
+  R.rows_per_token = rows_per_token;
+  hipLaunchKernelGGL(mmq_repack_kernel<kMoe>, dim3(nb, max_ctiles), dim3(256), 0, st, R);
+  int rc = launch_status();
+  if (rc != QMM_OK) return rc;
   MmqParams P{};
   P.w = w;
-  P.xq = xq;
+  P.xr = xr;
   P.y = out;
   P.M = M;
   P.nb = nb;
@@ -685,21 +960,20 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   P.offsets = offsets;
   P.bucket = bucket;
   P.work_off = work_off;
+  P.ct_off = ct_off;
   P.E = E;
-  P.top_k = top_k;
-  P.rows_per_token = rows_per_token;
   P.expert_stride = stride;
-  if (fmt == QMM_Q4_K) return launch_mmq<QMM_Q4_K, kMoeNT, kMoe>(P, 0, st);
-  return launch_mmq<QMM_Q6_K, kMoeNT, kMoe>(P, 0, st);
+  if (fmt == QMM_Q4_K) return launch_mmq<QMM_Q4_K, 1, kMoe>(P, 0, st);
+  return launch_mmq<QMM_Q6_K, 1, kMoe>(P, 0, st);
 }
 
 static int check_mmq(const void* w, const void* xq, const float* y, int64_t M, int64_t K, int64_t T,
                      const void* ws, size_t ws_bytes) {
   if (M < 1 || T < 1 || K < kQK || (K % kQK) != 0) return QMM_ERR_SHAPE;
-  if (M > (1 << 30) || T > (1 << 30) || K / kQK > (1 << 20)) return QMM_ERR_SHAPE;
+  if (M > (1 << 30) || T > (1 << 24) || K / kQK > (1 << 16)) return QMM_ERR_SHAPE;
   if (!w || !xq || !y || !ws) return QMM_ERR_NULL;
   if (!aligned16(w) || !aligned16(xq) || !aligned16(y) || !aligned16(ws)) return QMM_ERR_ALIGN;
-  if (ws_bytes < kCounterBytes) return QMM_ERR_WORKSPACE;
+  if (ws_bytes < mmq_workspace_bytes(K, T)) return QMM_ERR_WORKSPACE;
   return QMM_OK;
 }
 

@@ -16,8 +16,10 @@
 // per id bit, so a lane's rank among equal ids is a popcount.  Pass 1 counts
 // per (wave, expert), wave scans turn counts into offsets, pass 2 repeats the
 // ranking and writes every slot to its place.  It also writes the work
-// prefix (m_tiles * ceil(count / 32) per expert) and zeroes the queue
-// counters that the grouped kernel claims tiles from.
+// prefix (m_tiles * ceil(count / 32) per expert), the column-tile prefix
+// (ceil(count / 32) per expert: where each expert's repacked activation
+// chunks start) and zeroes the queue counters that the grouped kernel claims
+// tiles from.
 //
 // The combine y[t] = sum_k p[t][k] * y_slot[t*top_k + k] runs in increasing
 // k with no atomics, so results are bit-reproducible.
@@ -36,40 +38,47 @@ constexpr int kMoeBM = 128;  // weight rows per tile
 
 int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, const uint8_t* xq,
                    float* out, unsigned* counters, const int32_t* counts, const int32_t* offsets,
-                   const int32_t* bucket, const int32_t* work_off, int E, int top_k,
-                   int rows_per_token, hipStream_t st);
+                   const int32_t* bucket, const int32_t* work_off, const int32_t* ct_off, uint8_t* xr,
+                   int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st);
+int64_t moe_max_ctiles(int64_t slots, int64_t E);
+size_t moe_chunk_bytes(int64_t slots, int64_t E, int64_t K);
 
 struct MoeLayout {
   unsigned* counters;
   int32_t* counts;
   int32_t* offsets;
   int32_t* work_off;
+  int32_t* ct_off;
   int32_t* bucket;
   float* scratch;
+  uint8_t* chunks;
   size_t bytes;
 };
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-static MoeLayout moe_layout(void* ws, int64_t M, int64_t T, int64_t E, int64_t top_k) {
+static MoeLayout moe_layout(void* ws, int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k) {
   MoeLayout L{};
   uint8_t* b = static_cast<uint8_t*>(ws);
   size_t off = kMoeCounterBytes;
-  const size_t ints = static_cast<size_t>(E) + 2 * static_cast<size_t>(E + 1) + static_cast<size_t>(T * top_k);
+  const size_t ints = static_cast<size_t>(E) + 3 * static_cast<size_t>(E + 1) + static_cast<size_t>(T * top_k);
   L.counters = reinterpret_cast<unsigned*>(b);
   L.counts = reinterpret_cast<int32_t*>(b + off);
   L.offsets = L.counts + E;
   L.work_off = L.offsets + (E + 1);
-  L.bucket = L.work_off + (E + 1);
+  L.ct_off = L.work_off + (E + 1);
+  L.bucket = L.ct_off + (E + 1);
   off = align_up(off + ints * 4, 256);
   L.scratch = reinterpret_cast<float*>(b + off);
-  off += static_cast<size_t>(T * top_k) * static_cast<size_t>(M) * 4;
+  off = align_up(off + static_cast<size_t>(T * top_k) * static_cast<size_t>(M) * 4, 1024);
+  L.chunks = b + off;
+  off += moe_chunk_bytes(T * top_k, E, K);
   L.bytes = off;
   return L;
 }
 
-size_t moe_workspace_bytes(int64_t M, int64_t T, int64_t E, int64_t top_k) {
-  return moe_layout(nullptr, M, T, E, top_k).bytes;
+size_t moe_workspace_bytes(int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k) {
+  return moe_layout(nullptr, M, K, T, E, top_k).bytes;
 }
 
 __device__ __forceinline__ uint64_t peers_of(int e, bool v, int nbits) {
@@ -89,11 +98,12 @@ constexpr int kRouteBatch = 8;
 
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     const int32_t* __restrict__ ids, int n, int E, int mt, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ work_off, int32_t* __restrict__ bucket,
-    unsigned* __restrict__ counters) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ work_off, int32_t* __restrict__ ct_off,
+    int32_t* __restrict__ bucket, unsigned* __restrict__ counters) {
   __shared__ int cnt[kRouteWaves][kMoeMaxE];
   __shared__ int s_off[kMoeMaxE + 1];
   __shared__ int s_wsum[kMoeMaxE + 1];
+  __shared__ int s_ct[kMoeMaxE + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int i = tid; i < kRouteWaves * kMoeMaxE; i += kRouteThreads) (&cnt[0][0])[i] = 0;
   __syncthreads();
@@ -130,33 +140,37 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     }
     counts[e] = run;
     s_off[e] = run;
-    s_wsum[e] = ((run + kMoeBN - 1) / kMoeBN) * mt;
+    s_ct[e] = (run + kMoeBN - 1) / kMoeBN;
+    s_wsum[e] = s_ct[e] * mt;
   }
   __syncthreads();
   // exclusive scans over experts (E <= 512 fits one wave's 8 passes)
   if (wave == 0) {
-    int off = 0, woff = 0;
+    int off = 0, woff = 0, coff = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
       const int e = e0 + lane;
-      int c = e < E ? s_off[e] : 0, wv = e < E ? s_wsum[e] : 0;
+      int c = e < E ? s_off[e] : 0, wv = e < E ? s_wsum[e] : 0, cv = e < E ? s_ct[e] : 0;
       // inclusive wave scans
       for (int d = 1; d < 64; d <<= 1) {
-        const int cu = __shfl_up(c, d), wu = __shfl_up(wv, d);
-        if (lane >= d) { c += cu; wv += wu; }
+        const int cu = __shfl_up(c, d), wu = __shfl_up(wv, d), vu = __shfl_up(cv, d);
+        if (lane >= d) { c += cu; wv += wu; cv += vu; }
       }
-      const int cx = __shfl_up(c, 1), wx = __shfl_up(wv, 1);
-      const int ce = lane == 0 ? 0 : cx, we = lane == 0 ? 0 : wx;
+      const int cx = __shfl_up(c, 1), wx = __shfl_up(wv, 1), vx = __shfl_up(cv, 1);
+      const int ce = lane == 0 ? 0 : cx, we = lane == 0 ? 0 : wx, ve = lane == 0 ? 0 : vx;
       if (e < E) {
         s_off[e] = off + ce;
         offsets[e] = off + ce;
         work_off[e] = woff + we;
+        ct_off[e] = coff + ve;
       }
       off += __shfl(c, 63);
       woff += __shfl(wv, 63);
+      coff += __shfl(cv, 63);
     }
     if (lane == 0) {
       offsets[E] = off;
       work_off[E] = woff;
+      ct_off[E] = coff;
     }
   }
   __syncthreads();
@@ -240,19 +254,20 @@ extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int
   if (!aligned16(w) || !aligned16(xq) || !aligned16(ids) || !aligned16(y) || !aligned16(ws) ||
       (expert_weights && !aligned16(expert_weights)))
     return QMM_ERR_ALIGN;
-  const MoeLayout L = moe_layout(ws, M, T, E, top_k);
+  const MoeLayout L = moe_layout(ws, M, K, T, E, top_k);
   if (ws_bytes < L.bytes) return QMM_ERR_WORKSPACE;
   hipStream_t st = to_stream(stream);
   const int n = static_cast<int>(T * top_k);
   const int mt = static_cast<int>((M + kMoeBM - 1) / kMoeBM);
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ids, n, static_cast<int>(E),
-                     mt, L.counts, L.offsets, L.work_off, L.bucket, L.counters);
+                     mt, L.counts, L.offsets, L.work_off, L.ct_off, L.bucket, L.counters);
   int rc = launch_status();
   if (rc != QMM_OK) return rc;
   float* out = expert_weights ? L.scratch : y;
   rc = mmq_moe_launch(fmt, static_cast<const uint8_t*>(w), expert_stride_bytes, static_cast<int>(M),
                       static_cast<int>(K / kQK), static_cast<const uint8_t*>(xq), out, L.counters,
-                      L.counts, L.offsets, L.bucket, L.work_off, static_cast<int>(E),
+                      L.counts, L.offsets, L.bucket, L.work_off, L.ct_off, L.chunks,
+                      static_cast<int>(moe_max_ctiles(T * top_k, E)), static_cast<int>(E),
                       static_cast<int>(top_k), static_cast<int>(x_rows_per_token), st);
   if (rc != QMM_OK || !expert_weights) return rc;
   const bool vec = (M % 4) == 0;
