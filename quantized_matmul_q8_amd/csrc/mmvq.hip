@@ -40,7 +40,6 @@ namespace qmm {
 constexpr int kMmvqWaves = 8;             // rows per workgroup
 constexpr int kMmvqThreads = 64 * kMmvqWaves;
 constexpr int kMmvqLdsBudget = 64 * 1024; // bytes of staged activations per workgroup
-constexpr int kQ6Units = 3;               // max Q6_K units (64 weights) per lane per chunk
 
 // Super-blocks per K chunk so that T tokens of staged activations fit the
 // LDS budget (1.5 bytes per activation) and the lane unit limit.
@@ -274,33 +273,53 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w
   }
 }
 
-// 8 bytes from a 2-byte aligned address inside a block (third dword read only
-// when misaligned, so nothing past p + 8 is touched otherwise).
-__device__ __forceinline__ uint2 ld8_a2(const uint8_t* p) {
-  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
-  const uint32_t* base = reinterpret_cast<const uint32_t*>(p - sh);
-  const uint32_t w0 = base[0], w1 = base[1];
-  const uint32_t w2 = sh ? base[2] : 0u;
-  return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));
+// Q6_K rows are read as consecutive 16-byte pieces: 16 lanes per 210-byte
+// block, lane j of a block loading bytes 16j .. 16j+15 for j < 13 and bytes
+// 194 .. 209 for j = 13 (lanes 14, 15 idle), so one wave load instruction
+// covers four consecutive blocks (840 contiguous bytes) instead of scattered
+// pieces of sixteen (blocks are 2-byte aligned; gfx950 serves unaligned
+// 16-byte loads).  Rounds of loads are issued in order, a fixed number
+// ahead of the chunk being multiplied, and only kQ6Pre of them before the
+// activation staging: staging loads queue behind every weight load the CU
+// has already issued, so a deep prefetch there delays the staging barrier
+// (and with it all compute) until most of the matrix has arrived.
+// The pieces of 16 blocks at a time are written to a wave-private LDS region
+// (one 16-byte slot per piece, blocks kQ6BlkStride bytes apart so that the
+// reads below are free of bank conflicts), from where lane l takes its unit:
+// block l/4, half h = (l%4)/2 and 16-half hf = l%2 of it, i.e. 64 weights in
+// four 16-weight sub-blocks (g = 0..3 at positions 128h + 32g + 16hf + i).
+// Bytes used: ql[64h + 16hf ..+16] (g = 0, 2), ql[64h + 32 + 16hf ..+16]
+// (g = 1, 3), qh[32h + 16hf ..+16], sc[8h .. 8h+7] and d.
+constexpr int kQ6Chunk = 16;       // blocks per LDS chunk: 64 units, one per lane
+constexpr int kQ6BlkStride = 272;  // LDS bytes per block in the piece region
+// piece rounds per segment held in registers: 16 (64 blocks) for T <= 2,
+// fewer where the staged activations of more tokens shorten the segment
+__host__ __device__ constexpr int q6_rounds(int T) { return T <= 2 ? 16 : (T <= 4 ? 8 : 4); }
+constexpr int kQ6WaveRegion = kQ6Chunk * kQ6BlkStride;
+constexpr int kQ6Pre = 1;    // piece rounds issued before the activation staging
+constexpr int kQ6Ahead = 4;  // piece rounds issued ahead of the chunk being multiplied
+
+__device__ __forceinline__ uint4 ld16_u(const uint8_t* p) {
+  uint4 v;
+  __builtin_memcpy(&v, p, 16);  // one dwordx4 load at a 2-byte aligned address
+  return v;
 }
 
-// Q6_K unit: one half h of the super-block and 16 lanes l0..l0+15 of it, i.e.
-// 64 weights in four 16-weight sub-blocks (g = 0..3 at positions
-// 128h + 32g + l).  Bytes used: ql[64h + l0 ..+16], ql[64h + 32 + l0 ..+16],
-// qh[32h + l0 ..+16], sc[8h .. 8h+7] (four of them), d.  Blocks are 2-byte
-// aligned.
 template <int T, bool DEBUG>
 __global__ __launch_bounds__(kMmvqThreads) void mmvq_q6k_kernel(const uint8_t* w, const uint8_t* xq,
                                                                 float* __restrict__ y, int M, int nb,
                                                                 int cb, int32_t* __restrict__ dbgD) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int lane = threadIdx.x & 63;
-  const int row_raw = blockIdx.x * kMmvqWaves + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row_raw = blockIdx.x * kMmvqWaves + wave;
   const bool row_ok = row_raw < M;
   const int row = row_ok ? row_raw : M - 1;
   const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ6Bytes;
   const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
+  uint8_t* wreg = lds + static_cast<size_t>(T) * cb * 8 * 48 + wave * kQ6WaveRegion;
   constexpr int RS = (T * 64 * 8 + kMmvqThreads - 1) / kMmvqThreads;
+  const int pj = lane & 15, pb = lane >> 4;         // piece of a block, block within a round
+  const int poff = pj < 13 ? 16 * pj : 194;
   float acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = 0.0f;
@@ -308,76 +327,94 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q6k_kernel(const uint8_t* w
   for (int b0 = 0; b0 < nb; b0 += cb) {
     const int nbc = min(cb, nb - b0);
     const int nblk = nbc * 8;
-    const int nunits = nbc * 4;
+    // 1. activation staging loads, then every weight piece of the segment
     uint2 su[RS][5];
     int st[RS], sj[RS];
 #pragma unroll
     for (int r = 0; r < RS; ++r) stage_acts_load(xq, xstride, T, b0 * 8, nblk, r, su[r], st[r], sj[r]);
-    uint4 qa[kQ6Units], qb[kQ6Units], qh[kQ6Units];
-    uint2 scs[kQ6Units];
-    uint32_t dd[kQ6Units];
+    constexpr int NR = q6_rounds(T);
+    uint4 pc[NR];
+    // pieces of round r (blocks 4r .. 4r+3); a round past the segment is skipped
+    auto load_round = [&](int r) {
+      pc[r] = make_uint4(0u, 0u, 0u, 0u);
+      if (4 * r < nbc && pj < 14 && 4 * r + pb < nbc)
+        pc[r] = ld16_u(wrow + static_cast<size_t>(b0 + 4 * r + pb) * kQ6Bytes + poff);
+    };
 #pragma unroll
-    for (int i = 0; i < kQ6Units; ++i) {
-      const int u = min(lane + 64 * i, nunits - 1);  // unconditional: extra units re-read the last one
-      const int b = b0 + (u >> 2), c = u & 3, h = c >> 1, l0 = (c & 1) * 16;
-      const uint8_t* blk = wrow + static_cast<size_t>(b) * kQ6Bytes;
-      qa[i] = ld16_a2(blk + 64 * h + l0);        // g = 0 (low nibbles), g = 2 (high)
-      qb[i] = ld16_a2(blk + 64 * h + 32 + l0);   // g = 1 (low nibbles), g = 3 (high)
-      qh[i] = ld16_a2(blk + 128 + 32 * h + l0);  // bit pairs of g = 0..3
-      scs[i] = ld8_a2(blk + 192 + 8 * h);        // sc[8h .. 8h+7]
-      dd[i] = ld_u16(blk + 208);
-    }
+    for (int r = 0; r < kQ6Pre && r < NR; ++r) load_round(r);
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    // 2. publish the activations
+    __syncthreads();  // previous segment's LDS reads are done
 #pragma unroll
     for (int r = 0; r < RS; ++r) stage_acts_store<QMM_Q6_K>(lds, T, cb, su[r], st[r], sj[r]);
     __syncthreads();
+    // 3. chunks of 16 blocks: pieces to the wave's region, then one unit per lane
 #pragma unroll
-    for (int i = 0; i < kQ6Units; ++i) {
-      const int u = lane + 64 * i;
-      if (u >= nunits) break;
-      const int bl = u >> 2, c = u & 3, h = c >> 1, half16 = c & 1, l0 = half16 * 16;
-      const float d = h2f(dd[i]);
-      float dsc[4];
+    for (int ch = 0; ch < NR / 4; ++ch) {
+      if (16 * ch >= nbc) break;  // uniform
+      {
+        // rounds up to kQ6Ahead past this chunk, not issued yet
+        const int lo = ch == 0 ? kQ6Pre : 4 * ch + kQ6Ahead;
+        const int lo2 = lo > kQ6Pre ? lo : kQ6Pre;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // sc[8h + 2g + half16]: byte (2g + half16) of the 8 loaded bytes
-        const uint32_t word = g < 2 ? scs[i].x : scs[i].y;
-        const int sc = static_cast<int8_t>((word >> (8 * (2 * (g & 1) + half16))) & 0xffu);
-        dsc[g] = d * static_cast<float>(sc);
+        for (int r = 0; r < NR; ++r)
+          if (r >= lo2 && r < 4 * ch + 4 + kQ6Ahead) load_round(r);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const uint32_t qa_[4] = {qa[i].x, qa[i].y, qa[i].z, qa[i].w};
-      const uint32_t qb_[4] = {qb[i].x, qb[i].y, qb[i].z, qb[i].w};
-      const uint32_t qh_[4] = {qh[i].x, qh[i].y, qh[i].z, qh[i].w};
-      uint32_t q6[4][4];
+      // (this wave's reads of the previous chunk precede these writes in program order)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        q6[0][k] = (qa_[k] & 0x0f0f0f0fu) | ((qh_[k] << 4) & 0x30303030u);
-        q6[1][k] = (qb_[k] & 0x0f0f0f0fu) | ((qh_[k] << 2) & 0x30303030u);
-        q6[2][k] = ((qa_[k] >> 4) & 0x0f0f0f0fu) | (qh_[k] & 0x30303030u);
-        q6[3][k] = ((qb_[k] >> 4) & 0x0f0f0f0fu) | ((qh_[k] >> 2) & 0x30303030u);
-      }
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const size_t ix = (static_cast<size_t>(t) * cb + bl) * 4 + c;
-        const float4 z01 = reinterpret_cast<const float4*>(stage_array<QMM_Q6_K>(lds, T, cb, 4))[ix];
-        const float4 z23 = reinterpret_cast<const float4*>(stage_array<QMM_Q6_K>(lds, T, cb, 5))[ix];
-        const float zd[4] = {z01.x, z01.z, z23.x, z23.z}, zs[4] = {z01.y, z01.w, z23.y, z23.w};
+      for (int q = 0; q < 4; ++q)
+        if (pj < 14) *reinterpret_cast<uint4*>(wreg + (4 * q + pb) * kQ6BlkStride + 16 * pj) = pc[4 * ch + q];
+      const int bl = 16 * ch + (lane >> 2);  // segment-local block of this lane's unit
+      if (bl < nbc) {
+        const uint8_t* blk = wreg + (lane >> 2) * kQ6BlkStride;
+        const int c = lane & 3, h = c >> 1, half16 = c & 1;
+        const uint4 qa = *reinterpret_cast<const uint4*>(blk + 16 * (4 * h + half16));      // g = 0, 2
+        const uint4 qb = *reinterpret_cast<const uint4*>(blk + 16 * (4 * h + 2 + half16));  // g = 1, 3
+        const uint4 qh = *reinterpret_cast<const uint4*>(blk + 16 * (8 + 2 * h + half16));  // bit pairs
+        const uint2 scs = *reinterpret_cast<const uint2*>(blk + 192 + 8 * h);               // sc[8h .. 8h+7]
+        const float d = h2f(*reinterpret_cast<const uint16_t*>(blk + 16 * 13 + 14));        // byte 208
+        float dsc[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const uint4 xv = stage_array<QMM_Q6_K>(lds, T, cb, g)[ix];  // activations of block 4h+g, half l
-          int D = dot4(q6[g][0], xv.x, 0);
-          D = dot4(q6[g][1], xv.y, D);
-          D = dot4(q6[g][2], xv.z, D);
-          D = dot4(q6[g][3], xv.w, D);
-          // sum (q6 - 32) * q = D - 32 * S_half, exact in fp32 (|.| < 2^24)
-          const float D6 = static_cast<float>(D) - 32.0f * zs[g];
-          if constexpr (DEBUG) {
-            if (row_ok)
-              dbgD[(static_cast<size_t>(t) * M + row) * (nb * 16) + (b0 * 8 + bl * 8 + 4 * h + g) * 2 + half16] =
-                  static_cast<int>(D6);
-          } else {
-            acc[t] += zd[g] * dsc[g] * D6;
+          // sc[8h + 2g + half16]: byte (2g + half16) of the 8 loaded bytes
+          const uint32_t word = g < 2 ? scs.x : scs.y;
+          const int sc = static_cast<int8_t>((word >> (8 * (2 * (g & 1) + half16))) & 0xffu);
+          dsc[g] = d * static_cast<float>(sc);
+        }
+        const uint32_t qa_[4] = {qa.x, qa.y, qa.z, qa.w};
+        const uint32_t qb_[4] = {qb.x, qb.y, qb.z, qb.w};
+        const uint32_t qh_[4] = {qh.x, qh.y, qh.z, qh.w};
+        uint32_t q6[4][4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          q6[0][k] = (qa_[k] & 0x0f0f0f0fu) | ((qh_[k] << 4) & 0x30303030u);
+          q6[1][k] = (qb_[k] & 0x0f0f0f0fu) | ((qh_[k] << 2) & 0x30303030u);
+          q6[2][k] = ((qa_[k] >> 4) & 0x0f0f0f0fu) | (qh_[k] & 0x30303030u);
+          q6[3][k] = ((qb_[k] >> 4) & 0x0f0f0f0fu) | ((qh_[k] >> 2) & 0x30303030u);
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const size_t ix = (static_cast<size_t>(t) * cb + bl) * 4 + c;
+          const float4 z01 = reinterpret_cast<const float4*>(stage_array<QMM_Q6_K>(lds, T, cb, 4))[ix];
+          const float4 z23 = reinterpret_cast<const float4*>(stage_array<QMM_Q6_K>(lds, T, cb, 5))[ix];
+          const float zd[4] = {z01.x, z01.z, z23.x, z23.z}, zs[4] = {z01.y, z01.w, z23.y, z23.w};
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint4 xv = stage_array<QMM_Q6_K>(lds, T, cb, g)[ix];  // activations of block 4h+g, half
+            int D = dot4(q6[g][0], xv.x, 0);
+            D = dot4(q6[g][1], xv.y, D);
+            D = dot4(q6[g][2], xv.z, D);
+            D = dot4(q6[g][3], xv.w, D);
+            // sum (q6 - 32) * q = D - 32 * S_half, exact in fp32 (|.| < 2^24)
+            const float D6 = static_cast<float>(D) - 32.0f * zs[g];
+            if constexpr (DEBUG) {
+              if (row_ok)
+                dbgD[(static_cast<size_t>(t) * M + row) * (nb * 16) + (b0 * 8 + bl * 8 + 4 * h + g) * 2 + half16] =
+                    static_cast<int>(D6);
+            } else {
+              acc[t] += zd[g] * dsc[g] * D6;
+            }
           }
         }
       }
@@ -413,12 +450,21 @@ static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int n
   return launch_status();
 }
 
+// Q6_K segments: at most 4 * q6_rounds(T) blocks (the pieces held in
+// registers) and kQ6ActBudget bytes of staged activations (with the waves'
+// piece regions two workgroups fit a CU); the row is split into segments
+// of equal length.
+constexpr int kQ6ActBudget = 44 * 1024;
 template <bool DEBUG>
 static int launch_mmvq_q6k(const void* w, const void* xq, float* y, int M, int nb, int T,
                            int32_t* D, hipStream_t st) {
-  const int cb = mmvq_chunk_blocks(nb, T, 4, kQ6Units);
+  int cmax = kQ6ActBudget / (T * kQK * 3 / 2);
+  if (cmax > 4 * q6_rounds(T)) cmax = 4 * q6_rounds(T);
+  if (cmax < 1) cmax = 1;
+  const int nseg = (nb + cmax - 1) / cmax;
+  const int cb = (nb + nseg - 1) / nseg;
   const dim3 grid((M + kMmvqWaves - 1) / kMmvqWaves), block(kMmvqThreads);
-  const size_t lds = mmvq_lds_bytes(T, cb);
+  const size_t lds = mmvq_lds_bytes(T, cb) + static_cast<size_t>(kMmvqWaves) * kQ6WaveRegion;
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const uint8_t* xp = static_cast<const uint8_t*>(xq);
   switch (T) {
