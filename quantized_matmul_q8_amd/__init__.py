@@ -78,13 +78,13 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 _MMQ_WS: dict = {}
 
 
-def _mmq_ws(device: torch.device, K: int, T: int) -> torch.Tensor:
-    """Per-device cached GEMM workspace, grown to fit ``K`` and ``T``.
+def _mmq_ws(device: torch.device, M: int, K: int, T: int) -> torch.Tensor:
+    """Per-device cached GEMM workspace, grown to fit ``M``, ``K`` and ``T``.
 
     Calls that share it must be ordered on one stream (the queue counters
     and the repacked activations live in it)."""
     key = (device.index if device.index is not None else torch.cuda.current_device())
-    need = workspace_bytes(QMM_OP_MMQ, 0, K, T)
+    need = workspace_bytes(QMM_OP_MMQ, M, K, T)
     ws = _MMQ_WS.get(key)
     if ws is None or ws.numel() < need:
         if ws is not None:
@@ -131,7 +131,7 @@ def _mmq(name: str, fmt: int, w, xq, out, ws):
     if out is None:
         out = torch.empty((T, M), dtype=torch.float32, device=w.device)
     _need(out, torch.float32, "out", 2)
-    ws = _mmq_ws(w.device, K, T) if ws is None else ws
+    ws = _mmq_ws(w.device, M, K, T) if ws is None else ws
     _need(ws, torch.uint8, "ws", 1)
     _lib.call(name, _p(w), _p(xq), _p(out), M, K, T, _p(ws), ws.numel(), _stream(w.device))
     return out
@@ -210,7 +210,7 @@ def debug_subdots(fmt: int, path: int, w: torch.Tensor, xq: torch.Tensor):
     nsub = K // 32 if fmt == QMM_Q4_K else K // 16
     D = torch.empty((T, M, nsub), dtype=torch.int32, device=w.device)
     S = torch.empty((T, K // 32), dtype=torch.int32, device=w.device) if fmt == QMM_Q4_K else None
-    ws = _mmq_ws(w.device, K, T)
+    ws = _mmq_ws(w.device, M, K, T)
     _lib.call("qmm_debug_subdots", fmt, path, _p(w), _p(xq), _p(D), _p(S), M, K, T, _p(ws),
               ws.numel(), _stream(w.device))
     return D, S

@@ -42,10 +42,15 @@
 //   with its own atomic counter, so a range's weight rows stay in one XCD's
 //   L2.  A workgroup's first tile is fixed by its index; later tiles are
 //   claimed one ahead, with the atomic's latency hidden under the current
-//   tile.  Tiles run their whole K loop in one workgroup: no split across
-//   workgroups, no fixup, deterministic results.  The kernel that runs just
-//   before on the stream (activation repack, route preparation) zeroes the
-//   counters, so the workspace needs no initialisation and no memset.
+//   tile.  With enough tiles to fill the chip, a tile runs its whole K loop
+//   in one workgroup (no fixup).  A dense call with few tiles (few tokens,
+//   few rows) splits each tile's K range over up to kMaxSplit workgroups:
+//   each writes its fp32 partial tile to the workspace and bumps the tile's
+//   arrival counter; the last to arrive adds the partials in split order and
+//   stores the tile, so results stay deterministic without float atomics.
+//   The kernel that runs just before on the stream (activation repack, route
+//   preparation) zeroes the counters, so the workspace needs no
+//   initialisation and no memset.
 #include "qmm_common.hpp"
 
 #include <type_traits>
@@ -68,12 +73,25 @@ constexpr int kChunkKB = kChunkBytes / 1024;
 
 enum MmqMode { kDense = 0, kMoe = 1, kDebug = 2 };
 
+// Split-K of dense calls with few tiles: split until about kSplitTiles
+// tiles, at most kMaxSplit ways and at least four super-blocks per split.
+constexpr int kSplitTiles = 256;
+constexpr int kMaxSplit = 16;
+// Workspace head: queue counters at word 0, split-K arrival counters (one
+// per tile, fewer than kSplitTiles tiles when split) at word 256.
+constexpr size_t kCounterBytes = 2048;
+constexpr int kTileCntWord = 256;
+
 struct MmqParams {
   const uint8_t* w;
   const uint8_t* xr;            // repacked chunks: (ctile, sb) at (ctile * nb + sb) * kChunkBytes
   float* y;
   int M, nb, T;                 // rows, super-blocks per row, columns (dense)
   unsigned* counters;           // kXcds work-queue counters (zero at kernel start)
+  // dense split-K (nsplit == 1: none)
+  int nsplit;
+  float* part;                  // [tile][split] fp32 partial tiles
+  unsigned* tile_cnt;           // [tile] arrival counters (zero at kernel start)
   // MoE (mode kMoe)
   const int32_t* counts;        // [E] routed slots per expert
   const int32_t* offsets;       // [E+1] slot offsets into bucket
@@ -109,7 +127,10 @@ template <int MODE>
 __global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
   const int sb = blockIdx.x, ctile = blockIdx.y;
   const int s = threadIdx.x >> 5, col = threadIdx.x & 31;
-  if (P.counters != nullptr && sb == 0 && ctile == 0 && threadIdx.x < kXcds) P.counters[threadIdx.x] = 0u;
+  if (P.counters != nullptr && sb == 0 && ctile == 0) {
+    if (threadIdx.x < kXcds) P.counters[threadIdx.x] = 0u;
+    P.counters[kTileCntWord + threadIdx.x] = 0u;  // 256 threads: every split-K arrival counter
+  }
   int xrow = 0, ncols;
   if constexpr (MODE == kMoe) {
     if (ctile >= P.ct_off[P.E]) return;
@@ -502,6 +523,8 @@ struct TileRef {
   int nct;                // valid column tiles (chunks) in the tile
   int r0;                 // first row of this wave
   const uint8_t* wr;      // weight row of this lane
+  int s0, s1;             // steps of the tile's K range run here
+  int base, split;        // dense split-K: tile and split index
 };
 
 // MoE tables copied to LDS at kernel start: the tile search runs in LDS
@@ -537,8 +560,10 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
     wbase = P.w + static_cast<size_t>(e) * static_cast<size_t>(P.expert_stride);
   } else {
     const int ntile = (P.T + BN - 1) / BN;
-    m_tile = idx / ntile;
-    const int n_tile = idx % ntile;
+    R.base = __builtin_amdgcn_readfirstlane(idx / P.nsplit);
+    R.split = __builtin_amdgcn_readfirstlane(idx % P.nsplit);
+    m_tile = R.base / ntile;
+    const int n_tile = R.base % ntile;
     R.tc.n0 = n_tile * BN;
     R.tc.ncols = min(BN, P.T - R.tc.n0);
     R.tc.slot_base = 0;
@@ -552,6 +577,16 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
   R.ctile0 = __builtin_amdgcn_readfirstlane(R.ctile0);
   R.nct = (R.tc.ncols + kChunkCols - 1) / kChunkCols;
   m_tile = __builtin_amdgcn_readfirstlane(m_tile);
+  {
+    const int nsteps = FMT == QMM_Q4_K ? (P.nb + 1) >> 1 : P.nb;
+    if constexpr (MODE == kMoe) {
+      R.s0 = 0;
+      R.s1 = nsteps;
+    } else {
+      R.s0 = __builtin_amdgcn_readfirstlane(R.split * nsteps / P.nsplit);
+      R.s1 = __builtin_amdgcn_readfirstlane((R.split + 1) * nsteps / P.nsplit);
+    }
+  }
   const int rw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
   R.r0 = m_tile * kMmqBM + rw * 32;
   const int wrow = min(R.r0 + (threadIdx.x & 31), P.M - 1);
@@ -695,6 +730,52 @@ __device__ __forceinline__ void store_tile(const MmqParams& P, const TileCols& t
   }
 }
 
+// Split-K epilogue of a dense tile (all waves call it; the kh == 0 waves
+// hold the tile's partial sums).  The partial goes to the tile's slot in the
+// workspace; after a barrier, thread 0 releases the workgroup's stores at
+// device scope and bumps the tile's arrival counter.  The workgroup that
+// arrives last acquires the other splits' stores and adds the nsplit
+// partials in split order (its own from registers), so the sum does not
+// depend on which split finishes last.
+template <int NT, int MODE>
+__device__ __forceinline__ void split_store(const MmqParams& P, const TileRef& R, const v16f (&acc)[NT], int rw,
+                                            int lane, int kh, int& s_last) {
+  constexpr size_t kTile = static_cast<size_t>(4) * NT * 16 * 64;  // floats per partial tile
+  if (kh == 0) {
+    float* mine = P.part + (static_cast<size_t>(R.base) * P.nsplit + R.split) * kTile;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mine[((rw * NT + ct) * 16 + v) * 64 + lane] = acc[ct][v];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const unsigned old = atomicAdd(&P.tile_cnt[R.base], 1u);
+    s_last = old + 1 == static_cast<unsigned>(P.nsplit);
+  }
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(s_last)) {
+    __threadfence();
+    if (kh == 0) {
+      v16f sum[NT];
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sum[ct][v] = 0.0f;
+      for (int sp = 0; sp < P.nsplit; ++sp) {
+        const float* ps = P.part + (static_cast<size_t>(R.base) * P.nsplit + sp) * kTile;
+        const bool own = sp == R.split;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sum[ct][v] += own ? acc[ct][v] : ps[((rw * NT + ct) * 16 + v) * 64 + lane];
+      }
+      store_tile<NT, MODE>(P, R.tc, R.r0, sum);
+    }
+  }
+}
+
 // Work queues.  The tiles are split into kXcds contiguous ranges, one per
 // XCD (workgroup b runs on XCD b % kXcds), so a range's weight rows stay in
 // one XCD's L2.  Workgroup b takes tile b / kXcds of its range as its first
@@ -736,6 +817,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int kTab = MODE == kMoe ? kMoeMaxE + 1 : 1;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ int s_next[2];
+  __shared__ int s_last;
   __shared__ int s_work_off[kTab], s_counts[kTab], s_offsets[kTab], s_ct_off[kTab];
 
   MoeTables Tb{s_work_off, s_counts, s_offsets, s_ct_off};
@@ -752,7 +834,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 
     total = __builtin_amdgcn_readfirstlane(P.work_off[P.E]);
     __syncthreads();
   } else {
-    total = ((P.M + kMmqBM - 1) / kMmqBM) * ((P.T + 32 * NT - 1) / (32 * NT));
+    total = ((P.M + kMmqBM - 1) / kMmqBM) * ((P.T + 32 * NT - 1) / (32 * NT)) * P.nsplit;
   }
   const Queue Q = make_queue(total);
   const int b8 = static_cast<int>(blockIdx.x / kXcds);
@@ -761,7 +843,6 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kh = wave >> 2;
   float* wl = reinterpret_cast<float*>(smem + L::kWaveOff + wave * L::kWave);
-  const int nsteps = FMT == QMM_Q4_K ? (P.nb + 1) >> 1 : P.nb;
   v16i magic;
 #pragma unroll
   for (int v = 0; v < 16; ++v) magic[v] = static_cast<int>(kMagicBits);
@@ -773,7 +854,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 
   MmqPrefetch<FMT> F;
   const uint32_t lds0 = lds_addr(smem);
   {
-    const StepLoads<FMT, NT> first = step_loads<FMT, NT>(P, R, 0, lds0, true, wave, kh, g);
+    const StepLoads<FMT, NT> first = step_loads<FMT, NT>(P, R, R.s0, lds0, true, wave, kh, g);
     first.issue_all(F);
   }
   int k = 0;            // steps done by this workgroup (selects the LDS stage)
@@ -785,11 +866,11 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[ct][v] = 0.0f;
     int next = -1;
-    for (int step = 0; step < nsteps; ++step, ++k) {
+    for (int step = R.s0; step < R.s1; ++step, ++k) {
       uint8_t* st = smem + (k & 1) * L::kStage;
       const int sb = StepSplit<FMT>::sb(step, kh);
       const bool active = sb < P.nb;
-      const bool last = step + 1 == nsteps;
+      const bool last = step + 1 == R.s1;
       MmqOperand<FMT> A;
       if (active) {
         take_operand(F, A);
@@ -797,7 +878,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 
       }
       wait_vm_all();
       if (threadIdx.x == 0) {
-        if (step == 0) ticket = atomicAdd(&P.counters[Q.home], 1u);
+        if (step == R.s0) ticket = atomicAdd(&P.counters[Q.home], 1u);
         if (last) {
           const int j = Q.nw + static_cast<int>(ticket);
           s_next[it & 1] = j < Q.size ? Q.start + j : -1;
@@ -809,7 +890,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 
         if (next >= 0) tile_ref<FMT, NT, MODE>(P, Tb, next, Rn);
       }
       const uint32_t dst = lds0 + ((k + 1) & 1) * L::kStage;
-      const StepLoads<FMT, NT> pre = last ? step_loads<FMT, NT>(P, Rn, 0, dst, next >= 0, wave, kh, g)
+      const StepLoads<FMT, NT> pre = last ? step_loads<FMT, NT>(P, Rn, Rn.s0, dst, next >= 0, wave, kh, g)
                                           : step_loads<FMT, NT>(P, R, step + 1, dst, true, wave, kh, g);
       if (!StepLoads<FMT, NT>::kInLoop || !active) pre.issue_all(F);
       if (active) {
@@ -834,6 +915,10 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(2, 
         for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[ct][v] += red[((rw * NT + ct) * 16 + v) * 64 + lane];
+      }
+      if (MODE == kDense && P.nsplit > 1) {
+        split_store<NT, MODE>(P, R, acc, rw, lane, kh, s_last);
+      } else if (kh == 0) {
         store_tile<NT, MODE>(P, R.tc, R.r0, acc);
       }
     }
@@ -866,15 +951,40 @@ static int launch_mmq(const MmqParams& P, int total_tiles_hint, hipStream_t st) 
   return launch_status();
 }
 
-constexpr size_t kCounterBytes = 256;
-
 static size_t mmq_chunk_bytes(int64_t ctiles, int64_t nb) {
   return static_cast<size_t>(ctiles) * static_cast<size_t>(nb) * kChunkBytes;
 }
 
-size_t mmq_workspace_bytes(int64_t K, int64_t T) {
+// Column tiles per dense tile: two (64 tokens) for calls with more than 32
+// tokens, else one.
+static int mmq_dense_nt(int64_t T) { return T > 32 ? 2 : 1; }
+
+// Dense tiles of a call (without split) and its split-K factor.
+static int64_t mmq_dense_tiles(int64_t M, int64_t T) {
+  const int64_t bn = 32 * mmq_dense_nt(T);
+  return ((M + kMmqBM - 1) / kMmqBM) * ((T + bn - 1) / bn);
+}
+static int mmq_nsplit(int64_t M, int64_t K, int64_t T) {
+  const int64_t tiles = mmq_dense_tiles(M, T);
+  if (tiles >= kSplitTiles) return 1;
+  int64_t n = kSplitTiles / tiles;
+  const int64_t by_k = (K / kQK) / 4;  // at least four super-blocks per split
+  if (n > by_k) n = by_k;
+  if (n > kMaxSplit) n = kMaxSplit;
+  return n < 1 ? 1 : static_cast<int>(n);
+}
+static size_t mmq_part_bytes(int64_t M, int64_t K, int64_t T) {
+  const int ns = mmq_nsplit(M, K, T);
+  if (ns == 1) return 0;
+  return static_cast<size_t>(mmq_dense_tiles(M, T)) * ns * mmq_dense_nt(T) * 4 * 16 * 64 * sizeof(float);
+}
+static size_t mmq_part_offset(int64_t K, int64_t T) {
   const int64_t ctiles = (T + kChunkCols - 1) / kChunkCols;
-  return kCounterBytes + mmq_chunk_bytes(ctiles, K / kQK);
+  return (kCounterBytes + mmq_chunk_bytes(ctiles, K / kQK) + 255) / 256 * 256;
+}
+
+size_t mmq_workspace_bytes(int64_t M, int64_t K, int64_t T) {
+  return mmq_part_offset(K, T) + mmq_part_bytes(M, K, T);
 }
 
 // Upper bound of the column tiles of a grouped call: sum over experts of
@@ -887,12 +997,9 @@ size_t moe_chunk_bytes(int64_t slots, int64_t E, int64_t K) {
 // Dense tiles are 128 rows x 64 tokens (128 x 32 for calls with few tokens).
 template <int FMT>
 static int mmq_dense_fmt(const MmqParams& P, bool dbg, hipStream_t st) {
-  const int64_t mt = (P.M + kMmqBM - 1) / kMmqBM;
-  if (P.T > 32) {
-    const int tiles = static_cast<int>(mt * ((P.T + 63) / 64));
+  const int tiles = static_cast<int>(mmq_dense_tiles(P.M, P.T)) * P.nsplit;
+  if (mmq_dense_nt(P.T) == 2)
     return dbg ? launch_mmq<FMT, 2, kDebug>(P, tiles, st) : launch_mmq<FMT, 2, kDense>(P, tiles, st);
-  }
-  const int tiles = static_cast<int>(mt * ((P.T + 31) / 32));
   return dbg ? launch_mmq<FMT, 1, kDebug>(P, tiles, st) : launch_mmq<FMT, 1, kDense>(P, tiles, st);
 }
 
@@ -923,6 +1030,9 @@ int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64
   P.nb = nb;
   P.T = static_cast<int>(T);
   P.counters = static_cast<unsigned*>(ws);
+  P.tile_cnt = static_cast<unsigned*>(ws) + kTileCntWord;
+  P.nsplit = dbg ? 1 : mmq_nsplit(M, K, T);  // the integer-stage debug path writes per sub-block sums
+  P.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + mmq_part_offset(K, T));
   P.dbgD = dbgD;
   return fmt == QMM_Q4_K ? mmq_dense_fmt<QMM_Q4_K>(P, dbg, st) : mmq_dense_fmt<QMM_Q6_K>(P, dbg, st);
 }
@@ -955,6 +1065,7 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   P.M = M;
   P.nb = nb;
   P.T = 0;
+  P.nsplit = 1;
   P.counters = counters;
   P.counts = counts;
   P.offsets = offsets;
@@ -973,7 +1084,7 @@ static int check_mmq(const void* w, const void* xq, const float* y, int64_t M, i
   if (M > (1 << 30) || T > (1 << 24) || K / kQK > (1 << 16)) return QMM_ERR_SHAPE;
   if (!w || !xq || !y || !ws) return QMM_ERR_NULL;
   if (!aligned16(w) || !aligned16(xq) || !aligned16(y) || !aligned16(ws)) return QMM_ERR_ALIGN;
-  if (ws_bytes < mmq_workspace_bytes(K, T)) return QMM_ERR_WORKSPACE;
+  if (ws_bytes < mmq_workspace_bytes(M, K, T)) return QMM_ERR_WORKSPACE;
   return QMM_OK;
 }
 

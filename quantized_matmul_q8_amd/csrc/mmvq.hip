@@ -39,16 +39,19 @@ namespace qmm {
 
 constexpr int kMmvqWaves = 8;             // rows per workgroup
 constexpr int kMmvqThreads = 64 * kMmvqWaves;
-constexpr int kMmvqLdsBudget = 64 * 1024; // bytes of staged activations per workgroup
+constexpr int kMmvqLdsBudget = 68 * 1024; // bytes of staged activations per workgroup
 
-// Super-blocks per K chunk so that T tokens of staged activations fit the
-// LDS budget (1.5 bytes per activation) and the lane unit limit.
+// Super-blocks per K segment: T tokens of staged activations must fit the
+// LDS budget (1.5 bytes per activation) and the lane unit limit; the row is
+// then split into segments of equal length (a short last segment would pay
+// a whole staging round trip for a few blocks).
 static int mmvq_chunk_blocks(int nb, int T, int units_per_block, int max_units) {
   int by_lds = kMmvqLdsBudget / (T * kQK * 3 / 2);
   int by_units = 64 * max_units / units_per_block;
   int c = by_lds < by_units ? by_lds : by_units;
   if (c < 1) c = 1;
-  return c < nb ? c : nb;
+  const int nseg = (nb + c - 1) / c;
+  return (nb + nseg - 1) / nseg;
 }
 
 // Staged activations, in the order the lanes consume them (consecutive

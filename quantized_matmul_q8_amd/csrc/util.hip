@@ -5,7 +5,7 @@
 namespace qmm {
 
 size_t moe_workspace_bytes(int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k);
-size_t mmq_workspace_bytes(int64_t K, int64_t T);
+size_t mmq_workspace_bytes(int64_t M, int64_t K, int64_t T);
 int debug_mmvq(int fmt, const void* w, const void* xq, int32_t* D, int32_t* S, int64_t M, int64_t K,
                int64_t T, hipStream_t st);
 int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
@@ -83,7 +83,7 @@ extern "C" const char* qmm_status_str(int status) {
 extern "C" size_t qmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t T, int64_t E,
                                       int64_t top_k) {
   if (M < 0 || K < 0 || T < 0 || E < 0 || top_k < 0) return 0;
-  if (op == QMM_OP_MMQ) return mmq_workspace_bytes(K, T);
+  if (op == QMM_OP_MMQ) return mmq_workspace_bytes(M, K, T);
   if (op == QMM_OP_MOE) return moe_workspace_bytes(M, K, T, E, top_k);
   return 0;
 }
@@ -104,7 +104,7 @@ extern "C" int qmm_debug_subdots(int fmt, int path, const void* w, const void* x
   if (!w || !xq || !D || (fmt == QMM_Q4_K && !S)) return QMM_ERR_NULL;
   if (!aligned16(w) || !aligned16(xq) || !aligned16(D) || (S && !aligned16(S))) return QMM_ERR_ALIGN;
   if (path == 1 && (!ws || !aligned16(ws))) return ws ? QMM_ERR_ALIGN : QMM_ERR_NULL;
-  if (path == 1 && ws_bytes < mmq_workspace_bytes(K, T)) return QMM_ERR_WORKSPACE;
+  if (path == 1 && ws_bytes < mmq_workspace_bytes(M, K, T)) return QMM_ERR_WORKSPACE;
   hipStream_t st = to_stream(stream);
   const int64_t nsub = fmt == QMM_Q4_K ? K / 32 : K / 16;
   int rc = zero_fill(D, static_cast<size_t>(T * M * nsub) * 4, st);

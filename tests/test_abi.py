@@ -55,6 +55,11 @@ def test_status_strings():
 
 def test_workspace_sizes():
     assert L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 4096, 4096, 512, 0, 0) >= 36
+    # few tiles (4096 rows, 8 tokens): room for the fp32 partial tiles of the K splits
+    small = L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 4096, 11008, 8, 0, 0)
+    assert small >= 43 * 11264 + 32 * 2 * 16384
+    # one row block with many tokens needs no partials: the size grows only with T
+    assert L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 4096, 4096, 512, 0, 0) < 2048 + 16 * 16 * 11264 + 256
     moe = L.qmm_workspace_bytes(_lib.QMM_OP_MOE, 2048, 768, 512, 128, 8)
     # per-slot fp32 scratch dominates: T*top_k*M*4
     assert moe >= 512 * 8 * 2048 * 4

@@ -59,6 +59,28 @@ def test_parity_ffn_up_t1024(fmt, M, K):
     _check(fmt, w, xq, f"mmq_{fmt} {M}x{K} T=1024")
 
 
+# Calls with few tiles split each tile's K range over several workgroups
+# (partial tiles added in split order by the last one to finish): several
+# splits with ragged step ranges, two column tiles per tile, one row, and
+# the decode shape 4096 x 11008 at T = 8 and 32.
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M,K,T", [(256, 4096, 8), (130, 2816, 33), (1, 11008, 1), (100, 11008, 3),
+                                   (4096, 11008, 8), (4096, 11008, 32)])
+def test_parity_split_k(fmt, M, K, T):
+    w, xq = _inputs(fmt, M, K, T, seed=M + K + T)
+    say(f"mmq_{fmt} split-K", f"M={M} K={K} T={T}")
+    _check(fmt, w, xq, f"mmq_{fmt} {M}x{K} T={T}")
+
+
+def test_split_k_deterministic():
+    w, xq = _inputs("q6k", 4096, 11008, 16, seed=12)
+    wd, xd = dev(w), dev(xq)
+    say("mmq_q6k split-K determinism M=4096 K=11008 T=16")
+    runs = [host(qmm.mmq_q6k(wd, xd)) for _ in range(3)]
+    for r in runs[1:]:
+        assert np.array_equal(runs[0].view(np.uint32), r.view(np.uint32))
+
+
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
 @pytest.mark.parametrize("M,K,T", [(128, 256, 32), (150, 512, 70)])
 def test_integer_stage_bit_exact(fmt, M, K, T):
