@@ -101,10 +101,15 @@ int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int6
  * accumulation per sub-block, then scaled in fp32.  A first kernel repacks
  * the Q8_1 activations into `ws` (MFMA operand order plus per-block fp32
  * factors); output tiles are then claimed from per-XCD atomic counters in
- * `ws`; each tile runs its whole K loop in one workgroup (its two K halves
- * summed in a fixed order, no split across workgroups, no fixup), so results
- * are deterministic.  `ws` must hold
- * qmm_workspace_bytes(QMM_OP_MMQ, M, K, T, 0, 0) bytes; its contents are
+ * `ws`.  When the call has enough 128 x 32/64 output tiles to fill the chip,
+ * each tile runs its whole K loop in one workgroup (its two K halves summed
+ * in a fixed order, no fixup).  A call with fewer than 256 tiles (few tokens
+ * and rows) splits each tile's K range over up to 16 workgroups, which write
+ * fp32 partial tiles to `ws`; the last to finish adds them in split order.
+ * Either way the result of a call depends only on its shapes and data (the
+ * split factor is a function of M, K and T), so results are deterministic.
+ * `ws` must hold qmm_workspace_bytes(QMM_OP_MMQ, M, K, T, 0, 0) bytes (M
+ * counts: it sizes the partial tiles); its contents are
  * scratch (the call initialises what it uses, no zero-fill is needed).
  * Calls sharing one workspace must be ordered on one stream.
  * Requires M >= 1, 1 <= T <= 2^24, K % 256 == 0, K/256 <= 65536.
