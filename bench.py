@@ -19,7 +19,8 @@ The same JSON line carries:
                 decode workload (whole passes over both matrices, repeated
                 for about 10 s), in GB/s;
   also          the other kernels and workloads measured the same way:
-                matvec at T = 4, the read-only HBM ceiling probe at the
+                matvec at T = 4, matvec vs GEMM at T = 8 (the small-T
+                crossover), the read-only HBM ceiling probe at the
                 matvec byte counts, the prefill GEMMs (int8 TOPS and
                 tokens/s at T = 512 / 1024) and the routed-expert MoE FFN.
 """
@@ -48,7 +49,7 @@ ROTATE_BYTES = 4096 << 20
 
 # traffic measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE for the
 # dominant kernel (profiles/); None until taken for the current kernel
-DOMINANT_TRAFFIC_BYTES = 37233642   # mmvq_q6k, profiles/mmvq_decode_4096x11008_t1.md
+DOMINANT_TRAFFIC_BYTES = 37353919   # mmvq_q6k, profiles/mmvq_decode_4096x11008_t1.md
 
 
 def log(*a):
@@ -276,6 +277,21 @@ def main():
             nbytes = nbw + 4 * xq_bytes + 4 * M * 4
             also[name] = {"us": round(m_ * 1e3, 3), "GBps": gbps(nbytes, m_),
                           "frac_hbm": round(gbps(nbytes, m_) / HBM_PEAK_GBPS, 4)}
+
+        # small-T crossover on the decode shape: matvec vs GEMM at T = 8
+        x8 = to(qmm_synth.activations(qmm_synth.rng(8), 8, K))
+        xq8 = qmm.q8_1_quantize(x8)
+        y8 = torch.empty((8, M), dtype=torch.float32, device=dev)
+        ws8 = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MMQ, M, K, 8), dev)
+        cross = {}
+        for key, ws_, mv, mq, nbw in (("q4k", w4, qmm.mmvq_q4k, qmm.mmq_q4k, w4h.nbytes),
+                                      ("q6k", w6, qmm.mmvq_q6k, qmm.mmq_q6k, w6h.nbytes)):
+            t_mv = time_graph(torch, [lambda c=c: mv(ws_[c], xq8, out=y8) for c in range(R)], 200)
+            t_mq = time_graph(torch, [lambda c=c: mq(ws_[c], xq8, out=y8, ws=ws8) for c in range(R)], 200)
+            cross[f"mmvq_{key}_us"] = round(t_mv * 1e3, 2)
+            cross[f"mmq_{key}_us"] = round(t_mq * 1e3, 2)
+            cross[f"best_{key}_GBps"] = gbps(nbw, min(t_mv, t_mq))
+        also["decode_4096x11008_t8"] = cross
         del w4, w6
 
         # prefill GEMMs
