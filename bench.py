@@ -21,7 +21,8 @@ The same JSON line carries:
   also          the other kernels and workloads measured the same way:
                 matvec at T = 4, matvec vs GEMM at T = 8 (the small-T
                 crossover), the read-only HBM ceiling probe at the
-                matvec byte counts, the prefill GEMMs (int8 TOPS and
+                matvec byte counts, the prefill GEMMs (also from fp32
+                activations: quantize + GEMM vs the fused quantizer) (int8 TOPS and
                 tokens/s at T = 512 / 1024) and the routed-expert MoE FFN.
 """
 from __future__ import annotations
@@ -314,6 +315,21 @@ def main():
 
         wl2 = qmm_synth.workload(2)
         mmq_case("mmq_q4k_4096x4096_t512", qmm.mmq_q4k, wl2["q4k"], wl2["x"])
+        # fused quantizer prologue: fp32 activations in, against quantize + GEMM
+        wd2 = [to(wl2["q4k"]) for _ in range(4)]
+        x2 = to(wl2["x"])
+        xq2 = torch.empty((x2.shape[0], x2.shape[1] // 32, 40), dtype=torch.uint8, device=dev)
+        y2g = torch.empty((x2.shape[0], wl2["q4k"].shape[0]), dtype=torch.float32, device=dev)
+
+        def two_pass(c):
+            qmm.q8_1_quantize(x2, out=xq2)
+            qmm.mmq_q4k(wd2[c], xq2, out=y2g)
+
+        t_two = time_graph(torch, [lambda c=c: two_pass(c) for c in range(4)], 20)
+        t_fused = time_graph(torch, [lambda c=c: qmm.mmq_q4k_f32(wd2[c], x2, out=y2g) for c in range(4)], 20)
+        also["mmq_q4k_4096x4096_t512_from_fp32"] = {"quantize_then_gemm_us": round(t_two * 1e3, 2),
+                                                     "fused_us": round(t_fused * 1e3, 2)}
+        del wd2
         del wl2
         wl3 = qmm_synth.workload(3)
         mmq_case("mmq_q4k_14336x4096_t1024", qmm.mmq_q4k, wl3["q4k"], wl3["x_q4k"])

@@ -120,6 +120,22 @@ int mmq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64
             void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mmq_q4k_f32 / mmq_q6k_f32 -- the same GEMM with fp32 activations x[T][K]
+ * (row-major, 16-byte aligned), quantized to Q8_1 inside the call: the
+ * activation repack quantizes each 32-block with the steps of q8_1_quantize
+ * ([8e] §3.2) and writes the GEMM's operand chunks directly, so the Q8_1
+ * rows never go to memory ([MMQ] "What they do right": activations
+ * quantized on the way into the GEMM).  The output is bit-identical to
+ * q8_1_quantize followed by mmq_q4k / mmq_q6k on the same stream.  Same
+ * workspace (qmm_workspace_bytes(QMM_OP_MMQ, M, K, T, 0, 0)), limits and
+ * errors as mmq_q4k; x must not alias y or ws.
+ */
+int mmq_q4k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, int64_t T,
+                void* ws, size_t ws_bytes, void* stream);
+int mmq_q6k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, int64_t T,
+                void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_grouped_mmq -- routed-expert grouped GEMM ([GAP] lever T2 and its
  * de-risk paragraph: histogram of expert ids, prefix-sum offsets, per-expert
  * slot buckets, one product per expert, scatter back; [MMQ] "MoE routing

@@ -23,7 +23,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "q8_1_quantize", "mmvq_q4k", "mmvq_q6k", "mmq_q4k", "mmq_q6k", "moe_grouped_mmq",
+    "q8_1_quantize", "mmvq_q4k", "mmvq_q6k", "mmq_q4k", "mmq_q6k", "mmq_q4k_f32", "mmq_q6k_f32",
+    "moe_grouped_mmq",
     "swiglu_q8_1", "workspace", "workspace_bytes", "debug_subdots", "probe_read", "QmmError",
     "QMM_Q4_K", "QMM_Q6_K", "LIB_PATH",
 ]
@@ -145,6 +146,31 @@ def mmq_q4k(w, xq, out=None, ws=None) -> torch.Tensor:
 def mmq_q6k(w, xq, out=None, ws=None) -> torch.Tensor:
     """Prefill GEMM, Q6_K weights x Q8_1 activations -> fp32 [T, M] (int8 MFMA)."""
     return _mmq("mmq_q6k", QMM_Q6_K, w, xq, out, ws)
+
+
+def _mmq_f32(name: str, fmt: int, w, x, out, ws):
+    M, K = _weights(w, fmt)
+    _need(x, torch.float32, "x", 2)
+    if x.shape[1] != K:
+        raise ValueError(f"x: expected [T, {K}], got {tuple(x.shape)}")
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, M), dtype=torch.float32, device=w.device)
+    _need(out, torch.float32, "out", 2)
+    ws = _mmq_ws(w.device, M, K, T) if ws is None else ws
+    _need(ws, torch.uint8, "ws", 1)
+    _lib.call(name, _p(w), _p(x), _p(out), M, K, T, _p(ws), ws.numel(), _stream(w.device))
+    return out
+
+
+def mmq_q4k_f32(w, x, out=None, ws=None) -> torch.Tensor:
+    """Prefill GEMM with fp32 activations ``x[T, K]`` quantized to Q8_1 inside the call."""
+    return _mmq_f32("mmq_q4k_f32", QMM_Q4_K, w, x, out, ws)
+
+
+def mmq_q6k_f32(w, x, out=None, ws=None) -> torch.Tensor:
+    """Prefill GEMM with fp32 activations ``x[T, K]`` quantized to Q8_1 inside the call."""
+    return _mmq_f32("mmq_q6k_f32", QMM_Q6_K, w, x, out, ws)
 
 
 def moe_grouped_mmq(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.Tensor,

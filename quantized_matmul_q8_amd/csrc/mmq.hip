@@ -110,6 +110,7 @@ struct MmqParams {
 // ----------------------------------------------------------------------------
 struct RepackParams {
   const uint8_t* xq;
+  const float* xf;              // fp32 rows instead of Q8_1 (fused quantizer), or nullptr
   uint8_t* xr;
   int nb;                       // super-blocks per row
   int T;                        // dense: rows
@@ -123,17 +124,14 @@ struct RepackParams {
   unsigned* counters;           // dense: work-queue counters, zeroed here for the GEMM that follows
 };
 
+// Activation row of column `col` of chunk row `ctile` (dense: token; MoE:
+// the routed slot's row), and the number of valid columns of the chunk row.
+// Returns false when the chunk row lies past the routed column tiles.
 template <int MODE>
-__global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
-  const int sb = blockIdx.x, ctile = blockIdx.y;
-  const int s = threadIdx.x >> 5, col = threadIdx.x & 31;
-  if (P.counters != nullptr && sb == 0 && ctile == 0) {
-    if (threadIdx.x < kXcds) P.counters[threadIdx.x] = 0u;
-    P.counters[kTileCntWord + threadIdx.x] = 0u;  // 256 threads: every split-K arrival counter
-  }
-  int xrow = 0, ncols;
+__device__ __forceinline__ bool repack_row(const RepackParams& P, int ctile, int col, int& xrow, int& ncols) {
+  xrow = 0;
   if constexpr (MODE == kMoe) {
-    if (ctile >= P.ct_off[P.E]) return;
+    if (ctile >= P.ct_off[P.E]) return false;
     int lo = 0, hi = P.E;  // expert e with ct_off[e] <= ctile < ct_off[e+1]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -149,6 +147,71 @@ __global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
     ncols = min(kChunkCols, P.T - ctile * kChunkCols);
     xrow = ctile * kChunkCols + col;
   }
+  return true;
+}
+
+// Fused quantizer ([MMQ] "What they do right": activations quantized to
+// Q8_1 on the way into the GEMM): the chunk is built from fp32 rows with the
+// block quantizer of q8_1_quantize, so its bytes equal those of
+// q8_1_quantize followed by the Q8_1 repack.  Eight lanes per block; the 32
+// blocks of one pass are 8 consecutive blocks of 4 rows, so a wave reads
+// 1 KB of contiguous fp32 per row.
+template <int MODE>
+__device__ __forceinline__ void repack_f32(const RepackParams& P, int sb, int ctile) {
+  __shared__ int s_rows[kChunkCols];
+  __shared__ int s_ncols;
+  if (threadIdx.x < kChunkCols) {
+    int xrow, ncols;
+    repack_row<MODE>(P, ctile, threadIdx.x, xrow, ncols);
+    s_rows[threadIdx.x] = xrow;
+    if (threadIdx.x == 0) s_ncols = ncols;
+  }
+  __syncthreads();
+  const int ncols = s_ncols;
+  const int part = threadIdx.x & 7;
+  const size_t kf = static_cast<size_t>(P.nb) * kQK;  // floats per row
+  uint8_t* ch = P.xr + (static_cast<size_t>(ctile) * P.nb + sb) * kChunkBytes;
+  uint32_t* pay = reinterpret_cast<uint32_t*>(ch + kChunkPay);
+  float2* fac = reinterpret_cast<float2*>(ch + kChunkFac);
+  float* sig = reinterpret_cast<float*>(ch + kChunkSig);
+#pragma unroll 2
+  for (int ps = 0; ps < 8; ++ps) {
+    const int b = ps * 32 + (threadIdx.x >> 3);
+    const int s = b & 7, col = b >> 3;
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (col < ncols)
+      v = *reinterpret_cast<const float4*>(P.xf + static_cast<size_t>(s_rows[col]) * kf +
+                                           static_cast<size_t>(sb * 8 + s) * 32 + 4 * part);
+    uint32_t packed;
+    float d;
+    int S;
+    q8_1_block_8lanes_vals(v, packed, d, S);
+    pay[((2 * s + (part >> 2)) * 32 + col) * 4 + (part & 3)] = packed;
+    if (part == 0) {
+      const float beta = h2f(f2h_bits(d) & 0xffffu);  // the stored f16 scale
+      fac[s * 32 + col] = make_float2(beta, -beta * kMagic);
+      sig[s * 32 + col] = beta * static_cast<float>(S);
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
+  const int sb = blockIdx.x, ctile = blockIdx.y;
+  const int s = threadIdx.x >> 5, col = threadIdx.x & 31;
+  if (P.counters != nullptr && sb == 0 && ctile == 0) {
+    if (threadIdx.x < kXcds) P.counters[threadIdx.x] = 0u;
+    P.counters[kTileCntWord + threadIdx.x] = 0u;  // 256 threads: every split-K arrival counter
+  }
+  if (MODE != kDebug && P.xf != nullptr) {  // uniform
+    if constexpr (MODE == kMoe) {
+      if (ctile >= P.ct_off[P.E]) return;
+    }
+    repack_f32<MODE>(P, sb, ctile);
+    return;
+  }
+  int xrow, ncols;
+  if (!repack_row<MODE>(P, ctile, col, xrow, ncols)) return;
   uint2 u[5];
   if (col < ncols) {
     const uint2* src = reinterpret_cast<const uint2*>(
@@ -1004,13 +1067,14 @@ static int mmq_dense_fmt(const MmqParams& P, bool dbg, hipStream_t st) {
 }
 
 int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
-              void* ws, hipStream_t st, int32_t* dbgD, int32_t* dbgS) {
+              void* ws, hipStream_t st, int32_t* dbgD, int32_t* dbgS, const float* xf) {
   const bool dbg = dbgD != nullptr;
   uint8_t* xr = static_cast<uint8_t*>(ws) + kCounterBytes;
   const int nb = static_cast<int>(K / kQK);
   const int ctiles = static_cast<int>((T + kChunkCols - 1) / kChunkCols);
   RepackParams R{};
   R.xq = static_cast<const uint8_t*>(xq);
+  R.xf = xf;
   R.xr = xr;
   R.nb = nb;
   R.T = static_cast<int>(T);
@@ -1096,12 +1160,26 @@ extern "C" int mmq_q4k(const void* w, const void* xq, float* y, int64_t M, int64
                        void* ws, size_t ws_bytes, void* stream) {
   const int st = check_mmq(w, xq, y, M, K, T, ws, ws_bytes);
   if (st != QMM_OK) return st;
-  return mmq_dense(QMM_Q4_K, w, xq, y, M, K, T, ws, to_stream(stream), nullptr, nullptr);
+  return mmq_dense(QMM_Q4_K, w, xq, y, M, K, T, ws, to_stream(stream), nullptr, nullptr, nullptr);
 }
 
 extern "C" int mmq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
                        void* ws, size_t ws_bytes, void* stream) {
   const int st = check_mmq(w, xq, y, M, K, T, ws, ws_bytes);
   if (st != QMM_OK) return st;
-  return mmq_dense(QMM_Q6_K, w, xq, y, M, K, T, ws, to_stream(stream), nullptr, nullptr);
+  return mmq_dense(QMM_Q6_K, w, xq, y, M, K, T, ws, to_stream(stream), nullptr, nullptr, nullptr);
+}
+
+extern "C" int mmq_q4k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, int64_t T,
+                           void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_mmq(w, x, y, M, K, T, ws, ws_bytes);
+  if (st != QMM_OK) return st;
+  return mmq_dense(QMM_Q4_K, w, nullptr, y, M, K, T, ws, to_stream(stream), nullptr, nullptr, x);
+}
+
+extern "C" int mmq_q6k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, int64_t T,
+                           void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_mmq(w, x, y, M, K, T, ws, ws_bytes);
+  if (st != QMM_OK) return st;
+  return mmq_dense(QMM_Q6_K, w, nullptr, y, M, K, T, ws, to_stream(stream), nullptr, nullptr, x);
 }

@@ -121,28 +121,39 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Quantize one 32-activation block to Q8_1 with eight consecutive lanes.
 // Lane `part` (0..7) holds x[4*part .. 4*part+3]; all eight lanes must be
-// active (they exchange values).  dst is the block's 40 bytes (4-byte
-// aligned); nothing is stored when `store` is false.  Steps of [8e] §3.2
-// (max |x|, d = am/127, reciprocal, round to nearest even, clamp, pack,
-// sum), in IEEE fp32 with no contraction so the bytes are reproducible.
-__device__ __forceinline__ void q8_1_block_8lanes(float4 v, int part, uint8_t* dst, bool store) {
+// active (they exchange values).  Steps of [8e] §3.2 (max |x|, d = am/127,
+// reciprocal, round to nearest even, clamp, pack, sum), in IEEE fp32 with
+// no contraction so the bytes are reproducible.  Returns this lane's four
+// int8 values packed little-endian, the fp32 scale d (stored as f16) and
+// the block's integer sum (in every lane of the group).  Every step is
+// independent of the order of the lanes, so any caller gets the same bytes.
+__device__ __forceinline__ void q8_1_block_8lanes_vals(float4 v, uint32_t& packed, float& d, int& s) {
 #pragma clang fp contract(off)
   float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   am = fmaxf(am, __shfl_xor(am, 1));
   am = fmaxf(am, __shfl_xor(am, 2));
   am = fmaxf(am, __shfl_xor(am, 4));
-  const float d = am / 127.0f;
+  d = am / 127.0f;
   const float di = d != 0.0f ? 1.0f / d : 0.0f;
   const int q0 = max(-128, min(127, static_cast<int>(rintf(v.x * di))));
   const int q1 = max(-128, min(127, static_cast<int>(rintf(v.y * di))));
   const int q2 = max(-128, min(127, static_cast<int>(rintf(v.z * di))));
   const int q3 = max(-128, min(127, static_cast<int>(rintf(v.w * di))));
-  const uint32_t packed = (static_cast<uint32_t>(q0) & 255u) | ((static_cast<uint32_t>(q1) & 255u) << 8) |
-                          ((static_cast<uint32_t>(q2) & 255u) << 16) | (static_cast<uint32_t>(q3) << 24);
-  int s = q0 + q1 + q2 + q3;
+  packed = (static_cast<uint32_t>(q0) & 255u) | ((static_cast<uint32_t>(q1) & 255u) << 8) |
+           ((static_cast<uint32_t>(q2) & 255u) << 16) | (static_cast<uint32_t>(q3) << 24);
+  s = q0 + q1 + q2 + q3;
   s += __shfl_xor(s, 1);
   s += __shfl_xor(s, 2);
   s += __shfl_xor(s, 4);
+}
+
+// The same, stored as the block's 40 bytes at dst (4-byte aligned; nothing
+// is stored when `store` is false).
+__device__ __forceinline__ void q8_1_block_8lanes(float4 v, int part, uint8_t* dst, bool store) {
+  uint32_t packed;
+  float d;
+  int s;
+  q8_1_block_8lanes_vals(v, packed, d, s);
   if (!store) return;
   reinterpret_cast<uint32_t*>(dst + 4)[part] = packed;
   if (part == 0) {

@@ -9,7 +9,7 @@ size_t mmq_workspace_bytes(int64_t M, int64_t K, int64_t T);
 int debug_mmvq(int fmt, const void* w, const void* xq, int32_t* D, int32_t* S, int64_t M, int64_t K,
                int64_t T, hipStream_t st);
 int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
-              void* ws, hipStream_t st, int32_t* dbgD, int32_t* dbgS);
+              void* ws, hipStream_t st, int32_t* dbgD, int32_t* dbgS, const float* xf);
 
 int device_cu_count() {
   static int cache[64] = {0};
@@ -111,7 +111,7 @@ extern "C" int qmm_debug_subdots(int fmt, int path, const void* w, const void* x
   if (rc == QMM_OK && fmt == QMM_Q4_K) rc = zero_fill(S, static_cast<size_t>(T * (K / 32)) * 4, st);
   if (rc != QMM_OK) return rc;
   if (path == 0) return debug_mmvq(fmt, w, xq, D, S, M, K, T, st);
-  return mmq_dense(fmt, w, xq, nullptr, M, K, T, ws, st, D, S);
+  return mmq_dense(fmt, w, xq, nullptr, M, K, T, ws, st, D, S, nullptr);
 }
 
 extern "C" int qmm_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

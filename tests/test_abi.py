@@ -31,7 +31,8 @@ def _declared():
 
 def test_header_declares_expected_entry_points():
     names = _declared()
-    for n in ("q8_1_quantize", "mmvq_q4k", "mmvq_q6k", "mmq_q4k", "mmq_q6k", "moe_grouped_mmq"):
+    for n in ("q8_1_quantize", "mmvq_q4k", "mmvq_q6k", "mmq_q4k", "mmq_q6k", "mmq_q4k_f32", "mmq_q6k_f32",
+              "moe_grouped_mmq"):
         assert n in names
 
 
@@ -84,7 +85,7 @@ def test_mmvq_errors(fn):
     assert f(FAKE, FAKE, MISAL, 4, 256, 1, NUL) == _lib.QMM_ERR_ALIGN
 
 
-@pytest.mark.parametrize("fn", ["mmq_q4k", "mmq_q6k"])
+@pytest.mark.parametrize("fn", ["mmq_q4k", "mmq_q6k", "mmq_q4k_f32", "mmq_q6k_f32"])
 def test_mmq_errors(fn):
     f = getattr(L, fn)
     assert f(FAKE, FAKE, FAKE, 4, 256, 0, FAKE, 256, NUL) == _lib.QMM_ERR_SHAPE

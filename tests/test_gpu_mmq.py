@@ -72,6 +72,33 @@ def test_parity_split_k(fmt, M, K, T):
     _check(fmt, w, xq, f"mmq_{fmt} {M}x{K} T={T}")
 
 
+# Fused quantizer: fp32 activations quantized inside the call give the bytes
+# of q8_1_quantize, so the output equals the Q8_1 path bit for bit (one
+# tile, ragged tiles, split K, the 4096 x 4096 prefill shape), and the
+# oracle on its own Q8_1 quantization.  Rows of zeros and 1 % outliers x20
+# are included.
+F32 = {"q4k": qmm.mmq_q4k_f32, "q6k": qmm.mmq_q6k_f32}
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M,K,T", [(128, 256, 1), (130, 512, 65), (300, 768, 130), (256, 4096, 8),
+                                   (4096, 4096, 512)])
+def test_fused_quantizer_bit_identical(fmt, M, K, T):
+    g = qmm_synth.rng(M + 7 * T)
+    w = FMTS[fmt][0](g, M, K)
+    x = qmm_synth.activations(g, T, K, outlier_frac=0.01)
+    x[T // 2] = 0.0
+    wd, xd = dev(w), dev(x)
+    say(f"mmq_{fmt}_f32", f"M={M} K={K} T={T}")
+    y1 = host(F32[fmt](wd, xd))
+    y0 = host(FMTS[fmt][2](wd, qmm.q8_1_quantize(xd)))
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    if M * K * T <= 1 << 26:
+        xq = oracle.quantize_q8_1(x)
+        W, X = FMTS[fmt][1](w), oracle.q8_1_dequant(xq)
+        assert_parity(y1, oracle.dense(W, X), oracle.abs_bound(W, X), f"mmq_{fmt}_f32 {M}x{K} T={T}")
+
+
 def test_split_k_deterministic():
     w, xq = _inputs("q6k", 4096, 11008, 16, seed=12)
     wd, xd = dev(w), dev(xq)
