@@ -21,9 +21,11 @@ The same JSON line carries:
   also          the other kernels and workloads measured the same way:
                 matvec at T = 4, matvec vs GEMM at T = 8 (the small-T
                 crossover), the read-only HBM ceiling probe at the
-                matvec byte counts, the prefill GEMMs (also from fp32
-                activations: quantize + GEMM vs the fused quantizer) (int8 TOPS and
-                tokens/s at T = 512 / 1024) and the routed-expert MoE FFN.
+                matvec byte counts, the prefill GEMMs (int8 TOPS and
+                tokens/s at T = 512 / 1024; also from fp32 activations:
+                quantize + GEMM vs the fused quantizer), the routed-expert
+                MoE FFN, and the per-slot expert matvec vs grouped GEMM
+                comparator at expert shapes.
 """
 from __future__ import annotations
 
@@ -146,6 +148,41 @@ def cpu_oracle_baseline(np, wl, rows, min_seconds=10.0):
             "sample": f"{reps} passes over rows 0..{rows - 1} of the 4096x11008 Q4_K and Q6_K "
                       f"matrices at T=1 (quantize, fp64 dequantize, fp64 matvec), {dt:.1f} s wall; "
                       "dequantization single-threaded numpy, matvec on the BLAS threads"}
+
+
+def moe_comparator(torch, qmm, qmm_synth, dev):
+    """Per-slot expert matvec vs grouped GEMM at expert shapes.
+
+    128 experts of M x 2048 Q4_K (M = 512, 704), top-8, balanced routing with
+    exactly N tokens per expert (N = 8..64, T = 16 N tokens): slot t*8 + k goes
+    to expert (t*8 + k) mod 128.  Both calls produce the per-slot rows; the
+    grouped call includes its route preparation and activation repack.
+    Weights rotate over >= 4 GB of copies.
+    """
+    import numpy as np
+    E, K, top_k = 128, 2048, 8
+    out = {}
+    for M in (512, 704):
+        g = qmm_synth.rng(40 + M)
+        w1 = np.stack([qmm_synth.q4k_weights(g, M, K) for _ in range(E)])
+        wd = torch.from_numpy(w1).to(dev)
+        R = copies_for(w1.nbytes)
+        ws_ = rotated(wd, R)
+        for N in (8, 16, 32, 64):
+            T = E * N // top_k
+            ids = torch.from_numpy((np.arange(T * top_k, dtype=np.int32) % E).reshape(T, top_k)).to(dev)
+            xq = qmm.q8_1_quantize(torch.from_numpy(qmm_synth.activations(g, T, K)).to(dev))
+            y = torch.empty((T * top_k, M), dtype=torch.float32, device=dev)
+            wsp = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE, M, K, T, E, top_k), dev)
+            t_mv = time_graph(torch, [lambda c=c: qmm.moe_slot_mmvq(qmm.QMM_Q4_K, ws_[c], xq, ids, out=y)
+                                      for c in range(R)], 100)
+            t_gr = time_graph(torch, [lambda c=c: qmm.moe_grouped_mmq(qmm.QMM_Q4_K, ws_[c], xq, ids, out=y, ws=wsp)
+                                      for c in range(R)], 100)
+            out[f"M{M}_N{N}"] = {"slot_matvec_us": round(t_mv * 1e3, 2), "grouped_us": round(t_gr * 1e3, 2),
+                                 "grouped_speedup": round(t_mv / t_gr, 2)}
+            log(f"moe comparator M={M} N={N}: slot matvec {t_mv * 1e3:.1f} us, grouped {t_gr * 1e3:.1f} us")
+        del ws_, wd
+    return out
 
 
 def main():
@@ -380,6 +417,7 @@ def main():
             "TOPS": round(tops, 1), "frac_attainable": round(tops / attain, 4),
             "tokens_per_s": round(T / (ms_moe * 1e-3), 1)}
         del gu, dn
+        also["moe_comparator_e128_k2048_top8"] = moe_comparator(torch, qmm, qmm_synth, dev)
 
     cpu = None
     if not args.no_cpu_baseline:

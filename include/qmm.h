@@ -168,6 +168,22 @@ int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
                     float* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_slot_mmvq -- the per-(token, slot) expert matvec that the grouped GEMM
+ * replaces ([GAP] lever T2: the batched expert matvec re-reads an expert's
+ * weights once per routed token; its de-risk step compares the two at
+ * expert shapes).  Same arguments and per-slot output as moe_grouped_mmq
+ * with expert_weights == NULL: y[(t*top_k + k)*M + i] = W[ids[t][k]] . x_row,
+ * one matvec (the mmvq_q4k / mmvq_q6k kernel at T = 1) per routed slot, no
+ * workspace.  ids outside [0, E) are clamped (precondition; no fault).
+ * Requires 1 <= top_k <= E, T*top_k <= 65535, K % 256 == 0, the same
+ * expert-stride alignment as moe_grouped_mmq (Q4_K: multiple of 16 bytes,
+ * Q6_K: of 2), 16-byte aligned pointers.
+ */
+int moe_slot_mmvq(int fmt, const void* w, int64_t E, int64_t M, int64_t K, int64_t expert_stride_bytes,
+                  const void* xq, int64_t x_rows_per_token, const int32_t* ids, int64_t T, int64_t top_k,
+                  float* y, void* stream);
+
+/*
  * swiglu_q8_1 -- glue between the grouped gate/up and down calls: reads the
  * per-slot gate||up rows g_u[R][2*F] (fp32; gate in columns 0..F-1, up in
  * F..2F-1), computes h = silu(gate) * up in fp32 and writes Q8_1 hq[R][F/32]

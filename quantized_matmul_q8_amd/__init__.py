@@ -24,7 +24,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "q8_1_quantize", "mmvq_q4k", "mmvq_q6k", "mmq_q4k", "mmq_q6k", "mmq_q4k_f32", "mmq_q6k_f32",
-    "moe_grouped_mmq",
+    "moe_grouped_mmq", "moe_slot_mmvq",
     "swiglu_q8_1", "workspace", "workspace_bytes", "debug_subdots", "probe_read", "QmmError",
     "QMM_Q4_K", "QMM_Q6_K", "LIB_PATH",
 ]
@@ -211,6 +211,34 @@ def moe_grouped_mmq(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.Tens
     stride = w.stride(0)
     _lib.call("moe_grouped_mmq", fmt, _p(w), E, M, K, stride, _p(xq), rows_per_token, _p(ids),
               _p(expert_weights), T, top_k, _p(out), _p(ws), ws.numel(), _stream(w.device))
+    return out
+
+
+def moe_slot_mmvq(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.Tensor,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-slot expert matvec (the path the grouped GEMM replaces).
+
+    Same layouts as :func:`moe_grouped_mmq` without ``expert_weights``:
+    result [T*top_k, M], row t*top_k + k = W[ids[t, k]] . x_row.
+    """
+    _need(w, torch.uint8, "w", 4)
+    if w.shape[3] != _BLOCK_BYTES[fmt]:
+        raise ValueError("w: wrong block size for fmt")
+    E, M, K = w.shape[0], w.shape[1], w.shape[2] * 256
+    _need(ids, torch.int32, "ids", 2)
+    T, top_k = ids.shape
+    rows = _acts(xq, K)
+    if rows == T:
+        rows_per_token = 1
+    elif rows == T * top_k:
+        rows_per_token = top_k
+    else:
+        raise ValueError("xq must have T or T*top_k rows")
+    if out is None:
+        out = torch.empty((T * top_k, M), dtype=torch.float32, device=w.device)
+    _need(out, torch.float32, "out", 2)
+    _lib.call("moe_slot_mmvq", fmt, _p(w), E, M, K, w.stride(0), _p(xq), rows_per_token, _p(ids), T, top_k,
+              _p(out), _stream(w.device))
     return out
 
 

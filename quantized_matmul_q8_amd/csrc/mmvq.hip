@@ -41,6 +41,29 @@ constexpr int kMmvqWaves = 8;             // rows per workgroup
 constexpr int kMmvqThreads = 64 * kMmvqWaves;
 constexpr int kMmvqLdsBudget = 68 * 1024; // bytes of staged activations per workgroup
 
+// Per-slot routed-expert matvec (SLOT mode, T = 1): workgroup row block
+// blockIdx.x of routed slot blockIdx.y = t * top_k + k multiplies expert
+// ids[slot]'s rows (w + e * stride) with activation row t (rows_per_token
+// == 1) or slot, into output row slot.  Each slot re-reads its expert's
+// weights, which is what the grouped GEMM avoids.
+struct SlotArgs {
+  const int32_t* ids;
+  int64_t stride;  // bytes between experts
+  int E, top_k, rows_per_token;
+};
+
+// Expert weights, activation row and output row of this workgroup's slot;
+// ids outside [0, E) are clamped (a documented precondition: no fault, but
+// the row is meaningless).
+__device__ __forceinline__ void slot_rebase(const SlotArgs& S, size_t xstride, int M, const uint8_t*& w,
+                                            const uint8_t*& xq, float* __restrict__& y) {
+  const int slot = blockIdx.y;
+  const int e = min(max(S.ids[slot], 0), S.E - 1);
+  w += static_cast<size_t>(e) * static_cast<size_t>(S.stride);
+  xq += static_cast<size_t>(S.rows_per_token == 1 ? slot / S.top_k : slot) * xstride;
+  y += static_cast<size_t>(slot) * M;
+}
+
 // Super-blocks per K segment: T tokens of staged activations must fit the
 // LDS budget (1.5 bytes per activation) and the lane unit limit; the row is
 // then split into segments of equal length (a short last segment would pay
@@ -158,18 +181,19 @@ constexpr int kQ4Ahead = 2;
 // S per (t, sub-block) from row 0) instead of the scaled result.  Same
 // loads, unpacking and dot products; the two 16-weight halves of D are
 // added with integer atomics into zeroed buffers.
-template <int T, bool DEBUG>
+template <int T, bool DEBUG, bool SLOT = false>
 __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w, const uint8_t* xq,
                                                                 float* __restrict__ y, int M, int nb,
                                                                 int cb, int32_t* __restrict__ dbgD,
-                                                                int32_t* __restrict__ dbgS) {
+                                                                int32_t* __restrict__ dbgS, SlotArgs SA) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row_raw = blockIdx.x * kMmvqWaves + wave;
   const bool row_ok = row_raw < M;
   const int row = row_ok ? row_raw : M - 1;  // out-of-range waves load a valid row, store nothing
-  const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ4Bytes;
   const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
+  if constexpr (SLOT) slot_rebase(SA, xstride, M, w, xq, y);
+  const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ4Bytes;
   const uint4* stA = stage_array<QMM_Q4_K>(lds, T, cb, 0);
   const uint4* stB = stage_array<QMM_Q4_K>(lds, T, cb, 1);
   const float4* stZ = reinterpret_cast<const float4*>(stage_array<QMM_Q4_K>(lds, T, cb, 2));
@@ -308,17 +332,18 @@ __device__ __forceinline__ uint4 ld16_u(const uint8_t* p) {
   return v;
 }
 
-template <int T, bool DEBUG>
+template <int T, bool DEBUG, bool SLOT = false>
 __global__ __launch_bounds__(kMmvqThreads) void mmvq_q6k_kernel(const uint8_t* w, const uint8_t* xq,
                                                                 float* __restrict__ y, int M, int nb,
-                                                                int cb, int32_t* __restrict__ dbgD) {
+                                                                int cb, int32_t* __restrict__ dbgD, SlotArgs SA) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row_raw = blockIdx.x * kMmvqWaves + wave;
   const bool row_ok = row_raw < M;
   const int row = row_ok ? row_raw : M - 1;
-  const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ6Bytes;
   const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
+  if constexpr (SLOT) slot_rebase(SA, xstride, M, w, xq, y);
+  const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ6Bytes;
   uint8_t* wreg = lds + static_cast<size_t>(T) * cb * 8 * 48 + wave * kQ6WaveRegion;
   constexpr int RS = (T * 64 * 8 + kMmvqThreads - 1) / kMmvqThreads;
   const int pj = lane & 15, pb = lane >> 4;         // piece of a block, block within a round
@@ -436,16 +461,24 @@ static size_t mmvq_lds_bytes(int T, int cb) { return static_cast<size_t>(T) * cb
 
 template <bool DEBUG>
 static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int nb, int T,
-                           int32_t* D, int32_t* S, hipStream_t st) {
+                           int32_t* D, int32_t* S, hipStream_t st, const SlotArgs* slots = nullptr,
+                           int nslots = 0) {
   // segment: whole blocks whose 9 chunks fit kQ4Rounds rounds, within the LDS budget
   const int cb = mmvq_chunk_blocks(nb, T, 9, kQ4Rounds);
   const dim3 grid((M + kMmvqWaves - 1) / kMmvqWaves), block(kMmvqThreads);
+  const SlotArgs SA = slots ? *slots : SlotArgs{};
   const size_t lds = mmvq_lds_bytes(T, cb) + static_cast<size_t>(kMmvqWaves) * kQ4Ring * 80;
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const uint8_t* xp = static_cast<const uint8_t*>(xq);
+  if (slots) {
+    if (DEBUG || T != 1) return QMM_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((mmvq_q4k_kernel<1, false, true>), dim3(grid.x, nslots), block, lds, st, wp, xp, y, M, nb,
+                       cb, D, S, SA);
+    return launch_status();
+  }
   switch (T) {
 #define QMM_CASE(TT) \
-  case TT: hipLaunchKernelGGL((mmvq_q4k_kernel<TT, DEBUG>), grid, block, lds, st, wp, xp, y, M, nb, cb, D, S); break;
+  case TT: hipLaunchKernelGGL((mmvq_q4k_kernel<TT, DEBUG>), grid, block, lds, st, wp, xp, y, M, nb, cb, D, S, SA); break;
     QMM_CASE(1) QMM_CASE(2) QMM_CASE(3) QMM_CASE(4) QMM_CASE(5) QMM_CASE(6) QMM_CASE(7) QMM_CASE(8)
 #undef QMM_CASE
     default: return QMM_ERR_SHAPE;
@@ -460,7 +493,8 @@ static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int n
 constexpr int kQ6ActBudget = 44 * 1024;
 template <bool DEBUG>
 static int launch_mmvq_q6k(const void* w, const void* xq, float* y, int M, int nb, int T,
-                           int32_t* D, hipStream_t st) {
+                           int32_t* D, hipStream_t st, const SlotArgs* slots = nullptr, int nslots = 0) {
+  const SlotArgs SA = slots ? *slots : SlotArgs{};
   int cmax = kQ6ActBudget / (T * kQK * 3 / 2);
   if (cmax > 4 * q6_rounds(T)) cmax = 4 * q6_rounds(T);
   if (cmax < 1) cmax = 1;
@@ -470,9 +504,15 @@ static int launch_mmvq_q6k(const void* w, const void* xq, float* y, int M, int n
   const size_t lds = mmvq_lds_bytes(T, cb) + static_cast<size_t>(kMmvqWaves) * kQ6WaveRegion;
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const uint8_t* xp = static_cast<const uint8_t*>(xq);
+  if (slots) {
+    if (DEBUG || T != 1) return QMM_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((mmvq_q6k_kernel<1, false, true>), dim3(grid.x, nslots), block, lds, st, wp, xp, y, M, nb,
+                       cb, D, SA);
+    return launch_status();
+  }
   switch (T) {
 #define QMM_CASE(TT) \
-  case TT: hipLaunchKernelGGL((mmvq_q6k_kernel<TT, DEBUG>), grid, block, lds, st, wp, xp, y, M, nb, cb, D); break;
+  case TT: hipLaunchKernelGGL((mmvq_q6k_kernel<TT, DEBUG>), grid, block, lds, st, wp, xp, y, M, nb, cb, D, SA); break;
     QMM_CASE(1) QMM_CASE(2) QMM_CASE(3) QMM_CASE(4) QMM_CASE(5) QMM_CASE(6) QMM_CASE(7) QMM_CASE(8)
 #undef QMM_CASE
     default: return QMM_ERR_SHAPE;
@@ -516,4 +556,27 @@ extern "C" int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int6
   if (st != QMM_OK) return st;
   return launch_mmvq_q6k<false>(w, xq, y, static_cast<int>(M), static_cast<int>(K / kQK),
                                 static_cast<int>(T), nullptr, to_stream(stream));
+}
+
+extern "C" int moe_slot_mmvq(int fmt, const void* w, int64_t E, int64_t M, int64_t K, int64_t expert_stride_bytes,
+                             const void* xq, int64_t x_rows_per_token, const int32_t* ids, int64_t T,
+                             int64_t top_k, float* y, void* stream) {
+  if (fmt != QMM_Q4_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
+  if (E < 1 || E > (1 << 20) || M < 1 || M > 0x7fffffff || K < kQK || (K % kQK) != 0 || K / kQK > (1 << 20) ||
+      T < 1 || top_k < 1 || top_k > E || T * top_k > 65535)
+    return QMM_ERR_SHAPE;
+  if (x_rows_per_token != 1 && x_rows_per_token != top_k) return QMM_ERR_SHAPE;
+  const int64_t row_bytes = (K / kQK) * (fmt == QMM_Q4_K ? kQ4Bytes : kQ6Bytes);
+  const int64_t stride_align = fmt == QMM_Q4_K ? 16 : 2;  // Q4_K rows are read with aligned 16-byte loads
+  if (expert_stride_bytes < M * row_bytes || (expert_stride_bytes % stride_align) != 0) return QMM_ERR_SHAPE;
+  if (!w || !xq || !ids || !y) return QMM_ERR_NULL;
+  if (!aligned16(w) || !aligned16(xq) || !aligned16(ids) || !aligned16(y)) return QMM_ERR_ALIGN;
+  SlotArgs S{ids, expert_stride_bytes, static_cast<int>(E), static_cast<int>(top_k),
+             static_cast<int>(x_rows_per_token)};
+  const int nslots = static_cast<int>(T * top_k);
+  if (fmt == QMM_Q4_K)
+    return launch_mmvq_q4k<false>(w, xq, y, static_cast<int>(M), static_cast<int>(K / kQK), 1, nullptr, nullptr,
+                                  to_stream(stream), &S, nslots);
+  return launch_mmvq_q6k<false>(w, xq, y, static_cast<int>(M), static_cast<int>(K / kQK), 1, nullptr,
+                                to_stream(stream), &S, nslots);
 }

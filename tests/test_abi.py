@@ -118,6 +118,26 @@ def test_moe_errors():
     assert call() == _lib.QMM_ERR_WORKSPACE              # 16 bytes is too small
 
 
+def test_slot_mmvq_errors():
+    f = L.moe_slot_mmvq
+    ok = dict(fmt=_lib.QMM_Q4_K, w=FAKE, E=8, M=64, K=256, stride=64 * 144, xq=FAKE, rpt=1,
+              ids=FAKE, T=4, top_k=2, y=FAKE, st=NUL)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["fmt"], a["w"], a["E"], a["M"], a["K"], a["stride"], a["xq"], a["rpt"], a["ids"],
+                 a["T"], a["top_k"], a["y"], a["st"])
+
+    assert call(fmt=7) == _lib.QMM_ERR_UNSUPPORTED
+    assert call(top_k=9) == _lib.QMM_ERR_SHAPE
+    assert call(rpt=3) == _lib.QMM_ERR_SHAPE
+    assert call(K=300) == _lib.QMM_ERR_SHAPE
+    assert call(stride=64 * 144 + 8) == _lib.QMM_ERR_SHAPE
+    assert call(T=40000, top_k=2) == _lib.QMM_ERR_SHAPE      # more than 65535 slots
+    assert call(ids=NUL) == _lib.QMM_ERR_NULL
+    assert call(y=MISAL) == _lib.QMM_ERR_ALIGN
+
+
 def test_debug_and_probe_errors():
     f = L.qmm_debug_subdots
     assert f(3, 0, FAKE, FAKE, FAKE, FAKE, 4, 256, 1, FAKE, 256, NUL) == _lib.QMM_ERR_UNSUPPORTED

@@ -37,6 +37,27 @@ def test_per_slot_parity(fmt, E, M, K, T, top_k):
     assert_parity(y, ref, bound, "per-slot")
 
 
+# The per-slot expert matvec (the path the grouped GEMM replaces): parity
+# with the oracle for activation rows per token and per slot, ragged rows,
+# and agreement with the grouped GEMM's per-slot output.
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("E,M,K,T,top_k,per_slot_rows", [(8, 200, 512, 40, 2, False), (16, 99, 768, 13, 4, True),
+                                                         (128, 512, 2048, 16, 8, False)])
+def test_slot_matvec_parity(fmt, E, M, K, T, top_k, per_slot_rows):
+    g = qmm_synth.rng(3 * E + M + T)
+    w = _experts(fmt, E, M, K, g)
+    rows = T * top_k if per_slot_rows else T
+    xq = oracle.quantize_q8_1(qmm_synth.activations(g, rows, K))
+    ids, _ = qmm_synth.router(g, T, E, top_k)
+    say(f"moe_slot_mmvq {fmt}", f"E={E} M={M} K={K} T={T} top_k={top_k} rows={rows}")
+    wd, xd, idd = dev(w), dev(xq), dev(ids)
+    y = host(qmm.moe_slot_mmvq(GEN[fmt][2], wd, xd, idd))
+    ref, bound = oracle.grouped_blocks(GEN[fmt][1], w, oracle.q8_1_dequant(xq), ids, top_k if per_slot_rows else 1)
+    assert_parity(y, ref, bound, "slot matvec")
+    yg = host(qmm.moe_grouped_mmq(GEN[fmt][2], wd, xd, idd))
+    assert_parity(y, yg.astype(np.float64), 2 * bound, "slot matvec vs grouped")
+
+
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
 def test_weighted_slot_rows_parity(fmt):
     E, M, K, T, top_k = 8, 136, 512, 50, 3
