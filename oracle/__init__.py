@@ -1,4 +1,4 @@
-"""CPU oracle for the fused-dequant Q4_K / Q6_K x Q8_1 matmul path.
+"""CPU oracle for the fused-dequant Q4_K / Q5_K / Q6_K x Q8_1 matmul path.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the library imports, links or runs this
 package; only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
@@ -24,6 +24,10 @@ Readings where the pages are silent (each pinned by a test unless marked):
   not print ([8e] §3.2).  Read as the public GGUF K-quant packing.
   GGUF compatibility itself is parity unpinned (no GGUF file is available);
   the packing's bijectivity and a hand-packed block are pinned.
+* Q5_K layout: the pages name the format but do not give it.  Read as
+  GGUF's Q5_K (the Q4_K fields plus a 32-byte plane of fifth bits); GGUF
+  compatibility parity unpinned, a hand-packed block, bit bijectivity and
+  the reduction to Q4_K when the fifth bits are zero pinned.
 * Q6_K element -> (ql, qh) bit mapping: [8e] §3.1 says the formats follow
   GGUF semantics but prints no Q6_K code.  Read as GGUF's mapping; GGUF
   compatibility parity unpinned, bijectivity and hand-made blocks pinned.
@@ -35,10 +39,10 @@ Readings where the pages are silent (each pinned by a test unless marked):
   "swiglu producers", [8e] §3.2) -- parity unpinned beyond closed forms.
 """
 from .formats import (  # noqa: F401
-    q4k_fields, q4k_dequant, q6k_fields, q6k_dequant, q8_1_fields, q8_1_dequant,
+    q4k_fields, q4k_dequant, q5k_fields, q5k_dequant, q6k_fields, q6k_dequant, q8_1_fields, q8_1_dequant,
 )
 from .quantize import quantize_q8_1  # noqa: F401
 from .matmul import (  # noqa: F401
-    dense, abs_bound, q4k_subdots, q6k_subdots, q4k_factored, q6k_factored,
+    dense, abs_bound, q4k_subdots, q5k_subdots, q6k_subdots, q4k_factored, q5k_factored, q6k_factored,
 )
 from .moe import route_buckets, grouped, grouped_blocks, combine, swiglu  # noqa: F401

@@ -1,4 +1,4 @@
-"""Decoders for the Q4_K, Q6_K and Q8_1 block formats (oracle side).
+"""Decoders for the Q4_K, Q5_K, Q6_K and Q8_1 block formats (oracle side).
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -11,6 +11,7 @@ from __future__ import annotations
 import numpy as np
 
 Q4K_BYTES = 144
+Q5K_BYTES = 176
 Q6K_BYTES = 210
 Q8_1_BYTES = 40
 
@@ -19,6 +20,18 @@ def _f16_at(b: np.ndarray, off: int) -> np.ndarray:
     """Little-endian IEEE binary16 at byte offset ``off`` of the last axis, as float64."""
     two = np.ascontiguousarray(b[..., off:off + 2])
     return two.view("<f2")[..., 0].astype(np.float64)
+
+
+def _scales_mins(packed: np.ndarray):
+    """Eight 6-bit scales and mins from the 12 packed bytes of a Q4_K / Q5_K block."""
+    S = packed.astype(np.int64)
+    sc = np.empty(S.shape[:-1] + (8,), dtype=np.int64)
+    m = np.empty(S.shape[:-1] + (8,), dtype=np.int64)
+    sc[..., 0:4] = S[..., 0:4] & 63
+    m[..., 0:4] = S[..., 4:8] & 63
+    sc[..., 4:8] = (S[..., 8:12] & 15) | ((S[..., 0:4] >> 6) << 4)
+    m[..., 4:8] = (S[..., 8:12] >> 4) | ((S[..., 4:8] >> 6) << 4)
+    return sc, m
 
 
 def q4k_fields(blocks: np.ndarray):
@@ -44,13 +57,7 @@ def q4k_fields(blocks: np.ndarray):
         raise ValueError("Q4_K blocks are 144 bytes")
     d = _f16_at(b, 0)
     dmin = _f16_at(b, 2)
-    S = b[..., 4:16].astype(np.int64)
-    sc = np.empty(S.shape[:-1] + (8,), dtype=np.int64)
-    m = np.empty(S.shape[:-1] + (8,), dtype=np.int64)
-    sc[..., 0:4] = S[..., 0:4] & 63
-    m[..., 0:4] = S[..., 4:8] & 63
-    sc[..., 4:8] = (S[..., 8:12] & 15) | ((S[..., 0:4] >> 6) << 4)
-    m[..., 4:8] = (S[..., 8:12] >> 4) | ((S[..., 4:8] >> 6) << 4)
+    sc, m = _scales_mins(b[..., 4:16])
     qs = b[..., 16:144].astype(np.int64).reshape(b.shape[:-1] + (4, 32))  # [pair][l]
     lo = qs & 15          # sub-block 2*pair
     hi = qs >> 4          # sub-block 2*pair + 1
@@ -67,6 +74,45 @@ def q4k_dequant(blocks: np.ndarray) -> np.ndarray:
     d, dmin, sc, m, nib = q4k_fields(blocks)
     nib = nib.reshape(nib.shape[:-1] + (8, 32)).astype(np.float64)
     w = (d[..., None, None] * sc[..., :, None].astype(np.float64) * nib
+         - dmin[..., None, None] * m[..., :, None].astype(np.float64))
+    lead = blocks.shape[:-2]
+    return w.reshape(lead + (blocks.shape[-2] * 256,))
+
+
+def q5k_fields(blocks: np.ndarray):
+    """Fields of Q5_K super-blocks ``blocks[..., 176]``.
+
+    The pages name Q5_K as a third k-quant with matvec kernels of its own
+    ([8e] §1 and §6) but do not give its layout.  Reading: GGUF's Q5_K --
+    f16 ``d`` at byte 0, f16 ``dmin`` at 2, the 12 packed scale/min bytes of
+    Q4_K at 4, ``qh[32]`` at 16, ``qs[128]`` at 48.  Sub-block ``j`` (32
+    weights), lane ``l``: the low four bits are the nibble of
+    ``qs[32*(j // 2) + l]`` (low for even ``j``, high for odd ``j``), bit four
+    is bit ``j`` of ``qh[l]``; ``q5 = nib | hbit << 4`` (0..31).
+
+    Returns ``d, dmin`` (float64 [...]), ``sc, m`` (int64 [..., 8]) and
+    ``q5`` (int64 [..., 256]) in element order.
+    """
+    b = np.asarray(blocks, dtype=np.uint8)
+    if b.shape[-1] != Q5K_BYTES:
+        raise ValueError("Q5_K blocks are 176 bytes")
+    d = _f16_at(b, 0)
+    dmin = _f16_at(b, 2)
+    sc, m = _scales_mins(b[..., 4:16])
+    qh = b[..., 16:48].astype(np.int64)                                    # [l]
+    qs = b[..., 48:176].astype(np.int64).reshape(b.shape[:-1] + (4, 32))   # [pair][l]
+    nib = np.stack([qs & 15, qs >> 4], axis=-2).reshape(b.shape[:-1] + (8, 32))  # [j][l]
+    j = np.arange(8)[:, None]
+    hbit = (qh[..., None, :] >> j) & 1                                     # [j][l]
+    q5 = (nib | (hbit << 4)).reshape(b.shape[:-1] + (256,))
+    return d, dmin, sc, m, q5
+
+
+def q5k_dequant(blocks: np.ndarray) -> np.ndarray:
+    """Dequantised Q5_K weights ``d*sc_j*q5 - dmin*m_j``: [M, K/256, 176] -> float64 [M, K]."""
+    d, dmin, sc, m, q5 = q5k_fields(blocks)
+    q5 = q5.reshape(q5.shape[:-1] + (8, 32)).astype(np.float64)
+    w = (d[..., None, None] * sc[..., :, None].astype(np.float64) * q5
          - dmin[..., None, None] * m[..., :, None].astype(np.float64))
     lead = blocks.shape[:-2]
     return w.reshape(lead + (blocks.shape[-2] * 256,))

@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import q4k_fields, q6k_fields, q8_1_fields
+from .formats import q4k_fields, q5k_fields, q6k_fields, q8_1_fields
 
 
 def dense(W: np.ndarray, X: np.ndarray) -> np.ndarray:
@@ -84,3 +84,27 @@ def q6k_factored(wblocks: np.ndarray, xq: np.ndarray) -> np.ndarray:
     dx16 = np.repeat(dx, 2, axis=-1)                  # 32-block scale for each 16-sub-block
     scale = (d[:, :, None] * sc).reshape(M, nb * 16)
     return (dx16[:, None, :] * scale[None] * D6).sum(axis=-1)
+
+
+def q5k_subdots(wblocks: np.ndarray, xq: np.ndarray):
+    """Integer sub-block sums of a Q5_K x Q8_1 product: ``D[T, M, K/32] = sum q5 q``, ``S[T, K/32]``."""
+    M, nb = wblocks.shape[0], wblocks.shape[1]
+    _, _, _, _, q5 = q5k_fields(wblocks)
+    q5 = q5.reshape(M, nb * 8, 32)
+    _, q, _, _ = q8_1_fields(xq)
+    D = np.einsum("isk,tsk->tis", q5, q, dtype=np.int64)
+    S = q.sum(axis=-1)
+    return D, S
+
+
+def q5k_factored(wblocks: np.ndarray, xq: np.ndarray) -> np.ndarray:
+    """``y`` from the Q5_K integer sums through the min-term factorisation of [8e] §2 (fp64)."""
+    M, nb = wblocks.shape[0], wblocks.shape[1]
+    d, dmin, sc, m, _ = q5k_fields(wblocks)
+    D, S = q5k_subdots(wblocks, xq)
+    dx, _, _, _ = q8_1_fields(xq)
+    scale = (d[:, :, None] * sc).reshape(M, nb * 8)
+    mins = (dmin[:, :, None] * m).reshape(M, nb * 8)
+    main = (dx[:, None, :] * scale[None] * D).sum(axis=-1)
+    corr = (dx * S) @ mins.T
+    return main - corr

@@ -11,6 +11,10 @@ Block layouts placed here (little-endian):
   2, 12 bytes of packed 6-bit sub-block scales/mins at 4, 128 bytes of 4-bit
   values at 16 (minfer ch. 06 "decode MMVQ: dp4a integer dot products",
   section 3.2, the q4_K kernel's field reads).
+* Q5_K super-block, 256 weights in 176 bytes: f16 ``d`` at 0, f16 ``dmin`` at
+  2, the 12 packed scale/min bytes at 4, ``qh[32]`` (fifth bits) at 16,
+  ``qs[128]`` (4-bit values) at 48 (the pages name the format but not its
+  layout; GGUF's is taken).
 * Q6_K super-block, 256 weights in 210 bytes: ``ql[128]`` at 0, ``qh[64]`` at
   128, ``sc[16]`` (int8) at 192, f16 ``d`` at 208 (same page, section 3.3,
   the generator-layout pitfall).
@@ -28,14 +32,15 @@ from __future__ import annotations
 import numpy as np
 
 Q4K_BLOCK_BYTES = 144
+Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
 Q8_1_BLOCK_BYTES = 40
 SUPER_BLOCK = 256
 ACT_BLOCK = 32
 
 __all__ = [
-    "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "Q8_1_BLOCK_BYTES", "SUPER_BLOCK", "ACT_BLOCK",
-    "rng", "q4k_weights", "q6k_weights", "activations", "router", "workload",
+    "Q4K_BLOCK_BYTES", "Q5K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "Q8_1_BLOCK_BYTES", "SUPER_BLOCK", "ACT_BLOCK",
+    "rng", "q4k_weights", "q5k_weights", "q6k_weights", "activations", "router", "workload",
     "WORKLOADS",
 ]
 
@@ -63,6 +68,25 @@ def q4k_weights(g: np.random.Generator, M: int, K: int, d_sigma: float = 0.02) -
     out[:, 4:16] = scales
     out[:, 16:144] = qs
     return out.reshape(M, K // SUPER_BLOCK, Q4K_BLOCK_BYTES)
+
+
+def q5k_weights(g: np.random.Generator, M: int, K: int, d_sigma: float = 0.02) -> np.ndarray:
+    """Random Q5_K weight rows: uint8 array of shape [M, K // 256, 176]."""
+    if K % SUPER_BLOCK:
+        raise ValueError("K must be a multiple of 256")
+    nb = M * (K // SUPER_BLOCK)
+    d = _abs_normal_f16(g, nb, d_sigma)
+    dmin = _abs_normal_f16(g, nb, d_sigma)
+    scales = g.integers(0, 256, size=(nb, 12), dtype=np.uint8)
+    qh = g.integers(0, 256, size=(nb, 32), dtype=np.uint8)
+    qs = g.integers(0, 256, size=(nb, 128), dtype=np.uint8)
+    out = np.empty((nb, Q5K_BLOCK_BYTES), dtype=np.uint8)
+    out[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
+    out[:, 2:4] = dmin.view(np.uint8).reshape(nb, 2)
+    out[:, 4:16] = scales
+    out[:, 16:48] = qh
+    out[:, 48:176] = qs
+    return out.reshape(M, K // SUPER_BLOCK, Q5K_BLOCK_BYTES)
 
 
 def q6k_weights(g: np.random.Generator, M: int, K: int, d_sigma: float = 0.01) -> np.ndarray:
@@ -141,6 +165,7 @@ def workload(idx: int, T: int | None = None, rows: int | None = None, experts: i
         out["q4k"] = q4k_weights(g, M, w["K"])
         out["q6k"] = q6k_weights(g, M, w["K"])
         out["x"] = activations(g, T or max(w["T"]), w["K"])
+        out["q5k"] = q5k_weights(g, M, w["K"])      # drawn last: the tensors above keep their bytes
     elif idx == 2:
         M = rows or w["M"]
         out["q4k"] = q4k_weights(g, M, w["K"])
