@@ -57,8 +57,9 @@ typedef enum qmm_status {
     QMM_ERR_UNSUPPORTED = -6  /* unknown format / operation code                 */
 } qmm_status;
 
-/* Weight formats for moe_grouped_mmq / qmm_debug_subdots. */
+/* Weight formats for moe_grouped_mmq, moe_slot_mmvq and qmm_debug_subdots. */
 #define QMM_Q4_K 12
+#define QMM_Q5_K 13
 #define QMM_Q6_K 14
 
 /* Operation codes for qmm_workspace_bytes. */
@@ -90,6 +91,11 @@ int q8_1_quantize(const float* x, void* xq, int64_t T, int64_t K, void* stream);
  */
 int mmvq_q4k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
              void* stream);
+/* Q5_K weights ([M][K/256] blocks of 176 bytes; the pages name the format but
+ * not its layout, which is read as GGUF's: f16 d, f16 dmin, the 12 packed
+ * scale/min bytes of Q4_K, qh[32] fifth bits, qs[128] 4-bit values).  Same
+ * arguments, limits and errors as mmvq_q4k; w must be 16-byte aligned. */
+int mmvq_q5k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T, void* stream);
 int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
              void* stream);
 
@@ -173,11 +179,11 @@ int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
  * weights once per routed token; its de-risk step compares the two at
  * expert shapes).  Same arguments and per-slot output as moe_grouped_mmq
  * with expert_weights == NULL: y[(t*top_k + k)*M + i] = W[ids[t][k]] . x_row,
- * one matvec (the mmvq_q4k / mmvq_q6k kernel at T = 1) per routed slot, no
- * workspace.  ids outside [0, E) are clamped (precondition; no fault).
- * Requires 1 <= top_k <= E, T*top_k <= 65535, K % 256 == 0, the same
- * expert-stride alignment as moe_grouped_mmq (Q4_K: multiple of 16 bytes,
- * Q6_K: of 2), 16-byte aligned pointers.
+ * one matvec (the mmvq_q4k / mmvq_q5k / mmvq_q6k kernel at T = 1) per routed
+ * slot, no workspace; fmt may also be QMM_Q5_K.  ids outside [0, E) are clamped (precondition; no fault).
+ * Requires 1 <= top_k <= E, T*top_k <= 65535, K % 256 == 0, an expert
+ * stride of at least M rows and a multiple of 16 bytes (Q4_K, Q5_K) or 2
+ * (Q6_K), 16-byte aligned pointers.
  */
 int moe_slot_mmvq(int fmt, const void* w, int64_t E, int64_t M, int64_t K, int64_t expert_stride_bytes,
                   const void* xq, int64_t x_rows_per_token, const int32_t* ids, int64_t T, int64_t top_k,
@@ -210,8 +216,9 @@ const char* qmm_status_str(int status);
  * (path == 0) or MMQ (path == 1) kernel of format `fmt`, built from the same
  * source as the product kernels, writing the exact integer sub-block sums
  * instead of the scaled result.  Q4_K: D[T][M][K/32] = sum nib*q and
- * S[T][K/32] = sum q (the ones-dot on path 0, the stored sum on path 1).
- * Q6_K: D[T][M][K/16] = sum (q6-32)*q and S is not written.  T <= 8 for
+ * S[T][K/32] = sum q (the ones-dot on path 0, the stored sum on path 1);
+ * Q5_K the same with the 5-bit values (path 0 only until the GEMM reads
+ * Q5_K).  Q6_K: D[T][M][K/16] = sum (q6-32)*q and S is not written.  T <= 8 for
  * path 0.  Path 1 needs an MMQ workspace (ws, ws_bytes) like mmq_q4k; path 0
  * ignores it.  D and S are zero-filled by the call.  For tests on small
  * shapes only.

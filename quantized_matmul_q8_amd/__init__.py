@@ -6,7 +6,8 @@ raw device pointers and the current HIP stream.  Every step of the
 computation runs in the HIP kernels of ``libqmm.so``.
 
 Tensor layouts (uint8 unless stated):
-  Q4_K weights  [M, K/256, 144]      Q6_K weights  [M, K/256, 210]
+  Q4_K weights  [M, K/256, 144]      Q5_K weights  [M, K/256, 176]
+  Q6_K weights  [M, K/256, 210]
   Q8_1 blocks   [rows, K/32, 40]     outputs       float32 [T, M]
   MoE experts   [E, M, K/256, bytes] (contiguous; the expert stride is taken
                 from the tensor)
@@ -19,17 +20,17 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    QMM_MMVQ_MAX_T, QMM_OP_MMQ, QMM_OP_MOE, QMM_Q4_K, QMM_Q6_K, QmmError, LIB_PATH,
+    QMM_MMVQ_MAX_T, QMM_OP_MMQ, QMM_OP_MOE, QMM_Q4_K, QMM_Q5_K, QMM_Q6_K, QmmError, LIB_PATH,
 )
 
 __all__ = [
-    "q8_1_quantize", "mmvq_q4k", "mmvq_q6k", "mmq_q4k", "mmq_q6k", "mmq_q4k_f32", "mmq_q6k_f32",
+    "q8_1_quantize", "mmvq_q4k", "mmvq_q5k", "mmvq_q6k", "mmq_q4k", "mmq_q6k", "mmq_q4k_f32", "mmq_q6k_f32",
     "moe_grouped_mmq", "moe_slot_mmvq",
     "swiglu_q8_1", "workspace", "workspace_bytes", "debug_subdots", "probe_read", "QmmError",
-    "QMM_Q4_K", "QMM_Q6_K", "LIB_PATH",
+    "QMM_Q4_K", "QMM_Q5_K", "QMM_Q6_K", "LIB_PATH",
 ]
 
-_BLOCK_BYTES = {QMM_Q4_K: 144, QMM_Q6_K: 210}
+_BLOCK_BYTES = {QMM_Q4_K: 144, QMM_Q5_K: 176, QMM_Q6_K: 210}
 
 
 def _p(t: torch.Tensor | None):
@@ -119,6 +120,11 @@ def _mmvq(name: str, fmt: int, w, xq, out):
 def mmvq_q4k(w: torch.Tensor, xq: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Decode matvec, Q4_K weights x Q8_1 activations (T <= 8) -> fp32 [T, M]."""
     return _mmvq("mmvq_q4k", QMM_Q4_K, w, xq, out)
+
+
+def mmvq_q5k(w: torch.Tensor, xq: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode matvec, Q5_K weights x Q8_1 activations (T <= 8) -> fp32 [T, M]."""
+    return _mmvq("mmvq_q5k", QMM_Q5_K, w, xq, out)
 
 
 def mmvq_q6k(w: torch.Tensor, xq: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -257,13 +263,13 @@ def swiglu_q8_1(g_u: torch.Tensor, out: torch.Tensor | None = None) -> torch.Ten
 def debug_subdots(fmt: int, path: int, w: torch.Tensor, xq: torch.Tensor):
     """Integer stage of the MMVQ (path 0) or MMQ (path 1) kernel: (D, S) int32.
 
-    Q4_K: D [T, M, K/32], S [T, K/32]; Q6_K: D [T, M, K/16], S None.
+    Q4_K, Q5_K: D [T, M, K/32], S [T, K/32]; Q6_K: D [T, M, K/16], S None.
     """
     M, K = _weights(w, fmt)
     T = _acts(xq, K)
-    nsub = K // 32 if fmt == QMM_Q4_K else K // 16
+    nsub = K // 16 if fmt == QMM_Q6_K else K // 32
     D = torch.empty((T, M, nsub), dtype=torch.int32, device=w.device)
-    S = torch.empty((T, K // 32), dtype=torch.int32, device=w.device) if fmt == QMM_Q4_K else None
+    S = torch.empty((T, K // 32), dtype=torch.int32, device=w.device) if fmt != QMM_Q6_K else None
     ws = _mmq_ws(w.device, M, K, T)
     _lib.call("qmm_debug_subdots", fmt, path, _p(w), _p(xq), _p(D), _p(S), M, K, T, _p(ws),
               ws.numel(), _stream(w.device))

@@ -22,6 +22,7 @@ QMM_ERR_WORKSPACE = -4
 QMM_ERR_HIP = -5
 QMM_ERR_UNSUPPORTED = -6
 QMM_Q4_K = 12
+QMM_Q5_K = 13
 QMM_Q6_K = 14
 QMM_OP_MMQ = 1
 QMM_OP_MOE = 2
@@ -33,6 +34,7 @@ _vp, _i64, _sz, _i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_
 SIGNATURES = {
     "q8_1_quantize": (_i, [_vp, _vp, _i64, _i64, _vp]),
     "mmvq_q4k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "mmvq_q5k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "mmvq_q6k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "mmq_q4k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "mmq_q6k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),

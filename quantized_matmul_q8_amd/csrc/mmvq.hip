@@ -1,5 +1,5 @@
 // Decode matvec (MMVQ): y[t][i] = sum_k W[i][k] * x_t[k] for T <= 8 tokens,
-// Q4_K or Q6_K weights against Q8_1 activations.
+// Q4_K, Q5_K or Q6_K weights against Q8_1 activations.
 //
 // Method ([8e] §2 and §3.2): weights stay packed in HBM and are unpacked in
 // registers to small integers; each 4-weight group is multiplied with four
@@ -150,26 +150,38 @@ __device__ __forceinline__ void stage_acts_store(uint8_t* lds, int T, int cb, co
   }
 }
 
-// Q4_K rows are read as plain consecutive 16-byte chunks: lane l loads
-// chunks l, l + 64, l + 128, ... of its row, so each wave load instruction
-// covers 1 KB of contiguous bytes (the access pattern of the read-ceiling
-// probe; loads of 16 bytes at a 32-byte stride or per-lane header loads cost
-// 25-40% more time for the same bytes).  A 144-byte block is exactly nine
-// chunks: chunk 0 is the header (d, dmin, packed scales), chunk 1 + 2p + h
-// holds value bytes 16 + 32p + 16h .. +15, i.e. 16 weights of sub-block 2p
-// (low nibbles) and 16 of sub-block 2p + 1 (high nibbles).
+// Q4_K and Q5_K rows are read as plain consecutive 16-byte chunks: lane l
+// loads chunks l, l + 64, l + 128, ... of its row, so each wave load
+// instruction covers 1 KB of contiguous bytes (the access pattern of the
+// read-ceiling probe; loads of 16 bytes at a 32-byte stride or per-lane
+// header loads cost 25-40% more time for the same bytes).  A 144-byte Q4_K
+// block is exactly nine chunks: chunk 0 is the header (d, dmin, packed
+// scales), chunk 1 + 2p + h holds value bytes 16 + 32p + 16h .. +15, i.e. 16
+// weights of sub-block 2p (low nibbles) and 16 of sub-block 2p + 1 (high
+// nibbles).  A 176-byte Q5_K block is eleven: the same header, then the two
+// chunks of fifth bits qh[0..15] and qh[16..31], then the eight value
+// chunks; value chunk (p, h) takes its fifth bits from qh chunk h (bits 2p
+// and 2p + 1 of the bytes at the same positions).
 //
-// Rounds are consumed in load order.  In a round, header chunks are copied
-// to a per-wave ring of 16 block slots in LDS; then the (at most eight)
-// headers that arrived in this round are decoded by all 64 lanes at once,
-// lane l taking sub-block l % 8 of the (l / 8)-th of them, into a ring of
-// (d*sc, dmin*m) pairs; then each value chunk reads its two pairs with one
-// 16-byte LDS read.  Every scale is thus decoded once per row instead of
-// once per chunk, with no divergent decode path.  A block's header precedes
-// its values and a value chunk's header lies in the same or the previous
-// round (64 chunks > 9), so at most 15 blocks are live and 16 slots never
-// collide; one wave's LDS accesses execute in program order.
-constexpr int kQ4Rounds = 7;  // chunks per lane per segment (7 x 64 = 448 >= 43 blocks x 9)
+// Rounds are consumed in load order.  In a round, header (and fifth-bit)
+// chunks are copied to a per-wave ring of 16 block slots in LDS; then the
+// (at most eight) headers that arrived in this round are decoded by all 64
+// lanes at once, lane l taking sub-block l % 8 of the (l / 8)-th of them,
+// into a ring of (d*sc, dmin*m) pairs; then each value chunk reads its two
+// pairs with one 16-byte LDS read.  Every scale is thus decoded once per row
+// instead of once per chunk, with no divergent decode path.  A block's
+// header precedes its values and a value chunk's header lies in the same or
+// the previous round (64 chunks > 11), so at most 15 blocks are live and 16
+// slots never collide; one wave's LDS accesses execute in program order.
+template <int FMT>
+struct MvRow {
+  static constexpr bool kQ5 = FMT == QMM_Q5_K;
+  static constexpr int kBytes = kQ5 ? kQ5Bytes : kQ4Bytes;
+  static constexpr int kChunks = kBytes / 16;               // 16-byte chunks per block: 9 or 11
+  static constexpr int kVal0 = kQ5 ? 3 : 1;                 // first value chunk
+  static constexpr int kRounds = kQ5 ? 8 : 7;               // 64-chunk rounds per segment (43 blocks fit)
+  static constexpr int kSlot = 16 + (kQ5 ? 32 : 0) + 64;    // ring bytes per block: header, fifth bits, scales
+};
 constexpr int kQ4Ring = 16;   // block slots per wave in the header and scale rings
 // Rounds in flight ahead of the one being consumed.  Issuing every round up
 // front buys no memory parallelism (a CU's miss queue fills and the issue
@@ -181,11 +193,13 @@ constexpr int kQ4Ahead = 2;
 // S per (t, sub-block) from row 0) instead of the scaled result.  Same
 // loads, unpacking and dot products; the two 16-weight halves of D are
 // added with integer atomics into zeroed buffers.
-template <int T, bool DEBUG, bool SLOT = false>
-__global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w, const uint8_t* xq,
-                                                                float* __restrict__ y, int M, int nb,
-                                                                int cb, int32_t* __restrict__ dbgD,
-                                                                int32_t* __restrict__ dbgS, SlotArgs SA) {
+template <int FMT, int T, bool DEBUG, bool SLOT = false>
+__global__ __launch_bounds__(kMmvqThreads) void mmvq_q45k_kernel(const uint8_t* w, const uint8_t* xq,
+                                                                 float* __restrict__ y, int M, int nb,
+                                                                 int cb, int32_t* __restrict__ dbgD,
+                                                                 int32_t* __restrict__ dbgS, SlotArgs SA) {
+  using RL = MvRow<FMT>;
+  constexpr int C = RL::kChunks;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row_raw = blockIdx.x * kMmvqWaves + wave;
@@ -193,13 +207,14 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w
   const int row = row_ok ? row_raw : M - 1;  // out-of-range waves load a valid row, store nothing
   const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
   if constexpr (SLOT) slot_rebase(SA, xstride, M, w, xq, y);
-  const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ4Bytes;
+  const uint8_t* wrow = w + static_cast<size_t>(row) * nb * RL::kBytes;
   const uint4* stA = stage_array<QMM_Q4_K>(lds, T, cb, 0);
   const uint4* stB = stage_array<QMM_Q4_K>(lds, T, cb, 1);
   const float4* stZ = reinterpret_cast<const float4*>(stage_array<QMM_Q4_K>(lds, T, cb, 2));
-  uint8_t* rings = lds + static_cast<size_t>(T) * cb * 8 * 48 + static_cast<size_t>(wave) * kQ4Ring * 80;
+  uint8_t* rings = lds + static_cast<size_t>(T) * cb * 8 * 48 + static_cast<size_t>(wave) * kQ4Ring * RL::kSlot;
   uint4* hdr_ring = reinterpret_cast<uint4*>(rings);                  // [16] raw headers
-  float2* sc_ring = reinterpret_cast<float2*>(rings + kQ4Ring * 16);  // [16][8] (d*sc, dmin*m)
+  uint4* qh_ring = reinterpret_cast<uint4*>(rings + kQ4Ring * 16);    // Q5_K: [16][2] fifth-bit chunks
+  float2* sc_ring = reinterpret_cast<float2*>(rings + kQ4Ring * (RL::kSlot - 64));  // [16][8] (d*sc, dmin*m)
   constexpr int RS = (T * 64 * 8 + kMmvqThreads - 1) / kMmvqThreads;  // staging rounds bound
   float acc[T];
 #pragma unroll
@@ -208,15 +223,15 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w
   for (int b0 = 0; b0 < nb; b0 += cb) {
     const int nbc = min(cb, nb - b0);
     const int nblk = nbc * 8;   // Q8_1 blocks in this segment
-    const int nch = nbc * 9;    // 16-byte chunks of the row in this segment
+    const int nch = nbc * C;    // 16-byte chunks of the row in this segment
     // 1. activation staging loads (issued first)
     uint2 su[RS][5];
     int st[RS], sj[RS];
 #pragma unroll
     for (int r = 0; r < RS; ++r) stage_acts_load(xq, xstride, T, b0 * 8, nblk, r, su[r], st[r], sj[r]);
     // 2. every chunk of this lane (unconditional loads; extra lanes re-read the last chunk)
-    const uint8_t* seg = wrow + static_cast<size_t>(b0) * kQ4Bytes;
-    uint4 v[kQ4Rounds];
+    const uint8_t* seg = wrow + static_cast<size_t>(b0) * RL::kBytes;
+    uint4 v[RL::kRounds];
 #pragma unroll
     for (int r = 0; r < kQ4Ahead; ++r) v[r] = ld16_nt(seg + 16 * min(lane + 64 * r, nch - 1));
     __builtin_amdgcn_sched_barrier(0);
@@ -233,20 +248,23 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w
     }
     __syncthreads();
     // 4. consume the rounds in load order
-    int bl = lane / 9, k = lane - 9 * (lane / 9);  // block and chunk-in-block of chunk lane + 64 r
+    int bl = lane / C, k = lane - C * (lane / C);  // block and chunk-in-block of chunk lane + 64 r
 #pragma unroll
-    for (int r = 0; r < kQ4Rounds; ++r) {
-      if (r + kQ4Ahead < kQ4Rounds) {
+    for (int r = 0; r < RL::kRounds; ++r) {
+      if (r + kQ4Ahead < RL::kRounds) {
         v[r + kQ4Ahead] = ld16_nt(seg + 16 * min(lane + 64 * (r + kQ4Ahead), nch - 1));
         __builtin_amdgcn_sched_barrier(0);
       }
       if (64 * r >= nch) break;                 // uniform: round entirely past the segment
       const bool ok = lane + 64 * r < nch;
       if (ok && k == 0) hdr_ring[bl % kQ4Ring] = v[r];  // header chunk
+      if constexpr (RL::kQ5) {
+        if (ok && (k == 1 || k == 2)) qh_ring[(bl % kQ4Ring) * 2 + (k - 1)] = v[r];  // fifth bits
+      }
       {
-        // headers of blocks (64r + 8) / 9 .. (64r + 63) / 9 arrived in this round
-        const int bd = (64 * r + 8) / 9 + (lane >> 3), jd = lane & 7;
-        if (bd <= (64 * r + 63) / 9 && bd < nbc) {
+        // headers of blocks ceil(64r / C) .. (64r + 63) / C arrived in this round
+        const int bd = (64 * r + C - 1) / C + (lane >> 3), jd = lane & 7;
+        if (bd <= (64 * r + 63) / C && bd < nbc) {
           const uint4 hdr = hdr_ring[bd % kQ4Ring];
           int sc, m;
           q4k_scale_min(jd, hdr.y, hdr.z, hdr.w, sc, m);
@@ -254,14 +272,32 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w
               make_float2(h2f(hdr.x & 0xffffu) * static_cast<float>(sc), h2f(hdr.x >> 16) * static_cast<float>(m));
         }
       }
-      if (ok && k != 0) {
-        const int p = (k - 1) >> 1, h = (k - 1) & 1;
+      if (ok && k >= RL::kVal0) {
+        const int kv = k - RL::kVal0;  // value chunk 0..7
+        const int p = kv >> 1, h = kv & 1;
         const float4 dsm = *reinterpret_cast<const float4*>(sc_ring + (bl % kQ4Ring) * 8 + 2 * p);
         const float ds0 = dsm.x, dm0 = dsm.y, ds1 = dsm.z, dm1 = dsm.w;
         const uint32_t qw[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+        // 4-bit values of sub-blocks 2p (low nibbles) and 2p + 1 (high nibbles),
+        // with the Q5_K fifth bits as bit 4 (0..31)
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          lo[i4] = qw[i4] & 0x0f0f0f0fu;
+          hi[i4] = (qw[i4] >> 4) & 0x0f0f0f0fu;
+        }
+        if constexpr (RL::kQ5) {
+          const uint4 qhv = qh_ring[(bl % kQ4Ring) * 2 + h];
+          const uint32_t qh[4] = {qhv.x, qhv.y, qhv.z, qhv.w};
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            lo[i4] |= ((qh[i4] >> (2 * p)) & 0x01010101u) << 4;
+            hi[i4] |= ((qh[i4] >> (2 * p + 1)) & 0x01010101u) << 4;
+          }
+        }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          const size_t i = (static_cast<size_t>(t) * cb + bl) * 8 + (k - 1);
+          const size_t i = (static_cast<size_t>(t) * cb + bl) * 8 + kv;
           const uint4 xa = stA[i];  // 16 activations of sub-block 2p
           const uint4 xc = stB[i];  // 16 activations of sub-block 2p+1
           const float4 z = stZ[i];  // (d, S_h) of 2p, (d, S_h) of 2p+1
@@ -270,8 +306,8 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w
           int D0 = 0, D1 = 0;
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
-            D0 = dot4(qw[i4] & 0x0f0f0f0fu, x0[i4], D0);         // sub-block 2p: low nibbles
-            D1 = dot4((qw[i4] >> 4) & 0x0f0f0f0fu, x1[i4], D1);  // sub-block 2p+1: high nibbles
+            D0 = dot4(lo[i4], x0[i4], D0);  // sub-block 2p
+            D1 = dot4(hi[i4], x1[i4], D1);  // sub-block 2p+1
           }
           if constexpr (DEBUG) {
             if (row_ok) {
@@ -286,9 +322,13 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q4k_kernel(const uint8_t* w
           }
         }
       }
-      // chunk lane + 64 (r + 1): 64 = 7 * 9 + 1
-      bl += 7;
-      if (++k == 9) { k = 0; ++bl; }
+      // chunk lane + 64 (r + 1)
+      bl += 64 / C;
+      k += 64 % C;
+      if (k >= C) { k -= C; ++bl; }
+      // opaque, so the unrolled rounds do not precompute (and keep live)
+      // every round's ring and staging addresses from the start
+      __asm__ volatile("" : "+v"(bl), "+v"(k));
     }
   }
   if constexpr (!DEBUG) {
@@ -459,26 +499,27 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q6k_kernel(const uint8_t* w
 
 static size_t mmvq_lds_bytes(int T, int cb) { return static_cast<size_t>(T) * cb * 8 * 48; }
 
-template <bool DEBUG>
+template <bool DEBUG, int FMT = QMM_Q4_K>
 static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int nb, int T,
                            int32_t* D, int32_t* S, hipStream_t st, const SlotArgs* slots = nullptr,
                            int nslots = 0) {
-  // segment: whole blocks whose 9 chunks fit kQ4Rounds rounds, within the LDS budget
-  const int cb = mmvq_chunk_blocks(nb, T, 9, kQ4Rounds);
+  using RL = MvRow<FMT>;
+  // segment: whole blocks whose chunks fit the lane rounds, within the LDS budget
+  const int cb = mmvq_chunk_blocks(nb, T, RL::kChunks, RL::kRounds);
   const dim3 grid((M + kMmvqWaves - 1) / kMmvqWaves), block(kMmvqThreads);
   const SlotArgs SA = slots ? *slots : SlotArgs{};
-  const size_t lds = mmvq_lds_bytes(T, cb) + static_cast<size_t>(kMmvqWaves) * kQ4Ring * 80;
+  const size_t lds = mmvq_lds_bytes(T, cb) + static_cast<size_t>(kMmvqWaves) * kQ4Ring * RL::kSlot;
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const uint8_t* xp = static_cast<const uint8_t*>(xq);
   if (slots) {
     if (DEBUG || T != 1) return QMM_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((mmvq_q4k_kernel<1, false, true>), dim3(grid.x, nslots), block, lds, st, wp, xp, y, M, nb,
-                       cb, D, S, SA);
+    hipLaunchKernelGGL((mmvq_q45k_kernel<FMT, 1, false, true>), dim3(grid.x, nslots), block, lds, st, wp, xp, y,
+                       M, nb, cb, D, S, SA);
     return launch_status();
   }
   switch (T) {
 #define QMM_CASE(TT) \
-  case TT: hipLaunchKernelGGL((mmvq_q4k_kernel<TT, DEBUG>), grid, block, lds, st, wp, xp, y, M, nb, cb, D, S, SA); break;
+  case TT: hipLaunchKernelGGL((mmvq_q45k_kernel<FMT, TT, DEBUG>), grid, block, lds, st, wp, xp, y, M, nb, cb, D, S, SA); break;
     QMM_CASE(1) QMM_CASE(2) QMM_CASE(3) QMM_CASE(4) QMM_CASE(5) QMM_CASE(6) QMM_CASE(7) QMM_CASE(8)
 #undef QMM_CASE
     default: return QMM_ERR_SHAPE;
@@ -534,6 +575,9 @@ int debug_mmvq(int fmt, const void* w, const void* xq, int32_t* D, int32_t* S, i
   if (fmt == QMM_Q4_K)
     return launch_mmvq_q4k<true>(w, xq, nullptr, static_cast<int>(M), static_cast<int>(K / kQK),
                                  static_cast<int>(T), D, S, st);
+  if (fmt == QMM_Q5_K)
+    return launch_mmvq_q4k<true, QMM_Q5_K>(w, xq, nullptr, static_cast<int>(M), static_cast<int>(K / kQK),
+                                           static_cast<int>(T), D, S, st);
   return launch_mmvq_q6k<true>(w, xq, nullptr, static_cast<int>(M), static_cast<int>(K / kQK),
                                static_cast<int>(T), D, st);
 }
@@ -550,6 +594,14 @@ extern "C" int mmvq_q4k(const void* w, const void* xq, float* y, int64_t M, int6
                                 static_cast<int>(T), nullptr, nullptr, to_stream(stream));
 }
 
+extern "C" int mmvq_q5k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
+                        void* stream) {
+  const int st = check_mmvq(w, xq, y, M, K, T);
+  if (st != QMM_OK) return st;
+  return launch_mmvq_q4k<false, QMM_Q5_K>(w, xq, y, static_cast<int>(M), static_cast<int>(K / kQK),
+                                          static_cast<int>(T), nullptr, nullptr, to_stream(stream));
+}
+
 extern "C" int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
                         void* stream) {
   const int st = check_mmvq(w, xq, y, M, K, T);
@@ -561,13 +613,14 @@ extern "C" int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int6
 extern "C" int moe_slot_mmvq(int fmt, const void* w, int64_t E, int64_t M, int64_t K, int64_t expert_stride_bytes,
                              const void* xq, int64_t x_rows_per_token, const int32_t* ids, int64_t T,
                              int64_t top_k, float* y, void* stream) {
-  if (fmt != QMM_Q4_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
+  if (fmt != QMM_Q4_K && fmt != QMM_Q5_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
   if (E < 1 || E > (1 << 20) || M < 1 || M > 0x7fffffff || K < kQK || (K % kQK) != 0 || K / kQK > (1 << 20) ||
       T < 1 || top_k < 1 || top_k > E || T * top_k > 65535)
     return QMM_ERR_SHAPE;
   if (x_rows_per_token != 1 && x_rows_per_token != top_k) return QMM_ERR_SHAPE;
-  const int64_t row_bytes = (K / kQK) * (fmt == QMM_Q4_K ? kQ4Bytes : kQ6Bytes);
-  const int64_t stride_align = fmt == QMM_Q4_K ? 16 : 2;  // Q4_K rows are read with aligned 16-byte loads
+  const int64_t row_bytes = (K / kQK) * (fmt == QMM_Q4_K ? kQ4Bytes : fmt == QMM_Q5_K ? kQ5Bytes : kQ6Bytes);
+  // Q4_K / Q5_K rows are read with aligned 16-byte loads, Q6_K rows with 2-byte aligned ones
+  const int64_t stride_align = fmt == QMM_Q6_K ? 2 : 16;
   if (expert_stride_bytes < M * row_bytes || (expert_stride_bytes % stride_align) != 0) return QMM_ERR_SHAPE;
   if (!w || !xq || !ids || !y) return QMM_ERR_NULL;
   if (!aligned16(w) || !aligned16(xq) || !aligned16(ids) || !aligned16(y)) return QMM_ERR_ALIGN;
@@ -577,6 +630,9 @@ extern "C" int moe_slot_mmvq(int fmt, const void* w, int64_t E, int64_t M, int64
   if (fmt == QMM_Q4_K)
     return launch_mmvq_q4k<false>(w, xq, y, static_cast<int>(M), static_cast<int>(K / kQK), 1, nullptr, nullptr,
                                   to_stream(stream), &S, nslots);
+  if (fmt == QMM_Q5_K)
+    return launch_mmvq_q4k<false, QMM_Q5_K>(w, xq, y, static_cast<int>(M), static_cast<int>(K / kQK), 1, nullptr,
+                                            nullptr, to_stream(stream), &S, nslots);
   return launch_mmvq_q6k<false>(w, xq, y, static_cast<int>(M), static_cast<int>(K / kQK), 1, nullptr,
                                 to_stream(stream), &S, nslots);
 }

@@ -18,6 +18,7 @@ namespace qmm {
 constexpr int kQK = 256;       // weights per K-quant super-block
 constexpr int kQB = 32;        // activations per Q8_1 block
 constexpr int kQ4Bytes = 144;  // Q4_K super-block bytes
+constexpr int kQ5Bytes = 176;  // Q5_K super-block bytes
 constexpr int kQ6Bytes = 210;  // Q6_K super-block bytes
 constexpr int kQ8Bytes = 40;   // Q8_1 block bytes
 constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, each with its own L2

@@ -97,18 +97,19 @@ extern "C" int qmm_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 extern "C" int qmm_debug_subdots(int fmt, int path, const void* w, const void* xq, int32_t* D,
                                  int32_t* S, int64_t M, int64_t K, int64_t T, void* ws,
                                  size_t ws_bytes, void* stream) {
-  if (fmt != QMM_Q4_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
+  if (fmt != QMM_Q4_K && fmt != QMM_Q5_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
   if (path != 0 && path != 1) return QMM_ERR_UNSUPPORTED;
+  if (fmt == QMM_Q5_K && path == 1) return QMM_ERR_UNSUPPORTED;  // until the GEMM reads Q5_K
   if (M < 1 || K < kQK || (K % kQK) != 0 || T < 1 || M > (1 << 20) || T > (1 << 20)) return QMM_ERR_SHAPE;
   if (path == 0 && T > QMM_MMVQ_MAX_T) return QMM_ERR_SHAPE;
-  if (!w || !xq || !D || (fmt == QMM_Q4_K && !S)) return QMM_ERR_NULL;
+  if (!w || !xq || !D || (fmt != QMM_Q6_K && !S)) return QMM_ERR_NULL;
   if (!aligned16(w) || !aligned16(xq) || !aligned16(D) || (S && !aligned16(S))) return QMM_ERR_ALIGN;
   if (path == 1 && (!ws || !aligned16(ws))) return ws ? QMM_ERR_ALIGN : QMM_ERR_NULL;
   if (path == 1 && ws_bytes < mmq_workspace_bytes(M, K, T)) return QMM_ERR_WORKSPACE;
   hipStream_t st = to_stream(stream);
-  const int64_t nsub = fmt == QMM_Q4_K ? K / 32 : K / 16;
+  const int64_t nsub = fmt == QMM_Q6_K ? K / 16 : K / 32;
   int rc = zero_fill(D, static_cast<size_t>(T * M * nsub) * 4, st);
-  if (rc == QMM_OK && fmt == QMM_Q4_K) rc = zero_fill(S, static_cast<size_t>(T * (K / 32)) * 4, st);
+  if (rc == QMM_OK && fmt != QMM_Q6_K) rc = zero_fill(S, static_cast<size_t>(T * (K / 32)) * 4, st);
   if (rc != QMM_OK) return rc;
   if (path == 0) return debug_mmvq(fmt, w, xq, D, S, M, K, T, st);
   return mmq_dense(fmt, w, xq, nullptr, M, K, T, ws, st, D, S, nullptr);

@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 
 FMTS = {
     "q4k": (qmm_synth.q4k_weights, oracle.q4k_dequant, qmm.mmvq_q4k, qmm.QMM_Q4_K),
+    "q5k": (qmm_synth.q5k_weights, oracle.q5k_dequant, qmm.mmvq_q5k, qmm.QMM_Q5_K),
     "q6k": (qmm_synth.q6k_weights, oracle.q6k_dequant, qmm.mmvq_q6k, qmm.QMM_Q6_K),
 }
 CASES = [(1, 256, 1), (7, 512, 3), (37, 1280, 8), (64, 2304, 4), (5, 256, 2), (1024, 1024, 1),
@@ -32,7 +33,7 @@ def _inputs(fmt, M, K, T, seed):
     return w, x, oracle.quantize_q8_1(x)
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,K,T", CASES)
 def test_parity(fmt, M, K, T):
     w, x, xq = _inputs(fmt, M, K, T, seed=M + K + T)
@@ -42,7 +43,7 @@ def test_parity(fmt, M, K, T):
     assert_parity(y, oracle.dense(W, X), oracle.abs_bound(W, X), f"mmvq_{fmt} {M}x{K} T={T}")
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_end_to_end_from_fp32(fmt):
     # GPU quantizer feeding the GPU matvec, as in the decode step
     w, x, xq = _inputs(fmt, 300, 2048, 2, seed=5)
@@ -52,14 +53,14 @@ def test_end_to_end_from_fp32(fmt):
     assert_parity(y, oracle.dense(W, X), oracle.abs_bound(W, X), fmt)
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,K,T", [(3, 256, 1), (9, 768, 4), (33, 1024, 8)])
 def test_integer_stage_bit_exact(fmt, M, K, T):
     w, x, xq = _inputs(fmt, M, K, T, seed=7 * M + T)
     say(f"debug_subdots path=0 {fmt}", f"M={M} K={K} T={T}")
     D, S = qmm.debug_subdots(FMTS[fmt][3], 0, dev(w), dev(xq))
-    if fmt == "q4k":
-        Dr, Sr = oracle.q4k_subdots(w, xq)
+    if fmt in ("q4k", "q5k"):
+        Dr, Sr = (oracle.q4k_subdots if fmt == "q4k" else oracle.q5k_subdots)(w, xq)
         assert np.array_equal(host(S), Sr)
     else:
         Dr = oracle.q6k_subdots(w, xq)
@@ -74,6 +75,26 @@ def test_zero_scales_give_exact_zero():
     say("mmvq_q4k zero scales")
     y = host(qmm.mmvq_q4k(dev(w), dev(xq)))
     assert not y.any()
+
+
+def test_q5k_without_fifth_bits_equals_q4k():
+    # Blocks whose fifth bits are zero: the Q5_K kernel's integer sums equal
+    # the Q4_K kernel's on the same d, dmin, scales and values; the fp32
+    # results (summed in another lane order: 11 vs 9 chunks per block) both
+    # meet the Q4_K oracle.
+    g = qmm_synth.rng(17)
+    w5 = qmm_synth.q5k_weights(g, 300, 2304)
+    w5[..., 16:48] = 0
+    w4 = np.ascontiguousarray(np.concatenate([w5[..., 0:16], w5[..., 48:176]], axis=-1))
+    xq = oracle.quantize_q8_1(qmm_synth.activations(g, 3, 2304))
+    say("mmvq_q5k vs mmvq_q4k, zero fifth bits")
+    D5, S5 = qmm.debug_subdots(qmm.QMM_Q5_K, 0, dev(w5), dev(xq))
+    D4, S4 = qmm.debug_subdots(qmm.QMM_Q4_K, 0, dev(w4), dev(xq))
+    assert np.array_equal(host(D5), host(D4)) and np.array_equal(host(S5), host(S4))
+    W, X = oracle.q4k_dequant(w4), oracle.q8_1_dequant(xq)
+    ref, bound = oracle.dense(W, X), oracle.abs_bound(W, X)
+    assert_parity(host(qmm.mmvq_q5k(dev(w5), dev(xq))), ref, bound, "q5k zero fifth bits")
+    assert_parity(host(qmm.mmvq_q4k(dev(w4), dev(xq))), ref, bound, "q4k")
 
 
 def test_deterministic():
