@@ -19,7 +19,8 @@ The same JSON line carries:
                 decode workload (whole passes over both matrices, repeated
                 for about 10 s), in GB/s;
   also          the other kernels and workloads measured the same way:
-                matvec at T = 4, matvec vs GEMM at T = 8 (the small-T
+                matvec at T = 4, the Q5_K matvec (T = 1, 4) and GEMM
+                (4096 x 4096, T = 512), matvec vs GEMM at T = 8 (the small-T
                 crossover), the read-only HBM ceiling probe at the
                 matvec byte counts, the prefill GEMMs (int8 TOPS and
                 tokens/s at T = 512 / 1024; also from fp32 activations:
@@ -316,6 +317,18 @@ def main():
             also[name] = {"us": round(m_ * 1e3, 3), "GBps": gbps(nbytes, m_),
                           "frac_hbm": round(gbps(nbytes, m_) / HBM_PEAK_GBPS, 4)}
 
+        # third format: Q5_K matvec on the decode shape, T = 1 and 4
+        w5h = wl["q5k"]
+        w5 = rotated(to(w5h), copies_for(w5h.nbytes))
+        for name, xq_, T_ in (("mmvq_q5k_t1", xq1, 1), ("mmvq_q5k_t4", xq4, 4)):
+            y5 = torch.empty((T_, M), dtype=torch.float32, device=dev)
+            m_ = time_graph(torch, [lambda c=c, xq_=xq_, y5=y5: qmm.mmvq_q5k(w5[c], xq_, out=y5)
+                                    for c in range(len(w5))], 200)
+            nbytes = w5h.nbytes + T_ * xq_bytes + T_ * M * 4
+            also[name] = {"us": round(m_ * 1e3, 3), "GBps": gbps(nbytes, m_),
+                          "frac_hbm": round(gbps(nbytes, m_) / HBM_PEAK_GBPS, 4)}
+        del w5
+
         # small-T crossover on the decode shape: matvec vs GEMM at T = 8
         x8 = to(qmm_synth.activations(qmm_synth.rng(8), 8, K))
         xq8 = qmm.q8_1_quantize(x8)
@@ -352,6 +365,8 @@ def main():
 
         wl2 = qmm_synth.workload(2)
         mmq_case("mmq_q4k_4096x4096_t512", qmm.mmq_q4k, wl2["q4k"], wl2["x"])
+        mmq_case("mmq_q5k_4096x4096_t512", qmm.mmq_q5k, qmm_synth.q5k_weights(qmm_synth.rng(52), 4096, 4096),
+                 wl2["x"])
         # fused quantizer prologue: fp32 activations in, against quantize + GEMM
         wd2 = [to(wl2["q4k"]) for _ in range(4)]
         x2 = to(wl2["x"])

@@ -122,6 +122,11 @@ int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int6
  */
 int mmq_q4k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
             void* ws, size_t ws_bytes, void* stream);
+/* Q5_K weights (layout as for mmvq_q5k); same arguments, workspace, limits and
+ * errors as mmq_q4k.  The fifth bit of each weight joins its 4-bit value in
+ * the int8 MFMA operand (values 0..31). */
+int mmq_q5k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
+            void* ws, size_t ws_bytes, void* stream);
 int mmq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
             void* ws, size_t ws_bytes, void* stream);
 
@@ -138,6 +143,8 @@ int mmq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64
  */
 int mmq_q4k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, int64_t T,
                 void* ws, size_t ws_bytes, void* stream);
+int mmq_q5k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, int64_t T,
+                void* ws, size_t ws_bytes, void* stream);
 int mmq_q6k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, int64_t T,
                 void* ws, size_t ws_bytes, void* stream);
 
@@ -146,7 +153,7 @@ int mmq_q6k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, i
  * de-risk paragraph: histogram of expert ids, prefix-sum offsets, per-expert
  * slot buckets, one product per expert, scatter back; [MMQ] "MoE routing
  * (fused gather)": work entries (expert, m_tile, n_tile)).
- *   fmt                  QMM_Q4_K or QMM_Q6_K
+ *   fmt                  QMM_Q4_K, QMM_Q5_K or QMM_Q6_K
  *   w                    E experts, each M rows of K weights, expert e at
  *                        (const char*)w + e*expert_stride_bytes
  *   xq                   Q8_1 activations, rows of K/32 blocks: T rows when
@@ -217,8 +224,7 @@ const char* qmm_status_str(int status);
  * source as the product kernels, writing the exact integer sub-block sums
  * instead of the scaled result.  Q4_K: D[T][M][K/32] = sum nib*q and
  * S[T][K/32] = sum q (the ones-dot on path 0, the stored sum on path 1);
- * Q5_K the same with the 5-bit values (path 0 only until the GEMM reads
- * Q5_K).  Q6_K: D[T][M][K/16] = sum (q6-32)*q and S is not written.  T <= 8 for
+ * Q5_K the same with the 5-bit values.  Q6_K: D[T][M][K/16] = sum (q6-32)*q and S is not written.  T <= 8 for
  * path 0.  Path 1 needs an MMQ workspace (ws, ws_bytes) like mmq_q4k; path 0
  * ignores it.  D and S are zero-filled by the call.  For tests on small
  * shapes only.

@@ -24,7 +24,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "q8_1_quantize", "mmvq_q4k", "mmvq_q5k", "mmvq_q6k", "mmq_q4k", "mmq_q6k", "mmq_q4k_f32", "mmq_q6k_f32",
+    "q8_1_quantize", "mmvq_q4k", "mmvq_q5k", "mmvq_q6k", "mmq_q4k", "mmq_q5k", "mmq_q6k", "mmq_q4k_f32", "mmq_q5k_f32",
+    "mmq_q6k_f32",
     "moe_grouped_mmq", "moe_slot_mmvq",
     "swiglu_q8_1", "workspace", "workspace_bytes", "debug_subdots", "probe_read", "QmmError",
     "QMM_Q4_K", "QMM_Q5_K", "QMM_Q6_K", "LIB_PATH",
@@ -149,6 +150,11 @@ def mmq_q4k(w, xq, out=None, ws=None) -> torch.Tensor:
     return _mmq("mmq_q4k", QMM_Q4_K, w, xq, out, ws)
 
 
+def mmq_q5k(w, xq, out=None, ws=None) -> torch.Tensor:
+    """Prefill GEMM, Q5_K weights x Q8_1 activations -> fp32 [T, M] (int8 MFMA)."""
+    return _mmq("mmq_q5k", QMM_Q5_K, w, xq, out, ws)
+
+
 def mmq_q6k(w, xq, out=None, ws=None) -> torch.Tensor:
     """Prefill GEMM, Q6_K weights x Q8_1 activations -> fp32 [T, M] (int8 MFMA)."""
     return _mmq("mmq_q6k", QMM_Q6_K, w, xq, out, ws)
@@ -172,6 +178,11 @@ def _mmq_f32(name: str, fmt: int, w, x, out, ws):
 def mmq_q4k_f32(w, x, out=None, ws=None) -> torch.Tensor:
     """Prefill GEMM with fp32 activations ``x[T, K]`` quantized to Q8_1 inside the call."""
     return _mmq_f32("mmq_q4k_f32", QMM_Q4_K, w, x, out, ws)
+
+
+def mmq_q5k_f32(w, x, out=None, ws=None) -> torch.Tensor:
+    """Prefill GEMM with fp32 activations ``x[T, K]`` quantized to Q8_1 inside the call."""
+    return _mmq_f32("mmq_q5k_f32", QMM_Q5_K, w, x, out, ws)
 
 
 def mmq_q6k_f32(w, x, out=None, ws=None) -> torch.Tensor:

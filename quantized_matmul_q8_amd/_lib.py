@@ -37,8 +37,10 @@ SIGNATURES = {
     "mmvq_q5k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "mmvq_q6k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "mmq_q4k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "mmq_q5k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "mmq_q6k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "mmq_q4k_f32": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "mmq_q5k_f32": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "mmq_q6k_f32": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "moe_grouped_mmq": (_i, [_i, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64,
                              _vp, _vp, _sz, _vp]),

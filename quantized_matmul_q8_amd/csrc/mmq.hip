@@ -73,6 +73,11 @@ constexpr int kChunkKB = kChunkBytes / 1024;
 
 enum MmqMode { kDense = 0, kMoe = 1, kDebug = 2 };
 
+// Q4_K and Q5_K share the kernel's structure (32-weight sub-blocks = Q8_1
+// blocks, a 6-bit scale and min per sub-block, the min term); Q5_K adds a
+// fifth bit per weight to the A operand.
+__host__ __device__ constexpr bool is_q4fam(int fmt) { return fmt == QMM_Q4_K || fmt == QMM_Q5_K; }
+
 // Split-K of dense calls with few tiles: split until about kSplitTiles
 // tiles, at most kMaxSplit ways and at least four super-blocks per split.
 constexpr int kSplitTiles = 256;
@@ -246,13 +251,13 @@ __global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
 // budget).  Either way a wave multiplies 8 MFMA sub-blocks per step.
 template <int FMT>
 struct StepSplit {
-  static constexpr int kSbPerStep = FMT == QMM_Q4_K ? 2 : 1;
+  static constexpr int kSbPerStep = is_q4fam(FMT) ? 2 : 1;
   static constexpr int kNU = 8;                        // MFMA sub-blocks per wave per step
-  static constexpr int kSubsPerSb = FMT == QMM_Q4_K ? 8 : 16;
-  __device__ __forceinline__ static int sb(int step, int kh) { return FMT == QMM_Q4_K ? 2 * step + kh : step; }
-  __device__ __forceinline__ static int u0(int kh) { return FMT == QMM_Q4_K ? 0 : 8 * kh; }   // first sub-block
-  __device__ __forceinline__ static int chunk_half(int kh) { return FMT == QMM_Q4_K ? kh : 0; }
-  static int nsteps(int nb) { return FMT == QMM_Q4_K ? (nb + 1) / 2 : nb; }
+  static constexpr int kSubsPerSb = is_q4fam(FMT) ? 8 : 16;
+  __device__ __forceinline__ static int sb(int step, int kh) { return is_q4fam(FMT) ? 2 * step + kh : step; }
+  __device__ __forceinline__ static int u0(int kh) { return is_q4fam(FMT) ? 0 : 8 * kh; }   // first sub-block
+  __device__ __forceinline__ static int chunk_half(int kh) { return is_q4fam(FMT) ? kh : 0; }
+  static int nsteps(int nb) { return is_q4fam(FMT) ? (nb + 1) / 2 : nb; }
 };
 
 template <int FMT, int NT>
@@ -260,7 +265,7 @@ struct MmqSmem {
   static constexpr int kChunks = StepSplit<FMT>::kSbPerStep * NT * kChunkBytes;  // [half][ct] chunks
   static constexpr int kRed = 4 * NT * 16 * 64 * 4;                             // split-K reduction
   static constexpr int kStage = kChunks > kRed ? kChunks : kRed;
-  static constexpr int kWave = (8 * 32 + (FMT == QMM_Q4_K ? 8 * 32 : 0)) * 4;  // alpha (+ -dmin*m), 8 sub-blocks
+  static constexpr int kWave = (8 * 32 + (is_q4fam(FMT) ? 8 * 32 : 0)) * 4;  // alpha (+ -dmin*m), 8 sub-blocks
   static constexpr int kWaveOff = 2 * kStage;
   static constexpr int kBytes = kWaveOff + kMmqWaves * kWave;
 };
@@ -273,6 +278,12 @@ template <>
 struct MmqPrefetch<QMM_Q4_K> {
   uint4 hdr;   // d, dmin, packed scales
   uint4 q[4];  // bytes 16 + 32p + 16g .. +15: nibbles of sub-blocks 2p, 2p+1 for this lane's k-group
+};
+template <>
+struct MmqPrefetch<QMM_Q5_K> {
+  uint4 hdr;   // d, dmin, packed scales
+  uint4 q[4];  // bytes 48 + 32p + 16g .. +15: nibbles of sub-blocks 2p, 2p+1 for this lane's k-group
+  uint4 qh;    // bytes 16 + 16g .. +15: the fifth bits of the same 16 weights of every sub-block
 };
 template <>
 struct MmqPrefetch<QMM_Q6_K> {
@@ -312,6 +323,17 @@ __device__ __forceinline__ void load_weight_slot(MmqPrefetch<QMM_Q4_K>& F, const
   for (int p = 0; p < 4; ++p)
     if (u == p + 1) F.q[p] = ld16_a16(blk + 16 + 32 * p + 16 * g);
 }
+//   Q5_K: as Q4_K with the values at 48 + 32p + 16g; slot 5 the fifth bits
+//   16 + 16g .. +15.
+__device__ __forceinline__ void load_weight_slot(MmqPrefetch<QMM_Q5_K>& F, const uint8_t* wr, int sb, int g,
+                                                 int u, int /*kh: whole block*/) {
+  const uint8_t* blk = wr + static_cast<size_t>(sb) * kQ5Bytes;
+  if (u == 0) F.hdr = ld16_a16(blk);
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    if (u == p + 1) F.q[p] = ld16_a16(blk + 48 + 32 * p + 16 * g);
+  if (u == 5) F.qh = ld16_a16(blk + 16 + 16 * g);
+}
 __device__ __forceinline__ void load_weight_slot(MmqPrefetch<QMM_Q6_K>& F, const uint8_t* wr, int sb, int g,
                                                  int u, int kh) {
   // half kh of the block: qh bytes 128 + 32kh + 16hf + 8g, ql bytes
@@ -343,6 +365,10 @@ struct MmqOperand<QMM_Q4_K> {
   uint4 q[4];
 };
 template <>
+struct MmqOperand<QMM_Q5_K> {
+  uint4 q[4], qh;
+};
+template <>
 struct MmqOperand<QMM_Q6_K> {
   uint2 ql[2][2], qh[2];  // this half's [parity][16-half] low-nibble bytes, [16-half] high-bit bytes
 };
@@ -350,6 +376,11 @@ struct MmqOperand<QMM_Q6_K> {
 __device__ __forceinline__ void take_operand(const MmqPrefetch<QMM_Q4_K>& F, MmqOperand<QMM_Q4_K>& A) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) A.q[p] = F.q[p];
+}
+__device__ __forceinline__ void take_operand(const MmqPrefetch<QMM_Q5_K>& F, MmqOperand<QMM_Q5_K>& A) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) A.q[p] = F.q[p];
+  A.qh = F.qh;
 }
 __device__ __forceinline__ void take_operand(const MmqPrefetch<QMM_Q6_K>& F, MmqOperand<QMM_Q6_K>& A) {
 #pragma unroll
@@ -362,7 +393,8 @@ __device__ __forceinline__ void take_operand(const MmqPrefetch<QMM_Q6_K>& F, Mmq
 
 // Decoded weight scales of this wave's rows to the wave's LDS region:
 // alpha[u][row] = d*sc and, for Q4_K, mu[j][row] = -dmin*m.
-__device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q4_K>& F, float* wave_lds, int col, int g) {
+template <int FMT>
+__device__ __forceinline__ void write_scales_q4fam(const MmqPrefetch<FMT>& F, float* wave_lds, int col, int g) {
   // lane (row col, half g) decodes sub-blocks 4g .. 4g+3 of its row
   const float d = h2f(F.hdr.x & 0xffffu), dmin = h2f(F.hdr.x >> 16);
   float* wa = wave_lds;
@@ -374,6 +406,12 @@ __device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q4_K>& F, flo
     wa[(4 * g + jj) * 32 + col] = d * static_cast<float>(sc);
     wm[(4 * g + jj) * 32 + col] = -(dmin * static_cast<float>(m));
   }
+}
+__device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q4_K>& F, float* wave_lds, int col, int g) {
+  write_scales_q4fam(F, wave_lds, col, g);
+}
+__device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q5_K>& F, float* wave_lds, int col, int g) {
+  write_scales_q4fam(F, wave_lds, col, g);
 }
 __device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q6_K>& F, float* wave_lds, int col, int g) {
   // lane (row col, k-group g) holds scales 8kh + 4g .. +3 of its row: local sub-blocks 4g .. 4g+3
@@ -389,7 +427,7 @@ __device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q6_K>& F, flo
 // and for Q4_K at odd u the min-term operands of sub-blocks u-1, u.
 template <int FMT, int NT>
 struct SubOps {
-  using BQ = std::conditional_t<FMT == QMM_Q4_K, v4i, long>;
+  using BQ = std::conditional_t<is_q4fam(FMT), v4i, long>;
   float al[16];
   float2 bp[NT];
   BQ bq[NT];
@@ -403,11 +441,11 @@ struct SubOps {
 template <int FMT, int NT>
 __device__ __forceinline__ void load_sub(const uint8_t* st, const float* wl, int u, int ul, SubOps<FMT, NT>& O) {
   const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
-  const int s = FMT == QMM_Q4_K ? u : u >> 1;
+  const int s = is_q4fam(FMT) ? u : u >> 1;
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
     const uint8_t* ch = st + ct * kChunkBytes;
-    if constexpr (FMT == QMM_Q4_K)
+    if constexpr (is_q4fam(FMT))
       O.bq[ct] = *reinterpret_cast<const v4i*>(ch + kChunkPay + ((2 * s + g) * 32 + col) * 16);
     else
       O.bq[ct] = *reinterpret_cast<const long*>(ch + kChunkPay + ((2 * s + (u & 1)) * 32 + col) * 16 + 8 * g);
@@ -419,7 +457,7 @@ __device__ __forceinline__ void load_sub(const uint8_t* st, const float* wl, int
     const float4 t4 = *reinterpret_cast<const float4*>(wa + 8 * k);
     O.al[4 * k] = t4.x; O.al[4 * k + 1] = t4.y; O.al[4 * k + 2] = t4.z; O.al[4 * k + 3] = t4.w;
   }
-  if constexpr (FMT == QMM_Q4_K) {
+  if constexpr (is_q4fam(FMT)) {
     if (u & 1) {
       O.am = wl[8 * 32 + (u - 1 + g) * 32 + col];
 #pragma unroll
@@ -439,6 +477,15 @@ __device__ __forceinline__ v4i build_a(const MmqOperand<QMM_Q4_K>& A, int u) {
   const int sh = (u & 1) * 4;
   return v4i{static_cast<int>((qv.x >> sh) & 0x0f0f0f0fu), static_cast<int>((qv.y >> sh) & 0x0f0f0f0fu),
              static_cast<int>((qv.z >> sh) & 0x0f0f0f0fu), static_cast<int>((qv.w >> sh) & 0x0f0f0f0fu)};
+}
+//   Q5_K: as Q4_K with bit u of the fifth-bit bytes as bit 4 (0..31).
+__device__ __forceinline__ v4i build_a(const MmqOperand<QMM_Q5_K>& A, int u) {
+  const uint4 qv = A.q[u >> 1];
+  const int sh = (u & 1) * 4;
+  return v4i{static_cast<int>(((qv.x >> sh) & 0x0f0f0f0fu) | (((A.qh.x >> u) & 0x01010101u) << 4)),
+             static_cast<int>(((qv.y >> sh) & 0x0f0f0f0fu) | (((A.qh.y >> u) & 0x01010101u) << 4)),
+             static_cast<int>(((qv.z >> sh) & 0x0f0f0f0fu) | (((A.qh.z >> u) & 0x01010101u) << 4)),
+             static_cast<int>(((qv.w >> sh) & 0x0f0f0f0fu) | (((A.qh.w >> u) & 0x01010101u) << 4))};
 }
 constexpr uint32_t kQ6HiTable = 0x1000F0E0u;  // bytes -32, -16, 0, 16 as int8
 __device__ __forceinline__ long build_a(const MmqOperand<QMM_Q6_K>& A, int u) {
@@ -504,7 +551,7 @@ __device__ __forceinline__ void mmq_epilogue(const MmqParams& P, const TileCols&
       const float t = __builtin_fmaf(bp.x, Xf[v], bp.y);
       acc[ct][v] = __builtin_fmaf(Ou.al[v], t, acc[ct][v]);
     }
-    if constexpr (FMT == QMM_Q4_K) {
+    if constexpr (is_q4fam(FMT)) {
       // min term, K = 2 fp32 MFMA over sub-blocks u-1, u (lane half g
       // takes u-1+g): A[i][k] = -dmin*m, B[k][j] = beta*S
       if (u & 1) acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ou.am, Ou.bm[ct], acc[ct], 0, 0, 0);
@@ -641,7 +688,7 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
   R.nct = (R.tc.ncols + kChunkCols - 1) / kChunkCols;
   m_tile = __builtin_amdgcn_readfirstlane(m_tile);
   {
-    const int nsteps = FMT == QMM_Q4_K ? (P.nb + 1) >> 1 : P.nb;
+    const int nsteps = is_q4fam(FMT) ? (P.nb + 1) >> 1 : P.nb;
     if constexpr (MODE == kMoe) {
       R.s0 = 0;
       R.s1 = nsteps;
@@ -653,7 +700,7 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
   const int rw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
   R.r0 = m_tile * kMmqBM + rw * 32;
   const int wrow = min(R.r0 + (threadIdx.x & 31), P.M - 1);
-  constexpr int kRowBytes = FMT == QMM_Q4_K ? kQ4Bytes : kQ6Bytes;
+  constexpr int kRowBytes = FMT == QMM_Q4_K ? kQ4Bytes : FMT == QMM_Q5_K ? kQ5Bytes : kQ6Bytes;
   R.wr = wbase + static_cast<size_t>(wrow) * P.nb * kRowBytes;
 }
 
@@ -689,12 +736,12 @@ struct StepLoads {
   static constexpr int NU = SP::kNU;                          // slots per step
   static constexpr int kInstr = SP::kSbPerStep * NT * kChunkKB;
   static constexpr int kDma = (kInstr + kMmqWaves - 1) / kMmqWaves;  // chunk copies per wave
-  static constexpr int kW = FMT == QMM_Q4_K ? 5 : 8;           // weight loads per wave
+  static constexpr int kW = FMT == QMM_Q4_K ? 5 : FMT == QMM_Q5_K ? 6 : 8;  // weight loads per wave
   // Q4_K spreads its loads over the sub-block loop of the previous step;
   // Q6_K issues them all before it (spread out, they keep enough address
   // registers live to overflow its register budget)
-  static constexpr bool kInLoop = FMT == QMM_Q4_K;
-  static constexpr int kWs = FMT == QMM_Q4_K ? kW : 0;  // weight loads spread over the slots
+  static constexpr bool kInLoop = is_q4fam(FMT);
+  static constexpr int kWs = is_q4fam(FMT) ? kW : 0;  // weight loads spread over the slots
   static constexpr int kL = kDma + kWs;                  // loads spread over the slots
   const uint8_t* xr;       // chunk (ctile0, 0) of the loaded tile
   const uint8_t* wr;       // this lane's weight row of the loaded tile
@@ -736,7 +783,7 @@ struct StepLoads {
         wi = kPair + (i - 2 * kPair);
       }
       if (di >= 0) dma(di);
-      if constexpr (FMT == QMM_Q4_K) {
+      if constexpr (is_q4fam(FMT)) {
         if (wi >= 0 && sbw < nb) load_weight_slot(F, wr, sbw, g, wi, kh);
       }
     }
@@ -1098,7 +1145,9 @@ int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64
   P.nsplit = dbg ? 1 : mmq_nsplit(M, K, T);  // the integer-stage debug path writes per sub-block sums
   P.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + mmq_part_offset(K, T));
   P.dbgD = dbgD;
-  return fmt == QMM_Q4_K ? mmq_dense_fmt<QMM_Q4_K>(P, dbg, st) : mmq_dense_fmt<QMM_Q6_K>(P, dbg, st);
+  if (fmt == QMM_Q4_K) return mmq_dense_fmt<QMM_Q4_K>(P, dbg, st);
+  if (fmt == QMM_Q5_K) return mmq_dense_fmt<QMM_Q5_K>(P, dbg, st);
+  return mmq_dense_fmt<QMM_Q6_K>(P, dbg, st);
 }
 
 // Grouped launch used by moe_grouped_mmq (after route preparation on the
@@ -1139,6 +1188,7 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   P.E = E;
   P.expert_stride = stride;
   if (fmt == QMM_Q4_K) return launch_mmq<QMM_Q4_K, 1, kMoe>(P, 0, st);
+  if (fmt == QMM_Q5_K) return launch_mmq<QMM_Q5_K, 1, kMoe>(P, 0, st);
   return launch_mmq<QMM_Q6_K, 1, kMoe>(P, 0, st);
 }
 
@@ -1163,6 +1213,13 @@ extern "C" int mmq_q4k(const void* w, const void* xq, float* y, int64_t M, int64
   return mmq_dense(QMM_Q4_K, w, xq, y, M, K, T, ws, to_stream(stream), nullptr, nullptr, nullptr);
 }
 
+extern "C" int mmq_q5k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
+                       void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_mmq(w, xq, y, M, K, T, ws, ws_bytes);
+  if (st != QMM_OK) return st;
+  return mmq_dense(QMM_Q5_K, w, xq, y, M, K, T, ws, to_stream(stream), nullptr, nullptr, nullptr);
+}
+
 extern "C" int mmq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
                        void* ws, size_t ws_bytes, void* stream) {
   const int st = check_mmq(w, xq, y, M, K, T, ws, ws_bytes);
@@ -1175,6 +1232,13 @@ extern "C" int mmq_q4k_f32(const void* w, const float* x, float* y, int64_t M, i
   const int st = check_mmq(w, x, y, M, K, T, ws, ws_bytes);
   if (st != QMM_OK) return st;
   return mmq_dense(QMM_Q4_K, w, nullptr, y, M, K, T, ws, to_stream(stream), nullptr, nullptr, x);
+}
+
+extern "C" int mmq_q5k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, int64_t T,
+                           void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_mmq(w, x, y, M, K, T, ws, ws_bytes);
+  if (st != QMM_OK) return st;
+  return mmq_dense(QMM_Q5_K, w, nullptr, y, M, K, T, ws, to_stream(stream), nullptr, nullptr, x);
 }
 
 extern "C" int mmq_q6k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, int64_t T,

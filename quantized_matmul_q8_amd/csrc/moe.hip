@@ -241,14 +241,14 @@ extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int
                                int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,
                                const int32_t* ids, const float* expert_weights, int64_t T,
                                int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream) {
-  if (fmt != QMM_Q4_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
+  if (fmt != QMM_Q4_K && fmt != QMM_Q5_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
   if (E < 1 || E > kMoeMaxE || M < 1 || M > (1 << 30) || K < kQK || (K % kQK) != 0 || T < 1 ||
       top_k < 1 || top_k > E || top_k > kMoeMaxTopK || T * top_k > (1 << 30))
     return QMM_ERR_SHAPE;
   if (x_rows_per_token != 1 && x_rows_per_token != top_k) return QMM_ERR_SHAPE;
-  const int64_t row_bytes = (K / kQK) * (fmt == QMM_Q4_K ? kQ4Bytes : kQ6Bytes);
-  // Q4_K blocks are read with 16-byte loads, Q6_K blocks with 2-byte aligned ones
-  const int64_t stride_align = fmt == QMM_Q4_K ? 16 : 2;
+  const int64_t row_bytes = (K / kQK) * (fmt == QMM_Q4_K ? kQ4Bytes : fmt == QMM_Q5_K ? kQ5Bytes : kQ6Bytes);
+  // Q4_K / Q5_K blocks are read with 16-byte loads, Q6_K blocks with 2-byte aligned ones
+  const int64_t stride_align = fmt == QMM_Q6_K ? 2 : 16;
   if (expert_stride_bytes < M * row_bytes || (expert_stride_bytes % stride_align) != 0) return QMM_ERR_SHAPE;
   if (!w || !xq || !ids || !y || !ws) return QMM_ERR_NULL;
   if (!aligned16(w) || !aligned16(xq) || !aligned16(ids) || !aligned16(y) || !aligned16(ws) ||

@@ -99,7 +99,6 @@ extern "C" int qmm_debug_subdots(int fmt, int path, const void* w, const void* x
                                  size_t ws_bytes, void* stream) {
   if (fmt != QMM_Q4_K && fmt != QMM_Q5_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
   if (path != 0 && path != 1) return QMM_ERR_UNSUPPORTED;
-  if (fmt == QMM_Q5_K && path == 1) return QMM_ERR_UNSUPPORTED;  // until the GEMM reads Q5_K
   if (M < 1 || K < kQK || (K % kQK) != 0 || T < 1 || M > (1 << 20) || T > (1 << 20)) return QMM_ERR_SHAPE;
   if (path == 0 && T > QMM_MMVQ_MAX_T) return QMM_ERR_SHAPE;
   if (!w || !xq || !D || (fmt != QMM_Q6_K && !S)) return QMM_ERR_NULL;

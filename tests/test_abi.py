@@ -75,7 +75,7 @@ def test_quantize_errors():
     assert L.q8_1_quantize(NUL, NUL, 0, 32, NUL) == _lib.QMM_OK      # T = 0 is a no-op
 
 
-@pytest.mark.parametrize("fn", ["mmvq_q4k", "mmvq_q6k"])
+@pytest.mark.parametrize("fn", ["mmvq_q4k", "mmvq_q5k", "mmvq_q6k"])
 def test_mmvq_errors(fn):
     f = getattr(L, fn)
     assert f(FAKE, FAKE, FAKE, 4, 300, 1, NUL) == _lib.QMM_ERR_SHAPE     # K % 256
@@ -85,7 +85,7 @@ def test_mmvq_errors(fn):
     assert f(FAKE, FAKE, MISAL, 4, 256, 1, NUL) == _lib.QMM_ERR_ALIGN
 
 
-@pytest.mark.parametrize("fn", ["mmq_q4k", "mmq_q6k", "mmq_q4k_f32", "mmq_q6k_f32"])
+@pytest.mark.parametrize("fn", ["mmq_q4k", "mmq_q5k", "mmq_q6k", "mmq_q4k_f32", "mmq_q5k_f32", "mmq_q6k_f32"])
 def test_mmq_errors(fn):
     f = getattr(L, fn)
     assert f(FAKE, FAKE, FAKE, 4, 256, 0, FAKE, 256, NUL) == _lib.QMM_ERR_SHAPE

@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 FMTS = {
     "q4k": (qmm_synth.q4k_weights, oracle.q4k_dequant, qmm.mmq_q4k, qmm.QMM_Q4_K),
+    "q5k": (qmm_synth.q5k_weights, oracle.q5k_dequant, qmm.mmq_q5k, qmm.QMM_Q5_K),
     "q6k": (qmm_synth.q6k_weights, oracle.q6k_dequant, qmm.mmq_q6k, qmm.QMM_Q6_K),
 }
 
@@ -37,7 +38,7 @@ def _check(fmt, w, xq, what):
     return y
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,K,T", [(128, 256, 64), (130, 512, 65), (300, 768, 130), (1, 256, 1),
                                    (129, 1024, 1), (64, 512, 200), (517, 256, 33)])
 def test_parity_small(fmt, M, K, T):
@@ -63,7 +64,7 @@ def test_parity_ffn_up_t1024(fmt, M, K):
 # (partial tiles added in split order by the last one to finish): several
 # splits with ragged step ranges, two column tiles per tile, one row, and
 # the decode shape 4096 x 11008 at T = 8 and 32.
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,K,T", [(256, 4096, 8), (130, 2816, 33), (1, 11008, 1), (100, 11008, 3),
                                    (4096, 11008, 8), (4096, 11008, 32)])
 def test_parity_split_k(fmt, M, K, T):
@@ -77,10 +78,10 @@ def test_parity_split_k(fmt, M, K, T):
 # tile, ragged tiles, split K, the 4096 x 4096 prefill shape), and the
 # oracle on its own Q8_1 quantization.  Rows of zeros and 1 % outliers x20
 # are included.
-F32 = {"q4k": qmm.mmq_q4k_f32, "q6k": qmm.mmq_q6k_f32}
+F32 = {"q4k": qmm.mmq_q4k_f32, "q5k": qmm.mmq_q5k_f32, "q6k": qmm.mmq_q6k_f32}
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,K,T", [(128, 256, 1), (130, 512, 65), (300, 768, 130), (256, 4096, 8),
                                    (4096, 4096, 512)])
 def test_fused_quantizer_bit_identical(fmt, M, K, T):
@@ -99,6 +100,12 @@ def test_fused_quantizer_bit_identical(fmt, M, K, T):
         assert_parity(y1, oracle.dense(W, X), oracle.abs_bound(W, X), f"mmq_{fmt}_f32 {M}x{K} T={T}")
 
 
+def test_q5k_prefill_4096x4096_t512():
+    w, xq = _inputs("q5k", 4096, 4096, 512, seed=5)
+    say("mmq_q5k", "M=4096 K=4096 T=512")
+    _check("q5k", w, xq, "mmq_q5k 4096x4096 T=512")
+
+
 def test_split_k_deterministic():
     w, xq = _inputs("q6k", 4096, 11008, 16, seed=12)
     wd, xd = dev(w), dev(xq)
@@ -108,21 +115,21 @@ def test_split_k_deterministic():
         assert np.array_equal(runs[0].view(np.uint32), r.view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,K,T", [(128, 256, 32), (150, 512, 70)])
 def test_integer_stage_bit_exact(fmt, M, K, T):
     w, xq = _inputs(fmt, M, K, T, seed=M + 2 * T)
     say(f"debug_subdots path=1 {fmt}", f"M={M} K={K} T={T}")
     D, S = qmm.debug_subdots(FMTS[fmt][3], 1, dev(w), dev(xq))
-    if fmt == "q4k":
-        Dr, Sr = oracle.q4k_subdots(w, xq)
+    if fmt in ("q4k", "q5k"):
+        Dr, Sr = (oracle.q4k_subdots if fmt == "q4k" else oracle.q5k_subdots)(w, xq)
         assert np.array_equal(host(S), Sr)
     else:
         Dr = oracle.q6k_subdots(w, xq)
     assert np.array_equal(host(D), Dr)
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_matvec_and_gemm_integer_stages_agree(fmt):
     w, xq = _inputs(fmt, 96, 1024, 4, seed=9)
     say(f"debug_subdots path 0 vs 1 {fmt}", "M=96 K=1024 T=4")

@@ -25,7 +25,7 @@ def _experts(fmt, E, M, K, g):
     return np.stack([GEN[fmt][0](g, M, K) for _ in range(E)])
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("E,M,K,T,top_k", [(8, 200, 512, 40, 2), (4, 128, 256, 70, 1), (16, 300, 768, 33, 4)])
 def test_per_slot_parity(fmt, E, M, K, T, top_k):
     g = qmm_synth.rng(E + M + T)
@@ -55,12 +55,11 @@ def test_slot_matvec_parity(fmt, E, M, K, T, top_k, per_slot_rows):
     y = host(qmm.moe_slot_mmvq(GEN[fmt][2], wd, xd, idd))
     ref, bound = oracle.grouped_blocks(GEN[fmt][1], w, oracle.q8_1_dequant(xq), ids, top_k if per_slot_rows else 1)
     assert_parity(y, ref, bound, "slot matvec")
-    if fmt != "q5k":   # the grouped GEMM reads Q4_K and Q6_K
-        yg = host(qmm.moe_grouped_mmq(GEN[fmt][2], wd, xd, idd))
-        assert_parity(y, yg.astype(np.float64), 2 * bound, "slot matvec vs grouped")
+    yg = host(qmm.moe_grouped_mmq(GEN[fmt][2], wd, xd, idd))
+    assert_parity(y, yg.astype(np.float64), 2 * bound, "slot matvec vs grouped")
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_weighted_slot_rows_parity(fmt):
     E, M, K, T, top_k = 8, 136, 512, 50, 3
     g = qmm_synth.rng(21)
