@@ -179,14 +179,22 @@ __device__ __forceinline__ void repack_f32(const RepackParams& P, int sb, int ct
   uint32_t* pay = reinterpret_cast<uint32_t*>(ch + kChunkPay);
   float2* fac = reinterpret_cast<float2*>(ch + kChunkFac);
   float* sig = reinterpret_cast<float*>(ch + kChunkSig);
-#pragma unroll 2
+  // every pass's load first (eight 16-byte loads in flight per thread)
+  float4 vs[8];
+#pragma unroll
   for (int ps = 0; ps < 8; ++ps) {
     const int b = ps * 32 + (threadIdx.x >> 3);
     const int s = b & 7, col = b >> 3;
-    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    vs[ps] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (col < ncols)
-      v = *reinterpret_cast<const float4*>(P.xf + static_cast<size_t>(s_rows[col]) * kf +
-                                           static_cast<size_t>(sb * 8 + s) * 32 + 4 * part);
+      vs[ps] = *reinterpret_cast<const float4*>(P.xf + static_cast<size_t>(s_rows[col]) * kf +
+                                                static_cast<size_t>(sb * 8 + s) * 32 + 4 * part);
+  }
+#pragma unroll
+  for (int ps = 0; ps < 8; ++ps) {
+    const int b = ps * 32 + (threadIdx.x >> 3);
+    const int s = b & 7, col = b >> 3;
+    const float4 v = vs[ps];
     uint32_t packed;
     float d;
     int S;
