@@ -81,9 +81,14 @@ size_t moe_workspace_bytes(int64_t M, int64_t K, int64_t T, int64_t E, int64_t t
   return moe_layout(nullptr, M, K, T, E, top_k).bytes;
 }
 
+// Lanes of the wave holding the same expert id as this lane (v: lane
+// valid): one ballot per id bit, for the ids' bits below nbits (<= 9, since
+// E <= kMoeMaxE = 512; the loop has a fixed trip count so it unrolls).
 __device__ __forceinline__ uint64_t peers_of(int e, bool v, int nbits) {
   uint64_t peers = __ballot(v);
-  for (int b = 0; b < nbits; ++b) {
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    if (b >= nbits) break;  // uniform
     const bool bit = (e >> b) & 1;
     const uint64_t m = __ballot(v && bit);
     peers &= bit ? m : ~m;
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
   const int beg = wave * per, end = min(n, beg + per);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  // pass 1: per-(wave, expert) counts
+  // pass 1: per-(wave, expert) counts (LDS atomics: counts need no order)
   for (int base = beg; base < end; base += 64 * kRouteBatch) {
     int ev[kRouteBatch];
 #pragma unroll
@@ -124,9 +129,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
 #pragma unroll
     for (int r = 0; r < kRouteBatch; ++r) {
       const int e = ev[r];
-      const bool v = e >= 0 && e < E;
-      const uint64_t peers = peers_of(e, v, nbits);
-      if (v && __popcll(peers & below) == 0) cnt[wave][e] += __popcll(peers);
+      if (e >= 0 && e < E) atomicAdd(&cnt[wave][e], 1);
     }
   }
   __syncthreads();
