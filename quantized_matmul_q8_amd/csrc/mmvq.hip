@@ -327,8 +327,9 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q45k_kernel(const uint8_t* 
       k += 64 % C;
       if (k >= C) { k -= C; ++bl; }
       // opaque, so the unrolled rounds do not precompute (and keep live)
-      // every round's ring and staging addresses from the start
-      __asm__ volatile("" : "+v"(bl), "+v"(k));
+      // every round's ring and staging addresses from the start; Q4_K at
+      // T = 1 fits four waves per SIMD either way and runs faster without
+      if constexpr (T >= 2 || RL::kQ5) __asm__ volatile("" : "+v"(bl), "+v"(k));
     }
   }
   if constexpr (!DEBUG) {
