@@ -1,5 +1,5 @@
 /*
- * qmm.h -- C ABI of libqmm: fused-dequant matmul of Q4_K / Q6_K weights with
+ * qmm.h -- C ABI of libqmm: fused-dequant matmul of Q4_K / Q5_K / Q6_K weights with
  * Q8_1-quantized activations on AMD Instinct MI355X (gfx950).
  *
  * Pages cited (title, then section):

@@ -1,4 +1,4 @@
-"""Python binding of libqmm: fused-dequant Q4_K / Q6_K x Q8_1 matmul on MI355X.
+"""Python binding of libqmm: fused-dequant Q4_K / Q5_K / Q6_K x Q8_1 matmul on MI355X.
 
 Thin marshalling over the C ABI of ``include/qmm.h``: each function checks
 tensor dtypes, devices and shapes, allocates outputs with torch, and passes

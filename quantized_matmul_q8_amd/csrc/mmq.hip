@@ -1,5 +1,5 @@
 // Prefill GEMM (MMQ) and its MoE grouped form: y[t][i] = sum_k W[i][k] x_t[k]
-// for many tokens, Q4_K or Q6_K weights against Q8_1 activations, on int8
+// for many tokens, Q4_K, Q5_K or Q6_K weights against Q8_1 activations, on int8
 // MFMA with int32 accumulation per sub-block and an fp32 epilogue.
 //
 // Prior art: [MMQ] "Kernel architecture" (tiles of weights x tokens, dequant

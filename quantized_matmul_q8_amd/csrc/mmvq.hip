@@ -13,26 +13,29 @@
 // Geometry for MI355X.  [8e] §2 describes the MMVQ geometry of a 48-SM
 // LPDDR part (256 threads per row, one row per block) and its lesson: the
 // kernel is latency-bound until enough loads are in flight.  Here:
-// * one wave64 per weight row, eight rows per 512-thread workgroup; the
-//   row's units of 64 weights (Q4_K: the 32 value bytes of sub-blocks 2p and
-//   2p+1 plus the block header; Q6_K: one half-block quarter) are dealt
-//   round-robin to the 64 lanes, so a wave's loads cover consecutive row
-//   bytes;
-// * weight loads run a fixed number of rounds ahead of their use (Q4_K) or
-//   are all issued before use (Q6_K); weight loads are non-temporal (each
-//   byte is used once);
+// * one wave64 per weight row, eight rows per 512-thread workgroup (at
+//   4096 rows every wave of the launch is resident at once, four per SIMD);
+// * a wave reads its row as contiguous 16-byte pieces, so each load
+//   instruction covers about 1 KB of consecutive row bytes (Q4_K / Q5_K:
+//   plain 16-byte chunks of the row; Q6_K: 16 lanes per 210-byte block),
+//   and re-deals the bytes to its lanes through LDS (per-wave rings or
+//   regions, see each kernel); weight loads are non-temporal (each byte is
+//   used once) and run a fixed number of rounds ahead of their use;
 // * the activations of all T tokens are staged once per workgroup into LDS
-//   as int8 payload plus, per 32-block, the fp32 scale and the activation
-//   sums of the block and of its two 16-halves (the ones dots, computed once
-//   per workgroup instead of once per row), so the eight rows share one read
-//   of them and per-unit activation reads are LDS reads.  Staging loads are
-//   issued before the weight loads, so waiting for them does not wait for the
-//   weights (loads complete in issue order).  The weight and activation
+//   as int8 payload plus, per 16 activations, the fp32 block scale and the
+//   activation sum (the ones dots, computed once per workgroup instead of
+//   once per row), so the eight rows share one read of them and per-unit
+//   activation reads are LDS reads.  Each wave issues its staging loads
+//   first and only one or two rounds of weight loads before the staging
+//   barrier: staging loads queue behind every weight load the CU has already
+//   issued, so a deep prefetch there would hold back the barrier and with it
+//   all compute.  The weight and activation
 //   pointers are deliberately not __restrict__: loads through restrict
 //   pointers count as invariant and the compiler then moves them past the
 //   barrier to their first use, serialising one HBM round trip per unit.
-// When T*K is too large for the LDS budget the row is processed in K chunks.
-// The row sum is a wave reduction; lane 0 writes y[t*M + row].
+// When T*K is too large for the LDS budget the row is processed in K
+// segments of equal length.  The row sum is a wave reduction; lane 0 writes
+// y[t*M + row].
 #include "qmm_common.hpp"
 
 namespace qmm {
@@ -562,7 +565,7 @@ static int launch_mmvq_q6k(const void* w, const void* xq, float* y, int M, int n
   return launch_status();
 }
 
-// Host checks shared by both formats.
+// Host checks shared by the three formats.
 static int check_mmvq(const void* w, const void* xq, const float* y, int64_t M, int64_t K, int64_t T) {
   if (M < 1 || K < kQK || (K % kQK) != 0 || T < 1 || T > QMM_MMVQ_MAX_T) return QMM_ERR_SHAPE;
   if (M > 0x7fffffff || K / kQK > (1 << 20)) return QMM_ERR_SHAPE;
