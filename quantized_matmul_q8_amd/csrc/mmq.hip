@@ -131,18 +131,21 @@ struct RepackParams {
 
 // Activation row of column `col` of chunk row `ctile` (dense: token; MoE:
 // the routed slot's row), and the number of valid columns of the chunk row.
-// Returns false when the chunk row lies past the routed column tiles.
+// Returns false when the chunk row lies past the routed column tiles.  MoE:
+// ct is the column-tile prefix ct_off[0..E] copied to LDS, so the search
+// over it is not a chain of dependent global loads.
 template <int MODE>
-__device__ __forceinline__ bool repack_row(const RepackParams& P, int ctile, int col, int& xrow, int& ncols) {
+__device__ __forceinline__ bool repack_row(const RepackParams& P, const int* ct, int ctile, int col, int& xrow,
+                                           int& ncols) {
   xrow = 0;
   if constexpr (MODE == kMoe) {
-    if (ctile >= P.ct_off[P.E]) return false;
+    if (ctile >= ct[P.E]) return false;
     int lo = 0, hi = P.E;  // expert e with ct_off[e] <= ctile < ct_off[e+1]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (P.ct_off[mid] <= ctile) lo = mid; else hi = mid;
+      if (ct[mid] <= ctile) lo = mid; else hi = mid;
     }
-    const int n0 = (ctile - P.ct_off[lo]) * kChunkCols;
+    const int n0 = (ctile - ct[lo]) * kChunkCols;
     ncols = min(kChunkCols, P.counts[lo] - n0);
     if (col < ncols) {
       const int slot = P.bucket[P.offsets[lo] + n0 + col];
@@ -162,12 +165,12 @@ __device__ __forceinline__ bool repack_row(const RepackParams& P, int ctile, int
 // blocks of one pass are 8 consecutive blocks of 4 rows, so a wave reads
 // 1 KB of contiguous fp32 per row.
 template <int MODE>
-__device__ __forceinline__ void repack_f32(const RepackParams& P, int sb, int ctile) {
+__device__ __forceinline__ void repack_f32(const RepackParams& P, const int* ct, int sb, int ctile) {
   __shared__ int s_rows[kChunkCols];
   __shared__ int s_ncols;
   if (threadIdx.x < kChunkCols) {
     int xrow, ncols;
-    repack_row<MODE>(P, ctile, threadIdx.x, xrow, ncols);
+    repack_row<MODE>(P, ct, ctile, threadIdx.x, xrow, ncols);
     s_rows[threadIdx.x] = xrow;
     if (threadIdx.x == 0) s_ncols = ncols;
   }
@@ -216,15 +219,18 @@ __global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
     if (threadIdx.x < kXcds) P.counters[threadIdx.x] = 0u;
     P.counters[kTileCntWord + threadIdx.x] = 0u;  // 256 threads: every split-K arrival counter
   }
+  __shared__ int s_ct[MODE == kMoe ? kMoeMaxE + 1 : 1];
+  if constexpr (MODE == kMoe) {
+    for (int i = threadIdx.x; i <= P.E; i += 256) s_ct[i] = P.ct_off[i];
+    __syncthreads();
+    if (ctile >= s_ct[P.E]) return;  // uniform: past the routed column tiles
+  }
   if (MODE != kDebug && P.xf != nullptr) {  // uniform
-    if constexpr (MODE == kMoe) {
-      if (ctile >= P.ct_off[P.E]) return;
-    }
-    repack_f32<MODE>(P, sb, ctile);
+    repack_f32<MODE>(P, s_ct, sb, ctile);
     return;
   }
   int xrow, ncols;
-  if (!repack_row<MODE>(P, ctile, col, xrow, ncols)) return;
+  if (!repack_row<MODE>(P, s_ct, ctile, col, xrow, ncols)) return;
   uint2 u[5];
   if (col < ncols) {
     const uint2* src = reinterpret_cast<const uint2*>(
