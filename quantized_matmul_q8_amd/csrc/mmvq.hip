@@ -44,6 +44,24 @@ constexpr int kMmvqWaves = 8;             // rows per workgroup
 constexpr int kMmvqThreads = 64 * kMmvqWaves;
 constexpr int kMmvqLdsBudget = 68 * 1024; // bytes of staged activations per workgroup
 
+// Issue priority from progress.  The SIMD arbiter prefers the oldest wave, so
+// with equal work per wave the oldest waves (and the CU's first workgroup)
+// run ahead and the youngest finish alone, with few loads in flight.  Each
+// wave lowers its priority as it gets through its row (3 in the first
+// quarter, 0 in the last), so waves that are behind are issued first and
+// the waves of a CU finish together.  (Q4_K at T = 1 is balanced enough
+// without and measures 2% faster so.)
+template <bool ON = true>
+__device__ __forceinline__ void progress_prio(int done, int total) {
+  if constexpr (ON) {
+    const int q = __builtin_amdgcn_readfirstlane((4 * done) / total);
+    if (q <= 0) __builtin_amdgcn_s_setprio(3);
+    else if (q == 1) __builtin_amdgcn_s_setprio(2);
+    else if (q == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
+}
+
 // Per-slot routed-expert matvec (SLOT mode, T = 1): workgroup row block
 // blockIdx.x of routed slot blockIdx.y = t * top_k + k multiplies expert
 // ids[slot]'s rows (w + e * stride) with activation row t (rows_per_token
@@ -195,12 +213,13 @@ constexpr int kQ4Ahead = 2;
 // DEBUG == true: write the integer sub-block sums (D per (t, row, sub-block),
 // S per (t, sub-block) from row 0) instead of the scaled result.  Same
 // loads, unpacking and dot products; the two 16-weight halves of D are
-// added with integer atomics into zeroed buffers.
+// added with integer atomics into zeroed buffers.  Up to T = 4 the kernel
+// is held to 128 VGPRs, four waves per SIMD (two workgroups per CU; Q5_K at
+// T = 4 would otherwise take 130 and run one workgroup per CU, 15% slower).
 template <int FMT, int T, bool DEBUG, bool SLOT = false>
-__global__ __launch_bounds__(kMmvqThreads) void mmvq_q45k_kernel(const uint8_t* w, const uint8_t* xq,
-                                                                 float* __restrict__ y, int M, int nb,
-                                                                 int cb, int32_t* __restrict__ dbgD,
-                                                                 int32_t* __restrict__ dbgS, SlotArgs SA) {
+__global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(T <= 4 ? 4 : 1)))
+void mmvq_q45k_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb, int cb,
+                      int32_t* __restrict__ dbgD, int32_t* __restrict__ dbgS, SlotArgs SA) {
   using RL = MvRow<FMT>;
   constexpr int C = RL::kChunks;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -259,6 +278,7 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q45k_kernel(const uint8_t* 
         __builtin_amdgcn_sched_barrier(0);
       }
       if (64 * r >= nch) break;                 // uniform: round entirely past the segment
+      progress_prio<!(FMT == QMM_Q4_K && T == 1)>(b0 * C + 64 * r, nb * C);
       const bool ok = lane + 64 * r < nch;
       if (ok && k == 0) hdr_ring[bl % kQ4Ring] = v[r];  // header chunk
       if constexpr (RL::kQ5) {
@@ -331,8 +351,9 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q45k_kernel(const uint8_t* 
       if (k >= C) { k -= C; ++bl; }
       // opaque, so the unrolled rounds do not precompute (and keep live)
       // every round's ring and staging addresses from the start; Q4_K at
-      // T = 1 fits four waves per SIMD either way and runs faster without
-      if constexpr (T >= 2 || RL::kQ5) __asm__ volatile("" : "+v"(bl), "+v"(k));
+      // T = 1 fits four waves per SIMD either way and runs faster without,
+      // except in slot mode (short rows: 1.45x slower without)
+      if constexpr (T >= 2 || RL::kQ5 || SLOT) __asm__ volatile("" : "+v"(bl), "+v"(k));
     }
   }
   if constexpr (!DEBUG) {
@@ -424,6 +445,7 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q6k_kernel(const uint8_t* w
 #pragma unroll
     for (int ch = 0; ch < NR / 4; ++ch) {
       if (16 * ch >= nbc) break;  // uniform
+      progress_prio(b0 + 16 * ch, nb);
       {
         // rounds up to kQ6Ahead past this chunk, not issued yet
         const int lo = ch == 0 ? kQ6Pre : 4 * ch + kQ6Ahead;
