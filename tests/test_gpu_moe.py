@@ -38,6 +38,21 @@ def test_per_slot_parity(fmt, E, M, K, T, top_k):
     assert_parity(y, ref, bound, "per-slot")
 
 
+# Larger routings than the cases above (several id batches per wave of the
+# route preparation, thousands of slots per call).
+@pytest.mark.parametrize("E,T,top_k", [(8, 768, 8), (16, 6145, 1), (32, 1700, 4)])
+def test_route_many_slots(E, T, top_k):
+    M, K = 40, 256
+    g = qmm_synth.rng(E * T + top_k)
+    w = _experts("q4k", E, M, K, g)
+    xq = oracle.quantize_q8_1(qmm_synth.activations(g, T, K))
+    ids, _ = qmm_synth.router(g, T, E, top_k)
+    say("moe_grouped_mmq q4k per-slot (route)", f"E={E} M={M} K={K} T={T} top_k={top_k} slots={T * top_k}")
+    y = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(w), dev(xq), dev(ids)))
+    ref, bound = oracle.grouped_blocks(oracle.q4k_dequant, w, oracle.q8_1_dequant(xq), ids, 1)
+    assert_parity(y, ref, bound, "per-slot")
+
+
 # The per-slot expert matvec (the path the grouped GEMM replaces): parity
 # with the oracle for activation rows per token and per slot, ragged rows,
 # and agreement with the grouped GEMM's per-slot output.
