@@ -197,7 +197,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is a design "
+        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is a design "
                                    "note only (row split for matvec/GEMM, expert split for MoE)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
