@@ -187,6 +187,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     }
 #pragma unroll
     for (int r = 0; r < kRouteBatch; ++r) {
+      if (base + 64 * r >= end) break;  // uniform: no slot of this wave left
       const int s = base + 64 * r + lane;
       const int e = ev[r];
       const bool v = e >= 0 && e < E;
