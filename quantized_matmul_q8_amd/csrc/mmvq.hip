@@ -213,11 +213,13 @@ constexpr int kQ4Ahead = 2;
 // DEBUG == true: write the integer sub-block sums (D per (t, row, sub-block),
 // S per (t, sub-block) from row 0) instead of the scaled result.  Same
 // loads, unpacking and dot products; the two 16-weight halves of D are
-// added with integer atomics into zeroed buffers.  Up to T = 4 the kernel
-// is held to 128 VGPRs, four waves per SIMD (two workgroups per CU; Q5_K at
-// T = 4 would otherwise take 130 and run one workgroup per CU, 15% slower).
+// added with integer atomics into zeroed buffers.  Up to T = 6 the kernel
+// is held to 128 VGPRs, four waves per SIMD (two workgroups per CU): Q5_K
+// at T = 4 would otherwise take 130 VGPRs and T = 5, 6 take 139-172, each
+// running one workgroup per CU (T = 4 15% and T = 5 20% slower so, even
+// though the cap spills a few registers at T = 5, 6).
 template <int FMT, int T, bool DEBUG, bool SLOT = false>
-__global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(T <= 4 ? 4 : 1)))
+__global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(T <= 6 ? 4 : 1)))
 void mmvq_q45k_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb, int cb,
                       int32_t* __restrict__ dbgD, int32_t* __restrict__ dbgS, SlotArgs SA) {
   using RL = MvRow<FMT>;
