@@ -611,6 +611,15 @@ __device__ __forceinline__ void mmq_epilogue(const MmqParams& P, const TileCols&
 template <int FMT, int NT>
 struct StepLoads;
 
+// Issue priority from the progress through a step's u of nu sub-blocks.
+__device__ __forceinline__ void step_prio(int u, int nu) {
+  const int q = (4 * u) / nu;
+  if (q <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Multiply-accumulate this wave's 8 MFMA sub-blocks of a step (its rows, its
 // half's chunks; ub = first sub-block of the half within the super-block),
 // issuing slot u of the next step's loads at sub-block u.  Software
@@ -635,29 +644,15 @@ __device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* s
       mmq_epilogue<FMT, NT, MODE>(P, tc, r0, sb, ub, u, 0, X, O, acc, wl, u);
       __builtin_amdgcn_sched_barrier(0);
     }
-  } else if constexpr (NT == 1) {
-    // One column tile: the MFMA of sub-block u+1 is issued before the
-    // epilogue of u (two result buffers), so it runs under that epilogue;
-    // LDS operands are read two sub-blocks ahead (three buffers).
-    SubOps<FMT, NT> O[3];
-    v16i X[2];
-    load_sub<FMT, NT>(st, wl, ub, 0, O[0]);
-    load_sub<FMT, NT>(st, wl, ub + 1, 1, O[1]);
-    X[0] = mfma_sub(build_a(A, 0), O[0].bq[0], magic);
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if constexpr (StepLoads<FMT, NT>::kInLoop) pre.issue(u, F);  // one slot of the next step's loads
-      if (u + 2 < NU) load_sub<FMT, NT>(st, wl, ub + u + 2, u + 2, O[(u + 2) % 3]);
-      if (u + 1 < NU) X[(u + 1) & 1] = mfma_sub(build_a(A, u + 1), O[(u + 1) % 3].bq[0], magic);
-      __builtin_amdgcn_sched_barrier(0);
-      mmq_epilogue<FMT, NT, MODE>(P, tc, r0, sb, ub, u, 0, X[u & 1], O[u % 3], acc);
-      __builtin_amdgcn_sched_barrier(0);
-    }
   } else {
-    // Several column tiles: the MFMA of (u+1, ct) is issued right after the
+    // Two column tiles: the MFMA of (u+1, ct) is issued right after the
     // epilogue of (u, ct) has consumed its result registers, so it runs under
     // the epilogue of the next column tile; LDS operands of u+1 are read
-    // while u is rescaled.
+    // while u is rescaled.  The two waves of a SIMD (the K halves of one row
+    // group) share its issue slots and the arbiter favours the older one; the
+    // issue priority falls as a wave gets through its step (3 in the first
+    // quarter of its sub-blocks, 0 in the last), so the wave that is behind
+    // is issued first and the pair reaches the step's barrier together.
     SubOps<FMT, NT> O[2];
     v16i X[NT];
     load_sub<FMT, NT>(st, wl, ub, 0, O[0]);
@@ -668,6 +663,7 @@ __device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* s
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
+      step_prio(u, NU);
       const int b = u & 1;
       const bool more = u + 1 < NU;
       if constexpr (StepLoads<FMT, NT>::kInLoop) pre.issue(u, F);  // one slot of the next step's loads
@@ -1016,10 +1012,10 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT 
   const int kh = wave >> 2;
   // The two waves of a SIMD (K halves 0 and 1) share its issue slots; the
   // arbiter favours the older one, so the second half used to finish each
-  // step alone, its matrix-core latency exposed.  For Q6_K (16 MFMA
-  // sub-blocks per super-block) raising the second half's priority evens
-  // them out (about 5% at 4096 x 14336 x 1024); Q4_K shows no gain.
-  if (FMT == QMM_Q6_K && kh == 1) __builtin_amdgcn_s_setprio(2);
+  // step alone, its matrix-core latency exposed.  The two-tile kernel sets
+  // the priority by progress through each step (see mmq_compute); the
+  // one-tile Q6_K kernel raises the second half's priority instead.
+  if (kLean<FMT, NT> && FMT == QMM_Q6_K && kh == 1) __builtin_amdgcn_s_setprio(2);
   float* wl = reinterpret_cast<float*>(smem + L::kWaveOff + wave * L::kWave);
   v16i magic;
 #pragma unroll
