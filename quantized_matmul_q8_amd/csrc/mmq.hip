@@ -630,9 +630,7 @@ __device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* s
                                             const MmqOperand<FMT>& A, v16f (&acc)[NT], const v16i& magic,
                                             const TileCols& tc, int r0, int sb, int ub,
                                             const StepLoads<FMT, NT>& pre, MmqPrefetch<FMT>& F) {
-  constexpr int NU = StepSplit<FMT>::kNU;         // MFMA sub-blocks of this wave per step
-  constexpr int NSB = StepSplit<FMT>::kSubsPerSb; // MFMA sub-blocks per super-block
-  const int g = (threadIdx.x & 63) >> 5, col = threadIdx.x & 31;
+  constexpr int NU = StepSplit<FMT>::kNU;  // MFMA sub-blocks of this wave per step
   if constexpr (kLean<FMT, NT>) {
     // one operand set and one result buffer per sub-block
     SubOps<FMT, NT> O;
@@ -771,13 +769,18 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // inline assembly so the compiler does not track it: its own tracking treats
 // every later LDS read as a possible alias and waits for all loads in flight,
 // which would serialise the prefetch of the next step into this one.  The
-// kernel waits for these copies explicitly (vmcnt(0), then a barrier).
+// kernel waits for these copies explicitly (vmcnt(0), then a barrier).  M0
+// is a reserved register the compiler may hold a value in, so the sequence
+// saves and restores it (the load takes its LDS base from M0 when it is
+// issued).
 __device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                   :
+  uint32_t saved;
+  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+                   "s_mov_b32 m0, %0"
+                   : "=&s"(saved)
                    : "v"(src), "s"(m0v)
-                   : "memory", "m0");
+                   : "memory");
 }
 
 // The loads of one step -- the chunks of its two super-blocks (copied into

@@ -88,10 +88,11 @@ __device__ __forceinline__ uint64_t peers_of(int e, bool v, int nbits) {
   uint64_t peers = __ballot(v);
 #pragma unroll
   for (int b = 0; b < 9; ++b) {
-    if (b >= nbits) break;  // uniform
-    const bool bit = (e >> b) & 1;
-    const uint64_t m = __ballot(v && bit);
-    peers &= bit ? m : ~m;
+    if (b < nbits) {  // uniform
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(v && bit);
+      peers &= bit ? m : ~m;
+    }
   }
   return peers;
 }
@@ -187,16 +188,17 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     }
 #pragma unroll
     for (int r = 0; r < kRouteBatch; ++r) {
-      if (base + 64 * r >= end) break;  // uniform: no slot of this wave left
-      const int s = base + 64 * r + lane;
-      const int e = ev[r];
-      const bool v = e >= 0 && e < E;
-      const uint64_t peers = peers_of(e, v, nbits);
-      const int rank = __popcll(peers & below);
-      int prior = 0;
-      if (v) prior = cnt[wave][e];
-      if (v) bucket[s_off[e] + prior + rank] = s;
-      if (v && rank == 0) cnt[wave][e] = prior + __popcll(peers);
+      if (base + 64 * r < end) {  // uniform: skip batches past this wave's slots
+        const int s = base + 64 * r + lane;
+        const int e = ev[r];
+        const bool v = e >= 0 && e < E;
+        const uint64_t peers = peers_of(e, v, nbits);
+        const int rank = __popcll(peers & below);
+        int prior = 0;
+        if (v) prior = cnt[wave][e];
+        if (v) bucket[s_off[e] + prior + rank] = s;
+        if (v && rank == 0) cnt[wave][e] = prior + __popcll(peers);
+      }
     }
   }
   if (tid <= kXcds) counters[tid] = 0u;
