@@ -194,6 +194,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true",
                     help="skip the secondary workloads (for profiling the decode step)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="after the headline, only the prefill GEMMs and the routed-expert FFN (for counter runs)")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -304,7 +306,23 @@ def main():
                       "frac_hbm": round(gbps(nb16, pm) / HBM_PEAK_GBPS, 4)}
         del bufs
 
-    if not args.only_headline:
+    if not args.only_headline and not args.prefill_only:
+        # single Q4_K matvec 1024 x 1024, T = 1 (reported only: launch-latency bound)
+        wl0 = qmm_synth.workload(0)
+        w0h = wl0["q4k"]
+        # one launch per copy, every copy distinct (about 7,000 copies, 4 GB, so
+        # no launch finds its weights in the MALL)
+        n0 = copies_for(w0h.nbytes)
+        w0 = to(w0h).unsqueeze(0).repeat(n0, 1, 1, 1)
+        xq0 = qmm.q8_1_quantize(to(wl0["x"]))
+        y0 = torch.empty((1, w0h.shape[0]), dtype=torch.float32, device=dev)
+        m_ = time_graph(torch, [lambda c=c: qmm.mmvq_q4k(w0[c], xq0, out=y0) for c in range(n0)], n0)
+        nbytes = w0h.nbytes + xq0.numel() + y0.numel() * 4
+        also["mmvq_q4k_1024x1024_t1"] = {"us": round(m_ * 1e3, 3), "GBps": gbps(nbytes, m_),
+                                         "frac_hbm": round(gbps(nbytes, m_) / HBM_PEAK_GBPS, 4)}
+        del w0, wl0
+
+    if not args.only_headline and not args.prefill_only:
         # matvec at T = 4
         x4 = to(wl["x"][:4])
         xq4 = qmm.q8_1_quantize(x4)
@@ -343,8 +361,9 @@ def main():
             cross[f"mmq_{key}_us"] = round(t_mq * 1e3, 2)
             cross[f"best_{key}_GBps"] = gbps(nbw, min(t_mv, t_mq))
         also["decode_4096x11008_t8"] = cross
-        del w4, w6
+    del w4, w6
 
+    if not args.only_headline:
         # prefill GEMMs
         def mmq_case(name, fn, wh, xh):
             Mg, Kg = wh.shape[0], wh.shape[1] * 256
@@ -415,24 +434,40 @@ def main():
         def down_only():
             qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dn, hq, ids, probs, out=y2, ws=ws2)
 
+        def glue_only():
+            qmm.q8_1_quantize(xm, out=xqm)
+            qmm.swiglu_q8_1(y1, out=hq)
+
         log("moe ffn")
         ms_moe = time_graph(torch, [moe_step], 10)
         ms_gu = time_graph(torch, [gate_up_only], 10)
         ms_dn = time_graph(torch, [down_only], 10)
+        ms_glue = time_graph(torch, [glue_only], 10)
         wbytes = wl4["gate_up"].nbytes + wl4["down"].nbytes
         macs = T * top_k * (2 * F * H + H * F)
         act_bytes = T * H * 4 + T * (H // 32) * 40 + T * top_k * (F // 32) * 40 + T * H * 4
         moe_bytes = wbytes + act_bytes
         tops = 2.0 * macs / (ms_moe * 1e-3) / 1e12
         attain = min(INT8_PEAK_TOPS, 2.0 * macs / moe_bytes * HBM_PEAK_GBPS / 1e3)
+        # the two grouped calls alone (route preparation, repack, GEMM and, for
+        # down, the combine), without the quantize and SwiGLU glue: weights,
+        # Q8_1 inputs, the gate||up per-slot rows and the combined output
+        g_bytes = wbytes + T * (H // 32) * 40 + T * top_k * 2 * F * 4 + T * top_k * (F // 32) * 40 + T * H * 4
+        ms_g = ms_gu + ms_dn
+        tops_g = 2.0 * macs / (ms_g * 1e-3) / 1e12
+        attain_g = min(INT8_PEAK_TOPS, 2.0 * macs / g_bytes * HBM_PEAK_GBPS / 1e3)
         also["moe_ffn_e128_t512_top8"] = {
             "us": round(ms_moe * 1e3, 2), "gate_up_us": round(ms_gu * 1e3, 2),
             "down_us": round(ms_dn * 1e3, 2), "GBps": gbps(moe_bytes, ms_moe),
             "frac_hbm": round(gbps(moe_bytes, ms_moe) / HBM_PEAK_GBPS, 4),
             "TOPS": round(tops, 1), "frac_attainable": round(tops / attain, 4),
-            "tokens_per_s": round(T / (ms_moe * 1e-3), 1)}
+            "tokens_per_s": round(T / (ms_moe * 1e-3), 1),
+            "glue_us": round(ms_glue * 1e3, 2),
+            "grouped_calls_only": {"us": round(ms_g * 1e3, 2), "GBps": gbps(g_bytes, ms_g),
+                                   "TOPS": round(tops_g, 1), "frac_attainable": round(tops_g / attain_g, 4)}}
         del gu, dn
-        also["moe_comparator_e128_k2048_top8"] = moe_comparator(torch, qmm, qmm_synth, dev)
+        if not args.prefill_only:
+            also["moe_comparator_e128_k2048_top8"] = moe_comparator(torch, qmm, qmm_synth, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
