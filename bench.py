@@ -120,8 +120,15 @@ def rotated(t, n):
     return [t] + [t.clone() for _ in range(n - 1)]
 
 
-def cpu_oracle_baseline(np, wl, rows, min_seconds=10.0):
-    """The fp64 oracle on the first `rows` rows of both decode matrices, T = 1."""
+def cpu_oracle_baseline(np, wl, rows, min_seconds=10.0, one_core=False):
+    """The fp64 oracle on the first `rows` rows of both decode matrices, T = 1
+    (on all BLAS threads, or with the BLAS limited to one thread)."""
+    if one_core:
+        import threadpoolctl
+        with threadpoolctl.threadpool_limits(1):
+            r = cpu_oracle_baseline(np, wl, rows, min_seconds)
+        r["cores"] = 1
+        return r
     import oracle
     try:
         import threadpoolctl
@@ -473,6 +480,7 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu oracle baseline")
         cpu = cpu_oracle_baseline(np, wl, min(args.cpu_rows, M))
+        also["cpu_oracle_1core"] = cpu_oracle_baseline(np, wl, min(args.cpu_rows, M), min_seconds=5.0, one_core=True)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
