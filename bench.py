@@ -53,7 +53,7 @@ ROTATE_BYTES = 4096 << 20
 
 # traffic measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE for the
 # dominant kernel (profiles/); None until taken for the current kernel
-DOMINANT_TRAFFIC_BYTES = 37439987   # mmvq_q6k, profiles/mmvq_decode_4096x11008_t1.md
+DOMINANT_TRAFFIC_BYTES = 37436841   # mmvq_q6k, profiles/mmvq_decode_4096x11008_t1.md
 
 
 def log(*a):
@@ -128,6 +128,7 @@ def cpu_oracle_baseline(np, wl, rows, min_seconds=10.0, one_core=False):
         with threadpoolctl.threadpool_limits(1):
             r = cpu_oracle_baseline(np, wl, rows, min_seconds)
         r["cores"] = 1
+        r["sample"] = r["sample"].replace("matvec on the BLAS threads", "matvec on one BLAS thread")
         return r
     import oracle
     try:
