@@ -66,6 +66,7 @@ namespace qmm {
 constexpr int kMmqWaves = 8;
 constexpr int kMmqThreads = 64 * kMmqWaves;
 constexpr int kMmqBM = 128;            // weight rows per tile (32 per row group)
+constexpr int kGroupM = 8;             // row tiles per run of the dense tile order
 constexpr uint32_t kMagicBits = 0x4B400000u;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
@@ -726,8 +727,15 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
     const int ntile = (P.T + BN - 1) / BN;
     R.base = __builtin_amdgcn_readfirstlane(idx / P.nsplit);
     R.split = __builtin_amdgcn_readfirstlane(idx % P.nsplit);
-    m_tile = R.base / ntile;
-    const int n_tile = R.base % ntile;
+    // tiles in runs of kGroupM row tiles x every column tile, row tile
+    // fastest: the 32 workgroups of an XCD work on 8 row tiles x 4 column
+    // tiles at a time, so their weight rows and activation chunks stay in
+    // the XCD's L2 (column tile fastest had them sweep all the chunks)
+    const int mtiles = (P.M + kMmqBM - 1) / kMmqBM;
+    const int grp = R.base / (kGroupM * ntile), inner = R.base % (kGroupM * ntile);
+    const int gm = min(kGroupM, mtiles - grp * kGroupM);
+    m_tile = grp * kGroupM + inner % gm;
+    const int n_tile = inner / gm;
     R.tc.n0 = n_tile * BN;
     R.tc.ncols = min(BN, P.T - R.tc.n0);
     R.tc.slot_base = 0;
