@@ -53,7 +53,7 @@ ROTATE_BYTES = 4096 << 20
 
 # traffic measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE for the
 # dominant kernel (profiles/); None until taken for the current kernel
-DOMINANT_TRAFFIC_BYTES = 37436841   # mmvq_q6k, profiles/mmvq_decode_4096x11008_t1.md
+DOMINANT_TRAFFIC_BYTES = 37436825   # mmvq_q6k, profiles/mmvq_decode_4096x11008_t1.md
 
 
 def log(*a):
