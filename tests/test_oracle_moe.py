@@ -92,3 +92,98 @@ def test_swiglu_closed_forms():
     g = np.array([2.0])
     assert np.isclose(oracle.swiglu(g, np.array([1.0]))[0], 2.0 / (1.0 + np.exp(-2.0)), rtol=1e-15)
     assert np.isclose(oracle.swiglu(np.array([50.0]), np.array([2.0]))[0], 100.0, rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# grouped_blocks (the reference of every grouped GPU test) and abs_bound (the
+# tolerance scale of every parity assertion), pinned against plain loops.
+# ---------------------------------------------------------------------------
+def _fsum_dot(a, b):
+    import math
+    return math.fsum(float(u) * float(v) for u, v in zip(a, b))
+
+
+def _slot_loop(W, X, ids, rows_per_token):
+    """y_slot and bound by the definition: slot s = t*top_k + k multiplies
+    expert ids[t, k] with activation row t (one row per token) or s (one row
+    per slot); exactly rounded sums (math.fsum), no BLAS."""
+    T, top_k = ids.shape
+    M = W.shape[1]
+    y = np.zeros((T * top_k, M))
+    b = np.zeros((T * top_k, M))
+    for t in range(T):
+        for k in range(top_k):
+            s = t * top_k + k
+            row = t if rows_per_token == 1 else s
+            e = int(ids[t, k])
+            for i in range(M):
+                y[s, i] = _fsum_dot(W[e, i], X[row])
+                b[s, i] = _fsum_dot(np.abs(W[e, i]), np.abs(X[row]))
+    return y, b
+
+
+@pytest.mark.parametrize("per_slot_rows", [False, True])
+def test_grouped_blocks_matches_definition_loop(per_slot_rows):
+    # expert 3 of 5 receives no slot; tokens route to 2 experts each
+    g, blocks, W = _experts(E=5, M=3, K=256, seed=11)
+    T, top_k = 4, 2
+    ids = np.array([[0, 4], [4, 1], [2, 0], [1, 4]], dtype=np.int32)
+    rows = T * top_k if per_slot_rows else T
+    X = oracle.q8_1_dequant(oracle.quantize_q8_1(qmm_synth.activations(g, rows, 256)))
+    r = top_k if per_slot_rows else 1
+    y, bound = oracle.grouped_blocks(oracle.q4k_dequant, blocks, X, ids, r)
+    y_ref, b_ref = _slot_loop(W, X, ids, r)
+    scale = np.abs(W).max() * np.abs(X).max() * 256
+    assert np.all(np.abs(y - y_ref) <= 1e-13 * scale)
+    assert np.all(np.abs(bound - b_ref) <= 1e-13 * b_ref + 1e-300)
+    assert np.all(bound >= np.abs(y) * (1 - 1e-13))
+
+
+@pytest.mark.parametrize("per_slot_rows", [False, True])
+def test_grouped_blocks_equals_grouped_on_dequantized_experts(per_slot_rows):
+    g, blocks, W = _experts(E=6, M=16, K=512, seed=12)
+    T, top_k = 9, 3
+    ids, _ = qmm_synth.router(g, T, 5, top_k)      # expert 5 never routed
+    rows = T * top_k if per_slot_rows else T
+    X = oracle.q8_1_dequant(oracle.quantize_q8_1(qmm_synth.activations(g, rows, 512)))
+    r = top_k if per_slot_rows else 1
+    y, bound = oracle.grouped_blocks(oracle.q4k_dequant, blocks, X, ids, r)
+    assert np.array_equal(y, oracle.grouped(W, X, ids, r))
+    # bound[s] = |x_row| . |W_e|^T, the per-slot abs_bound
+    T_, k_ = ids.shape
+    for t in range(T_):
+        for k in range(k_):
+            s = t * k_ + k
+            row = t if r == 1 else s
+            assert np.array_equal(bound[s], oracle.abs_bound(W[ids[t, k]], X[row:row + 1])[0])
+
+
+def test_grouped_blocks_expert_subset_fills_only_those_slots():
+    g, blocks, W = _experts(E=4, M=8, K=256, seed=13)
+    T, top_k = 10, 2
+    ids, _ = qmm_synth.router(g, T, 4, top_k)
+    X = oracle.q8_1_dequant(oracle.quantize_q8_1(qmm_synth.activations(g, T, 256)))
+    full, bfull = oracle.grouped_blocks(oracle.q4k_dequant, blocks, X, ids, 1)
+    part, bpart = oracle.grouped_blocks(oracle.q4k_dequant, blocks, X, ids, 1, experts=[1, 3])
+    sel = np.isin(ids.ravel(), [1, 3])
+    assert np.array_equal(part[sel], full[sel]) and np.array_equal(bpart[sel], bfull[sel])
+    assert not part[~sel].any() and not bpart[~sel].any()
+
+
+def test_abs_bound_brute_force():
+    # signs mixed on both sides; the bound is sum_k |w_ik| |x_tk|, never the
+    # magnitude of the signed sum
+    W = np.array([[1.0, -2.0, 0.5], [-0.25, 0.0, 3.0]])
+    X = np.array([[2.0, 1.0, -4.0], [-1.0, -1.0, -1.0], [0.0, 0.0, 0.0]])
+    b = oracle.abs_bound(W, X)
+    expect = [[1 * 2 + 2 * 1 + 0.5 * 4, 0.25 * 2 + 0 + 3 * 4],
+              [1 + 2 + 0.5, 0.25 + 0 + 3],
+              [0.0, 0.0]]
+    assert b.shape == (3, 2) and np.array_equal(b, np.array(expect))
+    g = np.random.default_rng(5)
+    W = g.standard_normal((3, 7))
+    X = g.standard_normal((4, 7))
+    b = oracle.abs_bound(W, X)
+    for t in range(4):
+        for i in range(3):
+            assert abs(b[t, i] - _fsum_dot(np.abs(W[i]), np.abs(X[t]))) <= 1e-14 * b[t, i]
