@@ -124,7 +124,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Lane `part` (0..7) holds x[4*part .. 4*part+3]; all eight lanes must be
 // active (they exchange values).  Steps of [8e] §3.2 (max |x|, d = am/127,
 // reciprocal, round to nearest even, clamp, pack, sum), in IEEE fp32 with
-// no contraction so the bytes are reproducible.  Returns this lane's four
+// no contraction so the bytes are reproducible; a subnormal d is taken as 0.  Returns this lane's four
 // int8 values packed little-endian, the fp32 scale d (stored as f16) and
 // the block's integer sum (in every lane of the group).  Every step is
 // independent of the order of the lanes, so any caller gets the same bytes.
@@ -135,7 +135,9 @@ __device__ __forceinline__ void q8_1_block_8lanes_vals(float4 v, uint32_t& packe
   am = fmaxf(am, __shfl_xor(am, 2));
   am = fmaxf(am, __shfl_xor(am, 4));
   d = am / 127.0f;
-  const float di = d != 0.0f ? 1.0f / d : 0.0f;
+  // a subnormal scale counts as zero (its reciprocal may overflow and its
+  // f16 rounding is 0): the block is stored as zeros
+  const float di = d >= 0x1p-126f ? 1.0f / d : 0.0f;
   const int q0 = max(-128, min(127, static_cast<int>(rintf(v.x * di))));
   const int q1 = max(-128, min(127, static_cast<int>(rintf(v.y * di))));
   const int q2 = max(-128, min(127, static_cast<int>(rintf(v.z * di))));

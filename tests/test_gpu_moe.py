@@ -144,10 +144,6 @@ def test_full_routed_ffn_workload():
     assert_parity(y1, ref1, b1, "gate_up")
     # down projection on an intermediate made by the oracle from its own gate/up
     h = oracle.swiglu(ref1[:, :F], ref1[:, F:]).astype(np.float32)
-    # silu of large negative gates underflows to float32 subnormals; a block
-    # whose max is below 127 * 2^-126 has a reciprocal scale that overflows,
-    # which is outside the quantizer's domain, so such values are flushed
-    h[np.abs(h) < np.float32(1e-30)] = 0.0
     hq = oracle.quantize_q8_1(h)
     say("moe down weighted", f"E={E} M={H} K={F} T={T} top_k={top_k}")
     y2 = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), dev(hq), dev(ids), dev(probs)))

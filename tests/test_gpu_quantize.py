@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _special_blocks(x):
-    """Overwrite a few blocks of row 0 with edge cases (zero, f16-subnormal d, exact ties)."""
+    """Overwrite a few blocks of row 0 with edge cases (zero, f16-subnormal d, exact ties, tiny scales)."""
     if x.shape[1] >= 128:
         x[0, 0:32] = 0.0
         g = np.random.default_rng(5)
@@ -22,6 +22,14 @@ def _special_blocks(x):
         k[0] = 127.0
         x[0, 64:96] = k * np.float32(2.0**-3)
         x[0, 96:128] = -x[0, 64:96]
+    if x.shape[1] >= 192:
+        # fp32-subnormal scale (stored as zeros) and the smallest normal scale
+        x[0, 128:160] = np.float32(0.0)
+        x[0, 128] = np.float32(127 * 2.0**-127)
+        x[0, 129] = np.float32(-3.0e-37)
+        x[0, 160:192] = np.float32(0.0)
+        x[0, 160] = np.float32(127 * 2.0**-126)
+        x[0, 161] = np.float32(-63.5 * 2.0**-126)
     return x
 
 
