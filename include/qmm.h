@@ -63,8 +63,9 @@ typedef enum qmm_status {
 #define QMM_Q6_K 14
 
 /* Operation codes for qmm_workspace_bytes. */
-#define QMM_OP_MMQ 1
-#define QMM_OP_MOE 2
+#define QMM_OP_MMQ 1        /* mmq_* and mmq_*_f32                               */
+#define QMM_OP_MOE 2        /* moe_grouped_mmq, weighted (expert_weights != NULL) */
+#define QMM_OP_MOE_SLOTS 3  /* moe_grouped_mmq, per-slot output (no weights)      */
 
 /* Largest token count accepted by the matvec entry points. */
 #define QMM_MMVQ_MAX_T 8
@@ -76,6 +77,11 @@ typedef enum qmm_status {
  * f16(d) (round to nearest even), zero pad and the int32 sum of q
  * ([8e] §2 and the quantizer of §3.2).  IEEE fp32 division, no contraction:
  * the bytes are bit-identical to the IEEE emulation of these steps.
+ * Tiny blocks: when d is below 2^-126 (max|x| < 127 * 2^-126, an fp32
+ * subnormal scale) 1/d would overflow, so di = 0 as for d == 0 and the block
+ * is stored as all zeros (its f16 scale rounds to 0 anyway, so the
+ * dequantized block is 0 either way).  Input must be finite with
+ * max|x| <= 127 * 65504 (f16 range of d).
  * Requires T >= 0, K > 0, K % 32 == 0.  T == 0 is a no-op.
  */
 int q8_1_quantize(const float* x, void* xq, int64_t T, int64_t K, void* stream);
@@ -110,15 +116,17 @@ int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int6
  * `ws`.  When the call has enough 128 x 32/64 output tiles to fill the chip,
  * each tile runs its whole K loop in one workgroup (its two K halves summed
  * in a fixed order, no fixup).  A call with fewer than 256 tiles (few tokens
- * and rows) splits each tile's K range over up to 16 workgroups, which write
- * fp32 partial tiles to `ws`; the last to finish adds them in split order.
+ * and rows) uses split-K with a deterministic in-kernel fixup instead: each
+ * tile's K range is split over up to 16 workgroups, which write fp32
+ * partial tiles to `ws`; the last to finish adds them in split order.
  * Either way the result of a call depends only on its shapes and data (the
  * split factor is a function of M, K and T), so results are deterministic.
  * `ws` must hold qmm_workspace_bytes(QMM_OP_MMQ, M, K, T, 0, 0) bytes (M
  * counts: it sizes the partial tiles); its contents are
  * scratch (the call initialises what it uses, no zero-fill is needed).
  * Calls sharing one workspace must be ordered on one stream.
- * Requires M >= 1, 1 <= T <= 2^24, K % 256 == 0, K/256 <= 65536.
+ * Requires M >= 1, 1 <= T <= 2^24, K % 256 == 0, K/256 <= 65536 and at most
+ * 2^30 output tiles (ceil(M/128) * ceil(T/64) * splits).
  */
 int mmq_q4k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
             void* ws, size_t ws_bytes, void* stream);
@@ -164,14 +172,17 @@ int mmq_q6k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, i
  *                        W[ids[t][k]] . x_row; otherwise fp32 [T][top_k] and
  *                        y[t*M + i] = sum_k p[t][k] * (W[ids[t][k]] . x_row)
  *                        summed in increasing k (deterministic, no atomics)
- *   ws                   qmm_workspace_bytes(QMM_OP_MOE, M, K, T, E, top_k)
- *                        bytes of scratch (no initialisation needed); holds
- *                        the buckets, the queue counters, the routed rows
- *                        repacked per expert and, in weighted mode, the
+ *   ws                   qmm_workspace_bytes(QMM_OP_MOE, ...) bytes for a
+ *                        weighted call, QMM_OP_MOE_SLOTS for a per-slot one
+ *                        (same sizes); scratch, no initialisation needed;
+ *                        holds the buckets, the queue counters, the routed
+ *                        rows repacked per expert and, in weighted mode, the
  *                        per-slot fp32 results
  * Work is tiled as 128 weight rows x 32 routed slots of one expert, so an
  * expert's weights are read once per 32 tokens routed to it.  Requires
- * 1 <= E <= 512, M >= 1, K % 256 == 0, 1 <= top_k <= min(E, 64), T >= 1,
+ * 1 <= E <= 512, M >= 1, K % 256 == 0, K/256 <= 65536, 1 <= top_k <= min(E, 64),
+ * T >= 1, T*top_k <= 2^30, at most 2^30 work entries (ceil(M/128) times the
+ * column-tile bound (T*top_k + 31*min(E, T*top_k))/32),
  * x_rows_per_token in {1, top_k}, expert_stride_bytes >= M*K/256*block bytes
  * and a multiple of 16 (Q4_K) or 2 (Q6_K).
  */
@@ -206,8 +217,12 @@ int moe_slot_mmvq(int fmt, const void* w, int64_t E, int64_t M, int64_t K, int64
  */
 int swiglu_q8_1(const float* g_u, void* hq, int64_t R, int64_t F, void* stream);
 
-/* Bytes of workspace needed by `op` (QMM_OP_MMQ or QMM_OP_MOE) for the given
- * sizes; unused sizes may be 0.  Returns 0 for an unknown op. */
+/* Bytes of workspace needed by `op` (QMM_OP_MMQ, QMM_OP_MOE or
+ * QMM_OP_MOE_SLOTS) for the given sizes; unused sizes may be 0.  Returns 0
+ * for an unknown op.  The workspace is the scratch the caller allocates
+ * once, outside any graph-capture window, and passes in: no entry point
+ * allocates ([8e] §3.1, the rule that the q8 activation scratch is never
+ * allocated inside a capture window). */
 size_t qmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k);
 
 /* Zero-fills a workspace on `stream` with a fill kernel (no memset node).
@@ -222,7 +237,9 @@ const char* qmm_status_str(int status);
  * qmm_debug_subdots -- test hook: the integer stage of the MMVQ
  * (path == 0) or MMQ (path == 1) kernel of format `fmt`, built from the same
  * source as the product kernels, writing the exact integer sub-block sums
- * instead of the scaled result.  Q4_K: D[T][M][K/32] = sum nib*q and
+ * instead of the scaled result.  Its signature extends the proposed
+ * (fmt, w, xq, D, S, M, K, T, stream) by `path` (which kernel's integer stage)
+ * and (ws, ws_bytes) (the GEMM path's workspace).  Q4_K: D[T][M][K/32] = sum nib*q and
  * S[T][K/32] = sum q (the ones-dot on path 0, the stored sum on path 1);
  * Q5_K the same with the 5-bit values.  Q6_K: D[T][M][K/16] = sum (q6-32)*q and S is not written.  T <= 8 for
  * path 0.  Path 1 needs an MMQ workspace (ws, ws_bytes) like mmq_q4k; path 0

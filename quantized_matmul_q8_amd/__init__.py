@@ -20,7 +20,7 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    QMM_MMVQ_MAX_T, QMM_OP_MMQ, QMM_OP_MOE, QMM_Q4_K, QMM_Q5_K, QMM_Q6_K, QmmError, LIB_PATH,
+    QMM_MMVQ_MAX_T, QMM_OP_MMQ, QMM_OP_MOE, QMM_OP_MOE_SLOTS, QMM_Q4_K, QMM_Q5_K, QMM_Q6_K, QmmError, LIB_PATH,
 )
 
 __all__ = [
@@ -55,6 +55,21 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int | None = Non
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
+def _out(out: torch.Tensor | None, shape: tuple, dtype: torch.dtype, device: torch.device, name: str = "out"):
+    """A new output of ``shape``, or the caller's ``out`` checked to match it exactly.
+
+    The C ABI cannot see buffer sizes, so a caller buffer of the wrong shape
+    is rejected here before any device write."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(out, dtype, name, len(shape))
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    if out.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    return out
+
+
 def _weights(w: torch.Tensor, fmt: int, name: str = "w"):
     _need(w, torch.uint8, name, 3)
     if w.shape[2] != _BLOCK_BYTES[fmt]:
@@ -82,16 +97,21 @@ _MMQ_WS: dict = {}
 
 
 def _mmq_ws(device: torch.device, M: int, K: int, T: int) -> torch.Tensor:
-    """Per-device cached GEMM workspace, grown to fit ``M``, ``K`` and ``T``.
+    """GEMM workspace cached per (device, current stream), grown to fit ``M``, ``K`` and ``T``.
 
-    Calls that share it must be ordered on one stream (the queue counters
-    and the repacked activations live in it)."""
-    key = (device.index if device.index is not None else torch.cuda.current_device())
+    The workspace holds the call's queue counters, split-K arrival counters
+    and repacked activations, so two calls may share one only if they are
+    ordered on one stream: each stream gets its own.  A workspace is
+    allocated while its stream is current, so the caching allocator reuses
+    a replaced one only for work ordered after it on that stream (no
+    synchronisation needed).  Pass ``ws`` explicitly to manage it yourself.
+    """
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    stream = torch.cuda.current_stream(device)
+    key = (idx, stream.cuda_stream)
     need = workspace_bytes(QMM_OP_MMQ, M, K, T)
     ws = _MMQ_WS.get(key)
     if ws is None or ws.numel() < need:
-        if ws is not None:
-            torch.cuda.current_stream(device).synchronize()
         ws = workspace(need, device)
         _MMQ_WS[key] = ws
     return ws
@@ -101,9 +121,9 @@ def q8_1_quantize(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Ten
     """fp32 ``x[T, K]`` -> Q8_1 blocks ``[T, K/32, 40]``."""
     _need(x, torch.float32, "x", 2)
     T, K = x.shape
-    if out is None:
-        out = torch.empty((T, K // 32, 40), dtype=torch.uint8, device=x.device)
-    _acts(out, K, "out")
+    if K % 32:
+        raise ValueError(f"x: K = {K} is not a multiple of 32")
+    out = _out(out, (T, K // 32, 40), torch.uint8, x.device)
     _lib.call("q8_1_quantize", _p(x), _p(out), T, K, _stream(x.device))
     return out
 
@@ -111,9 +131,7 @@ def q8_1_quantize(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Ten
 def _mmvq(name: str, fmt: int, w, xq, out):
     M, K = _weights(w, fmt)
     T = _acts(xq, K)
-    if out is None:
-        out = torch.empty((T, M), dtype=torch.float32, device=w.device)
-    _need(out, torch.float32, "out", 2)
+    out = _out(out, (T, M), torch.float32, w.device)
     _lib.call(name, _p(w), _p(xq), _p(out), M, K, T, _stream(w.device))
     return out
 
@@ -136,9 +154,7 @@ def mmvq_q6k(w: torch.Tensor, xq: torch.Tensor, out: torch.Tensor | None = None)
 def _mmq(name: str, fmt: int, w, xq, out, ws):
     M, K = _weights(w, fmt)
     T = _acts(xq, K)
-    if out is None:
-        out = torch.empty((T, M), dtype=torch.float32, device=w.device)
-    _need(out, torch.float32, "out", 2)
+    out = _out(out, (T, M), torch.float32, w.device)
     ws = _mmq_ws(w.device, M, K, T) if ws is None else ws
     _need(ws, torch.uint8, "ws", 1)
     _lib.call(name, _p(w), _p(xq), _p(out), M, K, T, _p(ws), ws.numel(), _stream(w.device))
@@ -166,9 +182,7 @@ def _mmq_f32(name: str, fmt: int, w, x, out, ws):
     if x.shape[1] != K:
         raise ValueError(f"x: expected [T, {K}], got {tuple(x.shape)}")
     T = x.shape[0]
-    if out is None:
-        out = torch.empty((T, M), dtype=torch.float32, device=w.device)
-    _need(out, torch.float32, "out", 2)
+    out = _out(out, (T, M), torch.float32, w.device)
     ws = _mmq_ws(w.device, M, K, T) if ws is None else ws
     _need(ws, torch.uint8, "ws", 1)
     _lib.call(name, _p(w), _p(x), _p(out), M, K, T, _p(ws), ws.numel(), _stream(w.device))
@@ -218,10 +232,8 @@ def moe_grouped_mmq(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.Tens
         if tuple(expert_weights.shape) != (T, top_k):
             raise ValueError("expert_weights must be [T, top_k]")
     out_rows = T if expert_weights is not None else T * top_k
-    if out is None:
-        out = torch.empty((out_rows, M), dtype=torch.float32, device=w.device)
-    _need(out, torch.float32, "out", 2)
-    need = workspace_bytes(QMM_OP_MOE, M, K, T, E, top_k)
+    out = _out(out, (out_rows, M), torch.float32, w.device)
+    need = workspace_bytes(QMM_OP_MOE if expert_weights is not None else QMM_OP_MOE_SLOTS, M, K, T, E, top_k)
     if ws is None:
         ws = workspace(need, w.device)
     _need(ws, torch.uint8, "ws", 1)
@@ -251,9 +263,7 @@ def moe_slot_mmvq(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.Tensor
         rows_per_token = top_k
     else:
         raise ValueError("xq must have T or T*top_k rows")
-    if out is None:
-        out = torch.empty((T * top_k, M), dtype=torch.float32, device=w.device)
-    _need(out, torch.float32, "out", 2)
+    out = _out(out, (T * top_k, M), torch.float32, w.device)
     _lib.call("moe_slot_mmvq", fmt, _p(w), E, M, K, w.stride(0), _p(xq), rows_per_token, _p(ids), T, top_k,
               _p(out), _stream(w.device))
     return out
@@ -263,10 +273,10 @@ def swiglu_q8_1(g_u: torch.Tensor, out: torch.Tensor | None = None) -> torch.Ten
     """Rows ``g_u[R, 2F]`` (gate | up) -> Q8_1 of silu(gate) * up, ``[R, F/32, 40]``."""
     _need(g_u, torch.float32, "g_u", 2)
     R, F2 = g_u.shape
+    if F2 % 64:
+        raise ValueError(f"g_u: width {F2} must be 2*F with F a multiple of 32")
     F = F2 // 2
-    if out is None:
-        out = torch.empty((R, F // 32, 40), dtype=torch.uint8, device=g_u.device)
-    _acts(out, F, "out")
+    out = _out(out, (R, F // 32, 40), torch.uint8, g_u.device)
     _lib.call("swiglu_q8_1", _p(g_u), _p(out), R, F, _stream(g_u.device))
     return out
 

@@ -26,6 +26,7 @@ QMM_Q5_K = 13
 QMM_Q6_K = 14
 QMM_OP_MMQ = 1
 QMM_OP_MOE = 2
+QMM_OP_MOE_SLOTS = 3
 QMM_MMVQ_MAX_T = 8
 
 _vp, _i64, _sz, _i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int

@@ -126,6 +126,7 @@ struct RepackParams {
   uint8_t* xr;
   int nb;                       // super-blocks per row
   int T;                        // dense: rows
+  int ct0;                      // column tile of blockIdx.y == 0 (grid y is launched in chunks)
   // MoE: column tile -> (expert, slots)
   const int32_t* counts;
   const int32_t* offsets;
@@ -220,7 +221,7 @@ __device__ __forceinline__ void repack_f32(const RepackParams& P, const int* ct,
 
 template <int MODE>
 __global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
-  const int sb = blockIdx.x, ctile = blockIdx.y;
+  const int sb = blockIdx.x, ctile = P.ct0 + static_cast<int>(blockIdx.y);
   const int s = threadIdx.x >> 5, col = threadIdx.x & 31;
   if (P.counters != nullptr && sb == 0 && ctile == 0) {
     if (threadIdx.x < kXcds) P.counters[threadIdx.x] = 0u;
@@ -1137,6 +1138,23 @@ static int launch_mmq(const MmqParams& P, int total_tiles_hint, hipStream_t st) 
   return launch_status();
 }
 
+// The repack grid is (super-blocks, column tiles); column tiles are launched
+// in chunks of at most kMaxGridY along grid y (tens of thousands of column
+// tiles for calls with millions of tokens or routed slots).
+constexpr int kMaxGridY = 65535;
+
+template <int MODE>
+static int launch_repack(RepackParams R, int nb, int ctiles, hipStream_t st) {
+  for (int c0 = 0; c0 < ctiles; c0 += kMaxGridY) {
+    R.ct0 = c0;
+    const int n = ctiles - c0 < kMaxGridY ? ctiles - c0 : kMaxGridY;
+    hipLaunchKernelGGL(mmq_repack_kernel<MODE>, dim3(nb, n), dim3(256), 0, st, R);
+    const int rc = launch_status();
+    if (rc != QMM_OK) return rc;
+  }
+  return QMM_OK;
+}
+
 static size_t mmq_chunk_bytes(int64_t ctiles, int64_t nb) {
   return static_cast<size_t>(ctiles) * static_cast<size_t>(nb) * kChunkBytes;
 }
@@ -1174,8 +1192,12 @@ size_t mmq_workspace_bytes(int64_t M, int64_t K, int64_t T) {
 }
 
 // Upper bound of the column tiles of a grouped call: sum over experts of
-// ceil(count / 32) <= (slots + 31 * E) / 32.
-int64_t moe_max_ctiles(int64_t slots, int64_t E) { return (slots + 31 * E) / 32; }
+// ceil(count / 32) <= (slots + 31 * n) / 32 with n = min(E, slots) the most
+// experts that can receive a slot.
+int64_t moe_max_ctiles(int64_t slots, int64_t E) {
+  const int64_t n = E < slots ? E : slots;
+  return (slots + 31 * n) / 32;
+}
 size_t moe_chunk_bytes(int64_t slots, int64_t E, int64_t K) {
   return mmq_chunk_bytes(moe_max_ctiles(slots, E), K / kQK);
 }
@@ -1203,11 +1225,7 @@ int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64
   R.T = static_cast<int>(T);
   R.dbgS = dbgS;
   R.counters = static_cast<unsigned*>(ws);
-  if (dbg)
-    hipLaunchKernelGGL(mmq_repack_kernel<kDebug>, dim3(nb, ctiles), dim3(256), 0, st, R);
-  else
-    hipLaunchKernelGGL(mmq_repack_kernel<kDense>, dim3(nb, ctiles), dim3(256), 0, st, R);
-  int rc = launch_status();
+  int rc = dbg ? launch_repack<kDebug>(R, nb, ctiles, st) : launch_repack<kDense>(R, nb, ctiles, st);
   if (rc != QMM_OK) return rc;
   MmqParams P{};
   P.w = static_cast<const uint8_t*>(w);
@@ -1244,8 +1262,7 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   R.E = E;
   R.top_k = top_k;
   R.rows_per_token = rows_per_token;
-  hipLaunchKernelGGL(mmq_repack_kernel<kMoe>, dim3(nb, max_ctiles), dim3(256), 0, st, R);
-  int rc = launch_status();
+  int rc = launch_repack<kMoe>(R, nb, max_ctiles, st);
   if (rc != QMM_OK) return rc;
   MmqParams P{};
   P.w = w;
@@ -1272,6 +1289,8 @@ static int check_mmq(const void* w, const void* xq, const float* y, int64_t M, i
                      const void* ws, size_t ws_bytes) {
   if (M < 1 || T < 1 || K < kQK || (K % kQK) != 0) return QMM_ERR_SHAPE;
   if (M > (1 << 30) || T > (1 << 24) || K / kQK > (1 << 16)) return QMM_ERR_SHAPE;
+  // tile indices are 32-bit in the kernel
+  if (mmq_dense_tiles(M, T) * mmq_nsplit(M, K, T) > (int64_t{1} << 30)) return QMM_ERR_SHAPE;
   if (!w || !xq || !y || !ws) return QMM_ERR_NULL;
   if (!aligned16(w) || !aligned16(xq) || !aligned16(y) || !aligned16(ws)) return QMM_ERR_ALIGN;
   if (ws_bytes < mmq_workspace_bytes(M, K, T)) return QMM_ERR_WORKSPACE;

@@ -57,7 +57,10 @@ struct MoeLayout {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-static MoeLayout moe_layout(void* ws, int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k) {
+// Workspace: counters, the route tables, the repacked routed rows and, for
+// weighted calls only, the per-slot fp32 results of the ordered combine
+// (last, so a per-slot call needs only the prefix).
+static MoeLayout moe_layout(void* ws, int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k, bool weighted) {
   MoeLayout L{};
   uint8_t* b = static_cast<uint8_t*>(ws);
   size_t off = kMoeCounterBytes;
@@ -68,17 +71,17 @@ static MoeLayout moe_layout(void* ws, int64_t M, int64_t K, int64_t T, int64_t E
   L.work_off = L.offsets + (E + 1);
   L.ct_off = L.work_off + (E + 1);
   L.bucket = L.ct_off + (E + 1);
-  off = align_up(off + ints * 4, 256);
-  L.scratch = reinterpret_cast<float*>(b + off);
-  off = align_up(off + static_cast<size_t>(T * top_k) * static_cast<size_t>(M) * 4, 1024);
+  off = align_up(off + ints * 4, 1024);
   L.chunks = b + off;
-  off += moe_chunk_bytes(T * top_k, E, K);
+  off = align_up(off + moe_chunk_bytes(T * top_k, E, K), 256);
+  L.scratch = weighted ? reinterpret_cast<float*>(b + off) : nullptr;
+  if (weighted) off += static_cast<size_t>(T * top_k) * static_cast<size_t>(M) * 4;
   L.bytes = off;
   return L;
 }
 
-size_t moe_workspace_bytes(int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k) {
-  return moe_layout(nullptr, M, K, T, E, top_k).bytes;
+size_t moe_workspace_bytes(int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k, bool weighted) {
+  return moe_layout(nullptr, M, K, T, E, top_k, weighted).bytes;
 }
 
 // Lanes of the wave holding the same expert id as this lane (v: lane
@@ -248,9 +251,11 @@ extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int
                                const int32_t* ids, const float* expert_weights, int64_t T,
                                int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream) {
   if (fmt != QMM_Q4_K && fmt != QMM_Q5_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
-  if (E < 1 || E > kMoeMaxE || M < 1 || M > (1 << 30) || K < kQK || (K % kQK) != 0 || T < 1 ||
-      top_k < 1 || top_k > E || top_k > kMoeMaxTopK || T * top_k > (1 << 30))
+  if (E < 1 || E > kMoeMaxE || M < 1 || M > (1 << 30) || K < kQK || (K % kQK) != 0 || K / kQK > (1 << 16) ||
+      T < 1 || top_k < 1 || top_k > E || top_k > kMoeMaxTopK || T * top_k > (1 << 30))
     return QMM_ERR_SHAPE;
+  // work entries (m_tile, column tile) are numbered in 32-bit
+  if (((M + kMoeBM - 1) / kMoeBM) * moe_max_ctiles(T * top_k, E) > (int64_t{1} << 30)) return QMM_ERR_SHAPE;
   if (x_rows_per_token != 1 && x_rows_per_token != top_k) return QMM_ERR_SHAPE;
   const int64_t row_bytes = (K / kQK) * (fmt == QMM_Q4_K ? kQ4Bytes : fmt == QMM_Q5_K ? kQ5Bytes : kQ6Bytes);
   // Q4_K / Q5_K blocks are read with 16-byte loads, Q6_K blocks with 2-byte aligned ones
@@ -260,7 +265,7 @@ extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int
   if (!aligned16(w) || !aligned16(xq) || !aligned16(ids) || !aligned16(y) || !aligned16(ws) ||
       (expert_weights && !aligned16(expert_weights)))
     return QMM_ERR_ALIGN;
-  const MoeLayout L = moe_layout(ws, M, K, T, E, top_k);
+  const MoeLayout L = moe_layout(ws, M, K, T, E, top_k, expert_weights != nullptr);
   if (ws_bytes < L.bytes) return QMM_ERR_WORKSPACE;
   hipStream_t st = to_stream(stream);
   const int n = static_cast<int>(T * top_k);

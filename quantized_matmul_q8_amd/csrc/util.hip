@@ -4,7 +4,7 @@
 
 namespace qmm {
 
-size_t moe_workspace_bytes(int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k);
+size_t moe_workspace_bytes(int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k, bool weighted);
 size_t mmq_workspace_bytes(int64_t M, int64_t K, int64_t T);
 int debug_mmvq(int fmt, const void* w, const void* xq, int32_t* D, int32_t* S, int64_t M, int64_t K,
                int64_t T, hipStream_t st);
@@ -84,7 +84,8 @@ extern "C" size_t qmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t T, i
                                       int64_t top_k) {
   if (M < 0 || K < 0 || T < 0 || E < 0 || top_k < 0) return 0;
   if (op == QMM_OP_MMQ) return mmq_workspace_bytes(M, K, T);
-  if (op == QMM_OP_MOE) return moe_workspace_bytes(M, K, T, E, top_k);
+  if (op == QMM_OP_MOE) return moe_workspace_bytes(M, K, T, E, top_k, true);
+  if (op == QMM_OP_MOE_SLOTS) return moe_workspace_bytes(M, K, T, E, top_k, false);
   return 0;
 }
 

@@ -149,3 +149,43 @@ def test_debug_and_probe_errors():
     assert L.qmm_probe_read(NUL, 16, FAKE, NUL) == _lib.QMM_ERR_NULL
     assert L.swiglu_q8_1(FAKE, FAKE, 1, 48, NUL) == _lib.QMM_ERR_SHAPE
     assert L.qmm_workspace_init(MISAL, 16, NUL) == _lib.QMM_ERR_ALIGN
+
+
+def test_mmq_limits_accepted_and_rejected_on_the_host():
+    # sizes at the documented limits pass the shape checks (the NULL
+    # workspace is reported next); one past them is a shape error
+    f = L.mmq_q4k
+    assert f(FAKE, FAKE, FAKE, 128, 256, 1 << 24, NUL, 0, NUL) == _lib.QMM_ERR_NULL      # T = 2^24
+    assert f(FAKE, FAKE, FAKE, 128, 256, (1 << 24) + 1, NUL, 0, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 128, 256 << 16, 64, NUL, 0, NUL) == _lib.QMM_ERR_NULL     # K/256 = 2^16
+    assert f(FAKE, FAKE, FAKE, 128, 256 << 17, 64, NUL, 0, NUL) == _lib.QMM_ERR_SHAPE
+    # output tiles: 2^14 row tiles x 2^18 column tiles = 2^32 > 2^30
+    assert f(FAKE, FAKE, FAKE, 1 << 21, 256, 1 << 24, NUL, 0, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 1 << 19, 256, 1 << 24, NUL, 0, NUL) == _lib.QMM_ERR_NULL   # 2^12 x 2^18 = 2^30
+    # the workspace of a call with many column tiles is sized for every chunk
+    # (the repack grid is launched in pieces of at most 65535 column tiles)
+    T = 65535 * 32 + 100
+    assert L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 128, 256, T, 0, 0) >= 2048 + ((T + 31) // 32) * 11264
+
+
+def test_moe_limits_and_workspace_ops():
+    f = L.moe_grouped_mmq
+
+    def call(T, top_k, E=8, M=64, K=256, ws=NUL, wsb=0, p=NUL):
+        return f(_lib.QMM_Q4_K, FAKE, E, M, K, M * (K // 256) * 144, FAKE, 1, FAKE, p, T, top_k, FAKE, ws, wsb, NUL)
+
+    assert call(1 << 27, 8) == _lib.QMM_ERR_NULL                   # T*top_k = 2^30 slots
+    assert call((1 << 27) + 1, 8) == _lib.QMM_ERR_SHAPE
+    assert call(4, 2, K=256 << 17) == _lib.QMM_ERR_SHAPE           # K/256 > 2^16
+    # work entries: ceil(M/128) x (slots + 31*min(E, slots))/32 > 2^30
+    assert call(1 << 22, 8, M=128 * 1024) == _lib.QMM_ERR_SHAPE
+    w = L.qmm_workspace_bytes
+    slots = L.qmm_workspace_bytes(_lib.QMM_OP_MOE_SLOTS, 2048, 768, 512, 128, 8)
+    weighted = w(_lib.QMM_OP_MOE, 2048, 768, 512, 128, 8)
+    assert weighted - slots >= 512 * 8 * 2048 * 4         # the per-slot fp32 scratch
+    assert slots < 512 * 8 * 2048 * 4
+    # one token routed to 8 of 512 experts: at most 8 column tiles are repacked
+    one = w(_lib.QMM_OP_MOE_SLOTS, 2048, 2048, 1, 512, 8)
+    assert one <= 256 + 4 * (512 + 3 * 513 + 8) + 1024 + 8 * 8 * 11264 + 256
+    # a weighted call rejects the per-slot size (no launch: the check fails)
+    assert call(4, 2, ws=FAKE, wsb=w(_lib.QMM_OP_MOE_SLOTS, 64, 256, 4, 8, 2), p=FAKE) == _lib.QMM_ERR_WORKSPACE
