@@ -54,7 +54,8 @@ typedef enum qmm_status {
     QMM_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned                */
     QMM_ERR_WORKSPACE = -4,   /* workspace smaller than qmm_workspace_bytes()    */
     QMM_ERR_HIP = -5,         /* the HIP runtime reported an error               */
-    QMM_ERR_UNSUPPORTED = -6  /* unknown format / operation code                 */
+    QMM_ERR_UNSUPPORTED = -6, /* unknown format / operation code                 */
+    QMM_ERR_SCRATCH = -7      /* needs more than QMM_STATIC_SCRATCH_BYTES        */
 } qmm_status;
 
 /* Weight formats for moe_grouped_mmq, moe_slot_mmvq and qmm_debug_subdots. */
@@ -137,6 +138,25 @@ int mmq_q5k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64
             void* ws, size_t ws_bytes, void* stream);
 int mmq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mmq_q4k_noalloc -- mmq_q4k for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and result, bit for bit, but the workspace is
+ * a static device array of QMM_STATIC_SCRATCH_BYTES inside the library, so
+ * the caller passes only inputs and outputs.  The call allocates nothing.
+ * A call whose qmm_workspace_bytes(QMM_OP_MMQ, M, K, T, 0, 0) exceeds
+ * QMM_STATIC_SCRATCH_BYTES returns QMM_ERR_SCRATCH before anything is
+ * enqueued (e.g. T = 1024 needs K <= 23552).  Each GPU holds one copy of the
+ * array for the life of the process, shared by every call on that GPU:
+ * calls that overlap on one GPU (different streams, or host threads without
+ * ordering) race and give wrong results; calls ordered on one stream are
+ * safe.  The call clears what must start at zero (its queue counters) in
+ * its first kernel.  Same arguments, limits and other errors as mmq_q4k.
+ */
+#define QMM_STATIC_SCRATCH_BYTES (32u << 20)
+int mmq_q4k_noalloc(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
+                    void* stream);
 
 /*
  * mmq_q4k_f32 / mmq_q6k_f32 -- the same GEMM with fp32 activations x[T][K]

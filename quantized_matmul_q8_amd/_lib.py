@@ -21,6 +21,8 @@ QMM_ERR_ALIGN = -3
 QMM_ERR_WORKSPACE = -4
 QMM_ERR_HIP = -5
 QMM_ERR_UNSUPPORTED = -6
+QMM_ERR_SCRATCH = -7
+QMM_STATIC_SCRATCH_BYTES = 32 << 20
 QMM_Q4_K = 12
 QMM_Q5_K = 13
 QMM_Q6_K = 14
@@ -40,6 +42,7 @@ SIGNATURES = {
     "mmq_q4k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "mmq_q5k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "mmq_q6k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "mmq_q4k_noalloc": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "mmq_q4k_f32": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "mmq_q5k_f32": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "mmq_q6k_f32": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),

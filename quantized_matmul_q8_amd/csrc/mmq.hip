@@ -59,6 +59,7 @@
 //   initialisation and no memset.
 #include "qmm_common.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 namespace qmm {
@@ -1285,21 +1286,72 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   return launch_mmq<QMM_Q6_K, 1, kMoe>(P, 0, st);
 }
 
-static int check_mmq(const void* w, const void* xq, const float* y, int64_t M, int64_t K, int64_t T,
-                     const void* ws, size_t ws_bytes) {
+// Host checks of a GEMM call's sizes and operand pointers, then of its workspace.
+static int check_mmq_args(const void* w, const void* xq, const float* y, int64_t M, int64_t K, int64_t T) {
   if (M < 1 || T < 1 || K < kQK || (K % kQK) != 0) return QMM_ERR_SHAPE;
   if (M > (1 << 30) || T > (1 << 24) || K / kQK > (1 << 16)) return QMM_ERR_SHAPE;
   // tile indices are 32-bit in the kernel
   if (mmq_dense_tiles(M, T) * mmq_nsplit(M, K, T) > (int64_t{1} << 30)) return QMM_ERR_SHAPE;
-  if (!w || !xq || !y || !ws) return QMM_ERR_NULL;
-  if (!aligned16(w) || !aligned16(xq) || !aligned16(y) || !aligned16(ws)) return QMM_ERR_ALIGN;
+  if (!w || !xq || !y) return QMM_ERR_NULL;
+  if (!aligned16(w) || !aligned16(xq) || !aligned16(y)) return QMM_ERR_ALIGN;
+  return QMM_OK;
+}
+
+static int check_mmq(const void* w, const void* xq, const float* y, int64_t M, int64_t K, int64_t T,
+                     const void* ws, size_t ws_bytes) {
+  const int st = check_mmq_args(w, xq, y, M, K, T);
+  if (st != QMM_OK) return st;
+  if (!ws) return QMM_ERR_NULL;
+  if (!aligned16(ws)) return QMM_ERR_ALIGN;
   if (ws_bytes < mmq_workspace_bytes(M, K, T)) return QMM_ERR_WORKSPACE;
+  return QMM_OK;
+}
+
+// Scratch of mmq_q4k_noalloc: a device array of fixed size in the library's
+// code object (each GPU the library runs on holds its own copy until the
+// process ends), used instead of a caller workspace.  Host code never passes
+// `scratch` itself to a kernel (on the host the name is only a stand-in for
+// the symbol); it takes the array's device address, once per device, from
+// hipGetSymbolAddress and passes that.
+static __device__ __align__(256) uint8_t scratch[QMM_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's `scratch`, looked up on the device's first
+// call (with the device current) and kept.
+static int static_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QMM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return QMM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return QMM_ERR_HIP;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
   return QMM_OK;
 }
 
 }  // namespace qmm
 
 using namespace qmm;
+
+extern "C" int mmq_q4k_noalloc(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
+                               void* stream) {
+  // the checks of mmq_q4k, with the static array in place of ws
+  const int st = check_mmq_args(w, xq, y, M, K, T);
+  if (st != QMM_OK) return st;
+  if (mmq_workspace_bytes(M, K, T) > QMM_STATIC_SCRATCH_BYTES) return QMM_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int rc = static_scratch(&ws);
+  if (rc != QMM_OK) return rc;
+  // the activation repack that runs first zeroes the queue and split-K
+  // counters in the scratch, so no clearing is needed here
+  return mmq_dense(QMM_Q4_K, w, xq, y, M, K, T, ws, to_stream(stream), nullptr, nullptr, nullptr);
+}
 
 extern "C" int mmq_q4k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int64_t T,
                        void* ws, size_t ws_bytes, void* stream) {

@@ -76,6 +76,7 @@ extern "C" const char* qmm_status_str(int status) {
     case QMM_ERR_WORKSPACE: return "workspace too small";
     case QMM_ERR_HIP: return "HIP runtime error";
     case QMM_ERR_UNSUPPORTED: return "unsupported format or operation";
+    case QMM_ERR_SCRATCH: return "call needs more scratch than the library's static array holds";
     default: return "unknown status";
   }
 }

@@ -49,7 +49,7 @@ def test_library_is_in_tree():
 
 def test_status_strings():
     assert L.qmm_status_str(0) == b"ok"
-    for st in range(-6, 0):
+    for st in range(-7, 0):
         assert L.qmm_status_str(st) not in (b"ok", b"unknown status")
     assert L.qmm_status_str(-99) == b"unknown status"
 
@@ -189,3 +189,13 @@ def test_moe_limits_and_workspace_ops():
     assert one <= 256 + 4 * (512 + 3 * 513 + 8) + 1024 + 8 * 8 * 11264 + 256
     # a weighted call rejects the per-slot size (no launch: the check fails)
     assert call(4, 2, ws=FAKE, wsb=w(_lib.QMM_OP_MOE_SLOTS, 64, 256, 4, 8, 2), p=FAKE) == _lib.QMM_ERR_WORKSPACE
+
+
+def test_noalloc_host_errors():
+    f = L.mmq_q4k_noalloc
+    assert f(FAKE, FAKE, FAKE, 4, 256, 0, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(NUL, FAKE, FAKE, 4, 256, 1, NUL) == _lib.QMM_ERR_NULL
+    assert f(FAKE, FAKE, MISAL, 4, 256, 1, NUL) == _lib.QMM_ERR_ALIGN
+    # 1M tokens need gigabytes of workspace: refused before anything runs
+    assert f(FAKE, FAKE, FAKE, 4096, 4096, 1 << 20, NUL) == _lib.QMM_ERR_SCRATCH
+    assert L.qmm_status_str(_lib.QMM_ERR_SCRATCH) != b"unknown status"
