@@ -278,6 +278,45 @@ int qmm_debug_subdots(int fmt, int path, const void* w, const void* xq, int32_t*
  */
 int qmm_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * qmm_probe_mfma -- measurement hook, not part of the method: int8 MFMA
+ * (v_mfma_i32_32x32x32_i8, 65536 int8 ops each) back to back from
+ * registers, four independent accumulators per wave, `iters` rounds of four
+ * per wave; one workgroup of eight waves per CU per two waves per SIMD
+ * (waves_per_simd 2, 4 or 8).  Ops per launch = CUs * waves_per_simd * 4 *
+ * iters * 4 * 65536.  The matrix-core rate the int8 peak assumes ([MMQ]
+ * "Revised priorities (post-M3 findings)": measure before tuning).
+ * 1 <= iters <= 2^24.  Writes sink[0] only for an improbable value.
+ */
+int qmm_probe_mfma(int64_t iters, int waves_per_simd, uint32_t* sink, void* stream);
+
+/*
+ * qmm_probe_mfma_epilogue -- measurement hook: the GEMM's per-sub-block
+ * inner loop without global memory ([GAP] root cause 1, the per-sub-block
+ * rescale epilogue).  Per iteration and wave: two int8 MFMAs (two 32-column
+ * blocks) started from the bits of 1.5*2^23 and, per output element, the two
+ * fp32 FMAs of the epilogue.  mode 1: operands in registers; mode 2: row
+ * scales, column factors and B operands read from LDS as the GEMM reads
+ * them; mode 3: mode 2 plus the Q4_K min-term fp32 MFMA every second
+ * iteration into the FMA accumulator; mode 4: that MFMA into an accumulator
+ * of its own; mode 5: the min term as three bf16 MFMAs per eight
+ * iterations into its own accumulator; mode 6: the same into the FMA
+ * accumulator.  int8 ops per launch = CUs * waves_per_simd * 4 * iters * 2 *
+ * 65536.  waves_per_simd 2 or 4; 1 <= iters <= 2^24.
+ */
+int qmm_probe_mfma_epilogue(int mode, int64_t iters, int waves_per_simd, uint32_t* sink, void* stream);
+
+/*
+ * qmm_probe_read_geom -- measurement hook: qmm_probe_read with its geometry
+ * as arguments, for sweeping the HBM read ceiling ([8e] §6: concurrency
+ * first).  Each thread of 256-thread workgroups issues loads_per_thread
+ * (1, 2, 4, 8 or 16) lane-contiguous 16-byte loads before using any;
+ * grid = 0 launches one pass over `bytes` (a multiple of 16), a smaller
+ * grid strides over the buffer persistently.
+ */
+int qmm_probe_read_geom(const void* buf, size_t bytes, int loads_per_thread, int64_t grid, uint32_t* sink,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,8 @@ __all__ = [
     "q8_1_quantize", "mmvq_q4k", "mmvq_q5k", "mmvq_q6k", "mmq_q4k", "mmq_q5k", "mmq_q6k", "mmq_q4k_f32", "mmq_q5k_f32",
     "mmq_q6k_f32",
     "moe_grouped_mmq", "moe_slot_mmvq",
-    "swiglu_q8_1", "workspace", "workspace_bytes", "debug_subdots", "probe_read", "QmmError",
+    "swiglu_q8_1", "workspace", "workspace_bytes", "debug_subdots", "probe_read", "probe_read_geom",
+    "probe_mfma", "probe_mfma_epilogue", "QmmError",
     "QMM_Q4_K", "QMM_Q5_K", "QMM_Q6_K", "LIB_PATH",
 ]
 
@@ -305,4 +306,32 @@ def probe_read(buf: torch.Tensor, nbytes: int | None = None, sink: torch.Tensor 
     if sink is None:
         sink = torch.zeros((4,), dtype=torch.int32, device=buf.device)
     _lib.call("qmm_probe_read", _p(buf), nbytes, _p(sink), _stream(buf.device))
+    return sink
+
+
+def probe_read_geom(buf: torch.Tensor, nbytes: int, loads_per_thread: int, grid: int = 0,
+                    sink: torch.Tensor | None = None):
+    """Enqueue the read probe with ``loads_per_thread`` loads in flight per thread and ``grid``
+    workgroups (0: one pass)."""
+    if buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    if sink is None:
+        sink = torch.zeros((4,), dtype=torch.int32, device=buf.device)
+    _lib.call("qmm_probe_read_geom", _p(buf), nbytes, loads_per_thread, grid, _p(sink), _stream(buf.device))
+    return sink
+
+
+def probe_mfma(iters: int, waves_per_simd: int, sink: torch.Tensor) -> torch.Tensor:
+    """Enqueue the int8-MFMA-only probe (see include/qmm.h for its op count)."""
+    _need(sink, torch.int32, "sink", 1)
+    _lib.call("qmm_probe_mfma", iters, waves_per_simd, _p(sink), _stream(sink.device))
+    return sink
+
+
+def probe_mfma_epilogue(mode: int, iters: int, waves_per_simd: int, sink: torch.Tensor) -> torch.Tensor:
+    """Enqueue the MFMA + fp32 epilogue probe (mode 1, 2 or 3; see include/qmm.h)."""
+    _need(sink, torch.int32, "sink", 1)
+    _lib.call("qmm_probe_mfma_epilogue", mode, iters, waves_per_simd, _p(sink), _stream(sink.device))
     return sink

@@ -55,6 +55,9 @@ SIGNATURES = {
     "qmm_status_str": (ctypes.c_char_p, [_i]),
     "qmm_debug_subdots": (_i, [_i, _i, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "qmm_probe_read": (_i, [_vp, _sz, _vp, _vp]),
+    "qmm_probe_mfma": (_i, [_i64, _i, _vp, _vp]),
+    "qmm_probe_mfma_epilogue": (_i, [_i, _i64, _i, _vp, _vp]),
+    "qmm_probe_read_geom": (_i, [_vp, _sz, _i, _i64, _vp, _vp]),
 }
 
 

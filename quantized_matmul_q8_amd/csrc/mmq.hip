@@ -28,8 +28,14 @@
 //     t   = fma(beta, X, -beta*1.5*2^23)   = beta*D, rounded once
 //     acc = fma(alpha, t, acc)
 //   is two fp32 VALU ops per output element per sub-block.  The Q4_K min
-//   term sum_s (-dmin*m_is) * (beta_js*S_js) runs on v_mfma_f32_32x32x2_f32
-//   straight into the accumulator.
+//   term sum_s (-dmin*m_is) * (beta_js*S_js) runs on bf16 MFMA straight into
+//   the accumulator: both factors are split exactly into three bf16 parts
+//   (-dmin*m has at most 17 significant bits, beta*S at most 23), and six of
+//   the nine part products -- all but those below 2^-23 of the whole --
+//   make up K = 48 per super-block, three v_mfma_f32_32x32x16_bf16.  The
+//   fp32 32x32x2 MFMA it replaces took 64 matrix cycles per two sub-blocks
+//   and held the epilogue back by a quarter (ceiling probe: 0.85 against
+//   1.0 POP/s).
 // * Workgroup.  Eight waves (two per SIMD, which the VALU-bound epilogue
 //   needs to reach the issue rate): a tile of 128 rows x 32*NT columns, row
 //   group rw = wave % 4 (32 rows), K half kh = wave / 4 taking the
@@ -71,12 +77,30 @@ constexpr int kGroupM = 8;             // row tiles per run of the dense tile or
 constexpr uint32_t kMagicBits = 0x4B400000u;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// x = p0 + p1 + p2 exactly for x with at most 24 significant bits (and no
+// bf16 underflow): each part keeps the top 8 bits of what remains.
+__device__ __forceinline__ void split3_bf16(float x, __bf16& p0, __bf16& p1, __bf16& p2) {
+  p0 = static_cast<__bf16>(x);
+  const float r = x - static_cast<float>(p0);
+  p1 = static_cast<__bf16>(r);
+  p2 = static_cast<__bf16>(r - static_cast<float>(p1));
+}
+
+// Min-term MFMA k (0..2), lane half h: partial product j = 2k + h is
+// A-part kMinP[j] times B-part kMinQ[j] over the 8 sub-blocks of a
+// super-block.  The six pairs are those with p + q <= 2 (the rest are below
+// 2^-23 of the product).
+__device__ __forceinline__ int min_part_a(int j) { return (0x210100 >> (4 * j)) & 3; }  // 0,0,1,0,1,2
+__device__ __forceinline__ int min_part_b(int j) { return (0x012010 >> (4 * j)) & 3; }  // 0,1,0,2,1,0
+
 // Repacked activation chunk: 32 columns x one super-block (8 Q8_1 blocks).
 constexpr int kChunkCols = 32;
 constexpr int kChunkPay = 0;       // [8 s][2 h][32 col] x 16 bytes: values 16h .. 16h+15 of block s
 constexpr int kChunkFac = 8192;    // [8 s][32 col] float2 (beta, -beta*C)
-constexpr int kChunkSig = 10240;   // [8 s][32 col] float beta*S
-constexpr int kChunkBytes = 11264; // 11 x 1 KB
+constexpr int kChunkMin = 10240;   // [3 q][32 col][8 s] bf16: part q of beta*S (min-term B operand)
+constexpr int kChunkBytes = 12288; // 12 x 1 KB (the last 512 bytes unused)
 constexpr int kChunkKB = kChunkBytes / 1024;
 
 enum MmqMode { kDense = 0, kMoe = 1, kDebug = 2 };
@@ -190,7 +214,7 @@ __device__ __forceinline__ void repack_f32(const RepackParams& P, const int* ct,
   uint8_t* ch = P.xr + (static_cast<size_t>(ctile) * P.nb + sb) * kChunkBytes;
   uint32_t* pay = reinterpret_cast<uint32_t*>(ch + kChunkPay);
   float2* fac = reinterpret_cast<float2*>(ch + kChunkFac);
-  float* sig = reinterpret_cast<float*>(ch + kChunkSig);
+  __bf16* bmin = reinterpret_cast<__bf16*>(ch + kChunkMin);
   // every pass's load first (eight 16-byte loads in flight per thread)
   float4 vs[8];
 #pragma unroll
@@ -215,7 +239,8 @@ __device__ __forceinline__ void repack_f32(const RepackParams& P, const int* ct,
     if (part == 0) {
       const float beta = h2f(f2h_bits(d) & 0xffffu);  // the stored f16 scale
       fac[s * 32 + col] = make_float2(beta, -beta * kMagic);
-      sig[s * 32 + col] = beta * static_cast<float>(S);
+      split3_bf16(beta * static_cast<float>(S), bmin[col * 8 + s], bmin[(32 + col) * 8 + s],
+                  bmin[(64 + col) * 8 + s]);
     }
   }
 }
@@ -257,7 +282,8 @@ __global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
   const float beta = h2f(u[0].x & 0xffffu);
   const int S = static_cast<int>(u[4].y);
   reinterpret_cast<float2*>(ch + kChunkFac)[s * 32 + col] = make_float2(beta, -beta * kMagic);
-  reinterpret_cast<float*>(ch + kChunkSig)[s * 32 + col] = beta * static_cast<float>(S);
+  __bf16* bmin = reinterpret_cast<__bf16*>(ch + kChunkMin);
+  split3_bf16(beta * static_cast<float>(S), bmin[col * 8 + s], bmin[(32 + col) * 8 + s], bmin[(64 + col) * 8 + s]);
   // debug: the stored sums, Q4_K only (the Q6_K hook passes no S buffer)
   if (MODE == kDebug && P.dbgS != nullptr && col < ncols)
     P.dbgS[static_cast<size_t>(xrow) * P.nb * 8 + sb * 8 + s] = S;
@@ -288,7 +314,9 @@ struct MmqSmem {
   static constexpr int kChunks = StepSplit<FMT>::kSbPerStep * NT * kChunkBytes;  // [half][ct] chunks
   static constexpr int kRed = 4 * NT * 16 * 64 * 4;                             // split-K reduction
   static constexpr int kStage = kChunks > kRed ? kChunks : kRed;
-  static constexpr int kWave = (8 * 32 + (is_q4fam(FMT) ? 8 * 32 : 0)) * 4;  // alpha (+ -dmin*m), 8 sub-blocks
+  // alpha [8 sub-blocks][32 rows] fp32, then for Q4_K / Q5_K the min-term A
+  // operand [3 parts][32 rows][8 sub-blocks] bf16
+  static constexpr int kWave = 8 * 32 * 4 + (is_q4fam(FMT) ? 3 * 32 * 8 * 2 : 0);
   static constexpr int kWaveOff = 2 * kStage;
   static constexpr int kBytes = kWaveOff + kMmqWaves * kWave;
 };
@@ -432,13 +460,15 @@ __device__ __forceinline__ void write_scales_q4fam(const MmqPrefetch<FMT>& F, fl
   // lane (row col, half g) decodes sub-blocks 4g .. 4g+3 of its row
   const float d = h2f(F.hdr.x & 0xffffu), dmin = h2f(F.hdr.x >> 16);
   float* wa = wave_lds;
-  float* wm = wave_lds + 8 * 32;
+  __bf16* wm = reinterpret_cast<__bf16*>(wave_lds + 8 * 32);
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     int sc, m;
     q4k_scale_min(4 * g + jj, F.hdr.y, F.hdr.z, F.hdr.w, sc, m);
     wa[(4 * g + jj) * 32 + col] = d * static_cast<float>(sc);
-    wm[(4 * g + jj) * 32 + col] = -(dmin * static_cast<float>(m));
+    // -dmin*m (exact in fp32: at most 17 significant bits) as three bf16 parts
+    const int e = col * 8 + 4 * g + jj;
+    split3_bf16(-(dmin * static_cast<float>(m)), wm[e], wm[256 + e], wm[512 + e]);
   }
 }
 __device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q4_K>& F, float* wave_lds, int col, int g) {
@@ -456,6 +486,25 @@ __device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q6_K>& F, flo
     wave_lds[(4 * g + q) * 32 + col] = d * static_cast<float>(static_cast<int8_t>((word >> (8 * q)) & 0xffu));
 }
 
+// Q4_K / Q5_K min term of a super-block: three bf16 MFMAs per column tile,
+// MFMA k (issued after the epilogue of sub-block 2k + 1) taking the (A part,
+// B part) products 2k and 2k + 1 in its two lane halves.  A[i][kk] = part of
+// -dmin*m of row i (the wave's LDS region), B[kk][j] = part of beta*S of
+// column j (the chunk), kk = 8 * half + sub-block.  Both kernel variants add
+// it to each accumulator at the same point, so a product computed by the
+// one- or the two-column-tile kernel has the same bits.
+__device__ __forceinline__ bool min_slot(int u) { return u == 1 || u == 3 || u == 5; }
+
+__device__ __forceinline__ v8bf min_a(const float* wl, int u) {
+  const int g = (threadIdx.x & 63) >> 5, col = threadIdx.x & 31;
+  return *reinterpret_cast<const v8bf*>(reinterpret_cast<const uint8_t*>(wl + 8 * 32) +
+                                        (min_part_a(2 * (u >> 1) + g) * 32 + col) * 16);
+}
+__device__ __forceinline__ v8bf min_b(const uint8_t* chunk, int u) {
+  const int g = (threadIdx.x & 63) >> 5, col = threadIdx.x & 31;
+  return *reinterpret_cast<const v8bf*>(chunk + kChunkMin + (min_part_b(2 * (u >> 1) + g) * 32 + col) * 16);
+}
+
 // LDS operands of one MFMA sub-block u for this lane: the 16 row scales
 // alpha of its rows, (beta, -beta*C) and the B operand of each column tile,
 // and for Q4_K at odd u the min-term operands of sub-blocks u-1, u.
@@ -465,7 +514,7 @@ struct SubOps {
   float al[16];
   float2 bp[NT];
   BQ bq[NT];
-  float am, bm[NT];
+  v8bf am, bm[NT];   // min-term operands (two-tile kernel, Q4_K / Q5_K, min_slot(u))
 };
 
 // u indexes MFMA sub-blocks of the super-block: Q4_K u = the 32-weight
@@ -485,20 +534,19 @@ __device__ __forceinline__ void load_sub(const uint8_t* st, const float* wl, int
       O.bq[ct] = *reinterpret_cast<const long*>(ch + kChunkPay + ((2 * s + (u & 1)) * 32 + col) * 16 + 8 * g);
     O.bp[ct] = reinterpret_cast<const float2*>(ch + kChunkFac)[s * 32 + col];
   }
+  if constexpr (is_q4fam(FMT)) {
+    if (min_slot(u)) {
+      O.am = min_a(wl, u);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) O.bm[ct] = min_b(st + ct * kChunkBytes, u);
+    }
+  }
   if constexpr (!kLean<FMT, NT>) {  // the lean epilogue reads them itself
     const float* wa = wl + ul * 32 + 4 * g;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float4 t4 = *reinterpret_cast<const float4*>(wa + 8 * k);
       O.al[4 * k] = t4.x; O.al[4 * k + 1] = t4.y; O.al[4 * k + 2] = t4.z; O.al[4 * k + 3] = t4.w;
-    }
-  }
-  if constexpr (is_q4fam(FMT)) {
-    if (u & 1) {
-      O.am = wl[8 * 32 + (u - 1 + g) * 32 + col];
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-        O.bm[ct] = reinterpret_cast<const float*>(st + ct * kChunkBytes + kChunkSig)[(u - 1 + g) * 32 + col];
     }
   }
 }
@@ -566,7 +614,8 @@ __device__ __forceinline__ int col_out_row(const MmqParams& P, const TileCols& t
 template <int FMT, int NT, int MODE>
 __device__ __forceinline__ void mmq_epilogue(const MmqParams& P, const TileCols& tc, int r0, int sb, int ub, int u,
                                              int ct, const v16i& Xc, const SubOps<FMT, NT>& Ou, v16f (&acc)[NT],
-                                             const float* wl = nullptr, int ul = 0) {
+                                             const float* wl = nullptr, int ul = 0,
+                                             const uint8_t* Xchunk = nullptr) {
   if constexpr (MODE == kDebug) {
     constexpr int NSB = StepSplit<FMT>::kSubsPerSb;
     const int g = (threadIdx.x & 63) >> 5, col = threadIdx.x & 31;
@@ -604,9 +653,9 @@ __device__ __forceinline__ void mmq_epilogue(const MmqParams& P, const TileCols&
       }
     }
     if constexpr (is_q4fam(FMT)) {
-      // min term, K = 2 fp32 MFMA over sub-blocks u-1, u (lane half g
-      // takes u-1+g): A[i][k] = -dmin*m, B[k][j] = beta*S
-      if (u & 1) acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ou.am, Ou.bm[ct], acc[ct], 0, 0, 0);
+      if (min_slot(u)) {
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ou.am, Ou.bm[ct], acc[ct], 0, 0, 0);
+      }
     }
   }
 }
@@ -642,7 +691,7 @@ __device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* s
       load_sub<FMT, NT>(st, wl, ub + u, u, O);
       const v16i X = mfma_sub(build_a(A, u), O.bq[0], magic);
       __builtin_amdgcn_sched_barrier(0);
-      mmq_epilogue<FMT, NT, MODE>(P, tc, r0, sb, ub, u, 0, X, O, acc, wl, u);
+      mmq_epilogue<FMT, NT, MODE>(P, tc, r0, sb, ub, u, 0, X, O, acc, wl, u, st);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -675,7 +724,7 @@ __device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* s
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
-        mmq_epilogue<FMT, NT, MODE>(P, tc, r0, sb, ub, u, ct, X[ct], O[b], acc);
+        mmq_epilogue<FMT, NT, MODE>(P, tc, r0, sb, ub, u, ct, X[ct], O[b], acc, wl);
         if (more) X[ct] = mfma_sub(an, O[b ^ 1].bq[ct], magic);
         __builtin_amdgcn_sched_barrier(0);
       }
