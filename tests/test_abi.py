@@ -58,9 +58,9 @@ def test_workspace_sizes():
     assert L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 4096, 4096, 512, 0, 0) >= 36
     # few tiles (4096 rows, 8 tokens): room for the fp32 partial tiles of the K splits
     small = L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 4096, 11008, 8, 0, 0)
-    assert small >= 43 * 11264 + 32 * 2 * 16384
+    assert small >= 43 * 12288 + 32 * 2 * 16384
     # one row block with many tokens needs no partials: the size grows only with T
-    assert L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 4096, 4096, 512, 0, 0) < 2048 + 16 * 16 * 11264 + 256
+    assert L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 4096, 4096, 512, 0, 0) < 2048 + 16 * 16 * 12288 + 256
     moe = L.qmm_workspace_bytes(_lib.QMM_OP_MOE, 2048, 768, 512, 128, 8)
     # per-slot fp32 scratch dominates: T*top_k*M*4
     assert moe >= 512 * 8 * 2048 * 4
@@ -165,7 +165,7 @@ def test_mmq_limits_accepted_and_rejected_on_the_host():
     # the workspace of a call with many column tiles is sized for every chunk
     # (the repack grid is launched in pieces of at most 65535 column tiles)
     T = 65535 * 32 + 100
-    assert L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 128, 256, T, 0, 0) >= 2048 + ((T + 31) // 32) * 11264
+    assert L.qmm_workspace_bytes(_lib.QMM_OP_MMQ, 128, 256, T, 0, 0) >= 2048 + ((T + 31) // 32) * 12288
 
 
 def test_moe_limits_and_workspace_ops():
@@ -186,7 +186,7 @@ def test_moe_limits_and_workspace_ops():
     assert slots < 512 * 8 * 2048 * 4
     # one token routed to 8 of 512 experts: at most 8 column tiles are repacked
     one = w(_lib.QMM_OP_MOE_SLOTS, 2048, 2048, 1, 512, 8)
-    assert one <= 256 + 4 * (512 + 3 * 513 + 8) + 1024 + 8 * 8 * 11264 + 256
+    assert one <= 256 + 4 * (512 + 3 * 513 + 8) + 1024 + 8 * 8 * 12288 + 256
     # a weighted call rejects the per-slot size (no launch: the check fails)
     assert call(4, 2, ws=FAKE, wsb=w(_lib.QMM_OP_MOE_SLOTS, 64, 256, 4, 8, 2), p=FAKE) == _lib.QMM_ERR_WORKSPACE
 
