@@ -5,7 +5,7 @@ Headline workload (the decode matvec shape the metric is quoted on):
 W 4096 x 11008 in Q4_K and the same shape in Q6_K, x fp32 N(0, 1) of length
 11008, T = 1.  One step = quantize x to Q8_1, then the Q4_K and the Q6_K
 matvec (the whole decode path), with inputs resident in HBM.  The weights
-rotate over enough copies (> 512 MB) that no step reads them from the
+rotate over >= 4 GB of on-device copies, so no step reads them from the
 256 MB Infinity Cache.  Steps are captured in one HIP graph and replayed;
 HIP events bracket the replay.  `value` is algorithmic bytes per step
 (quantized weights + Q8_1 activations + fp32 input/outputs) over step time.
@@ -15,18 +15,23 @@ The same JSON line carries:
                 algorithmic bytes over its launch duration (HIP events
                 around a graph of back-to-back launches on the launch
                 stream, divided by the launch count), against 8 TB/s HBM;
-  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same
-                decode workload (whole passes over both matrices, repeated
-                for about 10 s), in GB/s;
-  also          the other kernels and workloads measured the same way:
-                matvec at T = 4, the Q5_K matvec (T = 1, 4) and GEMM
-                (4096 x 4096, T = 512), matvec vs GEMM at T = 8 (the small-T
-                crossover), the read-only HBM ceiling probe at the
-                matvec byte counts, the prefill GEMMs (int8 TOPS and
-                tokens/s at T = 512 / 1024; also from fp32 activations:
-                quantize + GEMM vs the fused quantizer), the routed-expert
-                MoE FFN, and the per-slot expert matvec vs grouped GEMM
-                comparator at expert shapes.
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same decode
+                workload, in GB/s; `also.cpu_oracle` holds the oracle on
+                bounded samples of the prefill and MoE workloads (TOPS and
+                tokens/s), each on all host cores and on one core;
+  also          every other measured row.  Each launch-duration row reports
+                `us` (graph mean over >= 100 launches, weights rotated past
+                the MALL) and `median_us` (median of >= 100 launches
+                bracketed by event pairs on the launch stream; these include
+                ~1-2 us of event overhead).  Rows: the matvec at T = 1 and 4,
+                the Q5_K matvec, the small-T sweep (matvec T = 1..8 and GEMM
+                T = 1..64 on the decode shape), the read-only HBM ceiling at
+                the matvec byte counts (best of a geometry sweep), the
+                MFMA-only and MFMA + epilogue ceiling probes, the prefill
+                GEMMs (int8 TOPS, tokens/s, fraction of peak and of the
+                measured epilogue ceiling), the routed-expert MoE FFN and
+                the per-slot expert matvec vs grouped GEMM comparator.
+                `clocks` records SCLK/MCLK as read by amd-smi / rocm-smi.
 """
 from __future__ import annotations
 
@@ -34,6 +39,7 @@ import argparse
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -44,12 +50,12 @@ if ROOT not in sys.path:
 METRIC = "MMVQ HBM GB/s (T=1) + MMQ int8 TOPS & tokens/s at T=512/1024, %roofline"
 HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
-MALL_BYTES = 256 << 20
 # Weight copies rotated per launch.  The Infinity Cache (MALL, 256 MB) does
 # not evict strictly LRU: a cyclic working set of 2x its size still hits
-# measurably (apparent bandwidth above the HBM peak), so the rotation spans
-# 16x the MALL.
+# measurably (apparent bandwidth above the HBM peak), so every rotation spans
+# at least 4 GB (16x the MALL).
 ROTATE_BYTES = 4096 << 20
+MIN_LAUNCHES = 100
 
 # traffic measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE for the
 # dominant kernel (profiles/); None until taken for the current kernel
@@ -101,6 +107,24 @@ def time_launches(torch, fns, reps, sleep_cycles):
     return sum(ms) / len(ms), ms[len(ms) // 2]
 
 
+class Timer:
+    """Graph mean and event-pair median of a rotation of launches."""
+
+    def __init__(self, torch, ms_per_cycle):
+        self.torch = torch
+        self.cyc = ms_per_cycle
+
+    def __call__(self, fns, expect_us=50.0, reps=None):
+        reps = reps or max(MIN_LAUNCHES, len(fns))
+        mean = time_graph(self.torch, fns, reps)
+        n = max(MIN_LAUNCHES, min(len(fns), 400))
+        # the spin must outlast the host's enqueueing of n launches (~50-150
+        # us each from Python) so that no pair brackets a host gap
+        sleep = int(max(4.0, n * max(150.0, expect_us + 8.0) * 1e-3) / self.cyc)
+        _, med = time_launches(self.torch, fns, n, sleep)
+        return mean, med
+
+
 def calibrate_sleep(torch):
     a, b = _events(torch)
     torch.cuda.synchronize()
@@ -120,46 +144,155 @@ def rotated(t, n):
     return [t] + [t.clone() for _ in range(n - 1)]
 
 
-def cpu_oracle_baseline(np, wl, rows, min_seconds=10.0, one_core=False):
-    """The fp64 oracle on the first `rows` rows of both decode matrices, T = 1
-    (on all BLAS threads, or with the BLAS limited to one thread)."""
-    if one_core:
-        import threadpoolctl
-        with threadpoolctl.threadpool_limits(1):
-            r = cpu_oracle_baseline(np, wl, rows, min_seconds)
-        r["cores"] = 1
-        r["sample"] = r["sample"].replace("matvec on the BLAS threads", "matvec on one BLAS thread")
-        return r
-    import oracle
+def read_clocks():
+    """SCLK / MCLK in MHz as reported by amd-smi (else rocm-smi); None where unreadable."""
+    out = {"sclk_mhz": None, "mclk_mhz": None, "source": None}
     try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+        dev = data[0] if isinstance(data, list) else data
+        if isinstance(dev, dict) and "gpu_data" in dev:
+            dev = dev["gpu_data"][0]
+        clk = dev.get("clock", dev)
+
+        def cur(key):
+            v = clk.get(key)
+            if isinstance(v, dict):
+                v = v.get("clk", v.get("cur_clk"))
+                if isinstance(v, dict):
+                    v = v.get("value")
+            return float(v) if v not in (None, "N/A") else None
+        out["sclk_mhz"] = cur("gfx_0") or cur("GFX_0") or cur("gfx")
+        out["mclk_mhz"] = cur("mem_0") or cur("MEM_0") or cur("mem")
+        out["source"] = "amd-smi"
+        if out["sclk_mhz"] or out["mclk_mhz"]:
+            return out
+    except Exception as e:  # noqa: BLE001 - the tools may be absent or refuse
+        out["amd_smi_error"] = str(e)[:120]
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+        card = next(iter(data.values()))
+        for k, v in card.items():
+            try:
+                mhz = float(str(v).strip("()").lower().replace("mhz", "").split()[-1])
+            except ValueError:
+                continue
+            if "sclk" in k.lower():
+                out["sclk_mhz"] = mhz
+            if "mclk" in k.lower():
+                out["mclk_mhz"] = mhz
+        out["source"] = "rocm-smi"
+    except Exception as e:  # noqa: BLE001
+        out["rocm_smi_error"] = str(e)[:120]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baselines (bounded samples; the oracle as it stands)
+# ---------------------------------------------------------------------------
+def _blas_threads():
+    try:
+        import numpy as np
         import threadpoolctl
         a = np.ones((64, 64))
         _ = a @ a
-        cores = max([i["num_threads"] for i in threadpoolctl.threadpool_info()] + [1])
+        return max([i["num_threads"] for i in threadpoolctl.threadpool_info()] + [1])
     except Exception:  # pragma: no cover - threadpoolctl missing
-        cores = os.cpu_count() or 1
-    x = wl["x"][:1]
+        return os.cpu_count() or 1
+
+
+def _one_core(fn, *a, **kw):
+    import threadpoolctl
+    with threadpoolctl.threadpool_limits(1):
+        r = fn(*a, **kw)
+    r["cores"] = 1
+    r["sample"] = r["sample"].replace("on the BLAS threads", "on one BLAS thread")
+    return r
+
+
+def _repeat(body, min_seconds, max_reps=50):
     reps, t0 = 0, time.perf_counter()
     while True:
-        xq = oracle.quantize_q8_1(x)
-        X = oracle.q8_1_dequant(xq)
-        y4 = oracle.dense(oracle.q4k_dequant(wl["q4k"][:rows]), X)
-        y6 = oracle.dense(oracle.q6k_dequant(wl["q6k"][:rows]), X)
+        body()
         reps += 1
         dt = time.perf_counter() - t0
-        if dt >= min_seconds or reps >= 50:
-            break
-    del y4, y6
+        if dt >= min_seconds or reps >= max_reps:
+            return reps, dt
+
+
+def cpu_oracle_decode(wl, rows, min_seconds):
+    """The fp64 oracle on the first `rows` rows of both decode matrices, T = 1, in GB/s."""
+    import oracle
+    x = wl["x"][:1]
+
+    def body():
+        xq = oracle.quantize_q8_1(x)
+        X = oracle.q8_1_dequant(xq)
+        oracle.dense(oracle.q4k_dequant(wl["q4k"][:rows]), X)
+        oracle.dense(oracle.q6k_dequant(wl["q6k"][:rows]), X)
+    reps, dt = _repeat(body, min_seconds)
     K = x.shape[1]
-    nbytes = reps * (rows * (K // 256) * (144 + 210) + 2 * (xq.nbytes + rows * 4) + x.nbytes)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{reps} passes over rows 0..{rows - 1} of the 4096x11008 Q4_K and Q6_K "
-                      f"matrices at T=1 (quantize, fp64 dequantize, fp64 matvec), {dt:.1f} s wall; "
-                      "dequantization single-threaded numpy, matvec on the BLAS threads"}
+    xq_bytes = (K // 32) * 40
+    nbytes = reps * (rows * (K // 256) * (144 + 210) + 2 * (xq_bytes + rows * 4) + x.nbytes)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": f"{reps} passes over rows 0..{rows - 1} of the 4096x11008 Q4_K and Q6_K matrices at T=1 "
+                      f"(quantize, fp64 dequantize, fp64 matvec), {dt:.1f} s wall; dequantization single-threaded "
+                      "numpy, matvec on the BLAS threads"}
 
 
-def moe_comparator(torch, qmm, qmm_synth, dev):
+def cpu_oracle_gemm(name, wblocks, x, dequant, rows, min_seconds):
+    """The fp64 oracle GEMM on the first `rows` weight rows against all T tokens (TOPS, tokens/s)."""
+    import oracle
+    T, K = x.shape
+    xq = oracle.quantize_q8_1(x)
+    X = oracle.q8_1_dequant(xq)
+
+    def body():
+        oracle.dense(dequant(wblocks[:rows]), X)
+    reps, dt = _repeat(body, min_seconds)
+    ops = 2.0 * rows * K * T * reps
+    tops = ops / dt / 1e12
+    M = wblocks.shape[0]
+    return {"value": round(tops, 6), "unit": "TOPS", "cores": int(_blas_threads()), "kind": "oracle",
+            "tokens_per_s_full_matrix": round(T / (dt / reps * M / rows), 3),
+            "sample": f"{name}: {reps} passes of rows 0..{rows - 1} (of {M}) x all {T} tokens (fp64 dequantize + "
+                      f"fp64 matmul on the BLAS threads), {dt:.1f} s wall; tokens/s scaled to the whole matrix"}
+
+
+def cpu_oracle_moe(wl, n_exp, min_seconds):
+    """The fp64 oracle routed FFN on the slots of the first `n_exp` experts (TOPS, tokens/s)."""
+    import oracle
+    F = wl["down"].shape[2] * 256
+    x = wl["x"]
+    ids = wl["ids"]
+    T, top_k = ids.shape
+    xq = oracle.quantize_q8_1(x)
+    X = oracle.q8_1_dequant(xq)
+    experts = list(range(n_exp))
+    sel = np.isin(ids.ravel(), experts)
+
+    def body():
+        y1, _ = oracle.grouped_blocks(oracle.q4k_dequant, wl["gate_up"], X, ids, 1, experts=experts)
+        h = oracle.swiglu(y1[:, :F], y1[:, F:]).astype(np.float32)
+        H = oracle.q8_1_dequant(oracle.quantize_q8_1(h))
+        oracle.grouped_blocks(oracle.q4k_dequant, wl["down"], H, ids, top_k, experts=experts)
+    reps, dt = _repeat(body, min_seconds)
+    slots = int(sel.sum())
+    Hd = x.shape[1]
+    ops = 2.0 * slots * (2 * F * Hd + Hd * F) * reps
+    E = wl["gate_up"].shape[0]
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(_blas_threads()), "kind": "oracle",
+            "tokens_per_s_all_experts": round(T / (dt / reps * E / n_exp), 3),
+            "sample": f"routed FFN (gate||up, SwiGLU, quantize, down) of experts 0..{n_exp - 1} of {E} "
+                      f"({slots} of {T * top_k} slots), {reps} passes, {dt:.1f} s wall; per-slot combine omitted; "
+                      "tokens/s scaled to all experts"}
+
+
+np = None  # numpy, imported in main (the CPU helpers above use it)
+
+
+def moe_comparator(torch, qmm, qmm_synth, dev, timer):
     """Per-slot expert matvec vs grouped GEMM at expert shapes.
 
     128 experts of M x 2048 Q4_K (M = 512, 704), top-8, balanced routing with
@@ -168,7 +301,6 @@ def moe_comparator(torch, qmm, qmm_synth, dev):
     grouped call includes its route preparation and activation repack.
     Weights rotate over >= 4 GB of copies.
     """
-    import numpy as np
     E, K, top_k = 128, 2048, 8
     out = {}
     for M in (512, 704):
@@ -182,11 +314,11 @@ def moe_comparator(torch, qmm, qmm_synth, dev):
             ids = torch.from_numpy((np.arange(T * top_k, dtype=np.int32) % E).reshape(T, top_k)).to(dev)
             xq = qmm.q8_1_quantize(torch.from_numpy(qmm_synth.activations(g, T, K)).to(dev))
             y = torch.empty((T * top_k, M), dtype=torch.float32, device=dev)
-            wsp = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE, M, K, T, E, top_k), dev)
+            wsp = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE_SLOTS, M, K, T, E, top_k), dev)
             t_mv = time_graph(torch, [lambda c=c: qmm.moe_slot_mmvq(qmm.QMM_Q4_K, ws_[c], xq, ids, out=y)
-                                      for c in range(R)], 100)
+                                      for c in range(R)], MIN_LAUNCHES)
             t_gr = time_graph(torch, [lambda c=c: qmm.moe_grouped_mmq(qmm.QMM_Q4_K, ws_[c], xq, ids, out=y, ws=wsp)
-                                      for c in range(R)], 100)
+                                      for c in range(R)], MIN_LAUNCHES)
             out[f"M{M}_N{N}"] = {"slot_matvec_us": round(t_mv * 1e3, 2), "grouped_us": round(t_gr * 1e3, 2),
                                  "grouped_speedup": round(t_mv / t_gr, 2)}
             log(f"moe comparator M={M} N={N}: slot matvec {t_mv * 1e3:.1f} us, grouped {t_gr * 1e3:.1f} us")
@@ -195,6 +327,7 @@ def moe_comparator(torch, qmm, qmm_synth, dev):
 
 
 def main():
+    global np
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -212,20 +345,24 @@ def main():
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
-    import numpy as np
+    import numpy
     import torch
 
     import qmm_synth
     import quantized_matmul_q8_amd as qmm
+    np = numpy
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
 
     def to(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     cyc_ms = calibrate_sleep(torch)
+    timer = Timer(torch, cyc_ms)
     log(f"sleep calibration: {cyc_ms * 1e6:.3f} ns per cycle")
+    clocks_before = read_clocks()
 
     # ---------------- headline: decode step at T = 1 ----------------
     wl = qmm_synth.workload(1)
@@ -272,47 +409,50 @@ def main():
     step_bytes = bytes_q4 + bytes_q6 + bytes_quant
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # dominant kernel: Q6_K matvec, per-launch event pairs on the launch stream
-    n_launch = 120
-    sleep = int(max(4.0, n_launch * 0.1) / cyc_ms)
+    def gbps(nbytes, ms):
+        return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+    # dominant kernel: Q6_K matvec.  Launch duration = HIP events around a
+    # graph of back-to-back launches (rotating weight copies) / launches; this
+    # agrees with rocprofv3's kernel durations.
     q6_fns = [lambda c=c: qmm.mmvq_q6k(w6[c], xq1, out=y6) for c in range(R)]
     q4_fns = [lambda c=c: qmm.mmvq_q4k(w4[c], xq1, out=y4) for c in range(R)]
-    # launch duration = HIP events around a graph of back-to-back launches
-    # (rotating weight copies) / launches; this agrees with rocprofv3's
-    # kernel durations.  Per-launch event pairs add the dispatch overhead
-    # of the event packets and are reported beside it.
-    q6_graph = time_graph(torch, q6_fns, 200)
-    q4_graph = time_graph(torch, q4_fns, 200)
-    q6_mean, q6_med = time_launches(torch, q6_fns, n_launch, sleep)
+    q6_graph, q6_med = timer(q6_fns, 11.0, reps=200)
+    q4_graph, q4_med = timer(q4_fns, 8.0, reps=200)
     ach = bytes_q6 / (q6_graph * 1e-3) / 1e9
     roofline = {"kernel": "mmvq_q6k (4096x11008, T=1)", "bound": "hbm", "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                 "traffic": DOMINANT_TRAFFIC_BYTES, "algorithmic_bytes": bytes_q6,
-                "launch_us": round(q6_graph * 1e3, 3),
-                "event_pair_mean_us": round(q6_mean * 1e3, 3)}
-
-    log(f"mmvq_q6k {q6_graph * 1e3:.3f} us (graph), {q6_mean * 1e3:.3f} us (event pairs); "
+                "launch_us": round(q6_graph * 1e3, 3), "event_pair_median_us": round(q6_med * 1e3, 3)}
+    log(f"mmvq_q6k {q6_graph * 1e3:.3f} us (graph), {q6_med * 1e3:.3f} us (event-pair median); "
         f"mmvq_q4k {q4_graph * 1e3:.3f} us")
     also = {}
+    also["mmvq_q4k_t1"] = {"us": round(q4_graph * 1e3, 3), "median_us": round(q4_med * 1e3, 3),
+                           "GBps": gbps(bytes_q4, q4_graph), "frac_hbm": round(gbps(bytes_q4, q4_graph) / HBM_PEAK_GBPS, 4)}
+    also["mmvq_q6k_t1"] = {"us": round(q6_graph * 1e3, 3), "median_us": round(q6_med * 1e3, 3),
+                           "GBps": round(ach, 1), "frac_hbm": round(ach / HBM_PEAK_GBPS, 4)}
 
-    def gbps(nbytes, ms):
-        return round(nbytes / (ms * 1e-3) / 1e9, 1)
-
-    also["mmvq_q4k_t1"] = {"us": round(q4_graph * 1e3, 3), "GBps": gbps(bytes_q4, q4_graph),
-                           "frac_hbm": round(gbps(bytes_q4, q4_graph) / HBM_PEAK_GBPS, 4)}
-    also["mmvq_q6k_t1"] = {"us": round(q6_graph * 1e3, 3), "GBps": round(ach, 1),
-                           "frac_hbm": round(ach / HBM_PEAK_GBPS, 4)}
-
-    # read-only ceiling at the same byte counts (rotating buffers)
-    for name, nb in (("probe_read_25MB", w4h.nbytes), ("probe_read_37MB", w6h.nbytes)):
+    # read-only ceiling at the same byte counts: best of a geometry sweep
+    # (16-byte loads in flight per thread, one-pass grid or a persistent
+    # grid-stride loop), rotating buffers
+    sink = torch.zeros((4,), dtype=torch.int32, device=dev)
+    for name, nb, mv in (("probe_read_25MB", w4h.nbytes, "mmvq_q4k_t1"), ("probe_read_37MB", w6h.nbytes, "mmvq_q6k_t1")):
         nb16 = nb // 16 * 16
-        bufs = rotated(torch.zeros((nb16,), dtype=torch.uint8, device=dev), copies_for(nb16))
-        sink = torch.zeros((4,), dtype=torch.int32, device=dev)
-        fns = [lambda b_=b_: qmm.probe_read(b_, nb16, sink) for b_ in bufs]
-        pm = time_graph(torch, fns, 200)
-        also[name] = {"us": round(pm * 1e3, 3), "GBps": gbps(nb16, pm),
-                      "frac_hbm": round(gbps(nb16, pm) / HBM_PEAK_GBPS, 4)}
-        del bufs
+        ncop = copies_for(nb16)
+        big = torch.ones((ncop * nb16,), dtype=torch.uint8, device=dev)
+        bufs = [big[i * nb16:(i + 1) * nb16] for i in range(ncop)]
+        sweep = {}
+        for u, grid in ((1, 0), (2, 0), (4, 0), (8, 0), (1, 4 * n_cu * 4), (8, 2 * n_cu)):
+            pm = time_graph(torch, [lambda b_=b_, u=u, grid=grid: qmm.probe_read_geom(b_, nb16, u, grid, sink)
+                                    for b_ in bufs], max(MIN_LAUNCHES, ncop))
+            sweep[f"u{u}_g{grid or 'pass'}"] = round(pm * 1e3, 3)
+        best = min(sweep, key=sweep.get)
+        pm = sweep[best] * 1e-3
+        also[name] = {"us": sweep[best], "GBps": gbps(nb16, pm), "frac_hbm": round(gbps(nb16, pm) / HBM_PEAK_GBPS, 4),
+                      "best_geometry": best, "sweep_us": sweep}
+        also[mv]["frac_of_read_ceiling"] = round(also[name]["us"] / also[mv]["us"], 4)
+        del bufs, big
+        torch.cuda.empty_cache()
 
     if not args.only_headline and not args.prefill_only:
         # single Q4_K matvec 1024 x 1024, T = 1 (reported only: launch-latency bound)
@@ -330,18 +470,17 @@ def main():
                                          "frac_hbm": round(gbps(nbytes, m_) / HBM_PEAK_GBPS, 4)}
         del w0, wl0
 
-    if not args.only_headline and not args.prefill_only:
         # matvec at T = 4
         x4 = to(wl["x"][:4])
         xq4 = qmm.q8_1_quantize(x4)
         y44 = torch.empty((4, M), dtype=torch.float32, device=dev)
-        for name, ws_, fn, nbw in (("mmvq_q4k_t4", w4, qmm.mmvq_q4k, w4h.nbytes),
-                                    ("mmvq_q6k_t4", w6, qmm.mmvq_q6k, w6h.nbytes)):
-            fns = [lambda c=c, ws_=ws_, fn=fn: fn(ws_[c], xq4, out=y44) for c in range(R)]
-            m_ = time_graph(torch, fns, 200)
+        for name, ws_, fn, nbw, t1 in (("mmvq_q4k_t4", w4, qmm.mmvq_q4k, w4h.nbytes, q4_graph),
+                                       ("mmvq_q6k_t4", w6, qmm.mmvq_q6k, w6h.nbytes, q6_graph)):
+            mean, med = timer([lambda c=c, ws_=ws_, fn=fn: fn(ws_[c], xq4, out=y44) for c in range(R)], 20.0)
             nbytes = nbw + 4 * xq_bytes + 4 * M * 4
-            also[name] = {"us": round(m_ * 1e3, 3), "GBps": gbps(nbytes, m_),
-                          "frac_hbm": round(gbps(nbytes, m_) / HBM_PEAK_GBPS, 4)}
+            also[name] = {"us": round(mean * 1e3, 3), "median_us": round(med * 1e3, 3), "GBps": gbps(nbytes, mean),
+                          "frac_hbm": round(gbps(nbytes, mean) / HBM_PEAK_GBPS, 4),
+                          "ratio_to_t1": round(mean / t1, 3)}
 
         # third format: Q5_K matvec on the decode shape, T = 1 and 4
         w5h = wl["q5k"]
@@ -355,71 +494,95 @@ def main():
                           "frac_hbm": round(gbps(nbytes, m_) / HBM_PEAK_GBPS, 4)}
         del w5
 
-        # small-T crossover on the decode shape: matvec vs GEMM at T = 8
-        x8 = to(qmm_synth.activations(qmm_synth.rng(8), 8, K))
-        xq8 = qmm.q8_1_quantize(x8)
-        y8 = torch.empty((8, M), dtype=torch.float32, device=dev)
-        ws8 = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MMQ, M, K, 8), dev)
-        cross = {}
+        # small-T sweep on the decode shape: matvec (T <= 8) and GEMM (T <= 64)
+        xs = to(qmm_synth.activations(qmm_synth.rng(8), 64, K))
+        sweep = {"T": [1, 2, 4, 8, 16, 32, 64]}
         for key, ws_, mv, mq, nbw in (("q4k", w4, qmm.mmvq_q4k, qmm.mmq_q4k, w4h.nbytes),
                                       ("q6k", w6, qmm.mmvq_q6k, qmm.mmq_q6k, w6h.nbytes)):
-            t_mv = time_graph(torch, [lambda c=c: mv(ws_[c], xq8, out=y8) for c in range(R)], 200)
-            t_mq = time_graph(torch, [lambda c=c: mq(ws_[c], xq8, out=y8, ws=ws8) for c in range(R)], 200)
-            cross[f"mmvq_{key}_us"] = round(t_mv * 1e3, 2)
-            cross[f"mmq_{key}_us"] = round(t_mq * 1e3, 2)
-            cross[f"best_{key}_GBps"] = gbps(nbw, min(t_mv, t_mq))
-        also["decode_4096x11008_t8"] = cross
+            mv_us, mq_us = [], []
+            for T_ in sweep["T"]:
+                xqT = qmm.q8_1_quantize(xs[:T_].contiguous())
+                yT = torch.empty((T_, M), dtype=torch.float32, device=dev)
+                wsT = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MMQ, M, K, T_), dev)
+                mq_us.append(round(time_graph(torch, [lambda c=c: mq(ws_[c], xqT, out=yT, ws=wsT)
+                                                      for c in range(R)], 200) * 1e3, 2))
+                mv_us.append(round(time_graph(torch, [lambda c=c: mv(ws_[c], xqT, out=yT) for c in range(R)], 200)
+                                   * 1e3, 2) if T_ <= qmm.QMM_MMVQ_MAX_T else None)
+            sweep[f"mmvq_{key}_us"] = mv_us
+            sweep[f"mmq_{key}_us"] = mq_us
+            sweep[f"best_{key}_GBps"] = [gbps(nbw, min(u for u in (a_, b_) if u is not None) * 1e-3)
+                                         for a_, b_ in zip(mv_us, mq_us)]
+        also["decode_4096x11008_t_sweep"] = sweep
+        log(f"small-T sweep: {sweep}")
     del w4, w6
+    torch.cuda.empty_cache()
+
+    # ---------------- ceiling probes of the GEMM's inner loop ----------------
+    probes = {}
+    iters = 8000
+    for wps in (2, 4):
+        s_ = time_graph(torch, [lambda wps=wps: qmm.probe_mfma(iters, wps, sink)], 5) * 1e-3
+        probes[f"mfma_only_wps{wps}_TOPS"] = round(n_cu * wps * 4 * iters * 4 * 65536 / s_ / 1e12, 1)
+    for mode in (2, 3, 6):
+        s_ = time_graph(torch, [lambda mode=mode: qmm.probe_mfma_epilogue(mode, iters, 2, sink)], 5) * 1e-3
+        probes[f"epilogue_mode{mode}_TOPS"] = round(n_cu * 2 * 4 * iters * 2 * 65536 / s_ / 1e12, 1)
+    probes["note"] = ("mode 2: int8 MFMA + two-FMA epilogue with LDS operands (the Q6_K-style loop per 32-weight "
+                      "sub-block); 3: + fp32 32x32x2 min-term MFMA; 6: + three bf16 min-term MFMAs per "
+                      "super-block (the Q4_K loop as built)")
+    also["ceiling_probes"] = probes
+    ceil_q4 = probes["epilogue_mode6_TOPS"]
+    ceil_q6 = probes["epilogue_mode2_TOPS"] / 2.0   # 16-weight sub-blocks: twice the epilogue per weight
+    log(f"probes: {probes}")
 
     if not args.only_headline:
-        # prefill GEMMs
-        def mmq_case(name, fn, wh, xh):
+        # prefill GEMMs, weights rotated over >= 4 GB
+        def mmq_case(name, fn, wh, xh, ceiling, from_fp32=False):
             Mg, Kg = wh.shape[0], wh.shape[1] * 256
             Tg = xh.shape[0]
-            cop = 4
-            wd = [to(wh) for _ in range(cop)]
-            xqg = qmm.q8_1_quantize(to(xh))
+            cop = copies_for(wh.nbytes)
+            wd = rotated(to(wh), cop)
+            xg = to(xh)
+            xqg = qmm.q8_1_quantize(xg)
             yg = torch.empty((Tg, Mg), dtype=torch.float32, device=dev)
-            fns = [lambda c=c: fn(wd[c], xqg, out=yg) for c in range(cop)]
-            mean = time_graph(torch, fns, 20)
             ops = 2.0 * Mg * Kg * Tg
+            expect = ops / 400e12 * 1e6
+            mean, med = timer([lambda c=c: fn(wd[c], xqg, out=yg) for c in range(cop)], expect)
             tops = ops / (mean * 1e-3) / 1e12
-            log(f"{name}: {mean * 1e3:.2f} us")
-            also[name] = {"us": round(mean * 1e3, 2),
+            log(f"{name}: {mean * 1e3:.2f} us (median {med * 1e3:.2f})")
+            also[name] = {"us": round(mean * 1e3, 2), "median_us": round(med * 1e3, 2),
                           "TOPS": round(tops, 1), "frac_int8": round(tops / INT8_PEAK_TOPS, 4),
-                          "tokens_per_s": round(Tg / (mean * 1e-3), 1)}
+                          "frac_of_epilogue_ceiling": round(tops / ceiling, 4),
+                          "tokens_per_s": round(Tg / (mean * 1e-3), 1), "weight_copies_rotated": cop}
+            if from_fp32:
+                xq2 = torch.empty_like(xqg)
+
+                def two_pass(c):
+                    qmm.q8_1_quantize(xg, out=xq2)
+                    fn(wd[c], xq2, out=yg)
+                t_two = time_graph(torch, [lambda c=c: two_pass(c) for c in range(cop)], MIN_LAUNCHES)
+                t_fused = time_graph(torch, [lambda c=c: qmm.mmq_q4k_f32(wd[c], xg, out=yg) for c in range(cop)],
+                                     MIN_LAUNCHES)
+                also[name + "_from_fp32"] = {"quantize_then_gemm_us": round(t_two * 1e3, 2),
+                                             "fused_us": round(t_fused * 1e3, 2)}
             del wd
+            torch.cuda.empty_cache()
 
         wl2 = qmm_synth.workload(2)
-        mmq_case("mmq_q4k_4096x4096_t512", qmm.mmq_q4k, wl2["q4k"], wl2["x"])
+        mmq_case("mmq_q4k_4096x4096_t512", qmm.mmq_q4k, wl2["q4k"], wl2["x"], ceil_q4, from_fp32=True)
         mmq_case("mmq_q5k_4096x4096_t512", qmm.mmq_q5k, qmm_synth.q5k_weights(qmm_synth.rng(52), 4096, 4096),
-                 wl2["x"])
-        # fused quantizer prologue: fp32 activations in, against quantize + GEMM
-        wd2 = [to(wl2["q4k"]) for _ in range(4)]
-        x2 = to(wl2["x"])
-        xq2 = torch.empty((x2.shape[0], x2.shape[1] // 32, 40), dtype=torch.uint8, device=dev)
-        y2g = torch.empty((x2.shape[0], wl2["q4k"].shape[0]), dtype=torch.float32, device=dev)
-
-        def two_pass(c):
-            qmm.q8_1_quantize(x2, out=xq2)
-            qmm.mmq_q4k(wd2[c], xq2, out=y2g)
-
-        t_two = time_graph(torch, [lambda c=c: two_pass(c) for c in range(4)], 20)
-        t_fused = time_graph(torch, [lambda c=c: qmm.mmq_q4k_f32(wd2[c], x2, out=y2g) for c in range(4)], 20)
-        also["mmq_q4k_4096x4096_t512_from_fp32"] = {"quantize_then_gemm_us": round(t_two * 1e3, 2),
-                                                     "fused_us": round(t_fused * 1e3, 2)}
-        del wd2
-        del wl2
+                 wl2["x"], ceil_q4)
         wl3 = qmm_synth.workload(3)
-        mmq_case("mmq_q4k_14336x4096_t1024", qmm.mmq_q4k, wl3["q4k"], wl3["x_q4k"])
-        mmq_case("mmq_q6k_4096x14336_t1024", qmm.mmq_q6k, wl3["q6k"], wl3["x_q6k"])
-        del wl3
+        mmq_case("mmq_q4k_14336x4096_t1024", qmm.mmq_q4k, wl3["q4k"], wl3["x_q4k"], ceil_q4)
+        mmq_case("mmq_q6k_4096x14336_t1024", qmm.mmq_q6k, wl3["q6k"], wl3["x_q6k"], ceil_q6)
 
-        # routed-expert FFN: gate||up grouped, SwiGLU->Q8_1, down grouped weighted
+        # routed-expert FFN: gate||up grouped, SwiGLU->Q8_1, down grouped weighted;
+        # expert weights rotated over >= 4 GB of copies
         wl4 = qmm_synth.workload(4)
         E, H, F, T, top_k = 128, 2048, 768, 512, 8
-        gu = to(wl4["gate_up"])
-        dn = to(wl4["down"])
+        wbytes = wl4["gate_up"].nbytes + wl4["down"].nbytes
+        cop = copies_for(wbytes)
+        gus = rotated(to(wl4["gate_up"]), cop)
+        dns = rotated(to(wl4["down"]), cop)
         ids = to(wl4["ids"])
         probs = to(wl4["probs"])
         xm = to(wl4["x"])
@@ -427,31 +590,27 @@ def main():
         y1 = torch.empty((T * top_k, 2 * F), dtype=torch.float32, device=dev)
         hq = torch.empty((T * top_k, F // 32, 40), dtype=torch.uint8, device=dev)
         y2 = torch.empty((T, H), dtype=torch.float32, device=dev)
-        ws1 = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE, 2 * F, H, T, E, top_k), dev)
+        ws1 = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE_SLOTS, 2 * F, H, T, E, top_k), dev)
         ws2 = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k), dev)
 
-        def moe_step():
+        def moe_step(c):
             qmm.q8_1_quantize(xm, out=xqm)
-            qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gu, xqm, ids, out=y1, ws=ws1)
+            qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gus[c], xqm, ids, out=y1, ws=ws1)
             qmm.swiglu_q8_1(y1, out=hq)
-            qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dn, hq, ids, probs, out=y2, ws=ws2)
-
-        def gate_up_only():
-            qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gu, xqm, ids, out=y1, ws=ws1)
-
-        def down_only():
-            qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dn, hq, ids, probs, out=y2, ws=ws2)
-
-        def glue_only():
-            qmm.q8_1_quantize(xm, out=xqm)
-            qmm.swiglu_q8_1(y1, out=hq)
+            qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dns[c], hq, ids, probs, out=y2, ws=ws2)
 
         log("moe ffn")
-        ms_moe = time_graph(torch, [moe_step], 10)
-        ms_gu = time_graph(torch, [gate_up_only], 10)
-        ms_dn = time_graph(torch, [down_only], 10)
-        ms_glue = time_graph(torch, [glue_only], 10)
-        wbytes = wl4["gate_up"].nbytes + wl4["down"].nbytes
+        moe_step(0)
+        ms_moe, med_moe = timer([lambda c=c: moe_step(c) for c in range(cop)], 300.0)
+        ms_gu, med_gu = timer([lambda c=c: qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gus[c], xqm, ids, out=y1, ws=ws1)
+                               for c in range(cop)], 150.0)
+        ms_dn, med_dn = timer([lambda c=c: qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dns[c], hq, ids, probs, out=y2, ws=ws2)
+                               for c in range(cop)], 100.0)
+
+        def glue():
+            qmm.q8_1_quantize(xm, out=xqm)
+            qmm.swiglu_q8_1(y1, out=hq)
+        ms_glue = time_graph(torch, [glue], MIN_LAUNCHES)
         macs = T * top_k * (2 * F * H + H * F)
         act_bytes = T * H * 4 + T * (H // 32) * 40 + T * top_k * (F // 32) * 40 + T * H * 4
         moe_bytes = wbytes + act_bytes
@@ -465,23 +624,43 @@ def main():
         tops_g = 2.0 * macs / (ms_g * 1e-3) / 1e12
         attain_g = min(INT8_PEAK_TOPS, 2.0 * macs / g_bytes * HBM_PEAK_GBPS / 1e3)
         also["moe_ffn_e128_t512_top8"] = {
-            "us": round(ms_moe * 1e3, 2), "gate_up_us": round(ms_gu * 1e3, 2),
-            "down_us": round(ms_dn * 1e3, 2), "GBps": gbps(moe_bytes, ms_moe),
-            "frac_hbm": round(gbps(moe_bytes, ms_moe) / HBM_PEAK_GBPS, 4),
+            "us": round(ms_moe * 1e3, 2), "median_us": round(med_moe * 1e3, 2),
+            "gate_up_us": round(ms_gu * 1e3, 2), "gate_up_median_us": round(med_gu * 1e3, 2),
+            "down_us": round(ms_dn * 1e3, 2), "down_median_us": round(med_dn * 1e3, 2),
+            "GBps": gbps(moe_bytes, ms_moe), "frac_hbm": round(gbps(moe_bytes, ms_moe) / HBM_PEAK_GBPS, 4),
             "TOPS": round(tops, 1), "frac_attainable": round(tops / attain, 4),
-            "tokens_per_s": round(T / (ms_moe * 1e-3), 1),
-            "glue_us": round(ms_glue * 1e3, 2),
+            "tokens_per_s": round(T / (ms_moe * 1e-3), 1), "glue_us": round(ms_glue * 1e3, 2),
+            "weight_copies_rotated": cop,
             "grouped_calls_only": {"us": round(ms_g * 1e3, 2), "GBps": gbps(g_bytes, ms_g),
                                    "TOPS": round(tops_g, 1), "frac_attainable": round(tops_g / attain_g, 4)}}
-        del gu, dn
+        del gus, dns
+        torch.cuda.empty_cache()
         if not args.prefill_only:
-            also["moe_comparator_e128_k2048_top8"] = moe_comparator(torch, qmm, qmm_synth, dev)
+            also["moe_comparator_e128_k2048_top8"] = moe_comparator(torch, qmm, qmm_synth, dev, timer)
+
+    clocks_after = read_clocks()
+    also["clocks"] = {"before": clocks_before, "after": clocks_after,
+                      "note": "idle readings bracket the run; kernels under load run near 2.0-2.2 GHz (counter "
+                              "cycles over kernel time)"}
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu oracle baseline")
-        cpu = cpu_oracle_baseline(np, wl, min(args.cpu_rows, M))
-        also["cpu_oracle_1core"] = cpu_oracle_baseline(np, wl, min(args.cpu_rows, M), min_seconds=5.0, one_core=True)
+        log("cpu oracle baselines")
+        rows = min(args.cpu_rows, M)
+        cpu = cpu_oracle_decode(wl, rows, 6.0)
+        cpu1 = _one_core(cpu_oracle_decode, wl, rows, 3.0)
+        oracle_rows = {"decode_4096x11008_t1_1core": cpu1}
+        if not args.only_headline:
+            from oracle import q4k_dequant, q6k_dequant
+            cases = (("prefill_q4k_4096x4096_t512", wl2["q4k"], wl2["x"], q4k_dequant, 512),
+                     ("prefill_q4k_14336x4096_t1024", wl3["q4k"], wl3["x_q4k"], q4k_dequant, 256),
+                     ("prefill_q6k_4096x14336_t1024", wl3["q6k"], wl3["x_q6k"], q6k_dequant, 128))
+            for name, wb, xh, dq, r_ in cases:
+                oracle_rows[name] = cpu_oracle_gemm(name, wb, xh, dq, r_, 2.5)
+                oracle_rows[name + "_1core"] = _one_core(cpu_oracle_gemm, name, wb, xh, dq, max(16, r_ // 8), 1.5)
+            oracle_rows["moe_ffn_e128_t512_top8"] = cpu_oracle_moe(wl4, 4, 2.5)
+            oracle_rows["moe_ffn_e128_t512_top8_1core"] = _one_core(cpu_oracle_moe, wl4, 2, 1.5)
+        also["cpu_oracle"] = oracle_rows
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
