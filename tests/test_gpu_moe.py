@@ -132,23 +132,115 @@ def test_swiglu_glue_properties():
     assert np.all(err <= d[..., None] * (0.5 + 2.0**-15 + 127 * 2.0**-11) * (1 + 1e-5) + 1e-6 * np.abs(h))
 
 
-def test_full_routed_ffn_workload():
-    """128 experts, T = 512, top-8: gate||up per-slot, then down weighted."""
+def _q8_1_error_bound(hq):
+    """Per element bound of |x - d16*q| for a Q8_1 block of d16, from the
+    quantizer's round-trip pin: d32*(1/2 + 2^-15) + |q|*|d32 - d16|, with
+    d32 within one f16 rounding of d16 (relative 2^-11, absolute 2^-25)."""
+    d16, q, _, _ = oracle.q8_1_fields(hq)
+    d32_hi = d16 * (1 + 2.0**-10) + 2.0**-25
+    dd = d16 * 2.0**-10 + 2.0**-25
+    return (d32_hi * (0.5 + 2.0**-15))[..., None] + np.abs(q) * dd[..., None]
+
+
+def test_full_routed_ffn_gpu_chain():
+    """128 experts, T = 512, top-8, the whole routed FFN on the GPU (quantize,
+    grouped gate||up, SwiGLU -> Q8_1, grouped down with the routing weights)
+    against the oracle chain, with the tolerance carried through the glue:
+
+      |y2_gpu - y2_ora| <= sum_k p_k sum_j |W_down| |x_gpu - x_ora|  +  1e-4 sum_k p_k sum_j |W_down| |x_gpu|
+
+    (triangle inequality: the second term is the grouped GEMM's own parity
+    bound on the GPU intermediate, the first the exact effect of the
+    intermediate's difference), where x_gpu, x_ora are the dequantized
+    SwiGLU activations of the two chains, and |x_gpu - x_ora| is itself held
+    to the bound of the glue: the gate||up parity error carried through
+    SwiGLU plus both quantization errors."""
     wl = qmm_synth.workload(4)
     E, H, F, T, top_k = 128, 2048, 768, 512, 8
     gate_up, down, x, ids, probs = wl["gate_up"], wl["down"], wl["x"], wl["ids"], wl["probs"]
+    say("moe routed FFN GPU chain", f"E={E} H={H} F={F} T={T} top_k={top_k}")
+    xq_gpu = qmm.q8_1_quantize(dev(x))
     xq = oracle.quantize_q8_1(x)
-    say("moe gate||up per-slot", f"E={E} M={2 * F} K={H} T={T} top_k={top_k}")
-    y1 = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(gate_up), dev(xq), dev(ids)))
+    assert np.array_equal(host(xq_gpu), xq)
+    y1_d = qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(gate_up), xq_gpu, dev(ids))
+    hq_d = qmm.swiglu_q8_1(y1_d)
+    y2 = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), hq_d, dev(ids), dev(probs)))
+    y1, hq_gpu = host(y1_d), host(hq_d)
+    # step 1: gate||up parity
     ref1, b1 = oracle.grouped_blocks(oracle.q4k_dequant, gate_up, oracle.q8_1_dequant(xq), ids, 1)
     assert_parity(y1, ref1, b1, "gate_up")
-    # down projection on an intermediate made by the oracle from its own gate/up
-    h = oracle.swiglu(ref1[:, :F], ref1[:, F:]).astype(np.float32)
-    hq = oracle.quantize_q8_1(h)
-    say("moe down weighted", f"E={E} M={H} K={F} T={T} top_k={top_k}")
-    y2 = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), dev(hq), dev(ids), dev(probs)))
-    ys, bs = oracle.grouped_blocks(oracle.q4k_dequant, down, oracle.q8_1_dequant(hq), ids, top_k)
-    assert_parity(y2, oracle.combine(ys, probs), oracle.combine(bs, np.abs(probs)), "down")
-    # determinism of the full call
-    y2b = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), dev(hq), dev(ids), dev(probs)))
+    # step 2: the glue.  SwiGLU h = silu(g) u; |silu'| <= 1.1, so an error
+    # e_g in g and e_u in u move h by at most 1.1 e_g (|u| + e_u) + |silu(g)| e_u,
+    # plus the fp32 evaluation (a few ulps: 2^-20 |h| with margin)
+    g_r, u_r = ref1[:, :F], ref1[:, F:]
+    e_g, e_u = 1e-4 * b1[:, :F], 1e-4 * b1[:, F:]
+    h_ora = oracle.swiglu(g_r, u_r)
+    silu = oracle.swiglu(g_r, np.ones_like(g_r))
+    dh = 1.1 * e_g * (np.abs(u_r) + e_u) + np.abs(silu) * e_u + 2.0**-20 * np.abs(h_ora)
+    hq_ora = oracle.quantize_q8_1(h_ora.astype(np.float32))
+    x_gpu = oracle.q8_1_dequant(hq_gpu)
+    x_ora = oracle.q8_1_dequant(hq_ora)
+    qe = _q8_1_error_bound(hq_gpu).reshape(T * top_k, F) + _q8_1_error_bound(hq_ora).reshape(T * top_k, F)
+    dx = np.abs(x_gpu - x_ora)
+    assert np.all(dx <= (dh + qe) * (1 + 1e-9) + 1e-30), "SwiGLU glue outside its carried bound"
+    # step 3: down + ordered combine against the oracle chain
+    ys_g, bs_g = oracle.grouped_blocks(oracle.q4k_dequant, down, x_gpu, ids, top_k)
+    ys_o, _ = oracle.grouped_blocks(oracle.q4k_dequant, down, x_ora, ids, top_k)
+    carried, _ = oracle.grouped_blocks(lambda b: np.abs(oracle.q4k_dequant(b)), down, dx, ids, top_k)
+    pa = np.abs(probs)
+    y2_g, y2_o = oracle.combine(ys_g, probs), oracle.combine(ys_o, probs)
+    tol = oracle.combine(carried, pa) + 1e-4 * oracle.combine(bs_g, pa)
+    # the last step on the GPU's own intermediate (exact reference) ...
+    assert_parity(y2, y2_g, oracle.combine(bs_g, pa), "down on the GPU intermediate")
+    # ... and the whole chain against the oracle's
+    err = np.abs(y2.astype(np.float64) - y2_o)
+    bad = err > tol * (1 + 1e-9)
+    assert not bad.any(), f"{int(bad.sum())} outputs outside the carried tolerance (max excess {np.max(err - tol):.3e})"
+    # determinism of the full chain
+    y2b = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), qmm.swiglu_q8_1(
+        qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(gate_up), xq_gpu, dev(ids))), dev(ids), dev(probs)))
     assert np.array_equal(y2.view(np.uint32), y2b.view(np.uint32))
+
+
+def _near_half(v, ulps):
+    """fp32 value v within `ulps` of a rounding tie n + 1/2."""
+    v = np.asarray(v, np.float32)
+    frac = np.abs(v.astype(np.float64) - np.floor(v.astype(np.float64)) - 0.5)
+    return frac <= ulps * np.spacing(np.abs(v)).astype(np.float64)
+
+
+def test_swiglu_bytes_against_oracle_quantizer():
+    """swiglu_q8_1 bytes against the oracle's quantizer applied to an fp32
+    SwiGLU computed on the host.  The two fp32 SwiGLUs may differ by an ulp
+    (exp is not correctly rounded on either side), so a byte may differ only
+    at a rounding boundary: a value q may differ by one where the oracle's
+    fp32 product x * (1/d) lies within 8 ulps of a tie, and a block's f16 d
+    by one f16 ulp where the fp32 d lies within 8 ulps of an f16 tie."""
+    g = qmm_synth.rng(52)
+    R, F = 300, 768
+    gu = (g.standard_normal((R, 2 * F)) * 3).astype(np.float32)
+    say("swiglu_q8_1 bytes", f"R={R} F={F}")
+    hq = host(qmm.swiglu_q8_1(dev(gu)))
+    gt, ut = gu[:, :F], gu[:, F:]
+    with np.errstate(over="ignore"):
+        h32 = (gt / (np.float32(1) + np.exp(-gt)) * ut).astype(np.float32)
+    ref = oracle.quantize_q8_1(h32)
+    d_g, q_g, pad_g, s_g = oracle.q8_1_fields(hq)
+    d_o, q_o, _, _ = oracle.q8_1_fields(ref)
+    assert not pad_g.any() and np.array_equal(s_g, q_g.sum(-1))
+    # the oracle's fp32 intermediates, to locate rounding boundaries
+    hb = h32.reshape(R, F // 32, 32)
+    d32 = (np.abs(hb).max(-1) / np.float32(127)).astype(np.float32)
+    di = np.where(d32 >= np.float32(2.0**-126), (np.float32(1) / d32).astype(np.float32), np.float32(0))
+    v = (hb * di[..., None]).astype(np.float32)
+    dq = q_g.astype(np.int64) - q_o.astype(np.int64)
+    ok_q = (dq == 0) | ((np.abs(dq) == 1) & _near_half(v, 8))
+    dd_blocks = d_g != d_o
+    # a block whose f16 d differs: d32 must sit at an f16 tie; its q may then differ by one anywhere
+    d16_tie = np.abs(d32.astype(np.float64) - (d_g + d_o) / 2) <= 8 * np.spacing(d32).astype(np.float64)
+    assert np.all(~dd_blocks | d16_tie), "f16 scale differs away from a rounding tie"
+    ok = ok_q | (dd_blocks[..., None] & (np.abs(dq) <= 1))
+    assert ok.all(), f"{int((~ok).sum())} values differ away from a rounding boundary"
+    n_diff = int((dq != 0).sum())
+    say("  bytes differing at rounding boundaries:", n_diff, "of", dq.size)
+    assert n_diff <= dq.size // 1000
