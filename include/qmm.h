@@ -301,7 +301,9 @@ int qmm_probe_mfma(int64_t iters, int waves_per_simd, uint32_t* sink, void* stre
  * iteration into the FMA accumulator; mode 4: that MFMA into an accumulator
  * of its own; mode 5: the min term as three bf16 MFMAs per eight
  * iterations into its own accumulator; mode 6: the same into the FMA
- * accumulator.  int8 ops per launch = CUs * waves_per_simd * 4 * iters * 2 *
+ * accumulator; mode 7: mode 6 with a workgroup barrier every eight
+ * iterations; mode 8: mode 7 with the A operand unpacked from 4-bit values
+ * each iteration.  int8 ops per launch = CUs * waves_per_simd * 4 * iters * 2 *
  * 65536.  waves_per_simd 2 or 4; 1 <= iters <= 2^24.
  */
 int qmm_probe_mfma_epilogue(int mode, int64_t iters, int waves_per_simd, uint32_t* sink, void* stream);

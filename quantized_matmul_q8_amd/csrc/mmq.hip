@@ -673,10 +673,9 @@ __device__ __forceinline__ void step_prio(int u, int nu) {
 }
 
 // Multiply-accumulate this wave's 8 MFMA sub-blocks of a step (its rows, its
-// half's chunks; ub = first sub-block of the half within the super-block),
-// issuing slot u of the next step's loads at sub-block u.  Software
-// pipelined over sub-blocks so that the matrix core and the LDS reads run
-// under the epilogue (see the two cases below).
+// half's chunks; ub = first sub-block of the half within the super-block).
+// Software pipelined over sub-blocks so that the matrix core and the LDS
+// reads run under the epilogue (see the two cases below).
 template <int FMT, int NT, int MODE>
 __device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* st, const float* wl,
                                             const MmqOperand<FMT>& A, v16f (&acc)[NT], const v16i& magic,
@@ -716,7 +715,6 @@ __device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* s
       step_prio(u, NU);
       const int b = u & 1;
       const bool more = u + 1 < NU;
-      if constexpr (StepLoads<FMT, NT>::kInLoop) pre.issue(u, F);  // one slot of the next step's loads
       if (more) load_sub<FMT, NT>(st, wl, ub + u + 1, u + 1, O[b ^ 1]);
       const auto an = build_a(A, more ? u + 1 : u);
       // scheduling barriers pin the order: operand reads of u+1 first, then
@@ -842,92 +840,75 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
                    : "memory");
 }
 
-// The loads of one step -- the chunks of its two super-blocks (copied into
-// LDS stage dst, [kh][ct] chunks) and this wave's weight bytes -- issued one
-// slot at a time by issue(u), so they spread over the sub-block loop of the
-// previous step instead of queueing all at once in the address unit.  Chunk
-// copies: each wave instruction moves 1 KB (lane l the 16 bytes at 16*l);
-// wave w takes instructions w, w + 8, ...
+// The loads of one step -- the chunks of its super-blocks (copied into LDS
+// stage dst, [half][ct] chunks) and this wave's weight bytes -- all issued at
+// the top of the previous step's compute.  Chunk copies: each wave
+// instruction moves 1 KB (lane l the 16 bytes at 16*l); the step's kInstr
+// copies are split into runs of kDma consecutive ones, run w for wave w, so
+// that a wave's copies lie in one chunk: their addresses are one base plus
+// multiples of 1 KB, the base fixed per wave (DmaPlan) plus a per-step term.
 template <int FMT, int NT>
 struct StepLoads {
   using SP = StepSplit<FMT>;
-  static constexpr int NU = SP::kNU;                          // slots per step
   static constexpr int kInstr = SP::kSbPerStep * NT * kChunkKB;
   static constexpr int kDma = (kInstr + kMmqWaves - 1) / kMmqWaves;  // chunk copies per wave
+  static_assert(kChunkKB % kDma == 0, "a wave's chunk copies must stay inside one chunk");
   static constexpr int kW = FMT == QMM_Q4_K ? 5 : FMT == QMM_Q5_K ? 6 : 8;  // weight loads per wave
-  // Q4_K and Q5_K with two column tiles spread their loads over the
-  // sub-block loop of the previous step; Q6_K and the lean one-tile kernel
-  // issue them all before it (spread out, they keep enough address registers
-  // live to overflow the register budget)
-  static constexpr bool kInLoop = is_q4fam(FMT) && !kLean<FMT, NT>;
-  static constexpr int kWs = is_q4fam(FMT) ? kW : 0;  // weight loads spread over the slots
-  static constexpr int kL = kDma + kWs;                  // loads spread over the slots
-  const uint8_t* xr;       // chunk (ctile0, 0) of the loaded tile
+  const uint8_t* src;      // this lane's 16 bytes of the wave's first copy
+  uint32_t dst;            // LDS address of the wave's first copy
+  bool dma;                // the wave copies in this step
   const uint8_t* wr;       // this lane's weight row of the loaded tile
-  uint32_t dst;            // LDS address of the stage
-  int nb, nct, step;       // super-blocks per row, valid column tiles, step to load
-  bool any;                // false: nothing to load
-  int wave, kh, g;
+  int sbw;                 // super-block of the wave's weight loads (< 0: none)
+  int kh, g;
 
-  __device__ __forceinline__ void dma(int i) const {
-    const int j = wave + kMmqWaves * i;
-    if (j >= kInstr) return;
-    const int hj = j / (NT * kChunkKB), ct = (j / kChunkKB) % NT, q = j % kChunkKB;
-    const int sbj = SP::kSbPerStep * step + hj;
-    if (sbj < nb && ct < nct)
-      dma16(xr + (static_cast<size_t>(ct) * nb + sbj) * kChunkBytes + q * 1024 + (threadIdx.x & 63) * 16,
-            dst + (hj * NT + ct) * kChunkBytes + q * 1024);
-  }
-
-  // Load i of kL is issued at slot (i * NU) / kL, alternating chunk copies
-  // and weight loads while both remain; Q6_K's weight loads all at slot 0.
-  __device__ __forceinline__ void issue(int u, MmqPrefetch<FMT>& F) const {
-    if (!any) return;
-    const int sbw = SP::sb(step, kh);
-    if constexpr (FMT == QMM_Q6_K) {
-      if (u == 0 && sbw < nb)
-#pragma unroll
-        for (int w = 0; w < kW; ++w) load_weight_slot(F, wr, sbw, g, w, kh);
-    }
-#pragma unroll
-    for (int i = 0; i < kL; ++i) {
-      if ((i * NU) / kL != u) continue;
-      constexpr int kPair = kDma < kWs ? kDma : kWs;
-      int di = -1, wi = -1;
-      if (i < 2 * kPair) {
-        if (i & 1) wi = i >> 1; else di = i >> 1;
-      } else if (kDma > kWs) {
-        di = kPair + (i - 2 * kPair);
-      } else {
-        wi = kPair + (i - 2 * kPair);
-      }
-      if (di >= 0) dma(di);
-      if constexpr (is_q4fam(FMT)) {
-        if (wi >= 0 && sbw < nb) load_weight_slot(F, wr, sbw, g, wi, kh);
-      }
-    }
-  }
-
-  // everything at once (a wave with no compute in this step)
   __device__ __forceinline__ void issue_all(MmqPrefetch<FMT>& F) const {
+    if (dma) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u) issue(u, F);
+      for (int i = 0; i < kDma; ++i) dma16(src + i * 1024, dst + i * 1024);
+    }
+    if (sbw >= 0) {
+#pragma unroll
+      for (int w = 0; w < kW; ++w) load_weight_slot(F, wr, sbw, g, w, kh);
+    }
   }
+};
 
+// The part of a wave's chunk copies that does not change with the tile or the
+// step: which chunk (half hj, column tile ct) and which 1 KB slice q0 of it
+// its run starts at, as global and LDS offsets.
+struct DmaPlan {
+  size_t src_off;   // ((ct * nb) + hj) * kChunkBytes + q0 * 1 KB + 16 * lane
+  uint32_t dst_off; // (hj * NT + ct) * kChunkBytes + q0 * 1 KB
+  int hj, ct;
+  bool has;         // the wave has a run
 };
 
 template <int FMT, int NT>
-__device__ __forceinline__ StepLoads<FMT, NT> step_loads(const MmqParams& P, const TileRef& R, int step,
-                                                         uint32_t dst, bool any, int wave, int kh, int g) {
+__device__ __forceinline__ DmaPlan dma_plan(int wave, int nb) {
+  using L = StepLoads<FMT, NT>;
+  DmaPlan D;
+  const int first = wave * L::kDma;
+  D.has = first < L::kInstr;
+  const int pair = first / kChunkKB, q0 = first % kChunkKB;
+  D.hj = pair / NT;
+  D.ct = pair % NT;
+  D.src_off = (static_cast<size_t>(D.ct) * nb + D.hj) * kChunkBytes + q0 * 1024 + (threadIdx.x & 63) * 16;
+  D.dst_off = static_cast<uint32_t>((D.hj * NT + D.ct) * kChunkBytes + q0 * 1024);
+  return D;
+}
+
+template <int FMT, int NT>
+__device__ __forceinline__ StepLoads<FMT, NT> step_loads(const MmqParams& P, const TileRef& R, const DmaPlan& D,
+                                                         int step, uint32_t dst, bool any, int kh, int g) {
+  using SP = StepSplit<FMT>;
   StepLoads<FMT, NT> L;
-  L.xr = P.xr + static_cast<size_t>(R.ctile0) * P.nb * kChunkBytes;
+  const int sb0 = SP::kSbPerStep * step;
+  L.src = P.xr + (static_cast<size_t>(R.ctile0) * P.nb + sb0) * kChunkBytes + D.src_off;
+  L.dst = dst + D.dst_off;
+  L.dma = any && D.has && D.ct < R.nct && sb0 + D.hj < P.nb;
   L.wr = R.wr;
-  L.dst = dst;
-  L.nb = P.nb;
-  L.nct = R.nct;
-  L.step = step;
-  L.any = any;
-  L.wave = wave;
+  const int sbw = SP::sb(step, kh);
+  L.sbw = any && sbw < P.nb ? sbw : -1;
   L.kh = kh;
   L.g = g;
   return L;
@@ -1089,8 +1070,9 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT 
   tile_ref<FMT, NT, MODE>(P, Tb, Q.start + b8, R);
   MmqPrefetch<FMT> F;
   const uint32_t lds0 = lds_addr(smem);
+  const DmaPlan D = dma_plan<FMT, NT>(wave, P.nb);
   {
-    const StepLoads<FMT, NT> first = step_loads<FMT, NT>(P, R, R.s0, lds0, true, wave, kh, g);
+    const StepLoads<FMT, NT> first = step_loads<FMT, NT>(P, R, D, R.s0, lds0, true, kh, g);
     first.issue_all(F);
   }
   int k = 0;            // steps done by this workgroup (selects the LDS stage)
@@ -1126,9 +1108,9 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT 
         if (next >= 0) tile_ref<FMT, NT, MODE>(P, Tb, next, Rn);
       }
       const uint32_t dst = lds0 + ((k + 1) & 1) * L::kStage;
-      const StepLoads<FMT, NT> pre = last ? step_loads<FMT, NT>(P, Rn, Rn.s0, dst, next >= 0, wave, kh, g)
-                                          : step_loads<FMT, NT>(P, R, step + 1, dst, true, wave, kh, g);
-      if (!StepLoads<FMT, NT>::kInLoop || !active) pre.issue_all(F);
+      const StepLoads<FMT, NT> pre = last ? step_loads<FMT, NT>(P, Rn, D, Rn.s0, dst, next >= 0, kh, g)
+                                          : step_loads<FMT, NT>(P, R, D, step + 1, dst, true, kh, g);
+      pre.issue_all(F);
       if (active) {
         mmq_compute<FMT, NT, MODE>(P, st + StepSplit<FMT>::chunk_half(kh) * NT * kChunkBytes, wl, A, acc, magic,
                                    R.tc, R.r0, sb, StepSplit<FMT>::u0(kh), pre, F);

@@ -67,7 +67,9 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(int64_t iters
 // chain and the matrix core); 5: as 4 with the min term as three bf16 MFMAs
 // per super-block (K = 16 each: a three-way bf16 split of -dmin*m against one
 // of beta*S, six of the nine partial products); 6: as 5 into the epilogue's
-// accumulator.  Two column blocks (NT = 2).
+// accumulator; 7: as 6 with a workgroup barrier every eight sub-blocks (the
+// GEMM's step); 8: as 7 with the A operand unpacked from 4-bit values each
+// sub-block.  Two column blocks (NT = 2).
 template <int MODE>
 __global__ __launch_bounds__(kProbeThreads) void probe_epilogue_kernel(int64_t iters, uint32_t* sink) {
   constexpr int NT = 2;
@@ -158,7 +160,18 @@ __global__ __launch_bounds__(kProbeThreads) void probe_epilogue_kernel(int64_t i
         bm[ct] = am;
       }
     }
+    if constexpr (MODE >= 8) {
+      // the A operand unpacked from 4-bit values as the GEMM does
+      const int sh = (u & 1) * 4;
+      a = v4i{static_cast<int>((static_cast<uint32_t>(a[0]) >> sh) & 0x0f0f0f0fu),
+              static_cast<int>((static_cast<uint32_t>(a[1]) >> sh) & 0x0f0f0f0fu),
+              static_cast<int>((static_cast<uint32_t>(a[2]) >> sh) & 0x0f0f0f0fu),
+              static_cast<int>((static_cast<uint32_t>(a[3]) >> sh) & 0x0f0f0f0fu)};
+    }
     opaque(a);
+    if constexpr (MODE >= 7) {
+      if (u == 7) __syncthreads();   // one barrier per eight sub-blocks, as the GEMM's step
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
@@ -172,13 +185,15 @@ __global__ __launch_bounds__(kProbeThreads) void probe_epilogue_kernel(int64_t i
         if (u & 1) acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, bm[ct], acc[ct], 0, 0, 0);
       } else if constexpr (MODE == 4) {
         if (u & 1) accm[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, bm[ct], accm[ct], 0, 0, 0);
-      } else if constexpr (MODE == 5 || MODE == 6) {
+      } else if constexpr (MODE >= 5) {
         // once per super-block (8 sub-blocks): three bf16 MFMAs (K = 3 x 16),
         // spread over the sub-blocks; into an accumulator of its own (5) or
         // into the epilogue's (6)
         if (u == 1 || u == 3 || u == 5) {
           if constexpr (MODE == 5)
             accm[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abf, bbf[ct], accm[ct], 0, 0, 0);
+          else if constexpr (MODE >= 7)
+            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abf, bbf[ct], acc[ct], 0, 0, 0);
           else
             acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abf, bbf[ct], acc[ct], 0, 0, 0);
         }
@@ -245,7 +260,7 @@ extern "C" int qmm_probe_mfma(int64_t iters, int waves_per_simd, uint32_t* sink,
 extern "C" int qmm_probe_mfma_epilogue(int mode, int64_t iters, int waves_per_simd, uint32_t* sink, void* stream) {
   if (!sink) return QMM_ERR_NULL;
   if (!aligned16(sink)) return QMM_ERR_ALIGN;
-  if (mode < 1 || mode > 6) return QMM_ERR_UNSUPPORTED;
+  if (mode < 1 || mode > 8) return QMM_ERR_UNSUPPORTED;
   if (iters < 1 || iters > (int64_t{1} << 24)) return QMM_ERR_SHAPE;
   if (waves_per_simd != 2 && waves_per_simd != 4) return QMM_ERR_SHAPE;
   const dim3 grid(probe_grid(waves_per_simd)), block(kProbeThreads);
@@ -256,6 +271,8 @@ extern "C" int qmm_probe_mfma_epilogue(int mode, int64_t iters, int waves_per_si
   if (mode == 4) hipLaunchKernelGGL(probe_epilogue_kernel<4>, grid, block, 0, st, iters, sink);
   if (mode == 5) hipLaunchKernelGGL(probe_epilogue_kernel<5>, grid, block, 0, st, iters, sink);
   if (mode == 6) hipLaunchKernelGGL(probe_epilogue_kernel<6>, grid, block, 0, st, iters, sink);
+  if (mode == 7) hipLaunchKernelGGL(probe_epilogue_kernel<7>, grid, block, 0, st, iters, sink);
+  if (mode == 8) hipLaunchKernelGGL(probe_epilogue_kernel<8>, grid, block, 0, st, iters, sink);
   return launch_status();
 }
 
