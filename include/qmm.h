@@ -303,7 +303,10 @@ int qmm_probe_mfma(int64_t iters, int waves_per_simd, uint32_t* sink, void* stre
  * iterations into its own accumulator; mode 6: the same into the FMA
  * accumulator; mode 7: mode 6 with a workgroup barrier every eight
  * iterations; mode 8: mode 7 with the A operand unpacked from 4-bit values
- * each iteration.  int8 ops per launch = CUs * waves_per_simd * 4 * iters * 2 *
+ * each iteration; mode 9: the one-column-block loop of the grouped GEMM
+ * (no software pipelining, row scales read four at a time, two workgroups
+ * per CU whatever waves_per_simd says; its ops per launch are half those of
+ * modes 1-8 at four waves per SIMD).  int8 ops per launch = CUs * waves_per_simd * 4 * iters * 2 *
  * 65536.  waves_per_simd 2 or 4; 1 <= iters <= 2^24.
  */
 int qmm_probe_mfma_epilogue(int mode, int64_t iters, int waves_per_simd, uint32_t* sink, void* stream);

@@ -216,6 +216,67 @@ __global__ __launch_bounds__(kProbeThreads) void probe_epilogue_kernel(int64_t i
   probe_sink(h ^ __builtin_bit_cast(uint32_t, fs), sink);
 }
 
+// The one-column-block inner loop (the grouped-expert GEMM's): per sub-block
+// its B operand and column factors read from LDS, the int8 MFMA, then the
+// epilogue with the row scales read from LDS four at a time, no software
+// pipelining; three bf16 min-term MFMAs and one workgroup barrier per eight
+// sub-blocks.  Runs at four waves per SIMD (two workgroups per CU).
+__global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void probe_lean_kernel(int64_t iters, uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) float s_al[8][32];
+  __shared__ __attribute__((aligned(16))) float2 s_bp[8][32];
+  __shared__ __attribute__((aligned(16))) v4i s_bq[8][64];
+  const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
+  for (int i = threadIdx.x; i < 8 * 32; i += kProbeThreads) {
+    (&s_al[0][0])[i] = 1.0f + 1e-3f * (i & 15);
+    (&s_bp[0][0])[i] = make_float2(0.5f, -0.5f * kProbeMagic);
+  }
+  for (int i = threadIdx.x; i < 8 * 64; i += kProbeThreads) (&s_bq[0][0])[i] = v4i{i, 3 * i, 5 * i, 7 * i};
+  __syncthreads();
+  v4i a = {lane, lane * 3, lane * 5, lane * 7};
+  opaque(a);
+  v16i magic;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) magic[v] = static_cast<int>(kProbeMagicBits);
+  opaque(magic);
+  typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+  v8bf abf, bbf;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    abf[k] = static_cast<__bf16>(1.0f + k);
+    bbf[k] = static_cast<__bf16>(0.5f * k);
+  }
+  __asm__ volatile("" : "+v"(abf), "+v"(bbf));
+  v16f acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int64_t i = 0; i < iters; ++i) {
+    const int u = static_cast<int>(i & 7);
+    const v4i bq = s_bq[u][lane];
+    const float2 bp = s_bp[u][col];
+    opaque(a);
+    const v16i X = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq, magic, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const v16f Xf = __builtin_bit_cast(v16f, X);
+    const float* wa = &s_al[u][4 * g];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 a4 = *reinterpret_cast<const float4*>(wa + 8 * k);
+      const float al4[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[4 * k + j] = __builtin_fmaf(al4[j], __builtin_fmaf(bp.x, Xf[4 * k + j], bp.y),
+                                                                   acc[4 * k + j]);
+    }
+    if (u == 1 || u == 3 || u == 5) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(abf, bbf, acc, 0, 0, 0);
+    if (u == 7) __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float fs = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) fs += acc[v] * static_cast<float>(1 + v);
+  probe_sink(__builtin_bit_cast(uint32_t, fs), sink);
+}
+
 // Read-only streaming with a chosen geometry.  U 16-byte loads per thread
 // are issued before any is used (U in flight), lane-contiguous, one grid
 // stride apart; the grid then strides over the buffer until every chunk of
@@ -260,7 +321,7 @@ extern "C" int qmm_probe_mfma(int64_t iters, int waves_per_simd, uint32_t* sink,
 extern "C" int qmm_probe_mfma_epilogue(int mode, int64_t iters, int waves_per_simd, uint32_t* sink, void* stream) {
   if (!sink) return QMM_ERR_NULL;
   if (!aligned16(sink)) return QMM_ERR_ALIGN;
-  if (mode < 1 || mode > 8) return QMM_ERR_UNSUPPORTED;
+  if (mode < 1 || mode > 9) return QMM_ERR_UNSUPPORTED;
   if (iters < 1 || iters > (int64_t{1} << 24)) return QMM_ERR_SHAPE;
   if (waves_per_simd != 2 && waves_per_simd != 4) return QMM_ERR_SHAPE;
   const dim3 grid(probe_grid(waves_per_simd)), block(kProbeThreads);
@@ -273,6 +334,9 @@ extern "C" int qmm_probe_mfma_epilogue(int mode, int64_t iters, int waves_per_si
   if (mode == 6) hipLaunchKernelGGL(probe_epilogue_kernel<6>, grid, block, 0, st, iters, sink);
   if (mode == 7) hipLaunchKernelGGL(probe_epilogue_kernel<7>, grid, block, 0, st, iters, sink);
   if (mode == 8) hipLaunchKernelGGL(probe_epilogue_kernel<8>, grid, block, 0, st, iters, sink);
+  // mode 9: the one-column-block loop, ops per launch counted as one MFMA per
+  // iteration (half those of modes 1-8), always two workgroups per CU
+  if (mode == 9) hipLaunchKernelGGL(probe_lean_kernel, dim3(device_cu_count() * 2), block, 0, st, iters, sink);
   return launch_status();
 }
 

@@ -206,7 +206,7 @@ def test_probe_hooks_host_errors():
     assert L.qmm_probe_mfma(10, 3, FAKE, NUL) == _lib.QMM_ERR_SHAPE
     assert L.qmm_probe_mfma(10, 2, NUL, NUL) == _lib.QMM_ERR_NULL
     assert L.qmm_probe_mfma(10, 2, MISAL, NUL) == _lib.QMM_ERR_ALIGN
-    assert L.qmm_probe_mfma_epilogue(9, 10, 2, FAKE, NUL) == _lib.QMM_ERR_UNSUPPORTED
+    assert L.qmm_probe_mfma_epilogue(10, 10, 2, FAKE, NUL) == _lib.QMM_ERR_UNSUPPORTED
     assert L.qmm_probe_mfma_epilogue(1, (1 << 24) + 1, 2, FAKE, NUL) == _lib.QMM_ERR_SHAPE
     assert L.qmm_probe_mfma_epilogue(1, 10, 8, FAKE, NUL) == _lib.QMM_ERR_SHAPE
     assert L.qmm_probe_read_geom(FAKE, 32, 3, 0, FAKE, NUL) == _lib.QMM_ERR_SHAPE

@@ -38,7 +38,7 @@ def test_probe_mfma(wps):
     assert not sink.any()
 
 
-@pytest.mark.parametrize("mode", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("mode", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_probe_mfma_epilogue(mode):
     sink = torch.zeros((4,), dtype=torch.int32, device=DEV)
     iters = 2048
