@@ -815,31 +815,6 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
   R.wr = wbase + static_cast<size_t>(wrow) * P.nb * kRowBytes;
 }
 
-// LDS byte address of a (generic) pointer into shared memory: a flat
-// address in the LDS aperture carries the LDS offset in its low 32 bits.
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
-// 16 bytes per lane from global memory into LDS at lds + 16 * lane
-// (global_load_lds_dwordx4; the LDS base goes through M0).  Written as
-// inline assembly so the compiler does not track it: its own tracking treats
-// every later LDS read as a possible alias and waits for all loads in flight,
-// which would serialise the prefetch of the next step into this one.  The
-// kernel waits for these copies explicitly (vmcnt(0), then a barrier).  M0
-// is a reserved register the compiler may hold a value in, so the sequence
-// saves and restores it (the load takes its LDS base from M0 when it is
-// issued).
-__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
-  uint32_t saved;
-  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
-                   "s_mov_b32 m0, %0"
-                   : "=&s"(saved)
-                   : "v"(src), "s"(m0v)
-                   : "memory");
-}
-
 // The loads of one step -- the chunks of its super-blocks (copied into LDS
 // stage dst, [half][ct] chunks) and this wave's weight bytes -- all issued at
 // the top of the previous step's compute.  Chunk copies: each wave
@@ -1010,7 +985,7 @@ __device__ __forceinline__ Queue make_queue(int total) {
   return Q;
 }
 
-__device__ __forceinline__ void wait_vm_all() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm_all() { wait_vmcnt<0>(); }
 
 // Persistent loop over the tiles of the call.  Steps of two super-blocks
 // (one per K half); at the top of a step every wave waits for its own loads

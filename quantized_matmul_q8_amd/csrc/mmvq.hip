@@ -525,6 +525,181 @@ __global__ __launch_bounds__(kMmvqThreads) void mmvq_q6k_kernel(const uint8_t* w
   }
 }
 
+// One token (T = 1), Q4_K and Q5_K.  The whole matrix is one read, so the
+// time is set by how early and how many weight bytes are in flight.  Each
+// wave copies its row segment straight into its own LDS region with
+// global_load_lds (kRounds copies of 1 KB, all issued at the start: a deep
+// prefetch that holds no registers), after the workgroup's copy of the raw
+// Q8_1 activation blocks of the segment.  Lane l then takes unit 64u + l of
+// the segment -- super-block b = unit / 4, sub-block pair p = unit % 4: the
+// 32 value bytes 16 + 32p .. 16 + 32p + 31 (Q5_K: 48 + 32p, plus the 32
+// fifth-bit bytes), i.e. all 32 weights of sub-blocks 2p (low nibbles) and
+// 2p + 1 (high nibbles) -- decodes their two scales and mins from the
+// header itself and multiplies them with Q8_1 blocks 8b + 2p and 8b + 2p + 1,
+// whose stored integer sums give the min term ([8e] §2).  Unit round u
+// waits only for the copies that hold its 16 super-blocks, so it runs while
+// later rounds are still arriving; no lane takes a divergent path.
+
+template <int FMT>
+struct MvDma {
+  static constexpr bool kQ5 = FMT == QMM_Q5_K;
+  static constexpr int kBytes = kQ5 ? kQ5Bytes : kQ4Bytes;
+  static constexpr int kRounds = kQ5 ? 8 : 7;       // 1 KB copies per wave per segment
+  static constexpr int kMaxBlocks = kQ5 ? 46 : 48;  // super-blocks per segment (3 unit rounds)
+  static constexpr int kUnitRounds = 3;
+  static_assert(kMaxBlocks * kBytes <= kRounds * 1024 && 4 * kMaxBlocks <= 64 * kUnitRounds, "segment");
+  static constexpr int kQ8Seg = 8 * kQ8Bytes;       // Q8_1 bytes per super-block (320)
+  // copies still allowed in flight when unit round u starts: those past the
+  // last byte of its super-blocks (every copy is issued at the start: a
+  // schedule that issues later copies after the first unit rounds, or a
+  // barrier between copy rounds so they are issued round by round across the
+  // waves, measured no faster; the memory system serves the requests of all
+  // CUs in about the order they arrive)
+  static constexpr int in_flight(int u) {
+    const int b = 16 * (u + 1) < kMaxBlocks ? 16 * (u + 1) : kMaxBlocks;
+    const int need = (b * kBytes + 1023) / 1024;
+    return kRounds - (need < kRounds ? need : kRounds);
+  }
+};
+
+template <int FMT, bool DEBUG>
+__global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void mmvq_q45k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb, int cb,
+                         int32_t* __restrict__ dbgD, int32_t* __restrict__ dbgS) {
+  using DL = MvDma<FMT>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row_raw = blockIdx.x * kMmvqWaves + wave;
+  const bool row_ok = row_raw < M;
+  const int row = row_ok ? row_raw : M - 1;  // out-of-range waves read a valid row, store nothing
+  const uint8_t* wrow = w + static_cast<size_t>(row) * nb * DL::kBytes;
+  const uint8_t* wl = lds + wave * DL::kRounds * 1024;  // this wave's copy of its row segment
+  const uint8_t* xl = lds + kMmvqWaves * DL::kRounds * 1024;  // the segment's raw Q8_1 blocks
+  const uint32_t wl_a = lds_addr(wl), xl_a = lds_addr(xl);
+  float acc = 0.0f;
+  for (int b0 = 0; b0 < nb; b0 += cb) {
+    const int nbc = min(cb, nb - b0);
+    if (b0 > 0) __syncthreads();  // every wave is done with the previous segment's copies
+    // 1. the activation blocks of the segment (nbc * 320 contiguous bytes), copies i = wave + 8k
+    const int xs = nbc * (DL::kQ8Seg / 16);
+    const uint8_t* xseg = xq + static_cast<size_t>(b0) * DL::kQ8Seg;
+    for (int i = wave; 64 * i < xs; i += kMmvqWaves) dma16(xseg + 16 * min(64 * i + lane, xs - 1), xl_a + 1024 * i);
+    // 2. the row segment, 16 bytes per lane per copy (lanes past its end
+    // re-read its last 16 bytes)
+    const int nch = nbc * (DL::kBytes / 16);
+    const uint8_t* wseg = wrow + static_cast<size_t>(b0) * DL::kBytes;
+#pragma unroll
+    for (int r = 0; r < DL::kRounds; ++r) dma16<true>(wseg + 16 * min(64 * r + lane, nch - 1), wl_a + 1024 * r);
+    // 3. this wave's activation copies (issued first) are done; then everyone's
+    wait_vmcnt<DL::kRounds>();
+    __syncthreads();
+    // 4. unit rounds
+#pragma unroll
+    for (int u = 0; u < DL::kUnitRounds; ++u) {
+      if (u == 0) wait_vmcnt<DL::in_flight(0)>();  // (u is a constant once unrolled)
+      else if (u == 1) wait_vmcnt<DL::in_flight(1)>();
+      else wait_vmcnt<DL::in_flight(2)>();
+      const int n = 64 * u + lane, b = n >> 2, p = n & 3;
+      if (b < nbc) {  // (a unit round past the segment has no lanes: its waits stay in step)
+        const uint8_t* blk = wl + b * DL::kBytes;
+        const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+        int sc0, m0, sc1, m1;
+        q4k_scale_min(2 * p, hdr.y, hdr.z, hdr.w, sc0, m0);
+        q4k_scale_min(2 * p + 1, hdr.y, hdr.z, hdr.w, sc1, m1);
+        const uint8_t* qv = blk + (DL::kQ5 ? 48 : 16) + 32 * p;
+        const uint4 qa = *reinterpret_cast<const uint4*>(qv);
+        const uint4 qb = *reinterpret_cast<const uint4*>(qv + 16);
+        const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        uint32_t lo[8], hi[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          lo[k] = qw[k] & 0x0f0f0f0fu;
+          hi[k] = (qw[k] >> 4) & 0x0f0f0f0fu;
+        }
+        if constexpr (DL::kQ5) {
+          // fifth bit of weight i of sub-block j: bit j of byte i of bytes 16 .. 47
+          const uint4 ha = *reinterpret_cast<const uint4*>(blk + 16);
+          const uint4 hb = *reinterpret_cast<const uint4*>(blk + 32);
+          const uint32_t hw[8] = {ha.x, ha.y, ha.z, ha.w, hb.x, hb.y, hb.z, hb.w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            lo[k] |= ((hw[k] >> (2 * p)) & 0x01010101u) << 4;
+            hi[k] |= ((hw[k] >> (2 * p + 1)) & 0x01010101u) << 4;
+          }
+        }
+        // Q8_1 blocks 8b + 2p and 8b + 2p + 1: f16 d, pad, q[32], int32 sum (8-byte aligned)
+        const uint2* x0 = reinterpret_cast<const uint2*>(xl + (8 * b + 2 * p) * kQ8Bytes);
+        const uint2* x1 = x0 + kQ8Bytes / 8;
+        uint2 a[5], c[5];
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+          a[k] = x0[k];
+          c[k] = x1[k];
+        }
+        const uint32_t xa[8] = {a[0].y, a[1].x, a[1].y, a[2].x, a[2].y, a[3].x, a[3].y, a[4].x};
+        const uint32_t xc[8] = {c[0].y, c[1].x, c[1].y, c[2].x, c[2].y, c[3].x, c[3].y, c[4].x};
+        int D0 = 0, D1 = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          D0 = dot4(lo[k], xa[k], D0);
+          D1 = dot4(hi[k], xc[k], D1);
+        }
+        const int S0 = static_cast<int>(a[4].y), S1 = static_cast<int>(c[4].y);
+        if constexpr (DEBUG) {
+          const int sb = (b0 + b) * 8 + 2 * p;
+          if (row_ok) {
+            int32_t* Dr = dbgD + static_cast<size_t>(row) * (nb * 8);
+            Dr[sb] = D0;
+            Dr[sb + 1] = D1;
+          }
+          if (row_raw == 0) {
+            dbgS[sb] = S0;
+            dbgS[sb + 1] = S1;
+          }
+        } else {
+          const float d = h2f(hdr.x & 0xffffu), dmin = h2f(hdr.x >> 16);
+          const float dx0 = h2f(a[0].x & 0xffffu), dx1 = h2f(c[0].x & 0xffffu);
+          acc += dx0 * (d * static_cast<float>(sc0) * static_cast<float>(D0) -
+                        dmin * static_cast<float>(m0) * static_cast<float>(S0)) +
+                 dx1 * (d * static_cast<float>(sc1) * static_cast<float>(D1) -
+                        dmin * static_cast<float>(m1) * static_cast<float>(S1));
+        }
+      }
+    }
+    // no copy may still be writing LDS when the next segment reuses it or
+    // the workgroup ends
+    wait_vmcnt<0>();
+  }
+  if constexpr (!DEBUG) {
+    const float s = wave_sum(acc);
+    if (lane == 0 && row_ok) y[row] = s;
+  }
+}
+
+template <int FMT, bool DEBUG>
+static int launch_mmvq_t1(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, int32_t* S,
+                          hipStream_t st) {
+  using DL = MvDma<FMT>;
+  const int nseg = (nb + DL::kMaxBlocks - 1) / DL::kMaxBlocks;
+  const int cb = (nb + nseg - 1) / nseg;
+  const size_t lds = static_cast<size_t>(kMmvqWaves) * DL::kRounds * 1024 +
+                     (static_cast<size_t>(cb) * DL::kQ8Seg + 1023) / 1024 * 1024;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const size_t lmax = static_cast<size_t>(kMmvqWaves) * DL::kRounds * 1024 +
+                        (static_cast<size_t>(DL::kMaxBlocks) * DL::kQ8Seg + 1023) / 1024 * 1024;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q45k_t1_kernel<FMT, DEBUG>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lmax)) != hipSuccess)
+      return QMM_ERR_HIP;
+    attr_set = true;
+  }
+  const dim3 grid((M + kMmvqWaves - 1) / kMmvqWaves), block(kMmvqThreads);
+  hipLaunchKernelGGL((mmvq_q45k_t1_kernel<FMT, DEBUG>), grid, block, lds, st, static_cast<const uint8_t*>(w),
+                     static_cast<const uint8_t*>(xq), y, M, nb, cb, D, S);
+  return launch_status();
+}
+
 static size_t mmvq_lds_bytes(int T, int cb) { return static_cast<size_t>(T) * cb * 8 * 48; }
 
 template <bool DEBUG, int FMT = QMM_Q4_K>
@@ -539,6 +714,7 @@ static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int n
   const size_t lds = mmvq_lds_bytes(T, cb) + static_cast<size_t>(kMmvqWaves) * kQ4Ring * RL::kSlot;
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const uint8_t* xp = static_cast<const uint8_t*>(xq);
+  if (!slots && T == 1) return launch_mmvq_t1<FMT, DEBUG>(w, xq, y, M, nb, D, S, st);
   if (slots) {
     if (DEBUG || T != 1) return QMM_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((mmvq_q45k_kernel<FMT, 1, false, true>), dim3(grid.x, nslots), block, lds, st, wp, xp, y,

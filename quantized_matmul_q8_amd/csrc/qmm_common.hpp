@@ -113,6 +113,49 @@ __device__ __forceinline__ void q4k_scale_min(int j, uint32_t s0, uint32_t s1, u
   m = j < 4 ? m_lo : m_hi;
 }
 
+// LDS byte address of a (generic) pointer into shared memory: a flat
+// address in the LDS aperture carries the LDS offset in its low 32 bits.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4; the LDS base goes through M0).  Written as
+// inline assembly so the compiler does not track it: its own tracking treats
+// every later LDS read as a possible alias and waits for all loads in flight,
+// which would serialise a prefetch into the work that precedes its use.  The
+// caller waits for these copies explicitly (wait_vmcnt, plus a barrier when
+// other waves read the data).  M0 is a reserved register the compiler may
+// hold a value in, so the sequence saves and restores it (the load takes its
+// LDS base from M0 when it is issued).  NT marks the load non-temporal (data
+// read once, kept out of the way of reused lines).
+template <bool NT = false>
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  if constexpr (NT) {
+    __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(src), "s"(m0v)
+                     : "memory");
+  } else {
+    __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(src), "s"(m0v)
+                     : "memory");
+  }
+}
+
+// Wait until at most N of this wave's vector memory operations (loads,
+// stores, the copies above) are outstanding; they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Wave64 reductions.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -22,7 +22,9 @@ FMTS = {
     "q6k": (qmm_synth.q6k_weights, oracle.q6k_dequant, qmm.mmvq_q6k, qmm.QMM_Q6_K),
 }
 CASES = [(1, 256, 1), (7, 512, 3), (37, 1280, 8), (64, 2304, 4), (5, 256, 2), (1024, 1024, 1),
-         (129, 768, 5), (200, 1536, 6), (90, 2816, 7), (4096, 11008, 1), (4096, 11008, 4)]
+         (129, 768, 5), (200, 1536, 6), (90, 2816, 7), (4096, 11008, 1), (4096, 11008, 4),
+         # one token with rows longer than one LDS segment (two and three segments)
+         (40, 14336, 1), (11, 12032, 1), (19, 30720, 1)]
 
 
 def _inputs(fmt, M, K, T, seed):
@@ -54,7 +56,8 @@ def test_end_to_end_from_fp32(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
-@pytest.mark.parametrize("M,K,T", [(3, 256, 1), (9, 768, 4), (17, 512, 5), (21, 768, 6), (33, 1024, 8)])
+@pytest.mark.parametrize("M,K,T", [(3, 256, 1), (9, 768, 4), (17, 512, 5), (21, 768, 6), (33, 1024, 8),
+                                   (13, 12544, 1), (10, 11008, 1)])
 def test_integer_stage_bit_exact(fmt, M, K, T):
     w, x, xq = _inputs(fmt, M, K, T, seed=7 * M + T)
     say(f"debug_subdots path=0 {fmt}", f"M={M} K={K} T={T}")
