@@ -39,7 +39,6 @@ import argparse
 import json
 import math
 import os
-import subprocess
 import sys
 import time
 
@@ -59,7 +58,7 @@ MIN_LAUNCHES = 100
 
 # traffic measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE for the
 # dominant kernel (profiles/); None until taken for the current kernel
-DOMINANT_TRAFFIC_BYTES = 37436825   # mmvq_q6k, profiles/mmvq_decode_4096x11008_t1.md
+DOMINANT_TRAFFIC_BYTES = 37443050   # mmvq_q6k, profiles/mmvq_decode_4096x11008_t1.md
 
 
 def log(*a):
@@ -145,46 +144,27 @@ def rotated(t, n):
 
 
 def read_clocks():
-    """SCLK / MCLK in MHz as reported by amd-smi (else rocm-smi); None where unreadable."""
+    """SCLK / MCLK in MHz from the amdgpu driver's sysfs DPM tables (the level
+    marked '*' is the current one); None where unreadable.  Plain file reads:
+    no helper program is started from this GPU process."""
+    import glob
     out = {"sclk_mhz": None, "mclk_mhz": None, "source": None}
-    try:
-        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=30)
-        data = json.loads(r.stdout)
-        dev = data[0] if isinstance(data, list) else data
-        if isinstance(dev, dict) and "gpu_data" in dev:
-            dev = dev["gpu_data"][0]
-        clk = dev.get("clock", dev)
-
-        def cur(key):
-            v = clk.get(key)
-            if isinstance(v, dict):
-                v = v.get("clk", v.get("cur_clk"))
-                if isinstance(v, dict):
-                    v = v.get("value")
-            return float(v) if v not in (None, "N/A") else None
-        out["sclk_mhz"] = cur("gfx_0") or cur("GFX_0") or cur("gfx")
-        out["mclk_mhz"] = cur("mem_0") or cur("MEM_0") or cur("mem")
-        out["source"] = "amd-smi"
-        if out["sclk_mhz"] or out["mclk_mhz"]:
-            return out
-    except Exception as e:  # noqa: BLE001 - the tools may be absent or refuse
-        out["amd_smi_error"] = str(e)[:120]
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
-        data = json.loads(r.stdout)
-        card = next(iter(data.values()))
-        for k, v in card.items():
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        vals = {}
+        for key, fname in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
             try:
-                mhz = float(str(v).strip("()").lower().replace("mhz", "").split()[-1])
-            except ValueError:
+                with open(os.path.join(dev, fname)) as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            tok = [t for t in line.split() if t.lower().endswith("mhz")]
+                            if tok:
+                                vals[key] = float(tok[0][:-3])
+            except OSError:
                 continue
-            if "sclk" in k.lower():
-                out["sclk_mhz"] = mhz
-            if "mclk" in k.lower():
-                out["mclk_mhz"] = mhz
-        out["source"] = "rocm-smi"
-    except Exception as e:  # noqa: BLE001
-        out["rocm_smi_error"] = str(e)[:120]
+        if vals:
+            out.update(vals)
+            out["source"] = dev + "/pp_dpm_*"
+            return out
     return out
 
 
