@@ -91,8 +91,9 @@ int q8_1_quantize(const float* x, void* xq, int64_t T, int64_t K, void* stream);
  * mmvq_q4k / mmvq_q6k -- decode matvec y[T][M] = xq[T][K] . W[M][K]^T for
  * 1 <= T <= QMM_MMVQ_MAX_T ([8e] §2-§3.2: integer 4-way dot products of
  * unpacked 4-bit (6-bit) weights with int8 activations; the Q4_K min term
- * uses the activation sum from a dot product against ones).  One wave64 per
- * weight row streams the row's blocks.  Requires M >= 1, K % 256 == 0.
+ * uses the activation sums: a dot product against ones, or at T = 1 the
+ * integer sum stored in each Q8_1 block).  One wave64 per weight row streams
+ * the row's blocks.  Requires M >= 1, K % 256 == 0.
  * Output fp32, y[t*M + i].  Deterministic: identical inputs give identical
  * bits.
  */
