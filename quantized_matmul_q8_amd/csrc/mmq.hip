@@ -571,7 +571,6 @@ __device__ __forceinline__ v4i build_a(const MmqOperand<QMM_Q5_K>& A, int u) {
              static_cast<int>(((qv.z >> sh) & 0x0f0f0f0fu) | (((A.qh.z >> u) & 0x01010101u) << 4)),
              static_cast<int>(((qv.w >> sh) & 0x0f0f0f0fu) | (((A.qh.w >> u) & 0x01010101u) << 4))};
 }
-constexpr uint32_t kQ6HiTable = 0x1000F0E0u;  // bytes -32, -16, 0, 16 as int8
 __device__ __forceinline__ long build_a(const MmqOperand<QMM_Q6_K>& A, int u) {
   // u in this wave's half: its half h is implied by the operand bytes taken
   const int s = u >> 1, hf = u & 1;

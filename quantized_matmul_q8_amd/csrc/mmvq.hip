@@ -731,6 +731,145 @@ static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int n
   return launch_status();
 }
 
+// One token, Q6_K: the one-token Q4_K design adapted to 210-byte blocks.
+// A wave's row starts at any even byte, so it is copied as the 16-byte
+// aligned chunks that cover it (the row's offset in its first chunk is
+// `shift`); the first 8 KB (all of super-blocks 0 .. 37 for any shift) go
+// straight into the wave's LDS region with global_load_lds, and the rest of
+// the row (at most 8 more super-blocks) is loaded into registers, two 16-byte
+// chunks per lane, issued after the copies and written over the region's
+// first 2 KB (super-blocks 0 .. 9, done with by then) just before the last
+// unit round.  Lane l takes unit 64u + l: super-block b = unit / 4, half
+// h = (unit / 2) % 2 and 16-half q = unit % 2 of it, i.e. weights
+// 128h + 32k + l for l in [16q, 16q + 16) and k = 0 .. 3 -- the bytes
+// ql[64h + 16q ..], ql[64h + 32 + 16q ..] and qh[32h + 16q ..] (16 each), the
+// scales sc[8h + 2k + q] and d -- against half q of Q8_1 blocks 8b + 4h + k.
+// The signed values q6 - 32 are formed with a byte table lookup on the two
+// high bits, so no activation sum is needed.  Blocks sit at 2-byte aligned
+// LDS offsets: 16-byte pieces are read as aligned dwords and shifted.
+constexpr int kQ6T1Rounds = 8;     // 1 KB copies per wave (its LDS region)
+constexpr int kQ6T1ABlocks = 38;   // super-blocks always inside the copies
+constexpr int kQ6T1MaxBlocks = 46; // + at most 8 in registers (2 chunks per lane)
+
+// 16 bytes at a 2-byte aligned LDS address (the fifth dword read is inside
+// the LDS allocation: every caller's piece ends at least 4 bytes before the
+// end of its block or region).
+__device__ __forceinline__ uint4 lds16_a2(const uint8_t* p) {
+  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint32_t* a = reinterpret_cast<const uint32_t*>(p - sh);
+  const uint32_t w0 = a[0], w1 = a[1], w2 = a[2], w3 = a[3], w4 = a[4];
+  return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
+                    __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh));
+}
+__device__ __forceinline__ uint2 lds8_a2(const uint8_t* p) {
+  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint32_t* a = reinterpret_cast<const uint32_t*>(p - sh);
+  const uint32_t w0 = a[0], w1 = a[1], w2 = a[2];
+  return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));
+}
+
+template <bool DEBUG>
+__global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb,
+                        int32_t* __restrict__ dbgD) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row_raw = blockIdx.x * kMmvqWaves + wave;
+  const bool row_ok = row_raw < M;
+  const int row = row_ok ? row_raw : M - 1;  // out-of-range waves read a valid row, store nothing
+  const size_t row_off = static_cast<size_t>(row) * nb * kQ6Bytes;
+  const int shift = static_cast<int>(row_off & 15u);
+  const uint8_t* a0 = w + (row_off - shift);                          // 16-byte aligned
+  const int nch = (shift + nb * kQ6Bytes + 15) >> 4;                   // aligned chunks covering the row
+  const int cb0 = (shift + kQ6T1ABlocks * kQ6Bytes) >> 4;              // first chunk held in registers
+  uint8_t* wl = lds + wave * kQ6T1Rounds * 1024;                       // this wave's region
+  const uint8_t* xl = lds + kMmvqWaves * kQ6T1Rounds * 1024;           // raw Q8_1 blocks of the row
+  const uint32_t wl_a = lds_addr(wl), xl_a = lds_addr(xl);
+  // 1. the activation blocks (nb * 320 contiguous bytes), copies i = wave + 8k
+  const int xs = nb * 20;
+  for (int i = wave; 64 * i < xs; i += kMmvqWaves) dma16(xq + 16 * min(64 * i + lane, xs - 1), xl_a + 1024 * i);
+  // 2. chunks 0 .. 511 of the row into the region (chunks past the row re-read its last one)
+#pragma unroll
+  for (int r = 0; r < kQ6T1Rounds; ++r) dma16<true>(a0 + 16 * min(64 * r + lane, nch - 1), wl_a + 1024 * r);
+  // 3. chunks cb0 .. cb0 + 127 into registers (clamped the same way)
+  const uint4 rb0 = ld16_nt(a0 + 16 * min(cb0 + lane, nch - 1));
+  const uint4 rb1 = ld16_nt(a0 + 16 * min(cb0 + 64 + lane, nch - 1));
+  // 4. this wave's activation copies (issued first) are done; then everyone's
+  wait_vmcnt<kQ6T1Rounds + 2>();
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    // copies holding super-blocks 16u .. 16u + 15 (at most shift + 32 * 210 < 7 KB for u = 1)
+    if (u == 0) wait_vmcnt<4 + 2>();
+    else if (u == 1) wait_vmcnt<1 + 2>();
+    else {
+      // the register chunks over super-blocks 0 .. 9 of the region (this wave's reads of them are done)
+      *reinterpret_cast<uint4*>(wl + 16 * lane) = rb0;
+      *reinterpret_cast<uint4*>(wl + 1024 + 16 * lane) = rb1;
+      wait_vmcnt<0>();
+    }
+    const int n = 64 * u + lane, b = n >> 2, h = (n >> 1) & 1, q = n & 1;
+    if (b < nb) {
+      const int vb = shift + b * kQ6Bytes;
+      const uint8_t* blk = wl + (b < kQ6T1ABlocks ? vb : vb - 16 * cb0);
+      const uint4 pa = lds16_a2(blk + 64 * h + 16 * q);        // ql, k = 0 (low) and 2 (high nibbles)
+      const uint4 pb = lds16_a2(blk + 64 * h + 32 + 16 * q);   // ql, k = 1 and 3
+      const uint4 ph = lds16_a2(blk + 128 + 32 * h + 16 * q);  // qh: bits 2k, 2k + 1 for k = 0 .. 3
+      const uint2 sc8 = lds8_a2(blk + 192 + 8 * h);            // sc[8h .. 8h + 7]
+      const float d = h2f(*reinterpret_cast<const uint16_t*>(blk + 208));
+      const uint32_t qa[4] = {pa.x, pa.y, pa.z, pa.w}, qb[4] = {pb.x, pb.y, pb.z, pb.w};
+      const uint32_t qh[4] = {ph.x, ph.y, ph.z, ph.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // half q of Q8_1 block 8b + 4h + k: f16 d at 0, values 16q .. 16q + 15 at 4 + 16q
+        const uint8_t* xb = xl + (8 * b + 4 * h + k) * kQ8Bytes;
+        const uint32_t* xv = reinterpret_cast<const uint32_t*>(xb + 4 + 16 * q);
+        int D = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = ((k & 1) ? qb[i] : qa[i]) >> ((k >> 1) * 4);
+          const uint32_t hi = (qh[i] >> (2 * k)) & 0x03030303u;
+          const uint32_t v = (lo & 0x0f0f0f0fu) | __builtin_amdgcn_perm(kQ6HiTable, kQ6HiTable, hi);
+          D = dot4(v, xv[i], D);
+        }
+        const int sc = static_cast<int8_t>((((k >> 1) ? sc8.y : sc8.x) >> (8 * (q + 2 * (k & 1)))) & 0xffu);
+        if constexpr (DEBUG) {
+          if (row_ok) dbgD[static_cast<size_t>(row) * (nb * 16) + 16 * b + 8 * h + 2 * k + q] = D;
+        } else {
+          const float dx = h2f(*reinterpret_cast<const uint16_t*>(xb));
+          acc += dx * (d * static_cast<float>(sc)) * static_cast<float>(D);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  if constexpr (!DEBUG) {
+    const float s = wave_sum(acc);
+    if (lane == 0 && row_ok) y[row] = s;
+  }
+}
+
+template <bool DEBUG>
+static int launch_mmvq_q6k_t1(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, hipStream_t st) {
+  const size_t lds = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 +
+                     (static_cast<size_t>(nb) * 8 * kQ8Bytes + 1023) / 1024 * 1024;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const size_t lmax = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 +
+                        (static_cast<size_t>(kQ6T1MaxBlocks) * 8 * kQ8Bytes + 1023) / 1024 * 1024;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q6k_t1_kernel<DEBUG>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lmax)) != hipSuccess)
+      return QMM_ERR_HIP;
+    attr_set = true;
+  }
+  const dim3 grid((M + kMmvqWaves - 1) / kMmvqWaves), block(kMmvqThreads);
+  hipLaunchKernelGGL((mmvq_q6k_t1_kernel<DEBUG>), grid, block, lds, st, static_cast<const uint8_t*>(w),
+                     static_cast<const uint8_t*>(xq), y, M, nb, D);
+  return launch_status();
+}
+
 // Q6_K segments: at most 4 * q6_rounds(T) blocks (the pieces held in
 // registers) and kQ6ActBudget bytes of staged activations (with the waves'
 // piece regions two workgroups fit a CU); the row is split into segments
@@ -739,6 +878,11 @@ constexpr int kQ6ActBudget = 44 * 1024;
 template <bool DEBUG>
 static int launch_mmvq_q6k(const void* w, const void* xq, float* y, int M, int nb, int T,
                            int32_t* D, hipStream_t st, const SlotArgs* slots = nullptr, int nslots = 0) {
+  // one token: the LDS-copy kernel, for rows of at most 46 super-blocks whose
+  // matrix ends on a 16-byte boundary (its aligned chunk reads then stay
+  // inside the matrix)
+  if (!slots && T == 1 && nb <= kQ6T1MaxBlocks && (static_cast<int64_t>(M) * nb) % 8 == 0)
+    return launch_mmvq_q6k_t1<DEBUG>(w, xq, y, M, nb, D, st);
   const SlotArgs SA = slots ? *slots : SlotArgs{};
   int cmax = kQ6ActBudget / (T * kQK * 3 / 2);
   if (cmax > 4 * q6_rounds(T)) cmax = 4 * q6_rounds(T);

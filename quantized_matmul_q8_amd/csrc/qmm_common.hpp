@@ -156,6 +156,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Q6_K signed values q6 - 32 = low nibble + 16 * (hi - 2): a byte-table lookup
+// (v_perm) maps the two high bits hi to the int8 16 * (hi - 2), whose low
+// nibble is zero, so OR-ing in the low nibble gives the value.
+constexpr uint32_t kQ6HiTable = 0x1000F0E0u;  // bytes -32, -16, 0, 16 as int8
+
 // Wave64 reductions.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -24,7 +24,10 @@ FMTS = {
 CASES = [(1, 256, 1), (7, 512, 3), (37, 1280, 8), (64, 2304, 4), (5, 256, 2), (1024, 1024, 1),
          (129, 768, 5), (200, 1536, 6), (90, 2816, 7), (4096, 11008, 1), (4096, 11008, 4),
          # one token with rows longer than one LDS segment (two and three segments)
-         (40, 14336, 1), (11, 12032, 1), (19, 30720, 1)]
+         (40, 14336, 1), (11, 12032, 1), (19, 30720, 1),
+         # one token, Q6_K rows split between the LDS copy and registers: none, one and eight
+         # super-blocks in registers, and a matrix not ending on a 16-byte boundary
+         (8, 9728, 1), (24, 9984, 1), (16, 11776, 1), (8, 768, 1), (9, 11008, 1)]
 
 
 def _inputs(fmt, M, K, T, seed):
@@ -57,7 +60,7 @@ def test_end_to_end_from_fp32(fmt):
 
 @pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,K,T", [(3, 256, 1), (9, 768, 4), (17, 512, 5), (21, 768, 6), (33, 1024, 8),
-                                   (13, 12544, 1), (10, 11008, 1)])
+                                   (13, 12544, 1), (10, 11008, 1), (16, 11008, 1), (8, 11776, 1)])
 def test_integer_stage_bit_exact(fmt, M, K, T):
     w, x, xq = _inputs(fmt, M, K, T, seed=7 * M + T)
     say(f"debug_subdots path=0 {fmt}", f"M={M} K={K} T={T}")
