@@ -562,6 +562,85 @@ struct MvDma {
   }
 };
 
+// Unit (super-block at blk in LDS, sub-block pair p) of a Q4_K / Q5_K row:
+// the 4-bit values (Q5_K: with the fifth bit as bit 4) of sub-blocks 2p (lo)
+// and 2p + 1 (hi), four per dword, and their integer scales and mins.
+struct Q45Unit {
+  uint32_t lo[8], hi[8];
+  int sc0, m0, sc1, m1;
+  uint32_t dd;  // f16 d | f16 dmin << 16
+};
+template <int FMT>
+__device__ __forceinline__ void q45_unit(const uint8_t* blk, int p, Q45Unit& U) {
+  constexpr bool kQ5 = FMT == QMM_Q5_K;
+  const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+  q4k_scale_min(2 * p, hdr.y, hdr.z, hdr.w, U.sc0, U.m0);
+  q4k_scale_min(2 * p + 1, hdr.y, hdr.z, hdr.w, U.sc1, U.m1);
+  U.dd = hdr.x;
+  const uint8_t* qv = blk + (kQ5 ? 48 : 16) + 32 * p;
+  const uint4 qa = *reinterpret_cast<const uint4*>(qv);
+  const uint4 qb = *reinterpret_cast<const uint4*>(qv + 16);
+  const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    U.lo[k] = qw[k] & 0x0f0f0f0fu;
+    U.hi[k] = (qw[k] >> 4) & 0x0f0f0f0fu;
+  }
+  if constexpr (kQ5) {
+    // fifth bit of weight i of sub-block j: bit j of byte i of bytes 16 .. 47
+    const uint4 ha = *reinterpret_cast<const uint4*>(blk + 16);
+    const uint4 hb = *reinterpret_cast<const uint4*>(blk + 32);
+    const uint32_t hw[8] = {ha.x, ha.y, ha.z, ha.w, hb.x, hb.y, hb.z, hb.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      U.lo[k] |= ((hw[k] >> (2 * p)) & 0x01010101u) << 4;
+      U.hi[k] |= ((hw[k] >> (2 * p + 1)) & 0x01010101u) << 4;
+    }
+  }
+}
+
+// The unit against one token's Q8_1 blocks 8b + 2p, 8b + 2p + 1 (raw 40-byte
+// blocks at x0, 8-byte aligned): the integer sums D and the blocks' stored
+// sums S and scales.
+struct Q45Dot {
+  int D0, D1, S0, S1;
+  float dx0, dx1;
+};
+__device__ __forceinline__ Q45Dot q45_dot(const Q45Unit& U, const uint8_t* x0p) {
+  const uint2* x0 = reinterpret_cast<const uint2*>(x0p);
+  const uint2* x1 = x0 + kQ8Bytes / 8;
+  uint2 a[5], c[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    a[k] = x0[k];
+    c[k] = x1[k];
+  }
+  const uint32_t xa[8] = {a[0].y, a[1].x, a[1].y, a[2].x, a[2].y, a[3].x, a[3].y, a[4].x};
+  const uint32_t xc[8] = {c[0].y, c[1].x, c[1].y, c[2].x, c[2].y, c[3].x, c[3].y, c[4].x};
+  Q45Dot r;
+  r.D0 = 0;
+  r.D1 = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    r.D0 = dot4(U.lo[k], xa[k], r.D0);
+    r.D1 = dot4(U.hi[k], xc[k], r.D1);
+  }
+  r.S0 = static_cast<int>(a[4].y);
+  r.S1 = static_cast<int>(c[4].y);
+  r.dx0 = h2f(a[0].x & 0xffffu);
+  r.dx1 = h2f(c[0].x & 0xffffu);
+  return r;
+}
+
+// y contribution of a unit and token: dx * (d*sc*D - dmin*m*S) for both sub-blocks.
+__device__ __forceinline__ float q45_term(const Q45Unit& U, const Q45Dot& r) {
+  const float d = h2f(U.dd & 0xffffu), dmin = h2f(U.dd >> 16);
+  return r.dx0 * (d * static_cast<float>(U.sc0) * static_cast<float>(r.D0) -
+                  dmin * static_cast<float>(U.m0) * static_cast<float>(r.S0)) +
+         r.dx1 * (d * static_cast<float>(U.sc1) * static_cast<float>(r.D1) -
+                  dmin * static_cast<float>(U.m1) * static_cast<float>(r.S1));
+}
+
 template <int FMT, bool DEBUG>
 __global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void mmvq_q45k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb, int cb,
@@ -602,68 +681,23 @@ void mmvq_q45k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict_
       else wait_vmcnt<DL::in_flight(2)>();
       const int n = 64 * u + lane, b = n >> 2, p = n & 3;
       if (b < nbc) {  // (a unit round past the segment has no lanes: its waits stay in step)
-        const uint8_t* blk = wl + b * DL::kBytes;
-        const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
-        int sc0, m0, sc1, m1;
-        q4k_scale_min(2 * p, hdr.y, hdr.z, hdr.w, sc0, m0);
-        q4k_scale_min(2 * p + 1, hdr.y, hdr.z, hdr.w, sc1, m1);
-        const uint8_t* qv = blk + (DL::kQ5 ? 48 : 16) + 32 * p;
-        const uint4 qa = *reinterpret_cast<const uint4*>(qv);
-        const uint4 qb = *reinterpret_cast<const uint4*>(qv + 16);
-        const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-        uint32_t lo[8], hi[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          lo[k] = qw[k] & 0x0f0f0f0fu;
-          hi[k] = (qw[k] >> 4) & 0x0f0f0f0fu;
-        }
-        if constexpr (DL::kQ5) {
-          // fifth bit of weight i of sub-block j: bit j of byte i of bytes 16 .. 47
-          const uint4 ha = *reinterpret_cast<const uint4*>(blk + 16);
-          const uint4 hb = *reinterpret_cast<const uint4*>(blk + 32);
-          const uint32_t hw[8] = {ha.x, ha.y, ha.z, ha.w, hb.x, hb.y, hb.z, hb.w};
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            lo[k] |= ((hw[k] >> (2 * p)) & 0x01010101u) << 4;
-            hi[k] |= ((hw[k] >> (2 * p + 1)) & 0x01010101u) << 4;
-          }
-        }
-        // Q8_1 blocks 8b + 2p and 8b + 2p + 1: f16 d, pad, q[32], int32 sum (8-byte aligned)
-        const uint2* x0 = reinterpret_cast<const uint2*>(xl + (8 * b + 2 * p) * kQ8Bytes);
-        const uint2* x1 = x0 + kQ8Bytes / 8;
-        uint2 a[5], c[5];
-#pragma unroll
-        for (int k = 0; k < 5; ++k) {
-          a[k] = x0[k];
-          c[k] = x1[k];
-        }
-        const uint32_t xa[8] = {a[0].y, a[1].x, a[1].y, a[2].x, a[2].y, a[3].x, a[3].y, a[4].x};
-        const uint32_t xc[8] = {c[0].y, c[1].x, c[1].y, c[2].x, c[2].y, c[3].x, c[3].y, c[4].x};
-        int D0 = 0, D1 = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          D0 = dot4(lo[k], xa[k], D0);
-          D1 = dot4(hi[k], xc[k], D1);
-        }
-        const int S0 = static_cast<int>(a[4].y), S1 = static_cast<int>(c[4].y);
+        Q45Unit U;
+        q45_unit<FMT>(wl + b * DL::kBytes, p, U);
+        // Q8_1 blocks 8b + 2p and 8b + 2p + 1: f16 d, pad, q[32], int32 sum
+        const Q45Dot r = q45_dot(U, xl + (8 * b + 2 * p) * kQ8Bytes);
         if constexpr (DEBUG) {
           const int sb = (b0 + b) * 8 + 2 * p;
           if (row_ok) {
             int32_t* Dr = dbgD + static_cast<size_t>(row) * (nb * 8);
-            Dr[sb] = D0;
-            Dr[sb + 1] = D1;
+            Dr[sb] = r.D0;
+            Dr[sb + 1] = r.D1;
           }
           if (row_raw == 0) {
-            dbgS[sb] = S0;
-            dbgS[sb + 1] = S1;
+            dbgS[sb] = r.S0;
+            dbgS[sb + 1] = r.S1;
           }
         } else {
-          const float d = h2f(hdr.x & 0xffffu), dmin = h2f(hdr.x >> 16);
-          const float dx0 = h2f(a[0].x & 0xffffu), dx1 = h2f(c[0].x & 0xffffu);
-          acc += dx0 * (d * static_cast<float>(sc0) * static_cast<float>(D0) -
-                        dmin * static_cast<float>(m0) * static_cast<float>(S0)) +
-                 dx1 * (d * static_cast<float>(sc1) * static_cast<float>(D1) -
-                        dmin * static_cast<float>(m1) * static_cast<float>(S1));
+          acc += q45_term(U, r);
         }
       }
     }
@@ -700,6 +734,132 @@ static int launch_mmvq_t1(const void* w, const void* xq, float* y, int M, int nb
   return launch_status();
 }
 
+// Two to four tokens, Q4_K: the one-token design with one 16-wave workgroup
+// per CU, so the T tokens' raw activation blocks (13.8 KB per token at
+// K = 11008) are copied once per CU.  To fit them beside sixteen row
+// segments, a wave's copies write only the row's own bytes: the copies past
+// the segment are issued with their lanes masked off (a copy with no byte
+// left keeps lane 0 on a 16-byte dummy slot, so every wave issues the same
+// number of copies and the vmcnt waits stay exact).  Each lane decodes its
+// unit once and multiplies it with every token.
+constexpr int kTnWaves = 16;
+constexpr int kTnMaxBlocks = 48;  // three unit rounds
+constexpr int kTnRounds = 7;      // 1 KB copies per wave per segment (48 * 144 <= 7 KB)
+constexpr int kLdsMax = 160 * 1024;
+
+static int tn_max_blocks(int T) {
+  const int by_lds = (kLdsMax - kTnWaves * 16) / (kTnWaves * kQ4Bytes + T * 8 * kQ8Bytes);
+  return by_lds < kTnMaxBlocks ? by_lds : kTnMaxBlocks;
+}
+
+template <int T, bool DEBUG>
+__global__ __launch_bounds__(64 * kTnWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void mmvq_q4k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb, int cb,
+                        int32_t* __restrict__ dbgD, int32_t* __restrict__ dbgS) {
+  using DL = MvDma<QMM_Q4_K>;
+  static_assert(kTnRounds == DL::kRounds && kTnMaxBlocks == DL::kMaxBlocks, "unit-round waits");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row_raw = blockIdx.x * kTnWaves + wave;
+  const bool row_ok = row_raw < M;
+  const int row = row_ok ? row_raw : M - 1;  // out-of-range waves read a valid row, store nothing
+  const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
+  const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ4Bytes;
+  const int wreg = cb * kQ4Bytes;                                      // bytes per wave region
+  const uint8_t* wl = lds + wave * wreg;
+  const uint8_t* xl = lds + kTnWaves * wreg;                           // T tokens' raw Q8_1 blocks
+  const uint32_t wl_a = lds_addr(wl), xl_a = lds_addr(xl);
+  const uint32_t dummy_a = lds_addr(lds + kTnWaves * wreg + T * cb * 8 * kQ8Bytes) + 16 * wave;
+  float acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+  for (int b0 = 0; b0 < nb; b0 += cb) {
+    const int nbc = min(cb, nb - b0);
+    if (b0 > 0) __syncthreads();  // every wave is done with the previous segment's copies
+    // 1. the activation blocks of the segment, token after token (nbc * 320 bytes each)
+    const int tseg = nbc * (DL::kQ8Seg / 16), xs = T * tseg;  // 16-byte slots
+    for (int i = wave; 64 * i < xs; i += kTnWaves) {
+      const int sl = 64 * i + lane;
+      if (sl < xs) {
+        const int t = sl / tseg, j = sl - t * tseg;
+        dma16(xq + t * xstride + static_cast<size_t>(b0) * DL::kQ8Seg + 16 * j, xl_a + 1024 * i);
+      }
+    }
+    // 2. the row segment: lanes past its end are masked off
+    const int nch = nbc * (kQ4Bytes / 16);
+    const uint8_t* wseg = wrow + static_cast<size_t>(b0) * kQ4Bytes;
+#pragma unroll
+    for (int r = 0; r < kTnRounds; ++r) {
+      const bool full = 64 * r < nch;
+      if (full ? 64 * r + lane < nch : lane == 0)
+        dma16<true>(wseg + 16 * min(64 * r + lane, nch - 1), full ? wl_a + 1024 * r : dummy_a);
+    }
+    // 3. this wave's activation copies (issued first) are done; then everyone's
+    wait_vmcnt<kTnRounds>();
+    __syncthreads();
+    // 4. unit rounds
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      if (u == 0) wait_vmcnt<DL::in_flight(0)>();  // (u is a constant once unrolled)
+      else if (u == 1) wait_vmcnt<DL::in_flight(1)>();
+      else wait_vmcnt<DL::in_flight(2)>();
+      const int n = 64 * u + lane, b = n >> 2, p = n & 3;
+      if (b < nbc) {
+        Q45Unit U;
+        q45_unit<QMM_Q4_K>(wl + b * kQ4Bytes, p, U);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const Q45Dot r = q45_dot(U, xl + t * (nbc * DL::kQ8Seg) + (8 * b + 2 * p) * kQ8Bytes);
+          if constexpr (DEBUG) {
+            const int sb = (b0 + b) * 8 + 2 * p;
+            if (row_ok) {
+              int32_t* Dr = dbgD + (static_cast<size_t>(t) * M + row) * (nb * 8);
+              Dr[sb] = r.D0;
+              Dr[sb + 1] = r.D1;
+            }
+            if (row_raw == 0) {
+              dbgS[static_cast<size_t>(t) * nb * 8 + sb] = r.S0;
+              dbgS[static_cast<size_t>(t) * nb * 8 + sb + 1] = r.S1;
+            }
+          } else {
+            acc[t] += q45_term(U, r);
+          }
+        }
+      }
+    }
+    wait_vmcnt<0>();  // nothing may still write LDS when it is reused or the workgroup ends
+  }
+  if constexpr (!DEBUG) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0 && row_ok) y[static_cast<size_t>(t) * M + row] = s;
+    }
+  }
+}
+
+template <int T, bool DEBUG>
+static int launch_mmvq_q4k_tn(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, int32_t* S,
+                              hipStream_t st) {
+  const int cmax = tn_max_blocks(T);
+  const int nseg = (nb + cmax - 1) / cmax;
+  const int cb = (nb + nseg - 1) / nseg;
+  const size_t lds = static_cast<size_t>(kTnWaves) * cb * kQ4Bytes + static_cast<size_t>(T) * cb * 8 * kQ8Bytes +
+                     kTnWaves * 16;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q4k_tn_kernel<T, DEBUG>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess)
+      return QMM_ERR_HIP;
+    attr_set = true;
+  }
+  const dim3 grid((M + kTnWaves - 1) / kTnWaves), block(64 * kTnWaves);
+  hipLaunchKernelGGL((mmvq_q4k_tn_kernel<T, DEBUG>), grid, block, lds, st, static_cast<const uint8_t*>(w),
+                     static_cast<const uint8_t*>(xq), y, M, nb, cb, D, S);
+  return launch_status();
+}
+
 static size_t mmvq_lds_bytes(int T, int cb) { return static_cast<size_t>(T) * cb * 8 * 48; }
 
 template <bool DEBUG, int FMT = QMM_Q4_K>
@@ -715,6 +875,11 @@ static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int n
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const uint8_t* xp = static_cast<const uint8_t*>(xq);
   if (!slots && T == 1) return launch_mmvq_t1<FMT, DEBUG>(w, xq, y, M, nb, D, S, st);
+  if constexpr (FMT == QMM_Q4_K) {
+    if (!slots && T == 2) return launch_mmvq_q4k_tn<2, DEBUG>(w, xq, y, M, nb, D, S, st);
+    if (!slots && T == 3) return launch_mmvq_q4k_tn<3, DEBUG>(w, xq, y, M, nb, D, S, st);
+    if (!slots && T == 4) return launch_mmvq_q4k_tn<4, DEBUG>(w, xq, y, M, nb, D, S, st);
+  }
   if (slots) {
     if (DEBUG || T != 1) return QMM_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((mmvq_q45k_kernel<FMT, 1, false, true>), dim3(grid.x, nslots), block, lds, st, wp, xp, y,
