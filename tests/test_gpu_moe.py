@@ -39,9 +39,10 @@ def test_per_slot_parity(fmt, E, M, K, T, top_k):
 
 
 # Larger routings than the cases above (several id batches per wave of the
-# route preparation, thousands of slots per call), and the largest expert
-# count the route tables hold (512).
-@pytest.mark.parametrize("E,T,top_k", [(8, 768, 8), (16, 6145, 1), (32, 1700, 4), (512, 300, 4)])
+# route preparation, thousands of slots per call; above 8192 slots a wave's
+# slots take more than one batch and are ranked in the second pass), and the
+# largest expert count the route tables hold (512).
+@pytest.mark.parametrize("E,T,top_k", [(8, 768, 8), (16, 6145, 1), (32, 1700, 4), (512, 300, 4), (8, 2100, 4)])
 def test_route_many_slots(E, T, top_k):
     M, K = 40, 256
     g = qmm_synth.rng(E * T + top_k)
