@@ -30,7 +30,9 @@ CASES = [(1, 256, 1), (7, 512, 3), (37, 1280, 8), (64, 2304, 4), (5, 256, 2), (1
          (8, 9728, 1), (24, 9984, 1), (16, 11776, 1), (8, 768, 1), (9, 11008, 1),
          # two to four tokens, Q4_K rows copied into LDS by 16-row workgroups: rows of one and
          # two segments, a single super-block, a partial last workgroup
-         (33, 14336, 4), (17, 12288, 2), (19, 11776, 3), (3, 256, 4)]
+         (33, 14336, 4), (17, 12288, 2), (19, 11776, 3), (3, 256, 4),
+         # two to four tokens, Q6_K rows split between 16-row LDS copies and registers
+         (16, 11008, 4), (24, 7168, 2), (8, 9728, 3), (40, 6144, 4)]
 
 
 def _inputs(fmt, M, K, T, seed):
@@ -64,7 +66,7 @@ def test_end_to_end_from_fp32(fmt):
 @pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,K,T", [(3, 256, 1), (9, 768, 4), (17, 512, 5), (21, 768, 6), (33, 1024, 8),
                                    (13, 12544, 1), (10, 11008, 1), (16, 11008, 1), (8, 11776, 1),
-                                   (21, 14336, 2), (18, 11008, 3)])
+                                   (21, 14336, 2), (18, 11008, 3), (16, 11008, 4), (8, 7424, 2)])
 def test_integer_stage_bit_exact(fmt, M, K, T):
     w, x, xq = _inputs(fmt, M, K, T, seed=7 * M + T)
     say(f"debug_subdots path=0 {fmt}", f"M={M} K={K} T={T}")
