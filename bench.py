@@ -484,10 +484,12 @@ def main():
                 xqT = qmm.q8_1_quantize(xs[:T_].contiguous())
                 yT = torch.empty((T_, M), dtype=torch.float32, device=dev)
                 wsT = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MMQ, M, K, T_), dev)
-                mq_us.append(round(time_graph(torch, [lambda c=c: mq(ws_[c], xqT, out=yT, ws=wsT)
-                                                      for c in range(R)], 200) * 1e3, 2))
+                # the matvec before the GEMM (timed right after 200 GEMM launches the T = 1
+                # matvec read 1.3 us slower than in its own row above)
                 mv_us.append(round(time_graph(torch, [lambda c=c: mv(ws_[c], xqT, out=yT) for c in range(R)], 200)
                                    * 1e3, 2) if T_ <= qmm.QMM_MMVQ_MAX_T else None)
+                mq_us.append(round(time_graph(torch, [lambda c=c: mq(ws_[c], xqT, out=yT, ws=wsT)
+                                                      for c in range(R)], 200) * 1e3, 2))
             sweep[f"mmvq_{key}_us"] = mv_us
             sweep[f"mmq_{key}_us"] = mq_us
             sweep[f"best_{key}_GBps"] = [gbps(nbw, min(u for u in (a_, b_) if u is not None) * 1e-3)
