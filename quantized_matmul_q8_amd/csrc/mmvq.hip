@@ -912,23 +912,33 @@ static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int n
 // The signed values q6 - 32 are formed with a byte table lookup on the two
 // high bits, so no activation sum is needed.  Blocks sit at 2-byte aligned
 // LDS offsets: 16-byte pieces are read as aligned dwords and shifted.
+//
+// The activations are copied in the order the lanes read them, with
+// dword copies (global_load_lds_dword) whose lanes gather from the Q8_1
+// blocks: for k = 0 .. 3, unit n's 16 values at X_k + 16n, and the four f16
+// block scales (with the pad beside each) at DX + 16n.  Each read is then
+// one 16-byte LDS load by consecutive lanes at consecutive addresses; read in
+// place from the raw 40-byte blocks, the four dwords of every unit fell in 8
+// of the 32 banks and took twice as long.  sc * D is an integer product
+// (|D| <= 16 * 32 * 127) and the f16 scales enter the fma directly.
 constexpr int kQ6T1Rounds = 8;     // 1 KB copies per wave (its LDS region)
 constexpr int kQ6T1ABlocks = 38;   // super-blocks always inside the copies
 constexpr int kQ6T1MaxBlocks = 46; // + at most 8 in registers (2 chunks per lane)
 
-// 16 bytes at a 2-byte aligned LDS address (the fifth dword read is inside
-// the LDS allocation: every caller's piece ends at least 4 bytes before the
-// end of its block or region).
-__device__ __forceinline__ uint4 lds16_a2(const uint8_t* p) {
-  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
-  const uint32_t* a = reinterpret_cast<const uint32_t*>(p - sh);
+// Activation bytes of a row of nb super-blocks in unit order: G groups of 16
+// units, five 256-byte copies per group (X_0 .. X_3, DX).
+__host__ __device__ constexpr int q6t1_groups(int nb) { return (nb + 3) / 4; }
+__host__ __device__ constexpr int q6t1_act_bytes(int nb) { return 5 * 256 * q6t1_groups(nb); }
+
+// 16 (8) bytes that start sh bytes past the dword-aligned LDS address a (the
+// fifth (third) dword read is inside the LDS allocation: every caller's piece
+// ends at least 4 bytes before the end of its block or region).
+__device__ __forceinline__ uint4 lds16_sh(const uint32_t* a, uint32_t sh) {
   const uint32_t w0 = a[0], w1 = a[1], w2 = a[2], w3 = a[3], w4 = a[4];
   return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh),
                     __builtin_amdgcn_alignbyte(w3, w2, sh), __builtin_amdgcn_alignbyte(w4, w3, sh));
 }
-__device__ __forceinline__ uint2 lds8_a2(const uint8_t* p) {
-  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
-  const uint32_t* a = reinterpret_cast<const uint32_t*>(p - sh);
+__device__ __forceinline__ uint2 lds8_sh(const uint32_t* a, uint32_t sh) {
   const uint32_t w0 = a[0], w1 = a[1], w2 = a[2];
   return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));
 }
@@ -948,12 +958,19 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
   const uint8_t* a0 = w + (row_off - shift);                          // 16-byte aligned
   const int nch = (shift + nb * kQ6Bytes + 15) >> 4;                   // aligned chunks covering the row
   const int cb0 = (shift + kQ6T1ABlocks * kQ6Bytes) >> 4;              // first chunk held in registers
+  const int G = q6t1_groups(nb);
   uint8_t* wl = lds + wave * kQ6T1Rounds * 1024;                       // this wave's region
-  const uint8_t* xl = lds + kMmvqWaves * kQ6T1Rounds * 1024;           // raw Q8_1 blocks of the row
+  const uint8_t* xl = lds + kMmvqWaves * kQ6T1Rounds * 1024;           // activations in unit order
   const uint32_t wl_a = lds_addr(wl), xl_a = lds_addr(xl);
-  // 1. the activation blocks (nb * 320 contiguous bytes), copies i = wave + 8k
-  const int xs = nb * 20;
-  for (int i = wave; 64 * i < xs; i += kMmvqWaves) dma16(xq + 16 * min(64 * i + lane, xs - 1), xl_a + 1024 * i);
+  // 1. the activations: group g (units 16g .. 16g + 15) by wave g % 8; lane l
+  //    carries dword l % 4 of unit 16g + l / 4 (units past the row repeat the last)
+  for (int g = wave; g < G; g += kMmvqWaves) {
+    const int nc = min(16 * g + (lane >> 2), 4 * nb - 1);
+    const uint8_t* src = xq + (8 * (nc >> 2) + 4 * ((nc >> 1) & 1)) * kQ8Bytes;  // block 8b + 4h
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dma4(src + k * kQ8Bytes + 4 + 16 * (nc & 1) + 4 * (lane & 3), xl_a + 256 * (G * k + g));
+    dma4(src + (lane & 3) * kQ8Bytes, xl_a + 256 * (4 * G + g));  // block 8b + 4h + l % 4: f16 d + pad
+  }
   // 2. chunks 0 .. 511 of the row into the region (chunks past the row re-read its last one)
 #pragma unroll
   for (int r = 0; r < kQ6T1Rounds; ++r) dma16<true>(a0 + 16 * min(64 * r + lane, nch - 1), wl_a + 1024 * r);
@@ -979,18 +996,24 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
     if (b < nb) {
       const int vb = shift + b * kQ6Bytes;
       const uint8_t* blk = wl + (b < kQ6T1ABlocks ? vb : vb - 16 * cb0);
-      const uint4 pa = lds16_a2(blk + 64 * h + 16 * q);        // ql, k = 0 (low) and 2 (high nibbles)
-      const uint4 pb = lds16_a2(blk + 64 * h + 32 + 16 * q);   // ql, k = 1 and 3
-      const uint4 ph = lds16_a2(blk + 128 + 32 * h + 16 * q);  // qh: bits 2k, 2k + 1 for k = 0 .. 3
-      const uint2 sc8 = lds8_a2(blk + 192 + 8 * h);            // sc[8h .. 8h + 7]
-      const float d = h2f(*reinterpret_cast<const uint16_t*>(blk + 208));
+      // every piece sits a multiple of 4 bytes into the block: one shift for all
+      const uint32_t sh = static_cast<uint32_t>(vb) & 3u;
+      const uint32_t* ba = reinterpret_cast<const uint32_t*>(blk - sh);
+      const uint4 pa = lds16_sh(ba + 16 * h + 4 * q, sh);      // ql[64h + 16q ..]: k = 0 (low), 2 (high nibbles)
+      const uint4 pb = lds16_sh(ba + 16 * h + 8 + 4 * q, sh);  // ql[64h + 32 + 16q ..]: k = 1 and 3
+      const uint4 ph = lds16_sh(ba + 32 + 8 * h + 4 * q, sh);  // qh[32h + 16q ..]: bits 2k, 2k + 1
+      const uint2 sc8 = lds8_sh(ba + 48 + 2 * h, sh);          // sc[8h .. 8h + 7]: k's scale is byte 2k + q
+      const uint32_t scx = sc8.x >> (8 * q), scy = sc8.y >> (8 * q);
+      const uint4 dxw = *reinterpret_cast<const uint4*>(xl + 256 * 4 * G + 16 * n);
+      const uint32_t dx[4] = {dxw.x, dxw.y, dxw.z, dxw.w};
       const uint32_t qa[4] = {pa.x, pa.y, pa.z, pa.w}, qb[4] = {pb.x, pb.y, pb.z, pb.w};
       const uint32_t qh[4] = {ph.x, ph.y, ph.z, ph.w};
+      float accu = 0.0f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        // half q of Q8_1 block 8b + 4h + k: f16 d at 0, values 16q .. 16q + 15 at 4 + 16q
-        const uint8_t* xb = xl + (8 * b + 4 * h + k) * kQ8Bytes;
-        const uint32_t* xv = reinterpret_cast<const uint32_t*>(xb + 4 + 16 * q);
+        // half q of Q8_1 block 8b + 4h + k
+        const uint4 xw = *reinterpret_cast<const uint4*>(xl + 256 * G * k + 16 * n);
+        const uint32_t xv[4] = {xw.x, xw.y, xw.z, xw.w};
         int D = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -999,14 +1022,14 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
           const uint32_t v = (lo & 0x0f0f0f0fu) | __builtin_amdgcn_perm(kQ6HiTable, kQ6HiTable, hi);
           D = dot4(v, xv[i], D);
         }
-        const int sc = static_cast<int8_t>((((k >> 1) ? sc8.y : sc8.x) >> (8 * (q + 2 * (k & 1)))) & 0xffu);
+        const int sc = static_cast<int8_t>(((k < 2) ? scx : scy) >> (16 * (k & 1)));
         if constexpr (DEBUG) {
           if (row_ok) dbgD[static_cast<size_t>(row) * (nb * 16) + 16 * b + 8 * h + 2 * k + q] = D;
         } else {
-          const float dx = h2f(*reinterpret_cast<const uint16_t*>(xb));
-          acc += dx * (d * static_cast<float>(sc)) * static_cast<float>(D);
+          accu = fmaf(h2f(dx[k]), static_cast<float>(__mul24(sc, D)), accu);
         }
       }
+      if constexpr (!DEBUG) acc = fmaf(h2f(*reinterpret_cast<const uint16_t*>(blk + 208)), accu, acc);
     }
   }
   wait_vmcnt<0>();
@@ -1018,12 +1041,10 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
 
 template <bool DEBUG>
 static int launch_mmvq_q6k_t1(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, hipStream_t st) {
-  const size_t lds = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 +
-                     (static_cast<size_t>(nb) * 8 * kQ8Bytes + 1023) / 1024 * 1024;
+  const size_t lds = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 + q6t1_act_bytes(nb);
   static bool attr_set = false;
   if (!attr_set) {
-    const size_t lmax = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 +
-                        (static_cast<size_t>(kQ6T1MaxBlocks) * 8 * kQ8Bytes + 1023) / 1024 * 1024;
+    const size_t lmax = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 + q6t1_act_bytes(kQ6T1MaxBlocks);
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q6k_t1_kernel<DEBUG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lmax)) != hipSuccess)
       return QMM_ERR_HIP;

@@ -148,6 +148,19 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
   }
 }
 
+// 4 bytes per lane from global memory into LDS at lds + 4 * lane
+// (global_load_lds_dword), the same way as dma16: lanes may gather from any
+// addresses, so one instruction can rearrange 256 bytes into LDS order.
+__device__ __forceinline__ void dma4(const uint8_t* src, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  __asm__ volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\t"
+                   "s_mov_b32 m0, %0"
+                   : "=&s"(saved)
+                   : "v"(src), "s"(m0v)
+                   : "memory");
+}
+
 // Wait until at most N of this wave's vector memory operations (loads,
 // stores, the copies above) are outstanding; they complete in issue order.
 template <int N>
