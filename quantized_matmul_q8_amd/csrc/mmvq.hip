@@ -925,6 +925,12 @@ constexpr int kQ6T1Rounds = 8;     // 1 KB copies per wave (its LDS region)
 constexpr int kQ6T1ABlocks = 38;   // super-blocks always inside the copies
 constexpr int kQ6T1MaxBlocks = 46; // + at most 8 in registers (2 chunks per lane)
 
+// Weight copies issued before the workgroup's activation barrier; the rest
+// follow it.  Issuing all of them first let the CU's first workgroup take
+// all its bytes before the second got any, leaving the second's whole
+// compute after the last arrival.
+constexpr int kQ6T1Early = 5;
+
 // Activation bytes of a row of nb super-blocks in unit order: G groups of 16
 // units, five 256-byte copies per group (X_0 .. X_3, DX).
 __host__ __device__ constexpr int q6t1_groups(int nb) { return (nb + 3) / 4; }
@@ -971,15 +977,18 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
     for (int k = 0; k < 4; ++k) dma4(src + k * kQ8Bytes + 4 + 16 * (nc & 1) + 4 * (lane & 3), xl_a + 256 * (G * k + g));
     dma4(src + (lane & 3) * kQ8Bytes, xl_a + 256 * (4 * G + g));  // block 8b + 4h + l % 4: f16 d + pad
   }
-  // 2. chunks 0 .. 511 of the row into the region (chunks past the row re-read its last one)
+  // 2. the first copies of the row into the region (chunks past the row re-read its last one)
 #pragma unroll
-  for (int r = 0; r < kQ6T1Rounds; ++r) dma16<true>(a0 + 16 * min(64 * r + lane, nch - 1), wl_a + 1024 * r);
-  // 3. chunks cb0 .. cb0 + 127 into registers (clamped the same way)
+  for (int r = 0; r < kQ6T1Early; ++r) dma16<true>(a0 + 16 * min(64 * r + lane, nch - 1), wl_a + 1024 * r);
+  // 3. this wave's activation copies (issued first) are done; then everyone's
+  wait_vmcnt<kQ6T1Early>();
+  __syncthreads();
+  // 4. the rest of the row: the remaining copies, then chunks cb0 .. cb0 + 127
+  //    into registers (clamped the same way)
+#pragma unroll
+  for (int r = kQ6T1Early; r < kQ6T1Rounds; ++r) dma16<true>(a0 + 16 * min(64 * r + lane, nch - 1), wl_a + 1024 * r);
   const uint4 rb0 = ld16_nt(a0 + 16 * min(cb0 + lane, nch - 1));
   const uint4 rb1 = ld16_nt(a0 + 16 * min(cb0 + 64 + lane, nch - 1));
-  // 4. this wave's activation copies (issued first) are done; then everyone's
-  wait_vmcnt<kQ6T1Rounds + 2>();
-  __syncthreads();
   float acc = 0.0f;
 #pragma unroll
   for (int u = 0; u < 3; ++u) {
