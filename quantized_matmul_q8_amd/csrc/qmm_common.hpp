@@ -175,10 +175,27 @@ __device__ __forceinline__ void wait_vmcnt() {
 constexpr uint32_t kQ6HiTable = 0x1000F0E0u;  // bytes -32, -16, 0, 16 as int8
 
 // Wave64 reductions.
+// Sum over the 64 lanes (all active), returned in every lane: inclusive
+// prefix sums inside each 16-lane row by DPP row shifts (lanes shifted in
+// from outside the row read 0), so lane 15 of each row holds the row's sum;
+// the four row sums are then read out and added in row order.  No LDS
+// traffic (a butterfly of lane shuffles takes six LDS-crossbar round trips).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true);
+  return v + __builtin_bit_cast(float, s);
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = dpp_add<0x111>(v);  // row_shr:1
+  v = dpp_add<0x112>(v);  // row_shr:2
+  v = dpp_add<0x114>(v);  // row_shr:4
+  v = dpp_add<0x118>(v);  // row_shr:8
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 47));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // Quantize one 32-activation block to Q8_1 with eight consecutive lanes.
