@@ -198,6 +198,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// A value from another lane of the same group of eight, by DPP (no LDS
+// crossbar): CTRL 0xb1 and 0x4e are the quad permutations lane ^ 1 and
+// lane ^ 2, 0x141 mirrors each half-row (lane i of an 8-lane group takes lane
+// 7 - i, in the other quad).  Used where the group's values are all equal
+// within each quad, so the mirror acts as lane ^ 4.
+template <int CTRL>
+__device__ __forceinline__ float lane8_xchg(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int lane8_xchg(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+
 // Quantize one 32-activation block to Q8_1 with eight consecutive lanes.
 // Lane `part` (0..7) holds x[4*part .. 4*part+3]; all eight lanes must be
 // active (they exchange values).  Steps of [8e] §3.2 (max |x|, d = am/127,
@@ -209,9 +223,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ void q8_1_block_8lanes_vals(float4 v, uint32_t& packed, float& d, int& s) {
 #pragma clang fp contract(off)
   float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  am = fmaxf(am, __shfl_xor(am, 1));
-  am = fmaxf(am, __shfl_xor(am, 2));
-  am = fmaxf(am, __shfl_xor(am, 4));
+  am = fmaxf(am, lane8_xchg<0xb1>(am));   // quad_perm [1, 0, 3, 2]: lane ^ 1
+  am = fmaxf(am, lane8_xchg<0x4e>(am));   // quad_perm [2, 3, 0, 1]: lane ^ 2
+  am = fmaxf(am, lane8_xchg<0x141>(am));  // row_half_mirror: the other quad of the 8
   d = am / 127.0f;
   // a subnormal scale counts as zero (its reciprocal may overflow and its
   // f16 rounding is 0): the block is stored as zeros
@@ -223,9 +237,9 @@ __device__ __forceinline__ void q8_1_block_8lanes_vals(float4 v, uint32_t& packe
   packed = (static_cast<uint32_t>(q0) & 255u) | ((static_cast<uint32_t>(q1) & 255u) << 8) |
            ((static_cast<uint32_t>(q2) & 255u) << 16) | (static_cast<uint32_t>(q3) << 24);
   s = q0 + q1 + q2 + q3;
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 4);
+  s += lane8_xchg<0xb1>(s);
+  s += lane8_xchg<0x4e>(s);
+  s += lane8_xchg<0x141>(s);
 }
 
 // The same, stored as the block's 40 bytes at dst (4-byte aligned; nothing
