@@ -632,6 +632,31 @@ __device__ __forceinline__ Q45Dot q45_dot(const Q45Unit& U, const uint8_t* x0p) 
   return r;
 }
 
+// The same reading the two blocks (80 bytes at xu, 16-byte aligned) as five
+// 16-byte chunks: block 2p has d at byte 0, values at 4 .. 35 and its sum at
+// 36, block 2p + 1 the same 40 bytes on.  Consecutive units are 80 bytes
+// apart, so eight lanes' chunks cover all 32 banks (the 8-byte reads of
+// q45_dot hit each bank twice).
+__device__ __forceinline__ Q45Dot q45_dot_c(const Q45Unit& U, const uint8_t* xu) {
+  const uint4* c = reinterpret_cast<const uint4*>(xu);
+  const uint4 c0 = c[0], c1 = c[1], c2 = c[2], c3 = c[3], c4 = c[4];
+  const uint32_t xa[8] = {c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w, c2.x};
+  const uint32_t xc[8] = {c2.w, c3.x, c3.y, c3.z, c3.w, c4.x, c4.y, c4.z};
+  Q45Dot r;
+  r.D0 = 0;
+  r.D1 = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    r.D0 = dot4(U.lo[k], xa[k], r.D0);
+    r.D1 = dot4(U.hi[k], xc[k], r.D1);
+  }
+  r.S0 = static_cast<int>(c2.y);
+  r.S1 = static_cast<int>(c4.w);
+  r.dx0 = h2f(c0.x & 0xffffu);
+  r.dx1 = h2f(c2.z & 0xffffu);
+  return r;
+}
+
 // y contribution of a unit and token: dx * (d*sc*D - dmin*m*S) for both sub-blocks.
 __device__ __forceinline__ float q45_term(const Q45Unit& U, const Q45Dot& r) {
   const float d = h2f(U.dd & 0xffffu), dmin = h2f(U.dd >> 16);
@@ -684,7 +709,7 @@ void mmvq_q45k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict_
         Q45Unit U;
         q45_unit<FMT>(wl + b * DL::kBytes, p, U);
         // Q8_1 blocks 8b + 2p and 8b + 2p + 1: f16 d, pad, q[32], int32 sum
-        const Q45Dot r = q45_dot(U, xl + (8 * b + 2 * p) * kQ8Bytes);
+        const Q45Dot r = q45_dot_c(U, xl + (8 * b + 2 * p) * kQ8Bytes);
         if constexpr (DEBUG) {
           const int sb = (b0 + b) * 8 + 2 * p;
           if (row_ok) {
