@@ -770,6 +770,7 @@ static int launch_mmvq_t1(const void* w, const void* xq, float* y, int M, int nb
 constexpr int kTnWaves = 16;
 constexpr int kTnMaxBlocks = 48;  // three unit rounds
 constexpr int kTnRounds = 7;      // 1 KB copies per wave per segment (48 * 144 <= 7 KB)
+constexpr int kTnEarly = 4;       // of them issued before the activation barrier (measured 3 .. 5)
 constexpr int kLdsMax = 160 * 1024;
 
 static int tn_max_blocks(int T) {
@@ -814,15 +815,19 @@ void mmvq_q4k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
     // 2. the row segment: lanes past its end are masked off
     const int nch = nbc * (kQ4Bytes / 16);
     const uint8_t* wseg = wrow + static_cast<size_t>(b0) * kQ4Bytes;
-#pragma unroll
-    for (int r = 0; r < kTnRounds; ++r) {
+    auto copy_round = [&](int r) {
       const bool full = 64 * r < nch;
       if (full ? 64 * r + lane < nch : lane == 0)
         dma16<true>(wseg + 16 * min(64 * r + lane, nch - 1), full ? wl_a + 1024 * r : dummy_a);
-    }
-    // 3. this wave's activation copies (issued first) are done; then everyone's
-    wait_vmcnt<kTnRounds>();
+    };
+#pragma unroll
+    for (int r = 0; r < kTnEarly; ++r) copy_round(r);
+    // 3. this wave's activation copies (issued first) are done; then everyone's;
+    //    then the rest of the row segment
+    wait_vmcnt<kTnEarly>();
     __syncthreads();
+#pragma unroll
+    for (int r = kTnEarly; r < kTnRounds; ++r) copy_round(r);
     // 4. unit rounds
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
@@ -835,7 +840,7 @@ void mmvq_q4k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
         q45_unit<QMM_Q4_K>(wl + b * kQ4Bytes, p, U);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          const Q45Dot r = q45_dot(U, xl + t * (nbc * DL::kQ8Seg) + (8 * b + 2 * p) * kQ8Bytes);
+          const Q45Dot r = q45_dot_c(U, xl + t * (nbc * DL::kQ8Seg) + (8 * b + 2 * p) * kQ8Bytes);
           if constexpr (DEBUG) {
             const int sb = (b0 + b) * 8 + 2 * p;
             if (row_ok) {
