@@ -1095,6 +1095,160 @@ static int launch_mmvq_q6k_t1(const void* w, const void* xq, float* y, int M, in
   return launch_status();
 }
 
+// Two to four tokens, Q6_K: the one-token Q6_K design with one 16-wave
+// workgroup per CU, so the T tokens' activations (gathered in unit order,
+// 14 KB per token at K = 11008) are copied once per CU.  To fit them beside
+// sixteen rows, a wave copies the first 6 KB of its row (super-blocks 0 .. 28
+// for any shift) into its LDS region and loads the rest (at most 14 more
+// super-blocks) as three 16-byte register chunks per lane, written over the
+// region's first 3 KB once unit round 0 (super-blocks 0 .. 15) is done.  Each
+// lane forms its unit's 64 signed values once and multiplies them with every
+// token.
+constexpr int kQ6TnWaves = 16;
+constexpr int kQ6TnRounds = 6;      // 1 KB copies per wave (its LDS region)
+constexpr int kQ6TnEarly = 4;       // of them issued before the activation barrier
+constexpr int kQ6TnABlocks = 29;    // super-blocks always inside the copies
+constexpr int kQ6TnMaxBlocks = 43;  // + at most 14 in the register chunks
+static_assert(kQ6TnWaves * kQ6TnRounds * 1024 + 4 * q6t1_act_bytes(kQ6TnMaxBlocks) <= 160 * 1024,
+              "sixteen row regions and four tokens");
+
+template <int T, bool DEBUG>
+__global__ __launch_bounds__(64 * kQ6TnWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void mmvq_q6k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb,
+                        int32_t* __restrict__ dbgD) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row_raw = blockIdx.x * kQ6TnWaves + wave;
+  const bool row_ok = row_raw < M;
+  const int row = row_ok ? row_raw : M - 1;  // out-of-range waves read a valid row, store nothing
+  const size_t row_off = static_cast<size_t>(row) * nb * kQ6Bytes;
+  const int shift = static_cast<int>(row_off & 15u);
+  const uint8_t* a0 = w + (row_off - shift);                          // 16-byte aligned
+  const int nch = (shift + nb * kQ6Bytes + 15) >> 4;                   // aligned chunks covering the row
+  const int cb0 = (shift + kQ6TnABlocks * kQ6Bytes) >> 4;              // first chunk held in registers
+  const int G = q6t1_groups(nb);
+  const int tb = q6t1_act_bytes(nb);                                   // activation bytes per token
+  uint8_t* wl = lds + wave * kQ6TnRounds * 1024;                       // this wave's region
+  const uint8_t* xl = lds + kQ6TnWaves * kQ6TnRounds * 1024;           // activations in unit order
+  const uint32_t wl_a = lds_addr(wl), xl_a = lds_addr(xl);
+  const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
+  // 1. the activations of token t, group g (units 16g .. 16g + 15), pair c = t * G + g by
+  //    wave c % 16: the layout of the one-token kernel, token t at xl + t * tb
+  for (int c = wave; c < T * G; c += kQ6TnWaves) {
+    const int t = c / G, g = c - t * G;
+    const int nc = min(16 * g + (lane >> 2), 4 * nb - 1);
+    const uint8_t* src = xq + t * xstride + (8 * (nc >> 2) + 4 * ((nc >> 1) & 1)) * kQ8Bytes;
+    const uint32_t dst = xl_a + t * tb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dma4(src + k * kQ8Bytes + 4 + 16 * (nc & 1) + 4 * (lane & 3), dst + 256 * (G * k + g));
+    dma4(src + (lane & 3) * kQ8Bytes, dst + 256 * (4 * G + g));
+  }
+  // 2. the first copies of the row (chunks past the row re-read its last one)
+#pragma unroll
+  for (int r = 0; r < kQ6TnEarly; ++r) dma16<true>(a0 + 16 * min(64 * r + lane, nch - 1), wl_a + 1024 * r);
+  // 3. this wave's activation copies (issued first) are done; then everyone's;
+  //    then the rest of the row and the register chunks
+  wait_vmcnt<kQ6TnEarly>();
+  __syncthreads();
+#pragma unroll
+  for (int r = kQ6TnEarly; r < kQ6TnRounds; ++r) dma16<true>(a0 + 16 * min(64 * r + lane, nch - 1), wl_a + 1024 * r);
+  uint4 rb[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) rb[j] = ld16_nt(a0 + 16 * min(cb0 + 64 * j + lane, nch - 1));
+  float acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    if (u == 0) {
+      // copies holding super-blocks 0 .. 15 (shift + 16 * 210 < 4 KB)
+      wait_vmcnt<kQ6TnRounds - 4 + 3>();
+    } else if (u == 1) {
+      // the register chunks over super-blocks 0 .. 14 of the region (this wave's reads of them are done);
+      // the copies are older than the register loads, so they are done too
+#pragma unroll
+      for (int j = 0; j < 3; ++j) *reinterpret_cast<uint4*>(wl + 1024 * j + 16 * lane) = rb[j];
+      wait_vmcnt<0>();
+    }
+    const int n = 64 * u + lane, b = n >> 2, h = (n >> 1) & 1, q = n & 1;
+    if (b < nb) {
+      const int vb = shift + b * kQ6Bytes;
+      const uint8_t* blk = wl + (b < kQ6TnABlocks ? vb : vb - 16 * cb0);
+      const uint32_t sh = static_cast<uint32_t>(vb) & 3u;
+      const uint32_t* ba = reinterpret_cast<const uint32_t*>(blk - sh);
+      const uint4 pa = lds16_sh(ba + 16 * h + 4 * q, sh);      // ql[64h + 16q ..]: k = 0 (low), 2 (high nibbles)
+      const uint4 pb = lds16_sh(ba + 16 * h + 8 + 4 * q, sh);  // ql[64h + 32 + 16q ..]: k = 1 and 3
+      const uint4 ph = lds16_sh(ba + 32 + 8 * h + 4 * q, sh);  // qh[32h + 16q ..]: bits 2k, 2k + 1
+      const uint2 sc8 = lds8_sh(ba + 48 + 2 * h, sh);          // sc[8h .. 8h + 7]: k's scale is byte 2k + q
+      const uint32_t scx = sc8.x >> (8 * q), scy = sc8.y >> (8 * q);
+      const float d = h2f(*reinterpret_cast<const uint16_t*>(blk + 208));
+      const uint32_t qa[4] = {pa.x, pa.y, pa.z, pa.w}, qb[4] = {pb.x, pb.y, pb.z, pb.w};
+      const uint32_t qh[4] = {ph.x, ph.y, ph.z, ph.w};
+      uint32_t v[4][4];  // signed values q6 - 32 of k = 0 .. 3
+      int sc[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = ((k & 1) ? qb[i] : qa[i]) >> ((k >> 1) * 4);
+          const uint32_t hi = (qh[i] >> (2 * k)) & 0x03030303u;
+          v[k][i] = (lo & 0x0f0f0f0fu) | __builtin_amdgcn_perm(kQ6HiTable, kQ6HiTable, hi);
+        }
+        sc[k] = static_cast<int8_t>(((k < 2) ? scx : scy) >> (16 * (k & 1)));
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint8_t* xt = xl + t * tb;
+        const uint4 dxw = *reinterpret_cast<const uint4*>(xt + 256 * 4 * G + 16 * n);
+        const uint32_t dx[4] = {dxw.x, dxw.y, dxw.z, dxw.w};
+        float accu = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // half q of Q8_1 block 8b + 4h + k of token t
+          const uint4 xw = *reinterpret_cast<const uint4*>(xt + 256 * G * k + 16 * n);
+          int D = dot4(v[k][0], xw.x, 0);
+          D = dot4(v[k][1], xw.y, D);
+          D = dot4(v[k][2], xw.z, D);
+          D = dot4(v[k][3], xw.w, D);
+          if constexpr (DEBUG) {
+            if (row_ok) dbgD[(static_cast<size_t>(t) * M + row) * (nb * 16) + 16 * b + 8 * h + 2 * k + q] = D;
+          } else {
+            accu = fmaf(h2f(dx[k]), static_cast<float>(__mul24(sc[k], D)), accu);
+          }
+        }
+        if constexpr (!DEBUG) acc[t] = fmaf(d, accu, acc[t]);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  if constexpr (!DEBUG) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0 && row_ok) y[static_cast<size_t>(t) * M + row] = s;
+    }
+  }
+}
+
+template <int T, bool DEBUG>
+static int launch_mmvq_q6k_tn(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, hipStream_t st) {
+  const size_t lds = static_cast<size_t>(kQ6TnWaves) * kQ6TnRounds * 1024 + static_cast<size_t>(T) * q6t1_act_bytes(nb);
+  static bool attr_set = false;
+  if (!attr_set) {
+    const size_t lmax = static_cast<size_t>(kQ6TnWaves) * kQ6TnRounds * 1024 +
+                        static_cast<size_t>(T) * q6t1_act_bytes(kQ6TnMaxBlocks);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q6k_tn_kernel<T, DEBUG>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lmax)) != hipSuccess)
+      return QMM_ERR_HIP;
+    attr_set = true;
+  }
+  const dim3 grid((M + kQ6TnWaves - 1) / kQ6TnWaves), block(64 * kQ6TnWaves);
+  hipLaunchKernelGGL((mmvq_q6k_tn_kernel<T, DEBUG>), grid, block, lds, st, static_cast<const uint8_t*>(w),
+                     static_cast<const uint8_t*>(xq), y, M, nb, D);
+  return launch_status();
+}
+
 // Q6_K segments: at most 4 * q6_rounds(T) blocks (the pieces held in
 // registers) and kQ6ActBudget bytes of staged activations (with the waves'
 // piece regions two workgroups fit a CU); the row is split into segments
@@ -1108,6 +1262,11 @@ static int launch_mmvq_q6k(const void* w, const void* xq, float* y, int M, int n
   // inside the matrix)
   if (!slots && T == 1 && nb <= kQ6T1MaxBlocks && (static_cast<int64_t>(M) * nb) % 8 == 0)
     return launch_mmvq_q6k_t1<DEBUG>(w, xq, y, M, nb, D, st);
+  if (!slots && T >= 2 && T <= 4 && nb <= kQ6TnMaxBlocks && (static_cast<int64_t>(M) * nb) % 8 == 0) {
+    if (T == 2) return launch_mmvq_q6k_tn<2, DEBUG>(w, xq, y, M, nb, D, st);
+    if (T == 3) return launch_mmvq_q6k_tn<3, DEBUG>(w, xq, y, M, nb, D, st);
+    return launch_mmvq_q6k_tn<4, DEBUG>(w, xq, y, M, nb, D, st);
+  }
   const SlotArgs SA = slots ? *slots : SlotArgs{};
   int cmax = kQ6ActBudget / (T * kQK * 3 / 2);
   if (cmax > 4 * q6_rounds(T)) cmax = 4 * q6_rounds(T);
