@@ -618,10 +618,10 @@ __device__ __forceinline__ Q45Dot q45_dot(const Q45Unit& U, const uint8_t* x0p) 
   const uint32_t xa[8] = {a[0].y, a[1].x, a[1].y, a[2].x, a[2].y, a[3].x, a[3].y, a[4].x};
   const uint32_t xc[8] = {c[0].y, c[1].x, c[1].y, c[2].x, c[2].y, c[3].x, c[3].y, c[4].x};
   Q45Dot r;
-  r.D0 = 0;
-  r.D1 = 0;
+  r.D0 = dot4_0(U.lo[0], xa[0]);
+  r.D1 = dot4_0(U.hi[0], xc[0]);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 1; k < 8; ++k) {
     r.D0 = dot4(U.lo[k], xa[k], r.D0);
     r.D1 = dot4(U.hi[k], xc[k], r.D1);
   }
@@ -643,10 +643,10 @@ __device__ __forceinline__ Q45Dot q45_dot_c(const Q45Unit& U, const uint8_t* xu)
   const uint32_t xa[8] = {c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w, c2.x};
   const uint32_t xc[8] = {c2.w, c3.x, c3.y, c3.z, c3.w, c4.x, c4.y, c4.z};
   Q45Dot r;
-  r.D0 = 0;
-  r.D1 = 0;
+  r.D0 = dot4_0(U.lo[0], xa[0]);
+  r.D1 = dot4_0(U.hi[0], xc[0]);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 1; k < 8; ++k) {
     r.D0 = dot4(U.lo[k], xa[k], r.D0);
     r.D1 = dot4(U.hi[k], xc[k], r.D1);
   }
@@ -995,6 +995,7 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
   const int nch = (shift + nb * kQ6Bytes + 15) >> 4;                   // aligned chunks covering the row
   const int cb0 = (shift + kQ6T1ABlocks * kQ6Bytes) >> 4;              // first chunk held in registers
   const int G = q6t1_groups(nb);
+  constexpr int kG = q6t1_groups(kQ6T1MaxBlocks);  // layout stride fixed: LDS offsets are immediates
   uint8_t* wl = lds + wave * kQ6T1Rounds * 1024;                       // this wave's region
   const uint8_t* xl = lds + kMmvqWaves * kQ6T1Rounds * 1024;           // activations in unit order
   const uint32_t wl_a = lds_addr(wl), xl_a = lds_addr(xl);
@@ -1004,8 +1005,8 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
     const int nc = min(16 * g + (lane >> 2), 4 * nb - 1);
     const uint8_t* src = xq + (8 * (nc >> 2) + 4 * ((nc >> 1) & 1)) * kQ8Bytes;  // block 8b + 4h
 #pragma unroll
-    for (int k = 0; k < 4; ++k) dma4(src + k * kQ8Bytes + 4 + 16 * (nc & 1) + 4 * (lane & 3), xl_a + 256 * (G * k + g));
-    dma4(src + (lane & 3) * kQ8Bytes, xl_a + 256 * (4 * G + g));  // block 8b + 4h + l % 4: f16 d + pad
+    for (int k = 0; k < 4; ++k) dma4(src + k * kQ8Bytes + 4 + 16 * (nc & 1) + 4 * (lane & 3), xl_a + 256 * (kG * k + g));
+    dma4(src + (lane & 3) * kQ8Bytes, xl_a + 256 * (4 * kG + g));  // block 8b + 4h + l % 4: f16 d + pad
   }
   // 2. the first copies of the row into the region (chunks past the row re-read its last one)
 #pragma unroll
@@ -1043,7 +1044,7 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
       const uint4 ph = lds16_sh(ba + 32 + 8 * h + 4 * q, sh);  // qh[32h + 16q ..]: bits 2k, 2k + 1
       const uint2 sc8 = lds8_sh(ba + 48 + 2 * h, sh);          // sc[8h .. 8h + 7]: k's scale is byte 2k + q
       const uint32_t scx = sc8.x >> (8 * q), scy = sc8.y >> (8 * q);
-      const uint4 dxw = *reinterpret_cast<const uint4*>(xl + 256 * 4 * G + 16 * n);
+      const uint4 dxw = *reinterpret_cast<const uint4*>(xl + 256 * 4 * kG + 16 * n);
       const uint32_t dx[4] = {dxw.x, dxw.y, dxw.z, dxw.w};
       const uint32_t qa[4] = {pa.x, pa.y, pa.z, pa.w}, qb[4] = {pb.x, pb.y, pb.z, pb.w};
       const uint32_t qh[4] = {ph.x, ph.y, ph.z, ph.w};
@@ -1051,7 +1052,7 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         // half q of Q8_1 block 8b + 4h + k
-        const uint4 xw = *reinterpret_cast<const uint4*>(xl + 256 * G * k + 16 * n);
+        const uint4 xw = *reinterpret_cast<const uint4*>(xl + 256 * kG * k + 16 * n);
         const uint32_t xv[4] = {xw.x, xw.y, xw.z, xw.w};
         int D = 0;
 #pragma unroll
@@ -1059,7 +1060,7 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
           const uint32_t lo = ((k & 1) ? qb[i] : qa[i]) >> ((k >> 1) * 4);
           const uint32_t hi = (qh[i] >> (2 * k)) & 0x03030303u;
           const uint32_t v = (lo & 0x0f0f0f0fu) | __builtin_amdgcn_perm(kQ6HiTable, kQ6HiTable, hi);
-          D = dot4(v, xv[i], D);
+          D = i == 0 ? dot4_0(v, xv[0]) : dot4(v, xv[i], D);
         }
         const int sc = static_cast<int8_t>(((k < 2) ? scx : scy) >> (16 * (k & 1)));
         if constexpr (DEBUG) {
@@ -1080,10 +1081,10 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
 
 template <bool DEBUG>
 static int launch_mmvq_q6k_t1(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, hipStream_t st) {
-  const size_t lds = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 + q6t1_act_bytes(nb);
+  const size_t lds = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 + q6t1_act_bytes(kQ6T1MaxBlocks);
   static bool attr_set = false;
   if (!attr_set) {
-    const size_t lmax = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 + q6t1_act_bytes(kQ6T1MaxBlocks);
+    const size_t lmax = lds;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q6k_t1_kernel<DEBUG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lmax)) != hipSuccess)
       return QMM_ERR_HIP;
@@ -1106,7 +1107,7 @@ static int launch_mmvq_q6k_t1(const void* w, const void* xq, float* y, int M, in
 // token.
 constexpr int kQ6TnWaves = 16;
 constexpr int kQ6TnRounds = 6;      // 1 KB copies per wave (its LDS region)
-constexpr int kQ6TnEarly = 4;       // of them issued before the activation barrier
+constexpr int kQ6TnEarly = 3;       // of them issued before the activation barrier (measured 3 .. 6)
 constexpr int kQ6TnABlocks = 29;    // super-blocks always inside the copies
 constexpr int kQ6TnMaxBlocks = 43;  // + at most 14 in the register chunks
 static_assert(kQ6TnWaves * kQ6TnRounds * 1024 + 4 * q6t1_act_bytes(kQ6TnMaxBlocks) <= 160 * 1024,
@@ -1128,7 +1129,8 @@ void mmvq_q6k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
   const int nch = (shift + nb * kQ6Bytes + 15) >> 4;                   // aligned chunks covering the row
   const int cb0 = (shift + kQ6TnABlocks * kQ6Bytes) >> 4;              // first chunk held in registers
   const int G = q6t1_groups(nb);
-  const int tb = q6t1_act_bytes(nb);                                   // activation bytes per token
+  // layout strides fixed at the largest row, so every LDS offset below is an immediate
+  constexpr int kG = q6t1_groups(kQ6TnMaxBlocks), tb = q6t1_act_bytes(kQ6TnMaxBlocks);
   uint8_t* wl = lds + wave * kQ6TnRounds * 1024;                       // this wave's region
   const uint8_t* xl = lds + kQ6TnWaves * kQ6TnRounds * 1024;           // activations in unit order
   const uint32_t wl_a = lds_addr(wl), xl_a = lds_addr(xl);
@@ -1141,8 +1143,8 @@ void mmvq_q6k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
     const uint8_t* src = xq + t * xstride + (8 * (nc >> 2) + 4 * ((nc >> 1) & 1)) * kQ8Bytes;
     const uint32_t dst = xl_a + t * tb;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) dma4(src + k * kQ8Bytes + 4 + 16 * (nc & 1) + 4 * (lane & 3), dst + 256 * (G * k + g));
-    dma4(src + (lane & 3) * kQ8Bytes, dst + 256 * (4 * G + g));
+    for (int k = 0; k < 4; ++k) dma4(src + k * kQ8Bytes + 4 + 16 * (nc & 1) + 4 * (lane & 3), dst + 256 * (kG * k + g));
+    dma4(src + (lane & 3) * kQ8Bytes, dst + 256 * (4 * kG + g));
   }
   // 2. the first copies of the row (chunks past the row re-read its last one)
 #pragma unroll
@@ -1200,14 +1202,14 @@ void mmvq_q6k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const uint8_t* xt = xl + t * tb;
-        const uint4 dxw = *reinterpret_cast<const uint4*>(xt + 256 * 4 * G + 16 * n);
+        const uint4 dxw = *reinterpret_cast<const uint4*>(xt + 256 * 4 * kG + 16 * n);
         const uint32_t dx[4] = {dxw.x, dxw.y, dxw.z, dxw.w};
         float accu = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           // half q of Q8_1 block 8b + 4h + k of token t
-          const uint4 xw = *reinterpret_cast<const uint4*>(xt + 256 * G * k + 16 * n);
-          int D = dot4(v[k][0], xw.x, 0);
+          const uint4 xw = *reinterpret_cast<const uint4*>(xt + 256 * kG * k + 16 * n);
+          int D = dot4_0(v[k][0], xw.x);
           D = dot4(v[k][1], xw.y, D);
           D = dot4(v[k][2], xw.z, D);
           D = dot4(v[k][3], xw.w, D);
@@ -1233,11 +1235,11 @@ void mmvq_q6k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
 
 template <int T, bool DEBUG>
 static int launch_mmvq_q6k_tn(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, hipStream_t st) {
-  const size_t lds = static_cast<size_t>(kQ6TnWaves) * kQ6TnRounds * 1024 + static_cast<size_t>(T) * q6t1_act_bytes(nb);
+  const size_t lds = static_cast<size_t>(kQ6TnWaves) * kQ6TnRounds * 1024 +
+                     static_cast<size_t>(T) * q6t1_act_bytes(kQ6TnMaxBlocks);
   static bool attr_set = false;
   if (!attr_set) {
-    const size_t lmax = static_cast<size_t>(kQ6TnWaves) * kQ6TnRounds * 1024 +
-                        static_cast<size_t>(T) * q6t1_act_bytes(kQ6TnMaxBlocks);
+    const size_t lmax = lds;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q6k_tn_kernel<T, DEBUG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lmax)) != hipSuccess)
       return QMM_ERR_HIP;

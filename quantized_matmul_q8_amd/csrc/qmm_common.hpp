@@ -98,6 +98,14 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
 }
 
+// The same with c = 0, as one instruction: the compiler's accumulating form
+// would first zero a register for it.
+__device__ __forceinline__ int dot4_0(uint32_t a, uint32_t b) {
+  int r;
+  asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Q4_K packed 6-bit scale and min of sub-block j (0..7).  s0, s1, s2 are the
 // 12 packed bytes as little-endian dwords (bytes 0-3, 4-7, 8-11).  Packing as
 // read for the Q4_K format (GGUF K-quant layout):
