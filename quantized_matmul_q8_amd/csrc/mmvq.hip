@@ -759,7 +759,7 @@ static int launch_mmvq_t1(const void* w, const void* xq, float* y, int M, int nb
   return launch_status();
 }
 
-// Two to four tokens, Q4_K: the one-token design with one 16-wave workgroup
+// Two to four tokens, Q4_K and Q5_K: the one-token design with one 16-wave workgroup
 // per CU, so the T tokens' raw activation blocks (13.8 KB per token at
 // K = 11008) are copied once per CU.  To fit them beside sixteen row
 // segments, a wave's copies write only the row's own bytes: the copies past
@@ -767,23 +767,25 @@ static int launch_mmvq_t1(const void* w, const void* xq, float* y, int M, int nb
 // left keeps lane 0 on a 16-byte dummy slot, so every wave issues the same
 // number of copies and the vmcnt waits stay exact).  Each lane decodes its
 // unit once and multiplies it with every token.
+// Q5_K works the same way with its 176-byte blocks (a segment of at most 46
+// super-blocks in 8 copies).
 constexpr int kTnWaves = 16;
-constexpr int kTnMaxBlocks = 48;  // three unit rounds
-constexpr int kTnRounds = 7;      // 1 KB copies per wave per segment (48 * 144 <= 7 KB)
-constexpr int kTnEarly = 4;       // of them issued before the activation barrier (measured 3 .. 5)
+constexpr int kTnEarly = 4;       // copies issued before the activation barrier (Q4_K: measured 3 .. 5 of 7)
 constexpr int kLdsMax = 160 * 1024;
 
+template <int FMT>
 static int tn_max_blocks(int T) {
-  const int by_lds = (kLdsMax - kTnWaves * 16) / (kTnWaves * kQ4Bytes + T * 8 * kQ8Bytes);
-  return by_lds < kTnMaxBlocks ? by_lds : kTnMaxBlocks;
+  using DL = MvDma<FMT>;
+  const int by_lds = (kLdsMax - kTnWaves * 16) / (kTnWaves * DL::kBytes + T * 8 * kQ8Bytes);
+  return by_lds < DL::kMaxBlocks ? by_lds : DL::kMaxBlocks;
 }
 
-template <int T, bool DEBUG>
+template <int FMT, int T, bool DEBUG>
 __global__ __launch_bounds__(64 * kTnWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void mmvq_q4k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb, int cb,
-                        int32_t* __restrict__ dbgD, int32_t* __restrict__ dbgS) {
-  using DL = MvDma<QMM_Q4_K>;
-  static_assert(kTnRounds == DL::kRounds && kTnMaxBlocks == DL::kMaxBlocks, "unit-round waits");
+void mmvq_q45k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb, int cb,
+                         int32_t* __restrict__ dbgD, int32_t* __restrict__ dbgS) {
+  using DL = MvDma<FMT>;
+  constexpr int kTnRounds = DL::kRounds;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -791,8 +793,8 @@ void mmvq_q4k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
   const bool row_ok = row_raw < M;
   const int row = row_ok ? row_raw : M - 1;  // out-of-range waves read a valid row, store nothing
   const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
-  const uint8_t* wrow = w + static_cast<size_t>(row) * nb * kQ4Bytes;
-  const int wreg = cb * kQ4Bytes;                                      // bytes per wave region
+  const uint8_t* wrow = w + static_cast<size_t>(row) * nb * DL::kBytes;
+  const int wreg = cb * DL::kBytes;                                     // bytes per wave region
   const uint8_t* wl = lds + wave * wreg;
   const uint8_t* xl = lds + kTnWaves * wreg;                           // T tokens' raw Q8_1 blocks
   const uint32_t wl_a = lds_addr(wl), xl_a = lds_addr(xl);
@@ -813,8 +815,8 @@ void mmvq_q4k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
       }
     }
     // 2. the row segment: lanes past its end are masked off
-    const int nch = nbc * (kQ4Bytes / 16);
-    const uint8_t* wseg = wrow + static_cast<size_t>(b0) * kQ4Bytes;
+    const int nch = nbc * (DL::kBytes / 16);
+    const uint8_t* wseg = wrow + static_cast<size_t>(b0) * DL::kBytes;
     auto copy_round = [&](int r) {
       const bool full = 64 * r < nch;
       if (full ? 64 * r + lane < nch : lane == 0)
@@ -837,7 +839,7 @@ void mmvq_q4k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
       const int n = 64 * u + lane, b = n >> 2, p = n & 3;
       if (b < nbc) {
         Q45Unit U;
-        q45_unit<QMM_Q4_K>(wl + b * kQ4Bytes, p, U);
+        q45_unit<FMT>(wl + b * DL::kBytes, p, U);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const Q45Dot r = q45_dot_c(U, xl + t * (nbc * DL::kQ8Seg) + (8 * b + 2 * p) * kQ8Bytes);
@@ -869,23 +871,24 @@ void mmvq_q4k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
   }
 }
 
-template <int T, bool DEBUG>
-static int launch_mmvq_q4k_tn(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, int32_t* S,
-                              hipStream_t st) {
-  const int cmax = tn_max_blocks(T);
+template <int FMT, int T, bool DEBUG>
+static int launch_mmvq_q45k_tn(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, int32_t* S,
+                               hipStream_t st) {
+  using DL = MvDma<FMT>;
+  const int cmax = tn_max_blocks<FMT>(T);
   const int nseg = (nb + cmax - 1) / cmax;
   const int cb = (nb + nseg - 1) / nseg;
-  const size_t lds = static_cast<size_t>(kTnWaves) * cb * kQ4Bytes + static_cast<size_t>(T) * cb * 8 * kQ8Bytes +
+  const size_t lds = static_cast<size_t>(kTnWaves) * cb * DL::kBytes + static_cast<size_t>(T) * cb * 8 * kQ8Bytes +
                      kTnWaves * 16;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q4k_tn_kernel<T, DEBUG>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q45k_tn_kernel<FMT, T, DEBUG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess)
       return QMM_ERR_HIP;
     attr_set = true;
   }
   const dim3 grid((M + kTnWaves - 1) / kTnWaves), block(64 * kTnWaves);
-  hipLaunchKernelGGL((mmvq_q4k_tn_kernel<T, DEBUG>), grid, block, lds, st, static_cast<const uint8_t*>(w),
+  hipLaunchKernelGGL((mmvq_q45k_tn_kernel<FMT, T, DEBUG>), grid, block, lds, st, static_cast<const uint8_t*>(w),
                      static_cast<const uint8_t*>(xq), y, M, nb, cb, D, S);
   return launch_status();
 }
@@ -905,11 +908,9 @@ static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int n
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   const uint8_t* xp = static_cast<const uint8_t*>(xq);
   if (!slots && T == 1) return launch_mmvq_t1<FMT, DEBUG>(w, xq, y, M, nb, D, S, st);
-  if constexpr (FMT == QMM_Q4_K) {
-    if (!slots && T == 2) return launch_mmvq_q4k_tn<2, DEBUG>(w, xq, y, M, nb, D, S, st);
-    if (!slots && T == 3) return launch_mmvq_q4k_tn<3, DEBUG>(w, xq, y, M, nb, D, S, st);
-    if (!slots && T == 4) return launch_mmvq_q4k_tn<4, DEBUG>(w, xq, y, M, nb, D, S, st);
-  }
+  if (!slots && T == 2) return launch_mmvq_q45k_tn<FMT, 2, DEBUG>(w, xq, y, M, nb, D, S, st);
+  if (!slots && T == 3) return launch_mmvq_q45k_tn<FMT, 3, DEBUG>(w, xq, y, M, nb, D, S, st);
+  if (!slots && T == 4) return launch_mmvq_q45k_tn<FMT, 4, DEBUG>(w, xq, y, M, nb, D, S, st);
   if (slots) {
     if (DEBUG || T != 1) return QMM_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((mmvq_q45k_kernel<FMT, 1, false, true>), dim3(grid.x, nslots), block, lds, st, wp, xp, y,
