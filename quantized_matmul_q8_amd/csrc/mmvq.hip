@@ -911,6 +911,10 @@ static int launch_mmvq_q4k(const void* w, const void* xq, float* y, int M, int n
   if (!slots && T == 2) return launch_mmvq_q45k_tn<FMT, 2, DEBUG>(w, xq, y, M, nb, D, S, st);
   if (!slots && T == 3) return launch_mmvq_q45k_tn<FMT, 3, DEBUG>(w, xq, y, M, nb, D, S, st);
   if (!slots && T == 4) return launch_mmvq_q45k_tn<FMT, 4, DEBUG>(w, xq, y, M, nb, D, S, st);
+  if (!slots && T == 5) return launch_mmvq_q45k_tn<FMT, 5, DEBUG>(w, xq, y, M, nb, D, S, st);
+  if (!slots && T == 6) return launch_mmvq_q45k_tn<FMT, 6, DEBUG>(w, xq, y, M, nb, D, S, st);
+  if (!slots && T == 7) return launch_mmvq_q45k_tn<FMT, 7, DEBUG>(w, xq, y, M, nb, D, S, st);
+  if (!slots && T == 8) return launch_mmvq_q45k_tn<FMT, 8, DEBUG>(w, xq, y, M, nb, D, S, st);
   if (slots) {
     if (DEBUG || T != 1) return QMM_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((mmvq_q45k_kernel<FMT, 1, false, true>), dim3(grid.x, nslots), block, lds, st, wp, xp, y,

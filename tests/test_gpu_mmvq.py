@@ -32,7 +32,9 @@ CASES = [(1, 256, 1), (7, 512, 3), (37, 1280, 8), (64, 2304, 4), (5, 256, 2), (1
          # two segments, a single super-block, a partial last workgroup
          (33, 14336, 4), (17, 12288, 2), (19, 11776, 3), (3, 256, 4),
          # two to four tokens, Q6_K rows split between 16-row LDS copies and registers
-         (16, 11008, 4), (24, 7168, 2), (8, 9728, 3), (40, 6144, 4)]
+         (16, 11008, 4), (24, 7168, 2), (8, 9728, 3), (40, 6144, 4),
+         # five to eight tokens, Q4_K / Q5_K rows in two and three LDS segments
+         (16, 11008, 8), (21, 14336, 6), (35, 11008, 5)]
 
 
 def _inputs(fmt, M, K, T, seed):
