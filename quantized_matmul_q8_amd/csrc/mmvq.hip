@@ -1256,6 +1256,153 @@ static int launch_mmvq_q6k_tn(const void* w, const void* xq, float* y, int M, in
   return launch_status();
 }
 
+// Five to eight tokens, Q6_K: the same 16-row workgroups with the row in
+// segments of at most 22 super-blocks (two at K = 11008), so the T tokens'
+// activations of a segment fit beside sixteen row segments.  A wave copies
+// the 16-byte aligned chunks that cover its row segment (at most 5 KB) into
+// its LDS region, after the workgroup's gather of the segment's
+// activations; each segment ends with every copy landed and a barrier
+// before the region is reused.
+constexpr int kQ6TsRounds = 5;     // 1 KB copies per wave per segment
+constexpr int kQ6TsMaxBlocks = 22; // super-blocks per segment (22 * 210 + 15 <= 5 KB)
+
+template <int T>
+static int q6ts_seg_blocks(int nb) {
+  constexpr int kBudget = 160 * 1024 - kQ6TnWaves * kQ6TsRounds * 1024;  // activation bytes
+  int cb = kQ6TsMaxBlocks;
+  while (cb > 4 && T * q6t1_act_bytes(cb) > kBudget) --cb;
+  const int nseg = (nb + cb - 1) / cb;
+  return (nb + nseg - 1) / nseg;
+}
+
+template <int T, bool DEBUG>
+__global__ __launch_bounds__(64 * kQ6TnWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void mmvq_q6k_ts_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb, int cb,
+                        int32_t* __restrict__ dbgD) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row_raw = blockIdx.x * kQ6TnWaves + wave;
+  const bool row_ok = row_raw < M;
+  const int row = row_ok ? row_raw : M - 1;  // out-of-range waves read a valid row, store nothing
+  const size_t row_off = static_cast<size_t>(row) * nb * kQ6Bytes;
+  const int tb = q6t1_act_bytes(cb);                                   // activation bytes per token
+  const int Gs = q6t1_groups(cb);                                      // layout stride (groups)
+  uint8_t* wl = lds + wave * kQ6TsRounds * 1024;                       // this wave's region
+  const uint8_t* xl = lds + kQ6TnWaves * kQ6TsRounds * 1024;           // activations in unit order
+  const uint32_t wl_a = lds_addr(wl), xl_a = lds_addr(xl);
+  const size_t xstride = static_cast<size_t>(nb) * 8 * kQ8Bytes;
+  float acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+  for (int b0 = 0; b0 < nb; b0 += cb) {
+    const int nbc = min(cb, nb - b0);
+    const int G = q6t1_groups(nbc);
+    if (b0 > 0) __syncthreads();  // every wave is done with the previous segment
+    // 1. the segment's activations, token t at xl + t * tb (groups of 16 units)
+    for (int c = wave; c < T * G; c += kQ6TnWaves) {
+      const int t = c / G, g = c - t * G;
+      const int nc = min(16 * g + (lane >> 2), 4 * nbc - 1);
+      const uint8_t* src = xq + t * xstride + (8 * (b0 + (nc >> 2)) + 4 * ((nc >> 1) & 1)) * kQ8Bytes;
+      const uint32_t dst = xl_a + t * tb;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        dma4(src + k * kQ8Bytes + 4 + 16 * (nc & 1) + 4 * (lane & 3), dst + 256 * (Gs * k + g));
+      dma4(src + (lane & 3) * kQ8Bytes, dst + 256 * (4 * Gs + g));
+    }
+    // 2. the chunks covering the row segment (chunks past it re-read its last one)
+    const size_t seg_off = row_off + static_cast<size_t>(b0) * kQ6Bytes;
+    const int shift = static_cast<int>(seg_off & 15u);
+    const uint8_t* a0 = w + (seg_off - shift);
+    const int nch = (shift + nbc * kQ6Bytes + 15) >> 4;
+#pragma unroll
+    for (int r = 0; r < kQ6TsRounds; ++r) dma16<true>(a0 + 16 * min(64 * r + lane, nch - 1), wl_a + 1024 * r);
+    // 3. this wave's activation copies (issued first) are done; then everyone's
+    wait_vmcnt<kQ6TsRounds>();
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // copies holding super-blocks 16u .. 16u + 15 (shift + 16 * 210 < 4 KB)
+      if (u == 0) wait_vmcnt<1>();
+      else wait_vmcnt<0>();
+      const int n = 64 * u + lane, b = n >> 2, h = (n >> 1) & 1, q = n & 1;
+      if (b < nbc) {
+        const int vb = shift + b * kQ6Bytes;
+        const uint8_t* blk = wl + vb;
+        const uint32_t sh = static_cast<uint32_t>(vb) & 3u;
+        const uint32_t* ba = reinterpret_cast<const uint32_t*>(blk - sh);
+        const uint4 pa = lds16_sh(ba + 16 * h + 4 * q, sh);      // ql[64h + 16q ..]: k = 0 (low), 2 (high nibbles)
+        const uint4 pb = lds16_sh(ba + 16 * h + 8 + 4 * q, sh);  // ql[64h + 32 + 16q ..]: k = 1 and 3
+        const uint4 ph = lds16_sh(ba + 32 + 8 * h + 4 * q, sh);  // qh[32h + 16q ..]: bits 2k, 2k + 1
+        const uint2 sc8 = lds8_sh(ba + 48 + 2 * h, sh);          // sc[8h .. 8h + 7]: k's scale is byte 2k + q
+        const uint32_t scx = sc8.x >> (8 * q), scy = sc8.y >> (8 * q);
+        const float d = h2f(*reinterpret_cast<const uint16_t*>(blk + 208));
+        const uint32_t qa[4] = {pa.x, pa.y, pa.z, pa.w}, qb[4] = {pb.x, pb.y, pb.z, pb.w};
+        const uint32_t qh[4] = {ph.x, ph.y, ph.z, ph.w};
+        uint32_t v[4][4];  // signed values q6 - 32 of k = 0 .. 3
+        int sc[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = ((k & 1) ? qb[i] : qa[i]) >> ((k >> 1) * 4);
+            const uint32_t hi = (qh[i] >> (2 * k)) & 0x03030303u;
+            v[k][i] = (lo & 0x0f0f0f0fu) | __builtin_amdgcn_perm(kQ6HiTable, kQ6HiTable, hi);
+          }
+          sc[k] = static_cast<int8_t>(((k < 2) ? scx : scy) >> (16 * (k & 1)));
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint8_t* xt = xl + t * tb;
+          const uint4 dxw = *reinterpret_cast<const uint4*>(xt + 256 * 4 * Gs + 16 * n);
+          const uint32_t dx[4] = {dxw.x, dxw.y, dxw.z, dxw.w};
+          float accu = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint4 xw = *reinterpret_cast<const uint4*>(xt + 256 * Gs * k + 16 * n);
+            int D = dot4_0(v[k][0], xw.x);
+            D = dot4(v[k][1], xw.y, D);
+            D = dot4(v[k][2], xw.z, D);
+            D = dot4(v[k][3], xw.w, D);
+            if constexpr (DEBUG) {
+              if (row_ok)
+                dbgD[(static_cast<size_t>(t) * M + row) * (nb * 16) + 16 * (b0 + b) + 8 * h + 2 * k + q] = D;
+            } else {
+              accu = fmaf(h2f(dx[k]), static_cast<float>(__mul24(sc[k], D)), accu);
+            }
+          }
+          if constexpr (!DEBUG) acc[t] = fmaf(d, accu, acc[t]);
+        }
+      }
+    }
+    wait_vmcnt<0>();
+  }
+  if constexpr (!DEBUG) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0 && row_ok) y[static_cast<size_t>(t) * M + row] = s;
+    }
+  }
+}
+
+template <int T, bool DEBUG>
+static int launch_mmvq_q6k_ts(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, hipStream_t st) {
+  const int cb = q6ts_seg_blocks<T>(nb);
+  const size_t lds = static_cast<size_t>(kQ6TnWaves) * kQ6TsRounds * 1024 + static_cast<size_t>(T) * q6t1_act_bytes(cb);
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q6k_ts_kernel<T, DEBUG>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+      return QMM_ERR_HIP;
+    attr_set = true;
+  }
+  const dim3 grid((M + kQ6TnWaves - 1) / kQ6TnWaves), block(64 * kQ6TnWaves);
+  hipLaunchKernelGGL((mmvq_q6k_ts_kernel<T, DEBUG>), grid, block, lds, st, static_cast<const uint8_t*>(w),
+                     static_cast<const uint8_t*>(xq), y, M, nb, cb, D);
+  return launch_status();
+}
+
 // Q6_K segments: at most 4 * q6_rounds(T) blocks (the pieces held in
 // registers) and kQ6ActBudget bytes of staged activations (with the waves'
 // piece regions two workgroups fit a CU); the row is split into segments
@@ -1273,6 +1420,12 @@ static int launch_mmvq_q6k(const void* w, const void* xq, float* y, int M, int n
     if (T == 2) return launch_mmvq_q6k_tn<2, DEBUG>(w, xq, y, M, nb, D, st);
     if (T == 3) return launch_mmvq_q6k_tn<3, DEBUG>(w, xq, y, M, nb, D, st);
     return launch_mmvq_q6k_tn<4, DEBUG>(w, xq, y, M, nb, D, st);
+  }
+  if (!slots && T >= 5 && T <= 8 && (static_cast<int64_t>(M) * nb) % 8 == 0) {
+    if (T == 5) return launch_mmvq_q6k_ts<5, DEBUG>(w, xq, y, M, nb, D, st);
+    if (T == 6) return launch_mmvq_q6k_ts<6, DEBUG>(w, xq, y, M, nb, D, st);
+    if (T == 7) return launch_mmvq_q6k_ts<7, DEBUG>(w, xq, y, M, nb, D, st);
+    return launch_mmvq_q6k_ts<8, DEBUG>(w, xq, y, M, nb, D, st);
   }
   const SlotArgs SA = slots ? *slots : SlotArgs{};
   int cmax = kQ6ActBudget / (T * kQK * 3 / 2);

@@ -68,7 +68,8 @@ def test_end_to_end_from_fp32(fmt):
 @pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,K,T", [(3, 256, 1), (9, 768, 4), (17, 512, 5), (21, 768, 6), (33, 1024, 8),
                                    (13, 12544, 1), (10, 11008, 1), (16, 11008, 1), (8, 11776, 1),
-                                   (21, 14336, 2), (18, 11008, 3), (16, 11008, 4), (8, 7424, 2)])
+                                   (21, 14336, 2), (18, 11008, 3), (16, 11008, 4), (8, 7424, 2),
+                                   (24, 11008, 6), (16, 7168, 8)])
 def test_integer_stage_bit_exact(fmt, M, K, T):
     w, x, xq = _inputs(fmt, M, K, T, seed=7 * M + T)
     say(f"debug_subdots path=0 {fmt}", f"M={M} K={K} T={T}")
