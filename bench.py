@@ -69,8 +69,12 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def time_graph(torch, fns, reps, warm=2):
-    """Capture fns[i % len(fns)] for i < reps into one graph; return ms per call."""
+def time_graph(torch, fns, reps, warm=2, replays=5):
+    """Capture fns[i % len(fns)] for i < reps into one graph; return ms per call.
+
+    The graph is replayed twice untimed (the clocks settle after lighter work),
+    then `replays` times with events around each replay; the median counts.
+    """
     for i in range(warm):
         fns[i % len(fns)]()
     torch.cuda.synchronize()
@@ -79,13 +83,17 @@ def time_graph(torch, fns, reps, warm=2):
         for i in range(reps):
             fns[i % len(fns)]()
     g.replay()
-    torch.cuda.synchronize()
-    a, b = _events(torch)
-    a.record()
     g.replay()
-    b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps
+    ts = []
+    for _ in range(replays):
+        a, b = _events(torch)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / reps)
+    return sorted(ts)[len(ts) // 2]
 
 
 def time_launches(torch, fns, reps, sleep_cycles):
