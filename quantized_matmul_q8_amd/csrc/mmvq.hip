@@ -567,15 +567,31 @@ struct MvDma {
 // and 2p + 1 (hi), four per dword, and their integer scales and mins.
 struct Q45Unit {
   uint32_t lo[8], hi[8];
-  int sc0, m0, sc1, m1;
-  uint32_t dd;  // f16 d | f16 dmin << 16
+  uint32_t scm;  // bytes: scale of sub-block 2p, of 2p + 1, min of 2p, of 2p + 1 (6 bits each)
+  uint32_t dd;   // f16 d | f16 dmin << 16
 };
+
+// Scales and mins of sub-blocks 2p and 2p + 1 from the 12 packed bytes
+// S = (s0, s1, s2) of a Q4_K / Q5_K header, as the bytes of one dword (the
+// packing of q4k_scale_min, for both sub-blocks at once, with byte
+// permutes whose selectors depend only on p):
+//   p < 2 (j = 2p, 2p + 1 < 4):  sc = S[j] & 63,  m = S[j + 4] & 63
+//   p >= 2 (j >= 4):  sc = S[j + 4] & 15 | (S[j - 4] >> 6) << 4,
+//                     m  = S[j + 4] >> 4 | (S[j] >> 6) << 4
+__device__ __forceinline__ uint32_t q4k_scale_min_pair(int p, uint32_t s0, uint32_t s1, uint32_t s2) {
+  const uint32_t b = 2u * (p & 1);                       // first byte of the pair within its dword
+  const uint32_t selx = b | (b + 1) << 8 | (b + 4) << 16 | (b + 5) << 24;
+  const uint32_t sely = p < 2 ? 0x0c0c0c0cu : (b | (b + 1) << 8 | b << 16 | (b + 1) << 24);  // 0x0c: zero
+  const uint32_t x = __builtin_amdgcn_perm(s1, s0, selx);  // S[j - 4 or j], S[j or j + 4] (p >= 2 / p < 2)
+  const uint32_t yv = __builtin_amdgcn_perm(s2, s2, sely); // S[j + 4] twice (p >= 2), else 0
+  const uint32_t hi = p < 2 ? (x & 0x3f3f3f3fu) : ((x >> 2) & 0x30303030u);
+  return hi | (yv & 0x00000f0fu) | ((yv >> 4) & 0x0f0f0000u);
+}
 template <int FMT>
 __device__ __forceinline__ void q45_unit(const uint8_t* blk, int p, Q45Unit& U) {
   constexpr bool kQ5 = FMT == QMM_Q5_K;
   const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
-  q4k_scale_min(2 * p, hdr.y, hdr.z, hdr.w, U.sc0, U.m0);
-  q4k_scale_min(2 * p + 1, hdr.y, hdr.z, hdr.w, U.sc1, U.m1);
+  U.scm = q4k_scale_min_pair(p, hdr.y, hdr.z, hdr.w);
   U.dd = hdr.x;
   const uint8_t* qv = blk + (kQ5 ? 48 : 16) + 32 * p;
   const uint4 qa = *reinterpret_cast<const uint4*>(qv);
@@ -660,10 +676,10 @@ __device__ __forceinline__ Q45Dot q45_dot_c(const Q45Unit& U, const uint8_t* xu)
 // y contribution of a unit and token: dx * (d*sc*D - dmin*m*S) for both sub-blocks.
 __device__ __forceinline__ float q45_term(const Q45Unit& U, const Q45Dot& r) {
   const float d = h2f(U.dd & 0xffffu), dmin = h2f(U.dd >> 16);
-  return r.dx0 * (d * static_cast<float>(U.sc0) * static_cast<float>(r.D0) -
-                  dmin * static_cast<float>(U.m0) * static_cast<float>(r.S0)) +
-         r.dx1 * (d * static_cast<float>(U.sc1) * static_cast<float>(r.D1) -
-                  dmin * static_cast<float>(U.m1) * static_cast<float>(r.S1));
+  const float sc0 = static_cast<float>(U.scm & 0xffu), sc1 = static_cast<float>((U.scm >> 8) & 0xffu);
+  const float m0 = static_cast<float>((U.scm >> 16) & 0xffu), m1 = static_cast<float>(U.scm >> 24);
+  return r.dx0 * (d * sc0 * static_cast<float>(r.D0) - dmin * m0 * static_cast<float>(r.S0)) +
+         r.dx1 * (d * sc1 * static_cast<float>(r.D1) - dmin * m1 * static_cast<float>(r.S1));
 }
 
 template <int FMT, bool DEBUG>
