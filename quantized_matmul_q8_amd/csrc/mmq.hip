@@ -47,7 +47,9 @@
 //   kernel is held to 128 VGPRs instead and runs two workgroups per CU,
 //   four waves per SIMD: the other workgroup's work covers a workgroup's
 //   barriers and load waits (13-19% faster grouped calls than software
-//   pipelining at two waves per SIMD).
+//   pipelining at two waves per SIMD).  Grouped Q4_K / Q5_K calls do not
+//   split K: the tile is 256 rows x 32 routed slots, each of the eight waves
+//   taking every super-block of its own 32 rows, one super-block per step.
 // * Work queue.  Persistent grid, one (one-tile kernel: two) workgroup(s)
 //   per CU; tiles are split into
 //   8 contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), each
@@ -292,27 +294,33 @@ __global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
 // ----------------------------------------------------------------------------
 // Main kernel
 // ----------------------------------------------------------------------------
-// How a step is split between the two K halves (wave groups) of a
-// workgroup.  Q4_K: a step is two super-blocks; half kh takes super-block
-// 2*step + kh (its 8 sub-blocks).  Q6_K: a step is one super-block; half kh
-// takes its elements 128kh .. 128kh+127, i.e. MFMA sub-blocks 8kh .. 8kh+7
-// (half the weight bytes per wave, so the 64-column tile fits the register
-// budget).  Either way a wave multiplies 8 MFMA sub-blocks per step.
-template <int FMT>
+// How a step is split between the K halves (wave groups) of a workgroup.
+// KS = 2 (the default): Q4_K: a step is two super-blocks; half kh takes
+// super-block 2*step + kh (its 8 sub-blocks).  Q6_K: a step is one
+// super-block; half kh takes its elements 128kh .. 128kh+127, i.e. MFMA
+// sub-blocks 8kh .. 8kh+7 (half the weight bytes per wave, so the 64-column
+// tile fits the register budget).  KS = 1 (Q4_K / Q5_K grouped calls): no K
+// split, a step is one super-block taken by every wave for its own 32 rows,
+// and the tile has 256 rows.  Either way a wave
+// multiplies 8 MFMA sub-blocks per step.
+template <int FMT, int KS = 2>
 struct StepSplit {
-  static constexpr int kSbPerStep = is_q4fam(FMT) ? 2 : 1;
+  static_assert(KS == 2 || (KS == 1 && is_q4fam(FMT)), "K split");
+  static constexpr int kSbPerStep = is_q4fam(FMT) ? KS : 1;
   static constexpr int kNU = 8;                        // MFMA sub-blocks per wave per step
   static constexpr int kSubsPerSb = is_q4fam(FMT) ? 8 : 16;
-  __device__ __forceinline__ static int sb(int step, int kh) { return is_q4fam(FMT) ? 2 * step + kh : step; }
+  static constexpr int kRowGroups = 8 / KS;            // 32-row groups per tile
+  static constexpr int kBM = 32 * kRowGroups;          // weight rows per tile
+  __device__ __forceinline__ static int sb(int step, int kh) { return is_q4fam(FMT) ? KS * step + kh : step; }
   __device__ __forceinline__ static int u0(int kh) { return is_q4fam(FMT) ? 0 : 8 * kh; }   // first sub-block
   __device__ __forceinline__ static int chunk_half(int kh) { return is_q4fam(FMT) ? kh : 0; }
-  static int nsteps(int nb) { return is_q4fam(FMT) ? (nb + 1) / 2 : nb; }
+  __host__ __device__ static int nsteps(int nb) { return is_q4fam(FMT) ? (nb + KS - 1) / KS : nb; }
 };
 
-template <int FMT, int NT>
+template <int FMT, int NT, int KS = 2>
 struct MmqSmem {
-  static constexpr int kChunks = StepSplit<FMT>::kSbPerStep * NT * kChunkBytes;  // [half][ct] chunks
-  static constexpr int kRed = 4 * NT * 16 * 64 * 4;                             // split-K reduction
+  static constexpr int kChunks = StepSplit<FMT, KS>::kSbPerStep * NT * kChunkBytes;  // [half][ct] chunks
+  static constexpr int kRed = KS == 2 ? 4 * NT * 16 * 64 * 4 : 0;                    // K-half / split-K reduction
   static constexpr int kStage = kChunks > kRed ? kChunks : kRed;
   // alpha [8 sub-blocks][32 rows] fp32, then for Q4_K / Q5_K the min-term A
   // operand [3 parts][32 rows][8 sub-blocks] bf16
@@ -659,7 +667,7 @@ __device__ __forceinline__ void mmq_epilogue(const MmqParams& P, const TileCols&
   }
 }
 
-template <int FMT, int NT>
+template <int FMT, int NT, int KS>
 struct StepLoads;
 
 // Issue priority from the progress through a step's u of nu sub-blocks.
@@ -678,8 +686,7 @@ __device__ __forceinline__ void step_prio(int u, int nu) {
 template <int FMT, int NT, int MODE>
 __device__ __forceinline__ void mmq_compute(const MmqParams& P, const uint8_t* st, const float* wl,
                                             const MmqOperand<FMT>& A, v16f (&acc)[NT], const v16i& magic,
-                                            const TileCols& tc, int r0, int sb, int ub,
-                                            const StepLoads<FMT, NT>& pre, MmqPrefetch<FMT>& F) {
+                                            const TileCols& tc, int r0, int sb, int ub) {
   constexpr int NU = StepSplit<FMT>::kNU;  // MFMA sub-blocks of this wave per step
   if constexpr (kLean<FMT, NT>) {
     // one operand set and one result buffer per sub-block
@@ -749,8 +756,9 @@ struct MoeTables {
   const int* ct_off;    // [E]
 };
 
-template <int FMT, int NT, int MODE>
+template <int FMT, int NT, int MODE, int KS>
 __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb, int idx, TileRef& R) {
+  using SP = StepSplit<FMT, KS>;
   constexpr int BN = 32 * NT;
   int m_tile;
   const uint8_t* wbase = P.w;
@@ -779,7 +787,7 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
     // fastest: the 32 workgroups of an XCD work on 8 row tiles x 4 column
     // tiles at a time, so their weight rows and activation chunks stay in
     // the XCD's L2 (column tile fastest had them sweep all the chunks)
-    const int mtiles = (P.M + kMmqBM - 1) / kMmqBM;
+    const int mtiles = (P.M + SP::kBM - 1) / SP::kBM;
     const int grp = R.base / (kGroupM * ntile), inner = R.base % (kGroupM * ntile);
     const int gm = min(kGroupM, mtiles - grp * kGroupM);
     m_tile = grp * kGroupM + inner % gm;
@@ -798,7 +806,7 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
   R.nct = (R.tc.ncols + kChunkCols - 1) / kChunkCols;
   m_tile = __builtin_amdgcn_readfirstlane(m_tile);
   {
-    const int nsteps = is_q4fam(FMT) ? (P.nb + 1) >> 1 : P.nb;
+    const int nsteps = SP::nsteps(P.nb);
     if constexpr (MODE == kMoe) {
       R.s0 = 0;
       R.s1 = nsteps;
@@ -807,8 +815,8 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
       R.s1 = __builtin_amdgcn_readfirstlane((R.split + 1) * nsteps / P.nsplit);
     }
   }
-  const int rw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
-  R.r0 = m_tile * kMmqBM + rw * 32;
+  const int rw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % SP::kRowGroups;
+  R.r0 = m_tile * SP::kBM + rw * 32;
   const int wrow = min(R.r0 + (threadIdx.x & 31), P.M - 1);
   constexpr int kRowBytes = FMT == QMM_Q4_K ? kQ4Bytes : FMT == QMM_Q5_K ? kQ5Bytes : kQ6Bytes;
   R.wr = wbase + static_cast<size_t>(wrow) * P.nb * kRowBytes;
@@ -821,9 +829,9 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
 // copies are split into runs of kDma consecutive ones, run w for wave w, so
 // that a wave's copies lie in one chunk: their addresses are one base plus
 // multiples of 1 KB, the base fixed per wave (DmaPlan) plus a per-step term.
-template <int FMT, int NT>
+template <int FMT, int NT, int KS>
 struct StepLoads {
-  using SP = StepSplit<FMT>;
+  using SP = StepSplit<FMT, KS>;
   static constexpr int kInstr = SP::kSbPerStep * NT * kChunkKB;
   static constexpr int kDma = (kInstr + kMmqWaves - 1) / kMmqWaves;  // chunk copies per wave
   static_assert(kChunkKB % kDma == 0, "a wave's chunk copies must stay inside one chunk");
@@ -857,9 +865,9 @@ struct DmaPlan {
   bool has;         // the wave has a run
 };
 
-template <int FMT, int NT>
+template <int FMT, int NT, int KS>
 __device__ __forceinline__ DmaPlan dma_plan(int wave, int nb) {
-  using L = StepLoads<FMT, NT>;
+  using L = StepLoads<FMT, NT, KS>;
   DmaPlan D;
   const int first = wave * L::kDma;
   D.has = first < L::kInstr;
@@ -871,11 +879,12 @@ __device__ __forceinline__ DmaPlan dma_plan(int wave, int nb) {
   return D;
 }
 
-template <int FMT, int NT>
-__device__ __forceinline__ StepLoads<FMT, NT> step_loads(const MmqParams& P, const TileRef& R, const DmaPlan& D,
-                                                         int step, uint32_t dst, bool any, int kh, int g) {
-  using SP = StepSplit<FMT>;
-  StepLoads<FMT, NT> L;
+template <int FMT, int NT, int KS>
+__device__ __forceinline__ StepLoads<FMT, NT, KS> step_loads(const MmqParams& P, const TileRef& R,
+                                                             const DmaPlan& D, int step, uint32_t dst, bool any,
+                                                             int kh, int g) {
+  using SP = StepSplit<FMT, KS>;
+  StepLoads<FMT, NT, KS> L;
   const int sb0 = SP::kSbPerStep * step;
   L.src = P.xr + (static_cast<size_t>(R.ctile0) * P.nb + sb0) * kChunkBytes + D.src_off;
   L.dst = dst + D.dst_off;
@@ -996,9 +1005,11 @@ __device__ __forceinline__ void wait_vm_all() { wait_vmcnt<0>(); }
 // tile's first step and reads its value at the top of the tile's last step
 // (after the full wait there, so with two or more steps it costs no stall),
 // then publishes it before that step's barrier.
-template <int FMT, int NT, int MODE>
+template <int FMT, int NT, int MODE, int KS = 2>
 __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 4 : 2, NT == 1 ? 4 : 2))) void mmq_kernel(MmqParams P) {
-  using L = MmqSmem<FMT, NT>;
+  using L = MmqSmem<FMT, NT, KS>;
+  using SP = StepSplit<FMT, KS>;
+  static_assert(KS == 2 || MODE == kMoe, "the dense and debug calls split K in two");
   constexpr int kTab = MODE == kMoe ? kMoeMaxE + 1 : 1;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ int s_next[2];
@@ -1026,7 +1037,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT 
   if (b8 >= Q.size) return;  // no tile for this workgroup (uniform)
   const int lane = threadIdx.x & 63, g = lane >> 5, col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kh = wave >> 2;
+  const int kh = KS == 2 ? wave >> 2 : 0;
   // The two waves of a SIMD (K halves 0 and 1) share its issue slots; the
   // arbiter favours the older one, so the second half used to finish each
   // step alone, its matrix-core latency exposed.  The two-tile kernel sets
@@ -1041,12 +1052,12 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT 
   // rebuilt (16 moves) in front of every MFMA
   __asm__ volatile("" : "+v"(magic));
   TileRef R, Rn;
-  tile_ref<FMT, NT, MODE>(P, Tb, Q.start + b8, R);
+  tile_ref<FMT, NT, MODE, KS>(P, Tb, Q.start + b8, R);
   MmqPrefetch<FMT> F;
   const uint32_t lds0 = lds_addr(smem);
-  const DmaPlan D = dma_plan<FMT, NT>(wave, P.nb);
+  const DmaPlan D = dma_plan<FMT, NT, KS>(wave, P.nb);
   {
-    const StepLoads<FMT, NT> first = step_loads<FMT, NT>(P, R, D, R.s0, lds0, true, kh, g);
+    const StepLoads<FMT, NT, KS> first = step_loads<FMT, NT, KS>(P, R, D, R.s0, lds0, true, kh, g);
     first.issue_all(F);
   }
   int k = 0;            // steps done by this workgroup (selects the LDS stage)
@@ -1060,7 +1071,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT 
     int next = -1;
     for (int step = R.s0; step < R.s1; ++step, ++k) {
       uint8_t* st = smem + (k & 1) * L::kStage;
-      const int sb = StepSplit<FMT>::sb(step, kh);
+      const int sb = SP::sb(step, kh);
       const bool active = sb < P.nb;
       const bool last = step + 1 == R.s1;
       MmqOperand<FMT> A;
@@ -1079,18 +1090,20 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT 
       __syncthreads();
       if (last) {
         next = __builtin_amdgcn_readfirstlane(s_next[it & 1]);
-        if (next >= 0) tile_ref<FMT, NT, MODE>(P, Tb, next, Rn);
+        if (next >= 0) tile_ref<FMT, NT, MODE, KS>(P, Tb, next, Rn);
       }
       const uint32_t dst = lds0 + ((k + 1) & 1) * L::kStage;
-      const StepLoads<FMT, NT> pre = last ? step_loads<FMT, NT>(P, Rn, D, Rn.s0, dst, next >= 0, kh, g)
-                                          : step_loads<FMT, NT>(P, R, D, step + 1, dst, true, kh, g);
+      const StepLoads<FMT, NT, KS> pre = last ? step_loads<FMT, NT, KS>(P, Rn, D, Rn.s0, dst, next >= 0, kh, g)
+                                              : step_loads<FMT, NT, KS>(P, R, D, step + 1, dst, true, kh, g);
       pre.issue_all(F);
       if (active) {
-        mmq_compute<FMT, NT, MODE>(P, st + StepSplit<FMT>::chunk_half(kh) * NT * kChunkBytes, wl, A, acc, magic,
-                                   R.tc, R.r0, sb, StepSplit<FMT>::u0(kh), pre, F);
+        mmq_compute<FMT, NT, MODE>(P, st + SP::chunk_half(kh) * NT * kChunkBytes, wl, A, acc, magic, R.tc, R.r0,
+                                   sb, SP::u0(kh));
       }
     }
-    if constexpr (MODE != kDebug) {
+    if constexpr (MODE != kDebug && KS == 1) {
+      store_tile<NT, MODE>(P, R.tc, R.r0, acc);  // every wave holds whole sums of its 32 rows
+    } else if constexpr (MODE != kDebug) {
       // sum the two K halves through the stage just computed from
       __syncthreads();
       float* red = reinterpret_cast<float*>(smem + ((k - 1) & 1) * L::kStage);
@@ -1129,18 +1142,18 @@ static int mmq_grid(int total_tiles_hint, int per_cu) {
   return g < kXcds ? kXcds : g;
 }
 
-template <int FMT, int NT, int MODE>
+template <int FMT, int NT, int MODE, int KS = 2>
 static int launch_mmq(const MmqParams& P, int total_tiles_hint, hipStream_t st) {
-  using L = MmqSmem<FMT, NT>;
+  using L = MmqSmem<FMT, NT, KS>;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmq_kernel<FMT, NT, MODE>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmq_kernel<FMT, NT, MODE, KS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, L::kBytes) != hipSuccess)
       return QMM_ERR_HIP;
     attr_set = true;
   }
   const int grid = mmq_grid(total_tiles_hint, kLean<FMT, NT> ? 2 : 1);
-  hipLaunchKernelGGL((mmq_kernel<FMT, NT, MODE>), dim3(grid), dim3(kMmqThreads), L::kBytes, st, P);
+  hipLaunchKernelGGL((mmq_kernel<FMT, NT, MODE, KS>), dim3(grid), dim3(kMmqThreads), L::kBytes, st, P);
   return launch_status();
 }
 
@@ -1250,9 +1263,19 @@ int mmq_dense(int fmt, const void* w, const void* xq, float* y, int64_t M, int64
   return mmq_dense_fmt<QMM_Q6_K>(P, dbg, st);
 }
 
+// Weight rows per tile of a grouped call: 256 for Q4_K / Q5_K, every wave
+// taking every super-block of its own 32 rows (no K halves: no idle half on
+// the last step of rows with an odd number of super-blocks, no reduction of
+// the halves per tile; the grouped FFN calls measured 4-8 % faster than with
+// 128-row tiles split in K), 128 for Q6_K (its K halves split each
+// super-block, so they never go idle).
+int moe_tile_rows(int fmt, int /*nb*/) {
+  return is_q4fam(fmt) ? StepSplit<QMM_Q4_K, 1>::kBM : StepSplit<QMM_Q6_K, 2>::kBM;
+}
+
 // Grouped launch used by moe_grouped_mmq (after route preparation on the
-// same stream): repack of the routed rows per expert, then tiles of 128 rows
-// x 32 routed slots.
+// same stream): repack of the routed rows per expert, then tiles of
+// moe_tile_rows rows x 32 routed slots.
 int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, const uint8_t* xq,
                    float* out, unsigned* counters, const int32_t* counts, const int32_t* offsets,
                    const int32_t* bucket, const int32_t* work_off, const int32_t* ct_off, uint8_t* xr,
@@ -1286,8 +1309,11 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   P.ct_off = ct_off;
   P.E = E;
   P.expert_stride = stride;
-  if (fmt == QMM_Q4_K) return launch_mmq<QMM_Q4_K, 1, kMoe>(P, 0, st);
-  if (fmt == QMM_Q5_K) return launch_mmq<QMM_Q5_K, 1, kMoe>(P, 0, st);
+  const bool whole_k = moe_tile_rows(fmt, nb) == StepSplit<QMM_Q4_K, 1>::kBM;
+  if (fmt == QMM_Q4_K)
+    return whole_k ? launch_mmq<QMM_Q4_K, 1, kMoe, 1>(P, 0, st) : launch_mmq<QMM_Q4_K, 1, kMoe>(P, 0, st);
+  if (fmt == QMM_Q5_K)
+    return whole_k ? launch_mmq<QMM_Q5_K, 1, kMoe, 1>(P, 0, st) : launch_mmq<QMM_Q5_K, 1, kMoe>(P, 0, st);
   return launch_mmq<QMM_Q6_K, 1, kMoe>(P, 0, st);
 }
 

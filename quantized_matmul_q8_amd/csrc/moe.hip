@@ -34,13 +34,14 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr size_t kMoeCounterBytes = 256;
 constexpr int kMoeBN = 32;   // routed tokens per tile (must match the grouped kernel)
-constexpr int kMoeBM = 128;  // weight rows per tile
+constexpr int kMoeBM = 128;  // weight rows of the smaller grouped tile (bounds the work entries)
 
 int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, const uint8_t* xq,
                    float* out, unsigned* counters, const int32_t* counts, const int32_t* offsets,
                    const int32_t* bucket, const int32_t* work_off, const int32_t* ct_off, uint8_t* xr,
                    int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st);
 int64_t moe_max_ctiles(int64_t slots, int64_t E);
+int moe_tile_rows(int fmt, int nb);
 size_t moe_chunk_bytes(int64_t slots, int64_t E, int64_t K);
 
 struct MoeLayout {
@@ -269,7 +270,8 @@ extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int
   if (ws_bytes < L.bytes) return QMM_ERR_WORKSPACE;
   hipStream_t st = to_stream(stream);
   const int n = static_cast<int>(T * top_k);
-  const int mt = static_cast<int>((M + kMoeBM - 1) / kMoeBM);
+  const int bm = moe_tile_rows(fmt, static_cast<int>(K / kQK));
+  const int mt = static_cast<int>((M + bm - 1) / bm);
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ids, n, static_cast<int>(E),
                      mt, L.counts, L.offsets, L.work_off, L.ct_off, L.bucket, L.counters);
   int rc = launch_status();
