@@ -76,8 +76,6 @@ constexpr int kMmqWaves = 8;
 constexpr int kMmqThreads = 64 * kMmqWaves;
 constexpr int kMmqBM = 128;            // weight rows per tile (32 per row group)
 constexpr int kGroupM = 8;             // row tiles per run of the dense tile order
-constexpr uint32_t kMagicBits = 0x4B400000u;
-constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 

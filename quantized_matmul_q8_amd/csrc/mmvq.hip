@@ -616,55 +616,32 @@ __device__ __forceinline__ void q45_unit(const uint8_t* blk, int p, Q45Unit& U) 
 }
 
 // The unit against one token's Q8_1 blocks 8b + 2p, 8b + 2p + 1 (raw 40-byte
-// blocks at x0, 8-byte aligned): the integer sums D and the blocks' stored
-// sums S and scales.
+// blocks): the integer sums D, each started at the bits
+// of 1.5 * 2^23 (X = that bit pattern + D; |D| <= 32 * 31 * 128 < 2^22), and
+// the blocks' stored sums S and scales.
 struct Q45Dot {
-  int D0, D1, S0, S1;
+  int X0, X1, S0, S1;
   float dx0, dx1;
+  __device__ __forceinline__ int D0() const { return X0 - static_cast<int>(kMagicBits); }
+  __device__ __forceinline__ int D1() const { return X1 - static_cast<int>(kMagicBits); }
 };
-__device__ __forceinline__ Q45Dot q45_dot(const Q45Unit& U, const uint8_t* x0p) {
-  const uint2* x0 = reinterpret_cast<const uint2*>(x0p);
-  const uint2* x1 = x0 + kQ8Bytes / 8;
-  uint2 a[5], c[5];
-#pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    a[k] = x0[k];
-    c[k] = x1[k];
-  }
-  const uint32_t xa[8] = {a[0].y, a[1].x, a[1].y, a[2].x, a[2].y, a[3].x, a[3].y, a[4].x};
-  const uint32_t xc[8] = {c[0].y, c[1].x, c[1].y, c[2].x, c[2].y, c[3].x, c[3].y, c[4].x};
-  Q45Dot r;
-  r.D0 = dot4_0(U.lo[0], xa[0]);
-  r.D1 = dot4_0(U.hi[0], xc[0]);
-#pragma unroll
-  for (int k = 1; k < 8; ++k) {
-    r.D0 = dot4(U.lo[k], xa[k], r.D0);
-    r.D1 = dot4(U.hi[k], xc[k], r.D1);
-  }
-  r.S0 = static_cast<int>(a[4].y);
-  r.S1 = static_cast<int>(c[4].y);
-  r.dx0 = h2f(a[0].x & 0xffffu);
-  r.dx1 = h2f(c[0].x & 0xffffu);
-  return r;
-}
-
-// The same reading the two blocks (80 bytes at xu, 16-byte aligned) as five
-// 16-byte chunks: block 2p has d at byte 0, values at 4 .. 35 and its sum at
-// 36, block 2p + 1 the same 40 bytes on.  Consecutive units are 80 bytes
-// apart, so eight lanes' chunks cover all 32 banks (the 8-byte reads of
-// q45_dot hit each bank twice).
+// The two blocks (80 bytes at xu, 16-byte aligned) are read as five 16-byte
+// chunks: block 2p has d at byte 0, values at 4 .. 35 and its sum at 36,
+// block 2p + 1 the same 40 bytes on.  Consecutive units are 80 bytes apart,
+// so eight lanes' chunks cover all 32 banks (8-byte reads hit each bank
+// twice).
 __device__ __forceinline__ Q45Dot q45_dot_c(const Q45Unit& U, const uint8_t* xu) {
   const uint4* c = reinterpret_cast<const uint4*>(xu);
   const uint4 c0 = c[0], c1 = c[1], c2 = c[2], c3 = c[3], c4 = c[4];
   const uint32_t xa[8] = {c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w, c2.x};
   const uint32_t xc[8] = {c2.w, c3.x, c3.y, c3.z, c3.w, c4.x, c4.y, c4.z};
   Q45Dot r;
-  r.D0 = dot4_0(U.lo[0], xa[0]);
-  r.D1 = dot4_0(U.hi[0], xc[0]);
+  r.X0 = dot4_magic(U.lo[0], xa[0]);
+  r.X1 = dot4_magic(U.hi[0], xc[0]);
 #pragma unroll
   for (int k = 1; k < 8; ++k) {
-    r.D0 = dot4(U.lo[k], xa[k], r.D0);
-    r.D1 = dot4(U.hi[k], xc[k], r.D1);
+    r.X0 = dot4(U.lo[k], xa[k], r.X0);
+    r.X1 = dot4(U.hi[k], xc[k], r.X1);
   }
   r.S0 = static_cast<int>(c2.y);
   r.S1 = static_cast<int>(c4.w);
@@ -673,13 +650,31 @@ __device__ __forceinline__ Q45Dot q45_dot_c(const Q45Unit& U, const uint8_t* xu)
   return r;
 }
 
-// y contribution of a unit and token: dx * (d*sc*D - dmin*m*S) for both sub-blocks.
-__device__ __forceinline__ float q45_term(const Q45Unit& U, const Q45Dot& r) {
+// Per-unit factors of the float combine, shared by every token: a = d*sc,
+// c = -a * 1.5 * 2^23 (exact: a has at most 17 significant bits), b =
+// -dmin*m, for sub-blocks 2p and 2p + 1.
+struct Q45Coef {
+  float a0, a1, c0, c1, b0, b1;
+};
+__device__ __forceinline__ Q45Coef q45_coef(const Q45Unit& U) {
   const float d = h2f(U.dd & 0xffffu), dmin = h2f(U.dd >> 16);
-  const float sc0 = static_cast<float>(U.scm & 0xffu), sc1 = static_cast<float>((U.scm >> 8) & 0xffu);
-  const float m0 = static_cast<float>((U.scm >> 16) & 0xffu), m1 = static_cast<float>(U.scm >> 24);
-  return r.dx0 * (d * sc0 * static_cast<float>(r.D0) - dmin * m0 * static_cast<float>(r.S0)) +
-         r.dx1 * (d * sc1 * static_cast<float>(r.D1) - dmin * m1 * static_cast<float>(r.S1));
+  Q45Coef C;
+  C.a0 = d * static_cast<float>(U.scm & 0xffu);
+  C.a1 = d * static_cast<float>((U.scm >> 8) & 0xffu);
+  C.c0 = -C.a0 * kMagic;
+  C.c1 = -C.a1 * kMagic;
+  C.b0 = -(dmin * static_cast<float>((U.scm >> 16) & 0xffu));
+  C.b1 = -(dmin * static_cast<float>(U.scm >> 24));
+  return C;
+}
+
+// acc + the unit's y contribution for one token, dx * (d*sc*D - dmin*m*S) for
+// both sub-blocks: d*sc*D in one fma from the biased sum, then the min term
+// and the activation scale in one fma each.
+__device__ __forceinline__ float q45_accum(const Q45Coef& C, const Q45Dot& r, float acc) {
+  const float t0 = __builtin_fmaf(C.b0, static_cast<float>(r.S0), __builtin_fmaf(C.a0, __int_as_float(r.X0), C.c0));
+  const float t1 = __builtin_fmaf(C.b1, static_cast<float>(r.S1), __builtin_fmaf(C.a1, __int_as_float(r.X1), C.c1));
+  return __builtin_fmaf(r.dx1, t1, __builtin_fmaf(r.dx0, t0, acc));
 }
 
 template <int FMT, bool DEBUG>
@@ -730,15 +725,15 @@ void mmvq_q45k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict_
           const int sb = (b0 + b) * 8 + 2 * p;
           if (row_ok) {
             int32_t* Dr = dbgD + static_cast<size_t>(row) * (nb * 8);
-            Dr[sb] = r.D0;
-            Dr[sb + 1] = r.D1;
+            Dr[sb] = r.D0();
+            Dr[sb + 1] = r.D1();
           }
           if (row_raw == 0) {
             dbgS[sb] = r.S0;
             dbgS[sb + 1] = r.S1;
           }
         } else {
-          acc += q45_term(U, r);
+          acc = q45_accum(q45_coef(U), r, acc);
         }
       }
     }
@@ -856,6 +851,7 @@ void mmvq_q45k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict_
       if (b < nbc) {
         Q45Unit U;
         q45_unit<FMT>(wl + b * DL::kBytes, p, U);
+        const Q45Coef C = q45_coef(U);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const Q45Dot r = q45_dot_c(U, xl + t * (nbc * DL::kQ8Seg) + (8 * b + 2 * p) * kQ8Bytes);
@@ -863,15 +859,15 @@ void mmvq_q45k_tn_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict_
             const int sb = (b0 + b) * 8 + 2 * p;
             if (row_ok) {
               int32_t* Dr = dbgD + (static_cast<size_t>(t) * M + row) * (nb * 8);
-              Dr[sb] = r.D0;
-              Dr[sb + 1] = r.D1;
+              Dr[sb] = r.D0();
+              Dr[sb + 1] = r.D1();
             }
             if (row_raw == 0) {
               dbgS[static_cast<size_t>(t) * nb * 8 + sb] = r.S0;
               dbgS[static_cast<size_t>(t) * nb * 8 + sb + 1] = r.S1;
             }
           } else {
-            acc[t] += q45_term(U, r);
+            acc[t] = q45_accum(C, r, acc[t]);
           }
         }
       }

@@ -106,6 +106,21 @@ __device__ __forceinline__ int dot4_0(uint32_t a, uint32_t b) {
   return r;
 }
 
+// An int32 sum started at the bits of 1.5 * 2^23 and read as fp32 is exactly
+// 1.5 * 2^23 + sum while |sum| < 2^22; a product a * sum then takes one fma
+// against the constant -a * 1.5 * 2^23 (exact whenever a has at most 22
+// significant bits), with no int-to-float conversion.
+constexpr uint32_t kMagicBits = 0x4B400000u;
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+
+// dot4 with c = the bits of 1.5 * 2^23 (held in a scalar register), as one
+// instruction.
+__device__ __forceinline__ int dot4_magic(uint32_t a, uint32_t b) {
+  int r;
+  asm("v_dot4_i32_i8 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(kMagicBits));
+  return r;
+}
+
 // Q4_K packed 6-bit scale and min of sub-block j (0..7).  s0, s1, s2 are the
 // 12 packed bytes as little-endian dwords (bytes 0-3, 4-7, 8-11).  Packing as
 // read for the Q4_K format (GGUF K-quant layout):
