@@ -580,21 +580,26 @@ def main():
         y1 = torch.empty((T * top_k, 2 * F), dtype=torch.float32, device=dev)
         hq = torch.empty((T * top_k, F // 32, 40), dtype=torch.uint8, device=dev)
         y2 = torch.empty((T, H), dtype=torch.float32, device=dev)
-        ws1 = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE_SLOTS, 2 * F, H, T, E, top_k), dev)
-        ws2 = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k), dev)
+        # one workspace for the layer: the down call reuses the route tables
+        # the gate||up call prepared (same ids)
+        ws1 = qmm.workspace(max(qmm.workspace_bytes(qmm.QMM_OP_MOE_SLOTS, 2 * F, H, T, E, top_k),
+                                qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k)), dev)
+        ws2 = ws1
 
         def moe_step(c):
             qmm.q8_1_quantize(xm, out=xqm)
             qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gus[c], xqm, ids, out=y1, ws=ws1)
             qmm.swiglu_q8_1(y1, out=hq)
-            qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dns[c], hq, ids, probs, out=y2, ws=ws2)
+            qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dns[c], hq, ids, probs, out=y2, ws=ws2, reuse_routing=True)
 
         log("moe ffn")
         moe_step(0)
         ms_moe, med_moe = timer([lambda c=c: moe_step(c) for c in range(cop)], 300.0)
         ms_gu, med_gu = timer([lambda c=c: qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gus[c], xqm, ids, out=y1, ws=ws1)
                                for c in range(cop)], 150.0)
-        ms_dn, med_dn = timer([lambda c=c: qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dns[c], hq, ids, probs, out=y2, ws=ws2)
+        # the down call as the layer runs it: on the route tables already in ws
+        ms_dn, med_dn = timer([lambda c=c: qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dns[c], hq, ids, probs, out=y2, ws=ws2,
+                                                               reuse_routing=True)
                                for c in range(cop)], 100.0)
 
         def glue():
@@ -606,8 +611,8 @@ def main():
         moe_bytes = wbytes + act_bytes
         tops = 2.0 * macs / (ms_moe * 1e-3) / 1e12
         attain = min(INT8_PEAK_TOPS, 2.0 * macs / moe_bytes * HBM_PEAK_GBPS / 1e3)
-        # the two grouped calls alone (route preparation, repack, GEMM and, for
-        # down, the combine), without the quantize and SwiGLU glue: weights,
+        # the two grouped calls alone (one route preparation, two repacks and GEMMs
+        # and the combine), without the quantize and SwiGLU glue: weights,
         # Q8_1 inputs, the gate||up per-slot rows and the combined output
         g_bytes = wbytes + T * (H // 32) * 40 + T * top_k * 2 * F * 4 + T * top_k * (F // 32) * 40 + T * H * 4
         ms_g = ms_gu + ms_dn

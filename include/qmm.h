@@ -199,8 +199,10 @@ int mmq_q6k_f32(const void* w, const float* x, float* y, int64_t M, int64_t K, i
  *                        holds the buckets, the queue counters, the routed
  *                        rows repacked per expert and, in weighted mode, the
  *                        per-slot fp32 results
- * Work is tiled as 128 weight rows x 32 routed slots of one expert, so an
- * expert's weights are read once per 32 tokens routed to it.  Requires
+ * Work is tiled as 256 (Q4_K, Q5_K) or 128 (Q6_K) weight rows x 32 routed
+ * slots of one expert, so an expert's weights are read once per 32 tokens
+ * routed to it.  The route tables (counts, offsets, column tiles, buckets)
+ * sit at the front of ws and depend only on ids, T, top_k and E.  Requires
  * 1 <= E <= 512, M >= 1, K % 256 == 0, K/256 <= 65536, 1 <= top_k <= min(E, 64),
  * T >= 1, T*top_k <= 2^30, at most 2^30 work entries (ceil(M/128) times the
  * column-tile bound (T*top_k + 31*min(E, T*top_k))/32),
@@ -211,6 +213,21 @@ int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
                     int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,
                     const int32_t* ids, const float* expert_weights, int64_t T, int64_t top_k,
                     float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_mmq_routed -- moe_grouped_mmq without the route preparation:
+ * the route tables already in ws are used.  For the second grouped call of a
+ * routed FFN (the down projection after gate||up), whose tokens are routed
+ * exactly as for the first ([GAP] lever T2: route once per layer).
+ * Precondition (not checked): the last grouped call on this ws, completed or
+ * earlier on the same stream, had the same ids contents, T, top_k and E;
+ * ws_bytes must cover this call's own qmm_workspace_bytes.  Same arguments,
+ * results, limits and errors as moe_grouped_mmq.
+ */
+int moe_grouped_mmq_routed(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
+                           int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,
+                           const int32_t* ids, const float* expert_weights, int64_t T, int64_t top_k,
+                           float* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_slot_mmvq -- the per-(token, slot) expert matvec that the grouped GEMM

@@ -207,13 +207,18 @@ def mmq_q6k_f32(w, x, out=None, ws=None) -> torch.Tensor:
 
 def moe_grouped_mmq(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.Tensor,
                     expert_weights: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                    ws: torch.Tensor | None = None) -> torch.Tensor:
+                    ws: torch.Tensor | None = None, reuse_routing: bool = False) -> torch.Tensor:
     """Grouped expert GEMM.
 
     ``w`` [E, M, K/256, bytes]; ``ids`` int32 [T, top_k]; ``xq`` has T rows
     (one per token) or T*top_k rows (one per slot).  Without
     ``expert_weights`` the result is per slot, [T*top_k, M]; with fp32
     ``expert_weights`` [T, top_k] it is the weighted sum over k, [T, M].
+
+    ``reuse_routing`` calls ``moe_grouped_mmq_routed``: the route tables that
+    the previous grouped call on ``ws`` (same ``ids``, T, top_k and E, issued
+    earlier on the current stream) left in ``ws`` are used instead of being
+    prepared again; ``ws`` must then be given and large enough for this call.
     """
     _need(w, torch.uint8, "w", 4)
     if w.shape[3] != _BLOCK_BYTES[fmt]:
@@ -236,11 +241,14 @@ def moe_grouped_mmq(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.Tens
     out = _out(out, (out_rows, M), torch.float32, w.device)
     need = workspace_bytes(QMM_OP_MOE if expert_weights is not None else QMM_OP_MOE_SLOTS, M, K, T, E, top_k)
     if ws is None:
+        if reuse_routing:
+            raise ValueError("reuse_routing needs the workspace of the call that prepared the routing")
         ws = workspace(need, w.device)
     _need(ws, torch.uint8, "ws", 1)
     stride = w.stride(0)
-    _lib.call("moe_grouped_mmq", fmt, _p(w), E, M, K, stride, _p(xq), rows_per_token, _p(ids),
-              _p(expert_weights), T, top_k, _p(out), _p(ws), ws.numel(), _stream(w.device))
+    _lib.call("moe_grouped_mmq_routed" if reuse_routing else "moe_grouped_mmq", fmt, _p(w), E, M, K, stride,
+              _p(xq), rows_per_token, _p(ids), _p(expert_weights), T, top_k, _p(out), _p(ws), ws.numel(),
+              _stream(w.device))
     return out
 
 

@@ -133,8 +133,8 @@ struct MmqParams {
   const int32_t* counts;        // [E] routed slots per expert
   const int32_t* offsets;       // [E+1] slot offsets into bucket
   const int32_t* bucket;        // [T*top_k] slots grouped by expert
-  const int32_t* work_off;      // [E+1] prefix of m_tiles * column tiles
   const int32_t* ct_off;        // [E+1] prefix of column tiles (chunk rows)
+  int mt;                       // row tiles per expert: work entry = mt * ct_off[e] + m_tile * tiles_e + n_tile
   int E;
   int64_t expert_stride;
   // debug (mode kDebug)
@@ -159,7 +159,7 @@ struct RepackParams {
   const int32_t* ct_off;
   int E, top_k, rows_per_token;
   int32_t* dbgS;                // dense debug: S[row][K/32]
-  unsigned* counters;           // dense: work-queue counters, zeroed here for the GEMM that follows
+  unsigned* counters;           // work-queue counters (and, dense, split-K arrival counters), zeroed here
 };
 
 // Activation row of column `col` of chunk row `ctile` (dense: token; MoE:
@@ -251,7 +251,9 @@ __global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
   const int s = threadIdx.x >> 5, col = threadIdx.x & 31;
   if (P.counters != nullptr && sb == 0 && ctile == 0) {
     if (threadIdx.x < kXcds) P.counters[threadIdx.x] = 0u;
-    P.counters[kTileCntWord + threadIdx.x] = 0u;  // 256 threads: every split-K arrival counter
+    // 256 threads: every split-K arrival counter (dense calls only: a grouped
+    // call's workspace holds its route tables there)
+    if (MODE != kMoe) P.counters[kTileCntWord + threadIdx.x] = 0u;
   }
   __shared__ int s_ct[MODE == kMoe ? kMoeMaxE + 1 : 1];
   if constexpr (MODE == kMoe) {
@@ -748,10 +750,9 @@ struct TileRef {
 // MoE tables copied to LDS at kernel start: the tile search runs in LDS
 // instead of as a chain of dependent global loads.
 struct MoeTables {
-  const int* work_off;  // [E+1]
   const int* counts;    // [E]
   const int* offsets;   // [E]
-  const int* ct_off;    // [E]
+  const int* ct_off;    // [E+1]
 };
 
 template <int FMT, int NT, int MODE, int KS>
@@ -761,15 +762,18 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
   int m_tile;
   const uint8_t* wbase = P.w;
   if constexpr (MODE == kMoe) {
+    // expert e owns work entries [mt * ct_off[e], mt * ct_off[e + 1]): the
+    // one with ct_off[e] <= idx / mt < ct_off[e + 1]
+    const int q = idx / P.mt;
     int lo = 0, hi = P.E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (Tb.work_off[mid] <= idx) lo = mid; else hi = mid;
+      if (Tb.ct_off[mid] <= q) lo = mid; else hi = mid;
     }
     const int e = __builtin_amdgcn_readfirstlane(lo);
     const int cnt = __builtin_amdgcn_readfirstlane(Tb.counts[e]);
     const int ntile = (cnt + BN - 1) / BN;
-    const int local = idx - __builtin_amdgcn_readfirstlane(Tb.work_off[e]);
+    const int local = idx - P.mt * __builtin_amdgcn_readfirstlane(Tb.ct_off[e]);
     m_tile = local / ntile;
     const int n_tile = local % ntile;
     R.tc.n0 = n_tile * BN;
@@ -1012,20 +1016,19 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT 
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ int s_next[2];
   __shared__ int s_last;
-  __shared__ int s_work_off[kTab], s_counts[kTab], s_offsets[kTab], s_ct_off[kTab];
+  __shared__ int s_counts[kTab], s_offsets[kTab], s_ct_off[kTab];
 
-  MoeTables Tb{s_work_off, s_counts, s_offsets, s_ct_off};
+  MoeTables Tb{s_counts, s_offsets, s_ct_off};
   int total;
   if constexpr (MODE == kMoe) {
     for (int i = threadIdx.x; i <= P.E; i += kMmqThreads) {
-      s_work_off[i] = P.work_off[i];
       s_ct_off[i] = P.ct_off[i];
       if (i < P.E) {
         s_counts[i] = P.counts[i];
         s_offsets[i] = P.offsets[i];
       }
     }
-    total = __builtin_amdgcn_readfirstlane(P.work_off[P.E]);
+    total = P.mt * __builtin_amdgcn_readfirstlane(P.ct_off[P.E]);
     __syncthreads();
   } else {
     total = ((P.M + kMmqBM - 1) / kMmqBM) * ((P.T + 32 * NT - 1) / (32 * NT)) * P.nsplit;
@@ -1276,7 +1279,7 @@ int moe_tile_rows(int fmt, int /*nb*/) {
 // moe_tile_rows rows x 32 routed slots.
 int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, const uint8_t* xq,
                    float* out, unsigned* counters, const int32_t* counts, const int32_t* offsets,
-                   const int32_t* bucket, const int32_t* work_off, const int32_t* ct_off, uint8_t* xr,
+                   const int32_t* bucket, const int32_t* ct_off, uint8_t* xr,
                    int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st) {
   RepackParams R{};
   R.xq = xq;
@@ -1289,6 +1292,7 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   R.E = E;
   R.top_k = top_k;
   R.rows_per_token = rows_per_token;
+  R.counters = counters;  // zeroed for the GEMM (route tables reused from an earlier call leave them dirty)
   int rc = launch_repack<kMoe>(R, nb, max_ctiles, st);
   if (rc != QMM_OK) return rc;
   MmqParams P{};
@@ -1303,11 +1307,12 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   P.counts = counts;
   P.offsets = offsets;
   P.bucket = bucket;
-  P.work_off = work_off;
   P.ct_off = ct_off;
   P.E = E;
   P.expert_stride = stride;
-  const bool whole_k = moe_tile_rows(fmt, nb) == StepSplit<QMM_Q4_K, 1>::kBM;
+  const int bm = moe_tile_rows(fmt, nb);
+  P.mt = (M + bm - 1) / bm;
+  const bool whole_k = bm == StepSplit<QMM_Q4_K, 1>::kBM;
   if (fmt == QMM_Q4_K)
     return whole_k ? launch_mmq<QMM_Q4_K, 1, kMoe, 1>(P, 0, st) : launch_mmq<QMM_Q4_K, 1, kMoe>(P, 0, st);
   if (fmt == QMM_Q5_K)

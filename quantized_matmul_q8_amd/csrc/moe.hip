@@ -38,7 +38,7 @@ constexpr int kMoeBM = 128;  // weight rows of the smaller grouped tile (bounds 
 
 int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, const uint8_t* xq,
                    float* out, unsigned* counters, const int32_t* counts, const int32_t* offsets,
-                   const int32_t* bucket, const int32_t* work_off, const int32_t* ct_off, uint8_t* xr,
+                   const int32_t* bucket, const int32_t* ct_off, uint8_t* xr,
                    int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st);
 int64_t moe_max_ctiles(int64_t slots, int64_t E);
 int moe_tile_rows(int fmt, int nb);
@@ -48,7 +48,6 @@ struct MoeLayout {
   unsigned* counters;
   int32_t* counts;
   int32_t* offsets;
-  int32_t* work_off;
   int32_t* ct_off;
   int32_t* bucket;
   float* scratch;
@@ -65,12 +64,11 @@ static MoeLayout moe_layout(void* ws, int64_t M, int64_t K, int64_t T, int64_t E
   MoeLayout L{};
   uint8_t* b = static_cast<uint8_t*>(ws);
   size_t off = kMoeCounterBytes;
-  const size_t ints = static_cast<size_t>(E) + 3 * static_cast<size_t>(E + 1) + static_cast<size_t>(T * top_k);
+  const size_t ints = static_cast<size_t>(E) + 2 * static_cast<size_t>(E + 1) + static_cast<size_t>(T * top_k);
   L.counters = reinterpret_cast<unsigned*>(b);
   L.counts = reinterpret_cast<int32_t*>(b + off);
   L.offsets = L.counts + E;
-  L.work_off = L.offsets + (E + 1);
-  L.ct_off = L.work_off + (E + 1);
+  L.ct_off = L.offsets + (E + 1);
   L.bucket = L.ct_off + (E + 1);
   off = align_up(off + ints * 4, 1024);
   L.chunks = b + off;
@@ -107,12 +105,10 @@ __device__ __forceinline__ uint64_t peers_of(int e, bool v, int nbits) {
 constexpr int kRouteBatch = 8;
 
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int mt, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ work_off, int32_t* __restrict__ ct_off,
-    int32_t* __restrict__ bucket, unsigned* __restrict__ counters) {
+    const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ ct_off, int32_t* __restrict__ bucket, unsigned* __restrict__ counters) {
   __shared__ int cnt[kRouteWaves][kMoeMaxE];
   __shared__ int s_off[kMoeMaxE + 1];
-  __shared__ int s_wsum[kMoeMaxE + 1];
   __shared__ int s_ct[kMoeMaxE + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int i = tid; i < kRouteWaves * kMoeMaxE; i += kRouteThreads) (&cnt[0][0])[i] = 0;
@@ -149,35 +145,31 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     counts[e] = run;
     s_off[e] = run;
     s_ct[e] = (run + kMoeBN - 1) / kMoeBN;
-    s_wsum[e] = s_ct[e] * mt;
   }
   __syncthreads();
   // exclusive scans over experts (E <= 512 fits one wave's 8 passes)
   if (wave == 0) {
-    int off = 0, woff = 0, coff = 0;
+    int off = 0, coff = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
       const int e = e0 + lane;
-      int c = e < E ? s_off[e] : 0, wv = e < E ? s_wsum[e] : 0, cv = e < E ? s_ct[e] : 0;
+      int c = e < E ? s_off[e] : 0, cv = e < E ? s_ct[e] : 0;
       // inclusive wave scans
       for (int d = 1; d < 64; d <<= 1) {
-        const int cu = __shfl_up(c, d), wu = __shfl_up(wv, d), vu = __shfl_up(cv, d);
-        if (lane >= d) { c += cu; wv += wu; cv += vu; }
+        const int cu = __shfl_up(c, d), vu = __shfl_up(cv, d);
+        if (lane >= d) { c += cu; cv += vu; }
       }
-      const int cx = __shfl_up(c, 1), wx = __shfl_up(wv, 1), vx = __shfl_up(cv, 1);
-      const int ce = lane == 0 ? 0 : cx, we = lane == 0 ? 0 : wx, ve = lane == 0 ? 0 : vx;
+      const int cx = __shfl_up(c, 1), vx = __shfl_up(cv, 1);
+      const int ce = lane == 0 ? 0 : cx, ve = lane == 0 ? 0 : vx;
       if (e < E) {
         s_off[e] = off + ce;
         offsets[e] = off + ce;
-        work_off[e] = woff + we;
         ct_off[e] = coff + ve;
       }
       off += __shfl(c, 63);
-      woff += __shfl(wv, 63);
       coff += __shfl(cv, 63);
     }
     if (lane == 0) {
       offsets[E] = off;
-      work_off[E] = woff;
       ct_off[E] = coff;
     }
   }
@@ -247,10 +239,13 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
 
 using namespace qmm;
 
-extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
-                               int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,
-                               const int32_t* ids, const float* expert_weights, int64_t T,
-                               int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream) {
+// One grouped call; with `routed`, the route tables already in ws (left by
+// an earlier grouped call on ws with the same ids, T, top_k and E) are used
+// instead of being prepared again.
+static int grouped_call(bool routed, int fmt, const void* w, int64_t E, int64_t M, int64_t K,
+                        int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token, const int32_t* ids,
+                        const float* expert_weights, int64_t T, int64_t top_k, float* y, void* ws, size_t ws_bytes,
+                        void* stream) {
   if (fmt != QMM_Q4_K && fmt != QMM_Q5_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
   if (E < 1 || E > kMoeMaxE || M < 1 || M > (1 << 30) || K < kQK || (K % kQK) != 0 || K / kQK > (1 << 16) ||
       T < 1 || top_k < 1 || top_k > E || top_k > kMoeMaxTopK || T * top_k > (1 << 30))
@@ -270,16 +265,17 @@ extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int
   if (ws_bytes < L.bytes) return QMM_ERR_WORKSPACE;
   hipStream_t st = to_stream(stream);
   const int n = static_cast<int>(T * top_k);
-  const int bm = moe_tile_rows(fmt, static_cast<int>(K / kQK));
-  const int mt = static_cast<int>((M + bm - 1) / bm);
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ids, n, static_cast<int>(E),
-                     mt, L.counts, L.offsets, L.work_off, L.ct_off, L.bucket, L.counters);
-  int rc = launch_status();
-  if (rc != QMM_OK) return rc;
+  int rc;
+  if (!routed) {
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ids, n, static_cast<int>(E),
+                       L.counts, L.offsets, L.ct_off, L.bucket, L.counters);
+    rc = launch_status();
+    if (rc != QMM_OK) return rc;
+  }
   float* out = expert_weights ? L.scratch : y;
   rc = mmq_moe_launch(fmt, static_cast<const uint8_t*>(w), expert_stride_bytes, static_cast<int>(M),
                       static_cast<int>(K / kQK), static_cast<const uint8_t*>(xq), out, L.counters,
-                      L.counts, L.offsets, L.bucket, L.work_off, L.ct_off, L.chunks,
+                      L.counts, L.offsets, L.bucket, L.ct_off, L.chunks,
                       static_cast<int>(moe_max_ctiles(T * top_k, E)), static_cast<int>(E),
                       static_cast<int>(top_k), static_cast<int>(x_rows_per_token), st);
   if (rc != QMM_OK || !expert_weights) return rc;
@@ -300,3 +296,20 @@ extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int
   }
   return launch_status();
 }
+
+extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
+                               int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,
+                               const int32_t* ids, const float* expert_weights, int64_t T,
+                               int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream) {
+  return grouped_call(false, fmt, w, E, M, K, expert_stride_bytes, xq, x_rows_per_token, ids, expert_weights,
+                           T, top_k, y, ws, ws_bytes, stream);
+}
+
+extern "C" int moe_grouped_mmq_routed(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
+                                      int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,
+                                      const int32_t* ids, const float* expert_weights, int64_t T,
+                                      int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream) {
+  return grouped_call(true, fmt, w, E, M, K, expert_stride_bytes, xq, x_rows_per_token, ids, expert_weights,
+                           T, top_k, y, ws, ws_bytes, stream);
+}
+

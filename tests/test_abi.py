@@ -95,8 +95,9 @@ def test_mmq_errors(fn):
     assert f(FAKE, FAKE, FAKE, 4, 256, 1, FAKE, 8, NUL) == _lib.QMM_ERR_WORKSPACE
 
 
-def test_moe_errors():
-    f = L.moe_grouped_mmq
+@pytest.mark.parametrize("entry", ["moe_grouped_mmq", "moe_grouped_mmq_routed"])
+def test_moe_errors(entry):
+    f = getattr(L, entry)
     ok = dict(fmt=_lib.QMM_Q4_K, w=FAKE, E=8, M=64, K=256, stride=64 * 144, xq=FAKE, rpt=1,
               ids=FAKE, p=NUL, T=4, top_k=2, y=FAKE, ws=FAKE, wsb=16, st=NUL)
 

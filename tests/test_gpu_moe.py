@@ -113,6 +113,31 @@ def test_top1_single_expert_matches_dense_gemm(K):
     assert_parity(y_moe, y_mmq.astype(np.float64), 2 * bound, "grouped vs dense")
 
 
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
+def test_routed_call_reuses_route_tables(fmt):
+    # a per-slot call (gate||up shape) prepares the routing in ws; the weighted
+    # call that follows on the same ws with reuse_routing (other M and K, one
+    # activation row per slot) must equal the same call routed afresh
+    E, T, top_k, H, F = 16, 70, 4, 512, 256
+    g = qmm_synth.rng(53)
+    w_gu = _experts(fmt, E, 2 * F, H, g)
+    w_dn = _experts(fmt, E, H, F, g)
+    xq = oracle.quantize_q8_1(qmm_synth.activations(g, T, H))
+    hq = oracle.quantize_q8_1(qmm_synth.activations(g, T * top_k, F))
+    ids, probs = qmm_synth.router(g, T, E, top_k)
+    need = max(qmm.workspace_bytes(qmm.QMM_OP_MOE_SLOTS, 2 * F, H, T, E, top_k),
+               qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k))
+    ws = qmm.workspace(need, dev(ids).device)
+    say(f"moe_grouped_mmq_routed {fmt}", f"E={E} T={T} top_k={top_k} H={H} F={F}")
+    d_ids, d_probs, d_hq, d_wdn = dev(ids), dev(probs), dev(hq), dev(w_dn)
+    qmm.moe_grouped_mmq(GEN[fmt][2], dev(w_gu), dev(xq), d_ids, ws=ws)
+    y_routed = host(qmm.moe_grouped_mmq(GEN[fmt][2], d_wdn, d_hq, d_ids, d_probs, ws=ws, reuse_routing=True))
+    y_fresh = host(qmm.moe_grouped_mmq(GEN[fmt][2], d_wdn, d_hq, d_ids, d_probs))
+    assert np.array_equal(y_routed.view(np.uint32), y_fresh.view(np.uint32))
+    ys, bs = oracle.grouped_blocks(GEN[fmt][1], w_dn, oracle.q8_1_dequant(hq), ids, top_k)
+    assert_parity(y_routed, oracle.combine(ys, probs), oracle.combine(bs, np.abs(probs)), "routed weighted")
+
+
 def test_token_permutation_permutes_outputs():
     g = qmm_synth.rng(41)
     E, M, K, T, top_k = 8, 128, 512, 60, 2
@@ -155,7 +180,8 @@ def _q8_1_error_bound(hq):
 
 def test_full_routed_ffn_gpu_chain():
     """128 experts, T = 512, top-8, the whole routed FFN on the GPU (quantize,
-    grouped gate||up, SwiGLU -> Q8_1, grouped down with the routing weights)
+    grouped gate||up, SwiGLU -> Q8_1, grouped down with the routing weights,
+    reusing the gate||up call's route tables)
     against the oracle chain, with the tolerance carried through the glue:
 
       |y2_gpu - y2_ora| <= sum_k p_k sum_j |W_down| |x_gpu - x_ora|  +  1e-4 sum_k p_k sum_j |W_down| |x_gpu|
@@ -173,9 +199,13 @@ def test_full_routed_ffn_gpu_chain():
     xq_gpu = qmm.q8_1_quantize(dev(x))
     xq = oracle.quantize_q8_1(x)
     assert np.array_equal(host(xq_gpu), xq)
-    y1_d = qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(gate_up), xq_gpu, dev(ids))
+    # one workspace for both calls; the down call reuses the gate||up routing
+    ws = qmm.workspace(max(qmm.workspace_bytes(qmm.QMM_OP_MOE_SLOTS, 2 * F, H, T, E, top_k),
+                           qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k)), xq_gpu.device)
+    d_ids = dev(ids)
+    y1_d = qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(gate_up), xq_gpu, d_ids, ws=ws)
     hq_d = qmm.swiglu_q8_1(y1_d)
-    y2 = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), hq_d, dev(ids), dev(probs)))
+    y2 = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), hq_d, d_ids, dev(probs), ws=ws, reuse_routing=True))
     y1, hq_gpu = host(y1_d), host(hq_d)
     # step 1: gate||up parity
     ref1, b1 = oracle.grouped_blocks(oracle.q4k_dequant, gate_up, oracle.q8_1_dequant(xq), ids, 1)
