@@ -465,19 +465,38 @@ constexpr bool kLean = NT == 1;
 // alpha[u][row] = d*sc and, for Q4_K, mu[j][row] = -dmin*m.
 template <int FMT>
 __device__ __forceinline__ void write_scales_q4fam(const MmqPrefetch<FMT>& F, float* wave_lds, int col, int g) {
-  // lane (row col, half g) decodes sub-blocks 4g .. 4g+3 of its row
+  // lane (row col, half g) decodes sub-blocks 4g .. 4g+3 of its row, whose
+  // four 6-bit scales and mins come out as the bytes of one dword each (the
+  // packing of q4k_scale_min, four sub-blocks at a time): sub-blocks 0-3
+  // take bits 0-5 of S[0..3] (scales) and S[4..7] (mins); sub-blocks 4-7 the
+  // nibbles of S[8..11] (low: scales, high: mins) with bits 6-7 of S[0..3]
+  // (scales) and S[4..7] (mins) as bits 4-5
   const float d = h2f(F.hdr.x & 0xffffu), dmin = h2f(F.hdr.x >> 16);
-  float* wa = wave_lds;
-  __bf16* wm = reinterpret_cast<__bf16*>(wave_lds + 8 * 32);
+  const uint32_t s0 = F.hdr.y, s1 = F.hdr.z, s2 = F.hdr.w;
+  const uint32_t sc = g == 0 ? s0 & 0x3f3f3f3fu : (s2 & 0x0f0f0f0fu) | ((s0 >> 2) & 0x30303030u);
+  const uint32_t mn = g == 0 ? s1 & 0x3f3f3f3fu : ((s2 >> 4) & 0x0f0f0f0fu) | ((s1 >> 2) & 0x30303030u);
+  float* wa = wave_lds + 4 * g * 32 + col;
+  // -dmin*m (exact in fp32: at most 17 significant bits) as three bf16 parts
+  // by truncation: p0 keeps its top 8 significant bits, p1 the next 8 of the
+  // exact remainder, p2 (at most one bit) the rest, so p0 + p1 + p2 = -dmin*m
+  uint32_t part[3][4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    int sc, m;
-    q4k_scale_min(4 * g + jj, F.hdr.y, F.hdr.z, F.hdr.w, sc, m);
-    wa[(4 * g + jj) * 32 + col] = d * static_cast<float>(sc);
-    // -dmin*m (exact in fp32: at most 17 significant bits) as three bf16 parts
-    const int e = col * 8 + 4 * g + jj;
-    split3_bf16(-(dmin * static_cast<float>(m)), wm[e], wm[256 + e], wm[512 + e]);
+    wa[jj * 32] = d * static_cast<float>((sc >> (8 * jj)) & 0xffu);
+    const float x = -(dmin * static_cast<float>((mn >> (8 * jj)) & 0xffu));
+    const uint32_t p0 = __float_as_uint(x) & 0xffff0000u;
+    const float r = x - __uint_as_float(p0);
+    const uint32_t p1 = __float_as_uint(r) & 0xffff0000u;
+    part[0][jj] = p0;
+    part[1][jj] = p1;
+    part[2][jj] = __float_as_uint(r - __uint_as_float(p1));
   }
+  // bf16 = the high half of each part; [3 parts][32 rows][8 sub-blocks]
+  uint2* wm = reinterpret_cast<uint2*>(wave_lds + 8 * 32);
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+    wm[(q * 32 + col) * 2 + g] = make_uint2((part[q][0] >> 16) | (part[q][1] & 0xffff0000u),
+                                            (part[q][2] >> 16) | (part[q][3] & 0xffff0000u));
 }
 __device__ __forceinline__ void write_scales(const MmqPrefetch<QMM_Q4_K>& F, float* wave_lds, int col, int g) {
   write_scales_q4fam(F, wave_lds, col, g);
