@@ -4,14 +4,16 @@
 Headline workload (the decode matvec shape the metric is quoted on):
 W 4096 x 11008 in Q4_K and the same shape in Q6_K, x fp32 N(0, 1) of length
 11008, T = 1.  One step = quantize x to Q8_1, then the Q4_K and the Q6_K
-matvec (the whole decode path), with inputs resident in HBM.  The weights
+matvec (the whole decode path) as one paired launch (mmvq_pair), with inputs
+resident in HBM.  The weights
 rotate over >= 4 GB of on-device copies, so no step reads them from the
 256 MB Infinity Cache.  Steps are captured in one HIP graph and replayed;
 HIP events bracket the replay.  `value` is algorithmic bytes per step
 (quantized weights + Q8_1 activations + fp32 input/outputs) over step time.
 
 The same JSON line carries:
-  roofline      the dominant kernel (the Q6_K matvec, 37 MB per launch):
+  roofline      the dominant kernel (the paired Q6_K + Q4_K matvec, 62 MB per
+                launch):
                 algorithmic bytes over its launch duration (HIP events
                 around a graph of back-to-back launches on the launch
                 stream, divided by the launch count), against 8 TB/s HBM;
@@ -23,7 +25,8 @@ The same JSON line carries:
                 `us` (graph mean over >= 100 launches, weights rotated past
                 the MALL) and `median_us` (median of >= 100 launches
                 bracketed by event pairs on the launch stream; these include
-                ~1-2 us of event overhead).  Rows: the matvec at T = 1 and 4,
+                ~1-2 us of event overhead).  Rows: the decode step with the
+                two matvecs as separate launches, the matvec at T = 1 and 4,
                 the Q5_K matvec, the small-T sweep (matvec T = 1..8 and GEMM
                 T = 1..64 on the decode shape), the read-only HBM ceiling at
                 the matvec byte counts (best of a geometry sweep), the
@@ -58,7 +61,7 @@ MIN_LAUNCHES = 100
 
 # traffic measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE for the
 # dominant kernel (profiles/); None until taken for the current kernel
-DOMINANT_TRAFFIC_BYTES = 37246159   # mmvq_q6k, profiles/mmvq_decode_4096x11008_t1.md
+DOMINANT_TRAFFIC_BYTES = 62736488   # mmvq_pair Q6_K + Q4_K, profiles/mmvq_decode_4096x11008_t1.md
 
 
 def log(*a):
@@ -365,60 +368,78 @@ def main():
     y4 = torch.empty((1, M), dtype=torch.float32, device=dev)
     y6 = torch.empty((1, M), dtype=torch.float32, device=dev)
 
-    def make_step(c):
+    def make_step(c, paired=True):
         def step():
             qmm.q8_1_quantize(x1, out=xq1)
-            qmm.mmvq_q4k(w4[c], xq1, out=y4)
-            qmm.mmvq_q6k(w6[c], xq1, out=y6)
+            if paired:    # both matvecs in one launch
+                qmm.mmvq_pair(qmm.QMM_Q6_K, w6[c], qmm.QMM_Q4_K, w4[c], xq1, out_a=y6, out_b=y4)
+            else:
+                qmm.mmvq_q4k(w4[c], xq1, out=y4)
+                qmm.mmvq_q6k(w6[c], xq1, out=y6)
         return step
 
-    steps = [make_step(c) for c in range(R)]
-    for i in range(args.warmup):
-        steps[i % R]()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(args.steps):
+    def time_steps(paired):
+        steps = [make_step(c, paired) for c in range(R)]
+        for i in range(args.warmup):
             steps[i % R]()
-    g.replay()                      # graph warm-up (untimed)
-    torch.cuda.synchronize()
-    a, b = _events(torch)
-    torch.cuda.synchronize()
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    ms_step = a.elapsed_time(b) / args.steps
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                steps[i % R]()
+        g.replay()                      # graph warm-up (untimed)
+        torch.cuda.synchronize()
+        a, b = _events(torch)
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms_step = time_steps(True)
     log(f"decode step: {ms_step * 1e3:.3f} us per step over {args.steps} graph-replayed steps")
+    ms_step_sep = time_steps(False)
+    log(f"decode step with separate matvec launches: {ms_step_sep * 1e3:.3f} us")
     xq_bytes = (K // 32) * 40
     bytes_q4 = w4h.nbytes + xq_bytes + M * 4
     bytes_q6 = w6h.nbytes + xq_bytes + M * 4
+    bytes_pair = w4h.nbytes + w6h.nbytes + xq_bytes + 2 * M * 4   # one read of the activation row
     bytes_quant = K * 4 + xq_bytes
-    step_bytes = bytes_q4 + bytes_q6 + bytes_quant
+    step_bytes = bytes_pair + bytes_quant
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
     def gbps(nbytes, ms):
         return round(nbytes / (ms * 1e-3) / 1e9, 1)
 
-    # dominant kernel: Q6_K matvec.  Launch duration = HIP events around a
-    # graph of back-to-back launches (rotating weight copies) / launches; this
-    # agrees with rocprofv3's kernel durations.
+    # dominant kernel: the paired Q6_K + Q4_K matvec.  Launch duration = HIP
+    # events around a graph of back-to-back launches (rotating weight copies)
+    # / launches; this agrees with rocprofv3's kernel durations.
+    pair_fns = [lambda c=c: qmm.mmvq_pair(qmm.QMM_Q6_K, w6[c], qmm.QMM_Q4_K, w4[c], xq1, out_a=y6, out_b=y4)
+                for c in range(R)]
     q6_fns = [lambda c=c: qmm.mmvq_q6k(w6[c], xq1, out=y6) for c in range(R)]
     q4_fns = [lambda c=c: qmm.mmvq_q4k(w4[c], xq1, out=y4) for c in range(R)]
+    pair_graph, pair_med = timer(pair_fns, 14.0, reps=200)
     q6_graph, q6_med = timer(q6_fns, 11.0, reps=200)
     q4_graph, q4_med = timer(q4_fns, 8.0, reps=200)
-    ach = bytes_q6 / (q6_graph * 1e-3) / 1e9
-    roofline = {"kernel": "mmvq_q6k (4096x11008, T=1)", "bound": "hbm", "achieved": round(ach, 1),
+    ach = bytes_pair / (pair_graph * 1e-3) / 1e9
+    roofline = {"kernel": "mmvq_pair (Q6_K + Q4_K, 2 x 4096x11008, T=1)", "bound": "hbm", "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                "traffic": DOMINANT_TRAFFIC_BYTES, "algorithmic_bytes": bytes_q6,
-                "launch_us": round(q6_graph * 1e3, 3), "event_pair_median_us": round(q6_med * 1e3, 3)}
-    log(f"mmvq_q6k {q6_graph * 1e3:.3f} us (graph), {q6_med * 1e3:.3f} us (event-pair median); "
-        f"mmvq_q4k {q4_graph * 1e3:.3f} us")
+                "traffic": DOMINANT_TRAFFIC_BYTES, "algorithmic_bytes": bytes_pair,
+                "launch_us": round(pair_graph * 1e3, 3), "event_pair_median_us": round(pair_med * 1e3, 3)}
+    log(f"mmvq_pair {pair_graph * 1e3:.3f} us (graph), {pair_med * 1e3:.3f} us (event-pair median); "
+        f"mmvq_q6k {q6_graph * 1e3:.3f} us; mmvq_q4k {q4_graph * 1e3:.3f} us")
     also = {}
+    also["decode_step_separate_launches"] = {"us": round(ms_step_sep * 1e3, 3),
+                                             "GBps": gbps(bytes_q4 + bytes_q6 + bytes_quant, ms_step_sep),
+                                             "step": "q8_1_quantize + mmvq_q4k + mmvq_q6k"}
+    also["mmvq_pair_t1"] = {"us": round(pair_graph * 1e3, 3), "median_us": round(pair_med * 1e3, 3),
+                            "GBps": round(ach, 1), "frac_hbm": round(ach / HBM_PEAK_GBPS, 4),
+                            "separate_launches_us": round((q6_graph + q4_graph) * 1e3, 3)}
     also["mmvq_q4k_t1"] = {"us": round(q4_graph * 1e3, 3), "median_us": round(q4_med * 1e3, 3),
                            "GBps": gbps(bytes_q4, q4_graph), "frac_hbm": round(gbps(bytes_q4, q4_graph) / HBM_PEAK_GBPS, 4)}
     also["mmvq_q6k_t1"] = {"us": round(q6_graph * 1e3, 3), "median_us": round(q6_med * 1e3, 3),
-                           "GBps": round(ach, 1), "frac_hbm": round(ach / HBM_PEAK_GBPS, 4)}
+                           "GBps": gbps(bytes_q6, q6_graph), "frac_hbm": round(gbps(bytes_q6, q6_graph) / HBM_PEAK_GBPS, 4)}
 
     # read-only ceiling at the same byte counts: best of a geometry sweep
     # (16-byte loads in flight per thread, one-pass grid or a persistent
@@ -663,7 +684,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": "decode_mmvq_4096x11008_q4k+q6k_t1", "M": M, "K": K, "T": 1,
-                   "step": "q8_1_quantize + mmvq_q4k + mmvq_q6k", "step_bytes": step_bytes,
+                   "step": "q8_1_quantize + mmvq_pair (mmvq_q6k and mmvq_q4k rows in one launch)",
+                   "step_bytes": step_bytes,
                    "weight_copies_rotated": R, "parallelism": "single_gpu"},
         "roofline": roofline, "cpu_baseline": cpu, "also": also,
     }

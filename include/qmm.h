@@ -108,6 +108,25 @@ int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int64_t K, int6
              void* stream);
 
 /*
+ * mmvq_pair -- two one-token matvecs on the same activation row, in one
+ * launch: ya[Ma] = xq . Wa^T and yb[Mb] = xq . Wb^T, Wa and Wb each in any
+ * of QMM_Q4_K, QMM_Q5_K, QMM_Q6_K (the decode matvec of [8e] §2-§3.2; one
+ * launch for products that share their input, as [GAP] lever T4 shares one
+ * activation preparation across same-input products).  xq holds one Q8_1
+ * row of K values; wa, wb are [Ma][K/256] and [Mb][K/256] blocks.  Each
+ * output has the bits the single matvec (mmvq_q4k / mmvq_q5k / mmvq_q6k at
+ * T = 1) gives for it: the workgroups of the two matrices run the same code
+ * in one grid, so the launch has one tail instead of two.  Where the Q6_K
+ * one-token kernel does not take a shape (rows of more than 46 super-blocks,
+ * or Mb * K/256 not a multiple of 8), the two matvecs run as two launches.
+ * Requires Ma, Mb >= 1, K % 256 == 0, 16-byte aligned pointers; ya and yb
+ * must not overlap.  Errors as mmvq_q4k; QMM_ERR_UNSUPPORTED for any other
+ * format.
+ */
+int mmvq_pair(int fmt_a, const void* wa, int64_t Ma, float* ya, int fmt_b, const void* wb, int64_t Mb,
+              float* yb, const void* xq, int64_t K, void* stream);
+
+/*
  * mmq_q4k / mmq_q6k -- prefill GEMM y[T][M] = xq[T][K] . W[M][K]^T for any
  * T >= 1 ([MMQ] "Kernel architecture": fused dequant inside the matrix
  * inner loop, Q8_1 activations; "Persistent kernel + atomic work queue").

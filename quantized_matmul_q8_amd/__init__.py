@@ -24,7 +24,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "q8_1_quantize", "mmvq_q4k", "mmvq_q5k", "mmvq_q6k", "mmq_q4k", "mmq_q5k", "mmq_q6k", "mmq_q4k_f32", "mmq_q5k_f32",
+    "q8_1_quantize", "mmvq_q4k", "mmvq_q5k", "mmvq_q6k", "mmvq_pair", "mmq_q4k", "mmq_q5k", "mmq_q6k", "mmq_q4k_f32", "mmq_q5k_f32",
     "mmq_q6k_f32",
     "moe_grouped_mmq", "moe_slot_mmvq",
     "swiglu_q8_1", "workspace", "workspace_bytes", "debug_subdots", "probe_read", "probe_read_geom",
@@ -150,6 +150,28 @@ def mmvq_q5k(w: torch.Tensor, xq: torch.Tensor, out: torch.Tensor | None = None)
 def mmvq_q6k(w: torch.Tensor, xq: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Decode matvec, Q6_K weights x Q8_1 activations (T <= 8) -> fp32 [T, M]."""
     return _mmvq("mmvq_q6k", QMM_Q6_K, w, xq, out)
+
+
+def mmvq_pair(fmt_a: int, wa: torch.Tensor, fmt_b: int, wb: torch.Tensor, xq: torch.Tensor,
+              out_a: torch.Tensor | None = None, out_b: torch.Tensor | None = None):
+    """Two one-token matvecs on the same Q8_1 row ``xq[1, K/32, 40]`` in one
+    launch -> (fp32 [1, Ma], fp32 [1, Mb]), each bit-identical to the single
+    matvec of its format."""
+    Ma, K = _weights(wa, fmt_a, "wa")
+    Mb, Kb = _weights(wb, fmt_b, "wb")
+    if Kb != K:
+        raise ValueError(f"wa and wb must have the same K, got {K} and {Kb}")
+    if _acts(xq, K) != 1:
+        raise ValueError("mmvq_pair takes one activation row")
+    if wb.device != wa.device or xq.device != wa.device:
+        raise ValueError("wa, wb and xq must be on one device")
+    out_a = _out(out_a, (1, Ma), torch.float32, wa.device, "out_a")
+    out_b = _out(out_b, (1, Mb), torch.float32, wa.device, "out_b")
+    if out_a.data_ptr() == out_b.data_ptr():
+        raise ValueError("out_a and out_b must be distinct")
+    _lib.call("mmvq_pair", fmt_a, _p(wa), Ma, _p(out_a), fmt_b, _p(wb), Mb, _p(out_b), _p(xq), K,
+              _stream(wa.device))
+    return out_a, out_b
 
 
 def _mmq(name: str, fmt: int, w, xq, out, ws):

@@ -39,6 +39,7 @@ SIGNATURES = {
     "mmvq_q4k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "mmvq_q5k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "mmvq_q6k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "mmvq_pair": (_i, [_i, _vp, _i64, _vp, _i, _vp, _i64, _vp, _vp, _i64, _vp]),
     "mmq_q4k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "mmq_q5k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "mmq_q6k": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),

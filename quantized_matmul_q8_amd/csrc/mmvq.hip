@@ -36,6 +36,10 @@
 // When T*K is too large for the LDS budget the row is processed in K
 // segments of equal length.  The row sum is a wave reduction; lane 0 writes
 // y[t*M + row].
+#include <algorithm>
+#include <initializer_list>
+#include <utility>
+
 #include "qmm_common.hpp"
 
 namespace qmm {
@@ -677,15 +681,16 @@ __device__ __forceinline__ float q45_accum(const Q45Coef& C, const Q45Dot& r, fl
   return __builtin_fmaf(r.dx1, t1, __builtin_fmaf(r.dx0, t0, acc));
 }
 
+// Workgroup blk of the one-token Q4_K / Q5_K matvec (rows 8 blk .. 8 blk + 7),
+// with the workgroup's LDS at lds.
 template <int FMT, bool DEBUG>
-__global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void mmvq_q45k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb, int cb,
-                         int32_t* __restrict__ dbgD, int32_t* __restrict__ dbgS) {
+__device__ __forceinline__ void q45_t1_body(uint8_t* lds, int blk, const uint8_t* w, const uint8_t* xq,
+                                            float* __restrict__ y, int M, int nb, int cb,
+                                            int32_t* __restrict__ dbgD, int32_t* __restrict__ dbgS) {
   using DL = MvDma<FMT>;
-  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row_raw = blockIdx.x * kMmvqWaves + wave;
+  const int row_raw = blk * kMmvqWaves + wave;
   const bool row_ok = row_raw < M;
   const int row = row_ok ? row_raw : M - 1;  // out-of-range waves read a valid row, store nothing
   const uint8_t* wrow = w + static_cast<size_t>(row) * nb * DL::kBytes;
@@ -748,17 +753,40 @@ void mmvq_q45k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict_
 }
 
 template <int FMT, bool DEBUG>
+__global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void mmvq_q45k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb, int cb,
+                         int32_t* __restrict__ dbgD, int32_t* __restrict__ dbgS) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  q45_t1_body<FMT, DEBUG>(lds, blockIdx.x, w, xq, y, M, nb, cb, dbgD, dbgS);
+}
+
+// LDS of the one-token Q4_K / Q5_K matvec: the eight row regions and the
+// activation segment of cb super-blocks.
+template <int FMT>
+static size_t t1_lds_bytes(int cb) {
+  using DL = MvDma<FMT>;
+  return static_cast<size_t>(kMmvqWaves) * DL::kRounds * 1024 +
+         (static_cast<size_t>(cb) * DL::kQ8Seg + 1023) / 1024 * 1024;
+}
+
+// Super-blocks per segment of the one-token Q4_K / Q5_K matvec (equal
+// segments of at most kMaxBlocks).
+template <int FMT>
+static int t1_seg_blocks(int nb) {
+  using DL = MvDma<FMT>;
+  const int nseg = (nb + DL::kMaxBlocks - 1) / DL::kMaxBlocks;
+  return (nb + nseg - 1) / nseg;
+}
+
+template <int FMT, bool DEBUG>
 static int launch_mmvq_t1(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, int32_t* S,
                           hipStream_t st) {
   using DL = MvDma<FMT>;
-  const int nseg = (nb + DL::kMaxBlocks - 1) / DL::kMaxBlocks;
-  const int cb = (nb + nseg - 1) / nseg;
-  const size_t lds = static_cast<size_t>(kMmvqWaves) * DL::kRounds * 1024 +
-                     (static_cast<size_t>(cb) * DL::kQ8Seg + 1023) / 1024 * 1024;
+  const int cb = t1_seg_blocks<FMT>(nb);
+  const size_t lds = t1_lds_bytes<FMT>(cb);
   static bool attr_set = false;
   if (!attr_set) {
-    const size_t lmax = static_cast<size_t>(kMmvqWaves) * DL::kRounds * 1024 +
-                        (static_cast<size_t>(DL::kMaxBlocks) * DL::kQ8Seg + 1023) / 1024 * 1024;
+    const size_t lmax = t1_lds_bytes<FMT>(DL::kMaxBlocks);
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_q45k_t1_kernel<FMT, DEBUG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lmax)) != hipSuccess)
       return QMM_ERR_HIP;
@@ -996,14 +1024,14 @@ __device__ __forceinline__ uint2 lds8_sh(const uint32_t* a, uint32_t sh) {
   return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));
 }
 
+// Workgroup blk of the one-token Q6_K matvec (rows 8 blk .. 8 blk + 7), with
+// the workgroup's LDS at lds.
 template <bool DEBUG>
-__global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb,
-                        int32_t* __restrict__ dbgD) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+__device__ __forceinline__ void q6k_t1_body(uint8_t* lds, int blk, const uint8_t* w, const uint8_t* xq,
+                                            float* __restrict__ y, int M, int nb, int32_t* __restrict__ dbgD) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row_raw = blockIdx.x * kMmvqWaves + wave;
+  const int row_raw = blk * kMmvqWaves + wave;
   const bool row_ok = row_raw < M;
   const int row = row_ok ? row_raw : M - 1;  // out-of-range waves read a valid row, store nothing
   const size_t row_off = static_cast<size_t>(row) * nb * kQ6Bytes;
@@ -1097,8 +1125,25 @@ void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__
 }
 
 template <bool DEBUG>
+__global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void mmvq_q6k_t1_kernel(const uint8_t* w, const uint8_t* xq, float* __restrict__ y, int M, int nb,
+                        int32_t* __restrict__ dbgD) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  q6k_t1_body<DEBUG>(lds, blockIdx.x, w, xq, y, M, nb, dbgD);
+}
+
+constexpr size_t kQ6T1Lds = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 + q6t1_act_bytes(kQ6T1MaxBlocks);
+
+// Whether the one-token Q6_K kernel takes the shape: rows of at most 46
+// super-blocks, and a matrix that ends on a 16-byte boundary (its aligned
+// chunk reads then stay inside the matrix).
+static bool q6k_t1_fits(int M, int nb) {
+  return nb <= kQ6T1MaxBlocks && (static_cast<int64_t>(M) * nb) % 8 == 0;
+}
+
+template <bool DEBUG>
 static int launch_mmvq_q6k_t1(const void* w, const void* xq, float* y, int M, int nb, int32_t* D, hipStream_t st) {
-  const size_t lds = static_cast<size_t>(kMmvqWaves) * kQ6T1Rounds * 1024 + q6t1_act_bytes(kQ6T1MaxBlocks);
+  const size_t lds = kQ6T1Lds;
   static bool attr_set = false;
   if (!attr_set) {
     const size_t lmax = lds;
@@ -1423,11 +1468,8 @@ constexpr int kQ6ActBudget = 44 * 1024;
 template <bool DEBUG>
 static int launch_mmvq_q6k(const void* w, const void* xq, float* y, int M, int nb, int T,
                            int32_t* D, hipStream_t st, const SlotArgs* slots = nullptr, int nslots = 0) {
-  // one token: the LDS-copy kernel, for rows of at most 46 super-blocks whose
-  // matrix ends on a 16-byte boundary (its aligned chunk reads then stay
-  // inside the matrix)
-  if (!slots && T == 1 && nb <= kQ6T1MaxBlocks && (static_cast<int64_t>(M) * nb) % 8 == 0)
-    return launch_mmvq_q6k_t1<DEBUG>(w, xq, y, M, nb, D, st);
+  // one token: the LDS-copy kernel where it takes the shape
+  if (!slots && T == 1 && q6k_t1_fits(M, nb)) return launch_mmvq_q6k_t1<DEBUG>(w, xq, y, M, nb, D, st);
   if (!slots && T >= 2 && T <= 4 && nb <= kQ6TnMaxBlocks && (static_cast<int64_t>(M) * nb) % 8 == 0) {
     if (T == 2) return launch_mmvq_q6k_tn<2, DEBUG>(w, xq, y, M, nb, D, st);
     if (T == 3) return launch_mmvq_q6k_tn<3, DEBUG>(w, xq, y, M, nb, D, st);
@@ -1474,6 +1516,108 @@ static int check_mmvq(const void* w, const void* xq, const float* y, int64_t M, 
   return QMM_OK;
 }
 
+// Two one-token matvecs on one activation row in one launch (say the two
+// weight matrices that read the same normalised hidden state in a decode
+// step): workgroups 0 .. na - 1 run matrix a, the rest matrix b, each with
+// the workgroup code of its own one-token kernel, so each output has the
+// bits that kernel gives.  The matrix with more bytes per row goes first,
+// since workgroups start in index order: the lighter workgroups then fill
+// the CUs as the heavier ones finish, and the launch ends with one tail
+// instead of two.
+struct PairSide {
+  const uint8_t* w;
+  float* y;
+  int M, nblk, cb;
+};
+
+template <int FMT>
+__device__ __forceinline__ void t1_body(uint8_t* lds, int blk, const PairSide& S, const uint8_t* xq, int nb) {
+  if constexpr (FMT == QMM_Q6_K)
+    q6k_t1_body<false>(lds, blk, S.w, xq, S.y, S.M, nb, nullptr);
+  else
+    q45_t1_body<FMT, false>(lds, blk, S.w, xq, S.y, S.M, nb, S.cb, nullptr, nullptr);
+}
+
+template <int FA, int FB>
+__global__ __launch_bounds__(kMmvqThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void mmvq_pair_t1_kernel(PairSide A, PairSide B, const uint8_t* xq, int nb) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int blk = blockIdx.x;
+  if (blk < A.nblk)  // uniform per workgroup
+    t1_body<FA>(lds, blk, A, xq, nb);
+  else
+    t1_body<FB>(lds, blk - A.nblk, B, xq, nb);
+}
+
+template <int FMT>
+static size_t pair_lds_bytes(int cb) {
+  if constexpr (FMT == QMM_Q6_K) return kQ6T1Lds;
+  else return t1_lds_bytes<FMT>(cb);
+}
+template <int FMT>
+static size_t pair_lds_max() {
+  if constexpr (FMT == QMM_Q6_K) return kQ6T1Lds;
+  else return t1_lds_bytes<FMT>(MvDma<FMT>::kMaxBlocks);
+}
+
+template <int FA, int FB>
+static int launch_pair(const PairSide& A, const PairSide& B, const void* xq, int nb, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const size_t lmax = std::max(pair_lds_max<FA>(), pair_lds_max<FB>());
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&mmvq_pair_t1_kernel<FA, FB>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lmax)) != hipSuccess)
+      return QMM_ERR_HIP;
+    attr_set = true;
+  }
+  const size_t lds = std::max(pair_lds_bytes<FA>(A.cb), pair_lds_bytes<FB>(B.cb));
+  hipLaunchKernelGGL((mmvq_pair_t1_kernel<FA, FB>), dim3(A.nblk + B.nblk), dim3(kMmvqThreads), lds, st, A, B,
+                     static_cast<const uint8_t*>(xq), nb);
+  return launch_status();
+}
+
+template <int FA>
+static int launch_pair_b(int fb, const PairSide& A, const PairSide& B, const void* xq, int nb, hipStream_t st) {
+  if (fb == QMM_Q4_K) return launch_pair<FA, QMM_Q4_K>(A, B, xq, nb, st);
+  if (fb == QMM_Q5_K) return launch_pair<FA, QMM_Q5_K>(A, B, xq, nb, st);
+  return launch_pair<FA, QMM_Q6_K>(A, B, xq, nb, st);
+}
+
+static int row_block_bytes(int fmt) { return fmt == QMM_Q4_K ? kQ4Bytes : fmt == QMM_Q5_K ? kQ5Bytes : kQ6Bytes; }
+
+static int seg_blocks_t1(int fmt, int nb) {
+  if (fmt == QMM_Q4_K) return t1_seg_blocks<QMM_Q4_K>(nb);
+  if (fmt == QMM_Q5_K) return t1_seg_blocks<QMM_Q5_K>(nb);
+  return nb;
+}
+
+static int mmvq_one(int fmt, const void* w, const void* xq, float* y, int M, int nb, hipStream_t st) {
+  if (fmt == QMM_Q4_K) return launch_mmvq_q4k<false>(w, xq, y, M, nb, 1, nullptr, nullptr, st);
+  if (fmt == QMM_Q5_K) return launch_mmvq_q4k<false, QMM_Q5_K>(w, xq, y, M, nb, 1, nullptr, nullptr, st);
+  return launch_mmvq_q6k<false>(w, xq, y, M, nb, 1, nullptr, st);
+}
+
+int mmvq_pair_launch(int fa, const void* wa, int Ma, float* ya, int fb, const void* wb, int Mb, float* yb,
+                     const void* xq, int nb, hipStream_t st) {
+  // one launch only where both one-token kernels take their shapes;
+  // otherwise the two matvecs one after the other
+  if ((fa == QMM_Q6_K && !q6k_t1_fits(Ma, nb)) || (fb == QMM_Q6_K && !q6k_t1_fits(Mb, nb))) {
+    const int r = mmvq_one(fa, wa, xq, ya, Ma, nb, st);
+    return r != QMM_OK ? r : mmvq_one(fb, wb, xq, yb, Mb, nb, st);
+  }
+  if (row_block_bytes(fb) > row_block_bytes(fa)) {
+    std::swap(fa, fb);
+    std::swap(wa, wb);
+    std::swap(Ma, Mb);
+    std::swap(ya, yb);
+  }
+  const PairSide A{static_cast<const uint8_t*>(wa), ya, Ma, (Ma + kMmvqWaves - 1) / kMmvqWaves, seg_blocks_t1(fa, nb)};
+  const PairSide B{static_cast<const uint8_t*>(wb), yb, Mb, (Mb + kMmvqWaves - 1) / kMmvqWaves, seg_blocks_t1(fb, nb)};
+  if (fa == QMM_Q4_K) return launch_pair_b<QMM_Q4_K>(fb, A, B, xq, nb, st);
+  if (fa == QMM_Q5_K) return launch_pair_b<QMM_Q5_K>(fb, A, B, xq, nb, st);
+  return launch_pair_b<QMM_Q6_K>(fb, A, B, xq, nb, st);
+}
+
 int debug_mmvq(int fmt, const void* w, const void* xq, int32_t* D, int32_t* S, int64_t M,
                int64_t K, int64_t T, hipStream_t st) {
   if (fmt == QMM_Q4_K)
@@ -1512,6 +1656,19 @@ extern "C" int mmvq_q6k(const void* w, const void* xq, float* y, int64_t M, int6
   if (st != QMM_OK) return st;
   return launch_mmvq_q6k<false>(w, xq, y, static_cast<int>(M), static_cast<int>(K / kQK),
                                 static_cast<int>(T), nullptr, to_stream(stream));
+}
+
+extern "C" int mmvq_pair(int fmt_a, const void* wa, int64_t Ma, float* ya, int fmt_b, const void* wb, int64_t Mb,
+                         float* yb, const void* xq, int64_t K, void* stream) {
+  for (int f : {fmt_a, fmt_b})
+    if (f != QMM_Q4_K && f != QMM_Q5_K && f != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
+  int st = check_mmvq(wa, xq, ya, Ma, K, 1);
+  if (st != QMM_OK) return st;
+  st = check_mmvq(wb, xq, yb, Mb, K, 1);
+  if (st != QMM_OK) return st;
+  if (Ma + Mb > 0x7fffffff) return QMM_ERR_SHAPE;
+  return mmvq_pair_launch(fmt_a, wa, static_cast<int>(Ma), ya, fmt_b, wb, static_cast<int>(Mb), yb, xq,
+                          static_cast<int>(K / kQK), to_stream(stream));
 }
 
 extern "C" int moe_slot_mmvq(int fmt, const void* w, int64_t E, int64_t M, int64_t K, int64_t expert_stride_bytes,

@@ -85,6 +85,18 @@ def test_mmvq_errors(fn):
     assert f(FAKE, FAKE, MISAL, 4, 256, 1, NUL) == _lib.QMM_ERR_ALIGN
 
 
+def test_mmvq_pair_errors():
+    f, Q4, Q6 = L.mmvq_pair, _lib.QMM_Q4_K, _lib.QMM_Q6_K
+    assert f(99, FAKE, 4, FAKE, Q4, FAKE, 4, FAKE, FAKE, 256, NUL) == _lib.QMM_ERR_UNSUPPORTED
+    assert f(Q4, FAKE, 4, FAKE, 7, FAKE, 4, FAKE, FAKE, 256, NUL) == _lib.QMM_ERR_UNSUPPORTED
+    assert f(Q4, FAKE, 4, FAKE, Q6, FAKE, 4, FAKE, FAKE, 300, NUL) == _lib.QMM_ERR_SHAPE     # K % 256
+    assert f(Q4, FAKE, 0, FAKE, Q6, FAKE, 4, FAKE, FAKE, 256, NUL) == _lib.QMM_ERR_SHAPE     # Ma < 1
+    assert f(Q4, FAKE, 4, FAKE, Q6, FAKE, 0, FAKE, FAKE, 256, NUL) == _lib.QMM_ERR_SHAPE     # Mb < 1
+    assert f(Q4, FAKE, 4, FAKE, Q6, NUL, 4, FAKE, FAKE, 256, NUL) == _lib.QMM_ERR_NULL
+    assert f(Q4, FAKE, 4, FAKE, Q6, FAKE, 4, FAKE, NUL, 256, NUL) == _lib.QMM_ERR_NULL
+    assert f(Q4, FAKE, 4, MISAL, Q6, FAKE, 4, FAKE, FAKE, 256, NUL) == _lib.QMM_ERR_ALIGN
+
+
 @pytest.mark.parametrize("fn", ["mmq_q4k", "mmq_q5k", "mmq_q6k", "mmq_q4k_f32", "mmq_q5k_f32", "mmq_q6k_f32"])
 def test_mmq_errors(fn):
     f = getattr(L, fn)

@@ -6,6 +6,7 @@ match the oracle's exactly.  The full 4096 x 11008 decode shape is checked at
 T = 1 and T = 4, in the launch configuration the bench uses.
 """
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -119,3 +120,48 @@ def test_deterministic():
     a = host(qmm.mmvq_q4k(wd, xd))
     b = host(qmm.mmvq_q4k(wd, xd))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# Paired one-token matvecs (one launch for two matrices on the same row): every
+# format pair against the oracle and bit for bit against the single matvecs; ragged
+# row counts (a partial last workgroup on either side), the decode shape, and
+# shapes the Q6_K one-token kernel does not take (then two launches).
+PAIR_SHAPES = [(72, 40, 2816), (9, 13, 256), (4096, 4096, 11008), (16, 24, 12288), (9, 8, 11008)]
+
+
+@pytest.mark.parametrize("fa", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("fb", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("Ma,Mb,K", PAIR_SHAPES)
+def test_pair_matches_single_matvecs(fa, fb, Ma, Mb, K):
+    if Ma * Mb > 1000 * 1000 and (fa, fb) not in (("q6k", "q4k"), ("q4k", "q4k")):
+        pytest.skip("the decode shape is taken for the pairs the decode step uses")
+    g = qmm_synth.rng(Ma + 3 * Mb + K)
+    wa, wb = FMTS[fa][0](g, Ma, K), FMTS[fb][0](g, Mb, K)
+    x = qmm_synth.activations(g, 1, K)
+    xq = oracle.quantize_q8_1(x)
+    say("mmvq_pair", f"{fa} Ma={Ma} {fb} Mb={Mb} K={K}")
+    dxq = dev(xq)
+    ya, yb = qmm.mmvq_pair(FMTS[fa][3], dev(wa), FMTS[fb][3], dev(wb), dxq)
+    ya, yb = host(ya), host(yb)
+    assert np.array_equal(ya, host(FMTS[fa][2](dev(wa), dxq)))
+    assert np.array_equal(yb, host(FMTS[fb][2](dev(wb), dxq)))
+    X = oracle.q8_1_dequant(xq)
+    rows = np.arange(Ma) if Ma <= 512 else np.random.default_rng(1).choice(Ma, 64, replace=False)
+    Wa = FMTS[fa][1](wa[rows])
+    assert_parity(ya[:, rows], oracle.dense(Wa, X), oracle.abs_bound(Wa, X), f"pair a {fa}")
+    rows = np.arange(Mb) if Mb <= 512 else np.random.default_rng(2).choice(Mb, 64, replace=False)
+    Wb = FMTS[fb][1](wb[rows])
+    assert_parity(yb[:, rows], oracle.dense(Wb, X), oracle.abs_bound(Wb, X), f"pair b {fb}")
+
+
+def test_pair_rejects_bad_arguments():
+    g = qmm_synth.rng(3)
+    w = dev(qmm_synth.q4k_weights(g, 8, 512))
+    xq = qmm.q8_1_quantize(dev(qmm_synth.activations(g, 2, 512)))
+    with pytest.raises(ValueError):
+        qmm.mmvq_pair(qmm.QMM_Q4_K, w, qmm.QMM_Q4_K, w, xq)  # two rows
+    y = torch.empty((1, 8), dtype=torch.float32, device=w.device)
+    with pytest.raises(ValueError):
+        qmm.mmvq_pair(qmm.QMM_Q4_K, w, qmm.QMM_Q4_K, w, xq[:1].contiguous(), out_a=y, out_b=y)
+    with pytest.raises(ValueError):
+        qmm.mmvq_pair(qmm.QMM_Q4_K, w, qmm.QMM_Q4_K, dev(qmm_synth.q4k_weights(g, 8, 768)), xq[:1].contiguous())
