@@ -126,15 +126,15 @@ def test_deterministic():
 # format pair against the oracle and bit for bit against the single matvecs; ragged
 # row counts (a partial last workgroup on either side), the decode shape, and
 # shapes the Q6_K one-token kernel does not take (then two launches).
-PAIR_SHAPES = [(72, 40, 2816), (9, 13, 256), (4096, 4096, 11008), (16, 24, 12288), (9, 8, 11008)]
+FMT_PAIRS = [(a, b) for a in ("q4k", "q5k", "q6k") for b in ("q4k", "q5k", "q6k")]
+PAIR_CASES = ([(a, b, Ma, Mb, K) for a, b in FMT_PAIRS
+               for Ma, Mb, K in [(72, 40, 2816), (9, 13, 256), (16, 24, 12288), (9, 8, 11008)]]
+              # the decode shape for the pairs a decode step uses
+              + [(a, b, 4096, 4096, 11008) for a, b in (("q6k", "q4k"), ("q4k", "q4k"))])
 
 
-@pytest.mark.parametrize("fa", ["q4k", "q5k", "q6k"])
-@pytest.mark.parametrize("fb", ["q4k", "q5k", "q6k"])
-@pytest.mark.parametrize("Ma,Mb,K", PAIR_SHAPES)
+@pytest.mark.parametrize("fa,fb,Ma,Mb,K", PAIR_CASES)
 def test_pair_matches_single_matvecs(fa, fb, Ma, Mb, K):
-    if Ma * Mb > 1000 * 1000 and (fa, fb) not in (("q6k", "q4k"), ("q4k", "q4k")):
-        pytest.skip("the decode shape is taken for the pairs the decode step uses")
     g = qmm_synth.rng(Ma + 3 * Mb + K)
     wa, wb = FMTS[fa][0](g, Ma, K), FMTS[fb][0](g, Mb, K)
     x = qmm_synth.activations(g, 1, K)
