@@ -586,8 +586,10 @@ def main():
         mmq_case("mmq_q4k_14336x4096_t1024", qmm.mmq_q4k, wl3["q4k"], wl3["x_q4k"], ceil_q4)
         mmq_case("mmq_q6k_4096x14336_t1024", qmm.mmq_q6k, wl3["q6k"], wl3["x_q6k"], ceil_q6)
 
-        # routed-expert FFN: gate||up grouped, SwiGLU->Q8_1, down grouped weighted;
-        # expert weights rotated over >= 4 GB of copies
+        # routed-expert FFN: gate||up grouped with SwiGLU->Q8_1 fused into its
+        # epilogue, down grouped weighted; expert weights rotated over >= 4 GB
+        # of copies.  The same layer with the SwiGLU as its own launch is timed
+        # beside it.
         wl4 = qmm_synth.workload(4)
         E, H, F, T, top_k = 128, 2048, 768, 512, 8
         wbytes = wl4["gate_up"].nbytes + wl4["down"].nbytes
@@ -607,15 +609,21 @@ def main():
                                 qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k)), dev)
         ws2 = ws1
 
-        def moe_step(c):
+        def moe_step(c, fused=True):
             qmm.q8_1_quantize(xm, out=xqm)
-            qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gus[c], xqm, ids, out=y1, ws=ws1)
-            qmm.swiglu_q8_1(y1, out=hq)
+            if fused:
+                qmm.moe_grouped_swiglu(qmm.QMM_Q4_K, gus[c], xqm, ids, out=hq, ws=ws1)
+            else:
+                qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gus[c], xqm, ids, out=y1, ws=ws1)
+                qmm.swiglu_q8_1(y1, out=hq)
             qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dns[c], hq, ids, probs, out=y2, ws=ws2, reuse_routing=True)
 
         log("moe ffn")
         moe_step(0)
         ms_moe, med_moe = timer([lambda c=c: moe_step(c) for c in range(cop)], 300.0)
+        ms_unf, _ = timer([lambda c=c: moe_step(c, False) for c in range(cop)], 300.0)
+        ms_gs, med_gs = timer([lambda c=c: qmm.moe_grouped_swiglu(qmm.QMM_Q4_K, gus[c], xqm, ids, out=hq, ws=ws1)
+                               for c in range(cop)], 150.0)
         ms_gu, med_gu = timer([lambda c=c: qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gus[c], xqm, ids, out=y1, ws=ws1)
                                for c in range(cop)], 150.0)
         # the down call as the layer runs it: on the route tables already in ws
@@ -625,7 +633,6 @@ def main():
 
         def glue():
             qmm.q8_1_quantize(xm, out=xqm)
-            qmm.swiglu_q8_1(y1, out=hq)
         ms_glue = time_graph(torch, [glue], MIN_LAUNCHES)
         macs = T * top_k * (2 * F * H + H * F)
         act_bytes = T * H * 4 + T * (H // 32) * 40 + T * top_k * (F // 32) * 40 + T * H * 4
@@ -633,15 +640,17 @@ def main():
         tops = 2.0 * macs / (ms_moe * 1e-3) / 1e12
         attain = min(INT8_PEAK_TOPS, 2.0 * macs / moe_bytes * HBM_PEAK_GBPS / 1e3)
         # the two grouped calls alone (one route preparation, two repacks and GEMMs
-        # and the combine), without the quantize and SwiGLU glue: weights,
-        # Q8_1 inputs, the gate||up per-slot rows and the combined output
-        g_bytes = wbytes + T * (H // 32) * 40 + T * top_k * 2 * F * 4 + T * top_k * (F // 32) * 40 + T * H * 4
-        ms_g = ms_gu + ms_dn
+        # with the SwiGLU epilogue, and the combine), without the quantizer:
+        # weights, Q8_1 inputs, the Q8_1 SwiGLU rows and the combined output
+        g_bytes = wbytes + T * (H // 32) * 40 + T * top_k * (F // 32) * 40 + T * H * 4
+        ms_g = ms_gs + ms_dn
         tops_g = 2.0 * macs / (ms_g * 1e-3) / 1e12
         attain_g = min(INT8_PEAK_TOPS, 2.0 * macs / g_bytes * HBM_PEAK_GBPS / 1e3)
         also["moe_ffn_e128_t512_top8"] = {
             "us": round(ms_moe * 1e3, 2), "median_us": round(med_moe * 1e3, 2),
+            "gate_up_swiglu_us": round(ms_gs * 1e3, 2), "gate_up_swiglu_median_us": round(med_gs * 1e3, 2),
             "gate_up_us": round(ms_gu * 1e3, 2), "gate_up_median_us": round(med_gu * 1e3, 2),
+            "unfused_swiglu_us": round(ms_unf * 1e3, 2),
             "down_us": round(ms_dn * 1e3, 2), "down_median_us": round(med_dn * 1e3, 2),
             "GBps": gbps(moe_bytes, ms_moe), "frac_hbm": round(gbps(moe_bytes, ms_moe) / HBM_PEAK_GBPS, 4),
             "TOPS": round(tops, 1), "frac_attainable": round(tops / attain, 4),

@@ -249,6 +249,26 @@ int moe_grouped_mmq_routed(int fmt, const void* w, int64_t E, int64_t M, int64_t
                            float* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_grouped_mmq_swiglu -- the grouped gate||up product of a routed FFN with
+ * the SwiGLU glue fused into its epilogue: per routed slot, h = silu(gate) *
+ * up quantized to Q8_1 ([GAP] lever T2's grouped expert GEMM; lever T4: the
+ * producer emits the next product's input format directly, no fp32 round
+ * trip).  Each expert's M = 2F rows hold gate in rows [0, F) and up in
+ * [F, 2F), as moe_grouped_mmq's gate||up call takes them; hq receives
+ * [T*top_k][F/32] Q8_1 blocks (40 bytes each), the same bytes as
+ * moe_grouped_mmq (no expert_weights) followed by swiglu_q8_1.  Routing,
+ * workspace (qmm_workspace_bytes(QMM_OP_MOE_SLOTS, M, K, T, E, top_k)) and
+ * the route tables it leaves in ws for moe_grouped_mmq_routed are those of
+ * moe_grouped_mmq.  Requires fmt QMM_Q4_K or QMM_Q5_K
+ * (QMM_ERR_UNSUPPORTED otherwise) and M a multiple of 256; hq 16-byte
+ * aligned.  Other arguments, limits and errors as moe_grouped_mmq.
+ */
+int moe_grouped_mmq_swiglu(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
+                           int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,
+                           const int32_t* ids, int64_t T, int64_t top_k, void* hq, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
  * moe_slot_mmvq -- the per-(token, slot) expert matvec that the grouped GEMM
  * replaces ([GAP] lever T2: the batched expert matvec re-reads an expert's
  * weights once per routed token; its de-risk step compares the two at

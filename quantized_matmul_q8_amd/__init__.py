@@ -26,7 +26,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "q8_1_quantize", "mmvq_q4k", "mmvq_q5k", "mmvq_q6k", "mmvq_pair", "mmq_q4k", "mmq_q5k", "mmq_q6k", "mmq_q4k_f32", "mmq_q5k_f32",
     "mmq_q6k_f32",
-    "moe_grouped_mmq", "moe_slot_mmvq",
+    "moe_grouped_mmq", "moe_grouped_swiglu", "moe_slot_mmvq",
     "swiglu_q8_1", "workspace", "workspace_bytes", "debug_subdots", "probe_read", "probe_read_geom",
     "probe_mfma", "probe_mfma_epilogue", "QmmError",
     "QMM_Q4_K", "QMM_Q5_K", "QMM_Q6_K", "LIB_PATH",
@@ -271,6 +271,36 @@ def moe_grouped_mmq(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.Tens
     _lib.call("moe_grouped_mmq_routed" if reuse_routing else "moe_grouped_mmq", fmt, _p(w), E, M, K, stride,
               _p(xq), rows_per_token, _p(ids), _p(expert_weights), T, top_k, _p(out), _p(ws), ws.numel(),
               _stream(w.device))
+    return out
+
+
+def moe_grouped_swiglu(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.Tensor,
+                       out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Grouped gate||up product with SwiGLU -> Q8_1 fused: ``w`` [E, 2F, K/256, bytes]
+    (gate rows then up rows per expert) -> Q8_1 ``[T*top_k, F/32, 40]``, the bytes
+    of :func:`moe_grouped_mmq` (per slot) followed by :func:`swiglu_q8_1`.  The
+    route tables it leaves in ``ws`` serve a following ``reuse_routing`` call."""
+    _need(w, torch.uint8, "w", 4)
+    if w.shape[3] != _BLOCK_BYTES[fmt]:
+        raise ValueError("w: wrong block size for fmt")
+    E, M, K = w.shape[0], w.shape[1], w.shape[2] * 256
+    if M % 256:
+        raise ValueError(f"w: 2F = {M} rows per expert must be a multiple of 256")
+    _need(ids, torch.int32, "ids", 2)
+    T, top_k = ids.shape
+    rows = _acts(xq, K)
+    if rows == T:
+        rows_per_token = 1
+    elif rows == T * top_k:
+        rows_per_token = top_k
+    else:
+        raise ValueError("xq must have T or T*top_k rows")
+    out = _out(out, (T * top_k, M // 64, 40), torch.uint8, w.device)
+    need = workspace_bytes(QMM_OP_MOE_SLOTS, M, K, T, E, top_k)
+    ws = workspace(need, w.device) if ws is None else ws
+    _need(ws, torch.uint8, "ws", 1)
+    _lib.call("moe_grouped_mmq_swiglu", fmt, _p(w), E, M, K, w.stride(0), _p(xq), rows_per_token, _p(ids), T, top_k,
+              _p(out), _p(ws), ws.numel(), _stream(w.device))
     return out
 
 

@@ -49,6 +49,8 @@ SIGNATURES = {
     "mmq_q6k_f32": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "moe_grouped_mmq": (_i, [_i, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64,
                              _vp, _vp, _sz, _vp]),
+    "moe_grouped_mmq_swiglu": (_i, [_i, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _sz,
+                                    _vp]),
     "moe_grouped_mmq_routed": (_i, [_i, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64,
                                     _vp, _vp, _sz, _vp]),
     "moe_slot_mmvq": (_i, [_i, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp]),

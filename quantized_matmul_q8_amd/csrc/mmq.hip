@@ -103,7 +103,10 @@ constexpr int kChunkMin = 10240;   // [3 q][32 col][8 s] bf16: part q of beta*S 
 constexpr int kChunkBytes = 12288; // 12 x 1 KB (the last 512 bytes unused)
 constexpr int kChunkKB = kChunkBytes / 1024;
 
-enum MmqMode { kDense = 0, kMoe = 1, kDebug = 2 };
+enum MmqMode { kDense = 0, kMoe = 1, kDebug = 2, kMoeGlu = 3 };
+// kMoeGlu: the grouped gate||up product with SwiGLU -> Q8_1 in the epilogue
+template <int MODE>
+constexpr bool kIsMoe = MODE == kMoe || MODE == kMoeGlu;
 
 // Q4_K and Q5_K share the kernel's structure (32-weight sub-blocks = Q8_1
 // blocks, a 6-bit scale and min per sub-block, the min term); Q5_K adds a
@@ -139,6 +142,10 @@ struct MmqParams {
   int64_t expert_stride;
   // debug (mode kDebug)
   int32_t* dbgD;
+  // grouped gate||up with SwiGLU (mode kMoeGlu): gate rows [0, glu_f), up
+  // rows [glu_f, 2 glu_f); Q8_1 output rows of glu_f / 32 blocks per slot
+  uint8_t* yq;
+  int glu_f;
 };
 
 // ----------------------------------------------------------------------------
@@ -627,7 +634,7 @@ struct TileCols {
 template <int MODE>
 __device__ __forceinline__ int col_out_row(const MmqParams& P, const TileCols& tc, int j, bool& valid) {
   valid = j < tc.ncols;
-  if constexpr (MODE == kMoe) {
+  if constexpr (kIsMoe<MODE>) {
     return valid ? P.bucket[tc.slot_base + tc.n0 + j] : 0;
   } else {
     return tc.n0 + j;
@@ -780,7 +787,7 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
   constexpr int BN = 32 * NT;
   int m_tile;
   const uint8_t* wbase = P.w;
-  if constexpr (MODE == kMoe) {
+  if constexpr (kIsMoe<MODE>) {
     // expert e owns work entries [mt * ct_off[e], mt * ct_off[e + 1]): the
     // one with ct_off[e] <= idx / mt < ct_off[e + 1]
     const int q = idx / P.mt;
@@ -828,7 +835,7 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
   m_tile = __builtin_amdgcn_readfirstlane(m_tile);
   {
     const int nsteps = SP::nsteps(P.nb);
-    if constexpr (MODE == kMoe) {
+    if constexpr (kIsMoe<MODE>) {
       R.s0 = 0;
       R.s1 = nsteps;
     } else {
@@ -837,8 +844,18 @@ __device__ __forceinline__ void tile_ref(const MmqParams& P, const MoeTables& Tb
     }
   }
   const int rw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % SP::kRowGroups;
-  R.r0 = m_tile * SP::kBM + rw * 32;
-  const int wrow = min(R.r0 + (threadIdx.x & 31), P.M - 1);
+  int wrow;
+  if constexpr (MODE == kMoeGlu) {
+    // wave rw: gate F-rows r0 .. r0 + 15 as MFMA rows 0..15, the matching
+    // up rows (F-row + glu_f) as MFMA rows 16..31
+    static_assert(SP::kRowGroups == 8, "the fused SwiGLU tile is 8 row groups");
+    R.r0 = m_tile * 128 + rw * 16;
+    const int i = threadIdx.x & 31;
+    wrow = R.r0 + (i & 15) + (i >> 4) * P.glu_f;
+  } else {
+    R.r0 = m_tile * SP::kBM + rw * 32;
+    wrow = min(R.r0 + (threadIdx.x & 31), P.M - 1);
+  }
   constexpr int kRowBytes = FMT == QMM_Q4_K ? kQ4Bytes : FMT == QMM_Q5_K ? kQ5Bytes : kQ6Bytes;
   R.wr = wbase + static_cast<size_t>(wrow) * P.nb * kRowBytes;
 }
@@ -945,6 +962,65 @@ __device__ __forceinline__ void store_tile(const MmqParams& P, const TileCols& t
   }
 }
 
+// Fused SwiGLU epilogue of a grouped gate||up tile (all waves call it).
+// Wave w's 32 MFMA rows are 16 gate rows, F-rows r0 .. r0 + 15, then the 16
+// matching up rows (tile_ref), so lane (col, g) holds gate row 8k + 4g + j in
+// acc[4k + j] and its up row in acc[4(k + 2) + j] (k = 0, 1): h = silu(gate) *
+// up is lane-local.  A Q8_1 block (32 F-rows of output row `slot`) spans the
+// wave pair 2b, 2b + 1; its max |h| and integer sum are combined through LDS
+// (the stage the tile last computed from, free after a barrier).  The steps
+// are those of swiglu_q8_1, so the bytes are too.
+template <int NT>
+__device__ __forceinline__ void glu_store(const MmqParams& P, const TileRef& R, const v16f (&acc)[NT], int wave,
+                                          int lane, uint8_t* stage) {
+#pragma clang fp contract(off)
+  const int g = lane >> 5, col = lane & 31;
+  float h[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) h[v] = silu_mul(acc[0][v], acc[0][v + 8]);
+  float am = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) am = fmaxf(am, fabsf(h[v]));
+  am = fmaxf(am, __shfl_xor(am, 32));
+  float* xa = reinterpret_cast<float*>(stage);        // [8 waves][32 columns] max |h|
+  int* xs = reinterpret_cast<int*>(stage + 1024);     // [8 waves][32 columns] sums
+  __syncthreads();  // every wave is done with the stage
+  if (g == 0) xa[wave * 32 + col] = am;
+  __syncthreads();
+  am = fmaxf(am, xa[(wave ^ 1) * 32 + col]);
+  const float d = am / 127.0f;
+  const float di = d >= 0x1p-126f ? 1.0f / d : 0.0f;
+  int s = 0;
+  uint32_t packed[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    uint32_t pk = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = max(-128, min(127, static_cast<int>(rintf(h[4 * k + j] * di))));
+      s += q;
+      pk |= (static_cast<uint32_t>(q) & 255u) << (8 * j);
+    }
+    packed[k] = pk;
+  }
+  s += __shfl_xor(s, 32);
+  if (g == 0) xs[wave * 32 + col] = s;
+  __syncthreads();
+  s += xs[(wave ^ 1) * 32 + col];
+  bool valid;
+  const int orow = col_out_row<kMoeGlu>(P, R.tc, col, valid);
+  if (valid) {
+    // block r0 / 32 along F; this wave's F-rows sit at 16 (w % 2) .. + 15 in it
+    uint8_t* dst = P.yq + (static_cast<size_t>(orow) * (P.glu_f / 32) + R.r0 / 32) * kQ8Bytes;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) reinterpret_cast<uint32_t*>(dst + 4 + 16 * (wave & 1) + 8 * k + 4 * g)[0] = packed[k];
+    if ((wave & 1) == 0 && g == 0) {
+      reinterpret_cast<uint32_t*>(dst)[0] = f2h_bits(d);  // f16 d, zero pad
+      reinterpret_cast<int32_t*>(dst + 36)[0] = s;
+    }
+  }
+}
+
 // Split-K epilogue of a dense tile (all waves call it; the kh == 0 waves
 // hold the tile's partial sums).  The partial goes to the tile's slot in the
 // workspace; after a barrier, thread 0 releases the workgroup's stores at
@@ -1030,8 +1106,9 @@ template <int FMT, int NT, int MODE, int KS = 2>
 __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 4 : 2, NT == 1 ? 4 : 2))) void mmq_kernel(MmqParams P) {
   using L = MmqSmem<FMT, NT, KS>;
   using SP = StepSplit<FMT, KS>;
-  static_assert(KS == 2 || MODE == kMoe, "the dense and debug calls split K in two");
-  constexpr int kTab = MODE == kMoe ? kMoeMaxE + 1 : 1;
+  static_assert(KS == 2 || kIsMoe<MODE>, "the dense and debug calls split K in two");
+  static_assert(MODE != kMoeGlu || (KS == 1 && NT == 1), "the fused SwiGLU runs on whole-K one-tile tiles");
+  constexpr int kTab = kIsMoe<MODE> ? kMoeMaxE + 1 : 1;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ int s_next[2];
   __shared__ int s_last;
@@ -1039,7 +1116,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT 
 
   MoeTables Tb{s_counts, s_offsets, s_ct_off};
   int total;
-  if constexpr (MODE == kMoe) {
+  if constexpr (kIsMoe<MODE>) {
     for (int i = threadIdx.x; i <= P.E; i += kMmqThreads) {
       s_ct_off[i] = P.ct_off[i];
       if (i < P.E) {
@@ -1121,7 +1198,9 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(NT 
                                    sb, SP::u0(kh));
       }
     }
-    if constexpr (MODE != kDebug && KS == 1) {
+    if constexpr (MODE == kMoeGlu) {
+      glu_store<NT>(P, R, acc, wave, lane, smem + ((k - 1) & 1) * L::kStage);
+    } else if constexpr (MODE != kDebug && KS == 1) {
       store_tile<NT, MODE>(P, R.tc, R.r0, acc);  // every wave holds whole sums of its 32 rows
     } else if constexpr (MODE != kDebug) {
       // sum the two K halves through the stage just computed from
@@ -1296,8 +1375,11 @@ int moe_tile_rows(int fmt, int /*nb*/) {
 // Grouped launch used by moe_grouped_mmq (after route preparation on the
 // same stream): repack of the routed rows per expert, then tiles of
 // moe_tile_rows rows x 32 routed slots.
+// hq != nullptr: the gate||up product (M = 2F rows) with SwiGLU -> Q8_1
+// fused into the epilogue, Q8_1 rows of F / 32 blocks into hq (Q4_K / Q5_K,
+// F % 128 == 0) instead of fp32 rows into out.
 int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, const uint8_t* xq,
-                   float* out, unsigned* counters, const int32_t* counts, const int32_t* offsets,
+                   float* out, uint8_t* hq, unsigned* counters, const int32_t* counts, const int32_t* offsets,
                    const int32_t* bucket, const int32_t* ct_off, uint8_t* xr,
                    int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st) {
   RepackParams R{};
@@ -1332,6 +1414,14 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   const int bm = moe_tile_rows(fmt, nb);
   P.mt = (M + bm - 1) / bm;
   const bool whole_k = bm == StepSplit<QMM_Q4_K, 1>::kBM;
+  if (hq != nullptr) {
+    if (!whole_k || (M % 256) != 0) return QMM_ERR_UNSUPPORTED;
+    P.yq = hq;
+    P.glu_f = M / 2;
+    P.mt = P.glu_f / 128;
+    if (fmt == QMM_Q4_K) return launch_mmq<QMM_Q4_K, 1, kMoeGlu, 1>(P, 0, st);
+    return launch_mmq<QMM_Q5_K, 1, kMoeGlu, 1>(P, 0, st);
+  }
   if (fmt == QMM_Q4_K)
     return whole_k ? launch_mmq<QMM_Q4_K, 1, kMoe, 1>(P, 0, st) : launch_mmq<QMM_Q4_K, 1, kMoe>(P, 0, st);
   if (fmt == QMM_Q5_K)

@@ -37,7 +37,7 @@ constexpr int kMoeBN = 32;   // routed tokens per tile (must match the grouped k
 constexpr int kMoeBM = 128;  // weight rows of the smaller grouped tile (bounds the work entries)
 
 int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, const uint8_t* xq,
-                   float* out, unsigned* counters, const int32_t* counts, const int32_t* offsets,
+                   float* out, uint8_t* hq, unsigned* counters, const int32_t* counts, const int32_t* offsets,
                    const int32_t* bucket, const int32_t* ct_off, uint8_t* xr,
                    int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st);
 int64_t moe_max_ctiles(int64_t slots, int64_t E);
@@ -242,11 +242,18 @@ using namespace qmm;
 // One grouped call; with `routed`, the route tables already in ws (left by
 // an earlier grouped call on ws with the same ids, T, top_k and E) are used
 // instead of being prepared again.
+// hq != nullptr: the fused SwiGLU call (Q8_1 rows into hq instead of fp32
+// rows into y; no routing weights).
 static int grouped_call(bool routed, int fmt, const void* w, int64_t E, int64_t M, int64_t K,
                         int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token, const int32_t* ids,
                         const float* expert_weights, int64_t T, int64_t top_k, float* y, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        void* stream, void* hq = nullptr) {
   if (fmt != QMM_Q4_K && fmt != QMM_Q5_K && fmt != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
+  if (hq != nullptr) {
+    // gate and up halves of 128-row multiples, on the whole-K Q4_K / Q5_K tiles
+    if (fmt == QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
+    if (M < 256 || (M % 256) != 0) return QMM_ERR_SHAPE;
+  }
   if (E < 1 || E > kMoeMaxE || M < 1 || M > (1 << 30) || K < kQK || (K % kQK) != 0 || K / kQK > (1 << 16) ||
       T < 1 || top_k < 1 || top_k > E || top_k > kMoeMaxTopK || T * top_k > (1 << 30))
     return QMM_ERR_SHAPE;
@@ -257,8 +264,9 @@ static int grouped_call(bool routed, int fmt, const void* w, int64_t E, int64_t 
   // Q4_K / Q5_K blocks are read with 16-byte loads, Q6_K blocks with 2-byte aligned ones
   const int64_t stride_align = fmt == QMM_Q6_K ? 2 : 16;
   if (expert_stride_bytes < M * row_bytes || (expert_stride_bytes % stride_align) != 0) return QMM_ERR_SHAPE;
-  if (!w || !xq || !ids || !y || !ws) return QMM_ERR_NULL;
-  if (!aligned16(w) || !aligned16(xq) || !aligned16(ids) || !aligned16(y) || !aligned16(ws) ||
+  if (!w || !xq || !ids || (!y && !hq) || !ws) return QMM_ERR_NULL;
+  if (!aligned16(w) || !aligned16(xq) || !aligned16(ids) || (y && !aligned16(y)) || (hq && !aligned16(hq)) ||
+      !aligned16(ws) ||
       (expert_weights && !aligned16(expert_weights)))
     return QMM_ERR_ALIGN;
   const MoeLayout L = moe_layout(ws, M, K, T, E, top_k, expert_weights != nullptr);
@@ -274,7 +282,8 @@ static int grouped_call(bool routed, int fmt, const void* w, int64_t E, int64_t 
   }
   float* out = expert_weights ? L.scratch : y;
   rc = mmq_moe_launch(fmt, static_cast<const uint8_t*>(w), expert_stride_bytes, static_cast<int>(M),
-                      static_cast<int>(K / kQK), static_cast<const uint8_t*>(xq), out, L.counters,
+                      static_cast<int>(K / kQK), static_cast<const uint8_t*>(xq), out, static_cast<uint8_t*>(hq),
+                      L.counters,
                       L.counts, L.offsets, L.bucket, L.ct_off, L.chunks,
                       static_cast<int>(moe_max_ctiles(T * top_k, E)), static_cast<int>(E),
                       static_cast<int>(top_k), static_cast<int>(x_rows_per_token), st);
@@ -303,6 +312,15 @@ extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int
                                int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream) {
   return grouped_call(false, fmt, w, E, M, K, expert_stride_bytes, xq, x_rows_per_token, ids, expert_weights,
                            T, top_k, y, ws, ws_bytes, stream);
+}
+
+extern "C" int moe_grouped_mmq_swiglu(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
+                                      int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,
+                                      const int32_t* ids, int64_t T, int64_t top_k, void* hq, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  if (!hq) return QMM_ERR_NULL;
+  return grouped_call(false, fmt, w, E, M, K, expert_stride_bytes, xq, x_rows_per_token, ids, nullptr, T, top_k,
+                      nullptr, ws, ws_bytes, stream, hq);
 }
 
 extern "C" int moe_grouped_mmq_routed(int fmt, const void* w, int64_t E, int64_t M, int64_t K,

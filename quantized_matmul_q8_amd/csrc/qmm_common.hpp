@@ -280,4 +280,37 @@ __device__ __forceinline__ void q8_1_block_8lanes(float4 v, int part, uint8_t* d
   }
 }
 
+// One 32-activation block quantized by two lanes, lane and lane ^ 32, each
+// holding 16 of its values (any split): the same steps as
+// q8_1_block_8lanes_vals, so the same bytes.  Both lanes must be active.
+// Returns this lane's 16 int8 values packed four per dword (h[4k .. 4k+3]
+// in dword k, little-endian), the fp32 scale d and the block's integer sum
+// (in both lanes).
+__device__ __forceinline__ void q8_1_block_2lanes_vals(const float (&h)[16], uint32_t (&packed)[4], float& d,
+                                                       int& s) {
+#pragma clang fp contract(off)
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(h[i]));
+  am = fmaxf(am, __shfl_xor(am, 32));
+  d = am / 127.0f;
+  const float di = d >= 0x1p-126f ? 1.0f / d : 0.0f;
+  s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t p = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = max(-128, min(127, static_cast<int>(rintf(h[4 * k + j] * di))));
+      s += q;
+      p |= (static_cast<uint32_t>(q) & 255u) << (8 * j);
+    }
+    packed[k] = p;
+  }
+  s += __shfl_xor(s, 32);
+}
+
+// SwiGLU of one gate value g and its up value u: silu(g) * u.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 }  // namespace qmm

@@ -42,10 +42,10 @@ __global__ __launch_bounds__(256) void swiglu_q8_1_kernel(const float* __restric
   const float4 g = *reinterpret_cast<const float4*>(row + c);
   const float4 u = *reinterpret_cast<const float4*>(row + F + c);
   float4 h;
-  h.x = g.x / (1.0f + expf(-g.x)) * u.x;
-  h.y = g.y / (1.0f + expf(-g.y)) * u.y;
-  h.z = g.z / (1.0f + expf(-g.z)) * u.z;
-  h.w = g.w / (1.0f + expf(-g.w)) * u.w;
+  h.x = silu_mul(g.x, u.x);
+  h.y = silu_mul(g.y, u.y);
+  h.z = silu_mul(g.z, u.z);
+  h.w = silu_mul(g.w, u.w);
   if (!valid) h = make_float4(0.f, 0.f, 0.f, 0.f);
   q8_1_block_8lanes(h, part, hq + b * kQ8Bytes, valid);
 }

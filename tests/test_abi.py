@@ -85,6 +85,18 @@ def test_mmvq_errors(fn):
     assert f(FAKE, FAKE, MISAL, 4, 256, 1, NUL) == _lib.QMM_ERR_ALIGN
 
 
+def test_moe_swiglu_errors():
+    f, Q4, Q6 = L.moe_grouped_mmq_swiglu, _lib.QMM_Q4_K, _lib.QMM_Q6_K
+    big = ctypes.c_size_t(1 << 40)
+    # fmt, w, E, M, K, stride, xq, rows_per_token, ids, T, top_k, hq, ws, ws_bytes, stream
+    assert f(Q6, FAKE, 4, 256, 256, 1 << 20, FAKE, 1, FAKE, 8, 2, FAKE, FAKE, big, NUL) == _lib.QMM_ERR_UNSUPPORTED
+    assert f(Q4, FAKE, 4, 128, 256, 1 << 20, FAKE, 1, FAKE, 8, 2, FAKE, FAKE, big, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(Q4, FAKE, 4, 384, 256, 1 << 20, FAKE, 1, FAKE, 8, 2, FAKE, FAKE, big, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(Q4, FAKE, 4, 256, 256, 1 << 20, FAKE, 1, FAKE, 8, 2, NUL, FAKE, big, NUL) == _lib.QMM_ERR_NULL
+    assert f(Q4, FAKE, 4, 256, 256, 1 << 20, FAKE, 1, FAKE, 8, 2, MISAL, FAKE, big, NUL) == _lib.QMM_ERR_ALIGN
+    assert f(Q4, FAKE, 4, 256, 256, 1 << 20, FAKE, 1, FAKE, 8, 2, FAKE, FAKE, 16, NUL) == _lib.QMM_ERR_WORKSPACE
+
+
 def test_mmvq_pair_errors():
     f, Q4, Q6 = L.mmvq_pair, _lib.QMM_Q4_K, _lib.QMM_Q6_K
     assert f(99, FAKE, 4, FAKE, Q4, FAKE, 4, FAKE, FAKE, 256, NUL) == _lib.QMM_ERR_UNSUPPORTED

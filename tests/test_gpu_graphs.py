@@ -47,7 +47,7 @@ def _check_replays(run, outs, change_inputs, what):
         torch.cuda.synchronize()
         ref = [o.clone() for o in outs]
         for o in outs:
-            o.fill_(float("nan") if o.dtype == torch.float32 else 0)
+            o.fill_(float("nan") if o.dtype == torch.float32 else 0xA5)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -119,14 +119,21 @@ def test_routed_ffn_graph():
     y = torch.empty((T, H), dtype=torch.float32, device=DEV)
     ws = qmm.workspace(max(qmm.workspace_bytes(qmm.QMM_OP_MOE_SLOTS, 2 * F, H, T, E, top_k),
                            qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k)), DEV)
-    say("graph: routed FFN (quantize, grouped gate||up, swiglu, routed down + combine)",
+    say("graph: routed FFN (quantize, grouped gate||up, swiglu, routed down + combine; fused SwiGLU)",
         f"E={E} H={H} F={F} T={T} top_k={top_k}")
+
+    ws_f = qmm.workspace(ws.numel(), DEV)
+    hq_f = torch.empty_like(hq)
+    y_f = torch.empty_like(y)
 
     def run():
         qmm.q8_1_quantize(x, out=xq)
         qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gate_up, xq, ids, out=gu, ws=ws)
         qmm.swiglu_q8_1(gu, out=hq)
         qmm.moe_grouped_mmq(qmm.QMM_Q4_K, down, hq, ids, probs, out=y, ws=ws, reuse_routing=True)
+        # the same layer with the SwiGLU fused into the gate||up call
+        qmm.moe_grouped_swiglu(qmm.QMM_Q4_K, gate_up, xq, ids, out=hq_f, ws=ws_f)
+        qmm.moe_grouped_mmq(qmm.QMM_Q4_K, down, hq_f, ids, probs, out=y_f, ws=ws_f, reuse_routing=True)
 
     # experts relabelled: each token keeps top_k distinct experts
     relabel = torch.randperm(E, generator=torch.Generator().manual_seed(3)).to(torch.int32).to(DEV)
@@ -136,4 +143,5 @@ def test_routed_ffn_graph():
         if r >= 2:   # new routing: the replay must prepare its route tables again
             ids.copy_(relabel[ids.long()])
 
-    _check_replays(run, [gu, y], change, "routed FFN")
+    _check_replays(run, [gu, y, hq_f, y_f], change, "routed FFN")
+    assert torch.equal(hq, hq_f) and torch.equal(y, y_f)

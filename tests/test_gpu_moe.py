@@ -237,10 +237,45 @@ def test_full_routed_ffn_gpu_chain():
     err = np.abs(y2.astype(np.float64) - y2_o)
     bad = err > tol * (1 + 1e-9)
     assert not bad.any(), f"{int(bad.sum())} outputs outside the carried tolerance (max excess {np.max(err - tol):.3e})"
+    # the fused gate||up + SwiGLU call gives the same bytes, and the down call
+    # on its route tables the same output
+    ws_f = qmm.workspace(ws.numel(), xq_gpu.device)
+    hq_f = qmm.moe_grouped_swiglu(qmm.QMM_Q4_K, dev(gate_up), xq_gpu, d_ids, ws=ws_f)
+    assert np.array_equal(host(hq_f), hq_gpu), "fused SwiGLU bytes differ from gate||up + swiglu_q8_1"
+    y2f = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), hq_f, d_ids, dev(probs), ws=ws_f, reuse_routing=True))
+    assert np.array_equal(y2f.view(np.uint32), y2.view(np.uint32))
     # determinism of the full chain
     y2b = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), qmm.swiglu_q8_1(
         qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(gate_up), xq_gpu, dev(ids))), dev(ids), dev(probs)))
     assert np.array_equal(y2.view(np.uint32), y2b.view(np.uint32))
+
+
+# The grouped gate||up call with SwiGLU -> Q8_1 fused into its epilogue: the
+# bytes of moe_grouped_mmq (per slot) followed by swiglu_q8_1, for both
+# formats it takes, activation rows per token and per slot, ragged routings
+# (experts with no slot, partial column tiles), two to four 128-row tiles per
+# half; the down call then reuses the route tables it left.
+@pytest.mark.parametrize("fmt", ["q4k", "q5k"])
+@pytest.mark.parametrize("E,F,H,T,top_k,per_slot_rows", [(16, 256, 512, 70, 4, False), (8, 512, 768, 33, 2, True),
+                                                         (40, 256, 256, 5, 3, False)])
+def test_fused_swiglu_matches_unfused(fmt, E, F, H, T, top_k, per_slot_rows):
+    g = qmm_synth.rng(E + F + T)
+    gate_up = _experts(fmt, E, 2 * F, H, g)
+    down = _experts("q4k", E, H, F, g)
+    rows = T * top_k if per_slot_rows else T
+    xq = dev(oracle.quantize_q8_1(qmm_synth.activations(g, rows, H)))
+    ids, probs = qmm_synth.router(g, T, E, top_k)
+    d_ids = dev(ids)
+    say(f"moe_grouped_swiglu {fmt}", f"E={E} F={F} H={H} T={T} top_k={top_k} per_slot_rows={per_slot_rows}")
+    ws = qmm.workspace(max(qmm.workspace_bytes(qmm.QMM_OP_MOE_SLOTS, 2 * F, H, T, E, top_k),
+                           qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k)), xq.device)
+    hq_f = qmm.moe_grouped_swiglu(GEN[fmt][2], dev(gate_up), xq, d_ids, ws=ws)
+    y_f = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), hq_f, d_ids, dev(probs), ws=ws, reuse_routing=True))
+    y1 = qmm.moe_grouped_mmq(GEN[fmt][2], dev(gate_up), xq, d_ids)
+    hq_u = host(qmm.swiglu_q8_1(y1))
+    assert np.array_equal(host(hq_f), hq_u)
+    y_u = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dev(down), dev(hq_u), d_ids, dev(probs)))
+    assert np.array_equal(y_f.view(np.uint32), y_u.view(np.uint32))
 
 
 def _near_half(v, ulps):
