@@ -586,9 +586,10 @@ def main():
         mmq_case("mmq_q4k_14336x4096_t1024", qmm.mmq_q4k, wl3["q4k"], wl3["x_q4k"], ceil_q4)
         mmq_case("mmq_q6k_4096x14336_t1024", qmm.mmq_q6k, wl3["q6k"], wl3["x_q6k"], ceil_q6)
 
-        # routed-expert FFN: gate||up grouped with SwiGLU->Q8_1 fused into its
-        # epilogue, down grouped weighted; expert weights rotated over >= 4 GB
-        # of copies.  The same layer with the SwiGLU as its own launch is timed
+        # routed-expert FFN: moe_ffn (gate||up grouped with SwiGLU->Q8_1 fused
+        # into its epilogue writing the down call's chunks, down grouped
+        # weighted); expert weights rotated over >= 4 GB of copies.  The same
+        # layer as separate calls with the SwiGLU as its own launch is timed
         # beside it.
         wl4 = qmm_synth.workload(4)
         E, H, F, T, top_k = 128, 2048, 768, 512, 8
@@ -609,13 +610,15 @@ def main():
                                 qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k)), dev)
         ws2 = ws1
 
+        ws_ffn = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE_FFN, H, F, T, E, top_k), dev)
+
         def moe_step(c, fused=True):
             qmm.q8_1_quantize(xm, out=xqm)
-            if fused:
-                qmm.moe_grouped_swiglu(qmm.QMM_Q4_K, gus[c], xqm, ids, out=hq, ws=ws1)
-            else:
-                qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gus[c], xqm, ids, out=y1, ws=ws1)
-                qmm.swiglu_q8_1(y1, out=hq)
+            if fused:   # the layer in one call: no SwiGLU rows, no second repack
+                qmm.moe_ffn(qmm.QMM_Q4_K, gus[c], qmm.QMM_Q4_K, dns[c], xqm, ids, probs, out=y2, ws=ws_ffn)
+                return
+            qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gus[c], xqm, ids, out=y1, ws=ws1)
+            qmm.swiglu_q8_1(y1, out=hq)
             qmm.moe_grouped_mmq(qmm.QMM_Q4_K, dns[c], hq, ids, probs, out=y2, ws=ws2, reuse_routing=True)
 
         log("moe ffn")

@@ -67,6 +67,7 @@ typedef enum qmm_status {
 #define QMM_OP_MMQ 1        /* mmq_* and mmq_*_f32                               */
 #define QMM_OP_MOE 2        /* moe_grouped_mmq, weighted (expert_weights != NULL) */
 #define QMM_OP_MOE_SLOTS 3  /* moe_grouped_mmq, per-slot output (no weights)      */
+#define QMM_OP_MOE_FFN 4    /* moe_ffn, with M = H and K = F                      */
 
 /* Largest token count accepted by the matvec entry points. */
 #define QMM_MMVQ_MAX_T 8
@@ -267,6 +268,26 @@ int moe_grouped_mmq_swiglu(int fmt, const void* w, int64_t E, int64_t M, int64_t
                            int64_t expert_stride_bytes, const void* xq, int64_t x_rows_per_token,
                            const int32_t* ids, int64_t T, int64_t top_k, void* hq, void* ws, size_t ws_bytes,
                            void* stream);
+
+/*
+ * moe_ffn -- a routed FFN layer in one call ([GAP] lever T2: route once, the
+ * grouped expert GEMM for both products; lever T4: each producer emits its
+ * consumer's input directly): y[T][H] = sum_k p[t][k] * down_e . SwiGLU(
+ * gate_up_e . x_t) with e = ids[t][k].  w_gu holds E experts of 2F x H
+ * (gate rows [0, F), up rows [F, 2F); fmt_gu QMM_Q4_K or QMM_Q5_K), w_dn E
+ * experts of H x F (fmt_dn any of the three), expert strides in bytes as in
+ * moe_grouped_mmq; xq the Q8_1 rows of x [T][H/32]; expert_weights p
+ * [T][top_k] fp32.  The gate||up epilogue forms SwiGLU -> Q8_1 and writes the
+ * down product's repacked activation chunks into ws itself, so there are no
+ * SwiGLU rows and no second repack; the output is bit-identical to
+ * moe_grouped_mmq_swiglu followed by moe_grouped_mmq_routed (weighted).
+ * ws: qmm_workspace_bytes(QMM_OP_MOE_FFN, H, F, T, E, top_k) bytes.
+ * Requires H % 256 == 0, F % 256 == 0, the limits of moe_grouped_mmq;
+ * QMM_ERR_UNSUPPORTED for other formats.
+ */
+int moe_ffn(int fmt_gu, const void* w_gu, int64_t stride_gu, int fmt_dn, const void* w_dn, int64_t stride_dn,
+            int64_t E, int64_t H, int64_t F, const void* xq, const int32_t* ids, const float* expert_weights,
+            int64_t T, int64_t top_k, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_slot_mmvq -- the per-(token, slot) expert matvec that the grouped GEMM

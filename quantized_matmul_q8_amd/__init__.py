@@ -20,13 +20,13 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    QMM_MMVQ_MAX_T, QMM_OP_MMQ, QMM_OP_MOE, QMM_OP_MOE_SLOTS, QMM_Q4_K, QMM_Q5_K, QMM_Q6_K, QmmError, LIB_PATH,
+    QMM_MMVQ_MAX_T, QMM_OP_MMQ, QMM_OP_MOE, QMM_OP_MOE_SLOTS, QMM_OP_MOE_FFN, QMM_Q4_K, QMM_Q5_K, QMM_Q6_K, QmmError, LIB_PATH,
 )
 
 __all__ = [
     "q8_1_quantize", "mmvq_q4k", "mmvq_q5k", "mmvq_q6k", "mmvq_pair", "mmq_q4k", "mmq_q5k", "mmq_q6k", "mmq_q4k_f32", "mmq_q5k_f32",
     "mmq_q6k_f32",
-    "moe_grouped_mmq", "moe_grouped_swiglu", "moe_slot_mmvq",
+    "moe_grouped_mmq", "moe_grouped_swiglu", "moe_ffn", "moe_slot_mmvq",
     "swiglu_q8_1", "workspace", "workspace_bytes", "debug_subdots", "probe_read", "probe_read_geom",
     "probe_mfma", "probe_mfma_epilogue", "QmmError",
     "QMM_Q4_K", "QMM_Q5_K", "QMM_Q6_K", "LIB_PATH",
@@ -301,6 +301,38 @@ def moe_grouped_swiglu(fmt: int, w: torch.Tensor, xq: torch.Tensor, ids: torch.T
     _need(ws, torch.uint8, "ws", 1)
     _lib.call("moe_grouped_mmq_swiglu", fmt, _p(w), E, M, K, w.stride(0), _p(xq), rows_per_token, _p(ids), T, top_k,
               _p(out), _p(ws), ws.numel(), _stream(w.device))
+    return out
+
+
+def moe_ffn(fmt_gu: int, w_gu: torch.Tensor, fmt_dn: int, w_dn: torch.Tensor, xq: torch.Tensor, ids: torch.Tensor,
+            expert_weights: torch.Tensor, out: torch.Tensor | None = None,
+            ws: torch.Tensor | None = None) -> torch.Tensor:
+    """A routed FFN layer in one call: ``w_gu`` [E, 2F, H/256, bytes] (gate rows
+    then up rows), ``w_dn`` [E, H, F/256, bytes], ``xq`` Q8_1 [T, H/32, 40],
+    ``ids`` int32 and ``expert_weights`` fp32 [T, top_k] -> fp32 [T, H]; the bits
+    of :func:`moe_grouped_swiglu` followed by the weighted routed down call."""
+    _need(w_gu, torch.uint8, "w_gu", 4)
+    _need(w_dn, torch.uint8, "w_dn", 4)
+    if w_gu.shape[3] != _BLOCK_BYTES[fmt_gu] or w_dn.shape[3] != _BLOCK_BYTES[fmt_dn]:
+        raise ValueError("w_gu / w_dn: wrong block size for the format")
+    E, F2, H = w_gu.shape[0], w_gu.shape[1], w_gu.shape[2] * 256
+    F = F2 // 2
+    if F2 % 512 or w_dn.shape[0] != E or w_dn.shape[1] != H or w_dn.shape[2] * 256 != F:
+        raise ValueError(f"expected w_gu [E, 2F, H/256] and w_dn [E, H, F/256] with F % 256 == 0, got "
+                         f"{tuple(w_gu.shape)} and {tuple(w_dn.shape)}")
+    _need(ids, torch.int32, "ids", 2)
+    T, top_k = ids.shape
+    if _acts(xq, H) != T:
+        raise ValueError("xq must have one row per token")
+    _need(expert_weights, torch.float32, "expert_weights", 2)
+    if tuple(expert_weights.shape) != (T, top_k):
+        raise ValueError("expert_weights must be [T, top_k]")
+    out = _out(out, (T, H), torch.float32, w_gu.device)
+    need = workspace_bytes(QMM_OP_MOE_FFN, H, F, T, E, top_k)
+    ws = workspace(need, w_gu.device) if ws is None else ws
+    _need(ws, torch.uint8, "ws", 1)
+    _lib.call("moe_ffn", fmt_gu, _p(w_gu), w_gu.stride(0), fmt_dn, _p(w_dn), w_dn.stride(0), E, H, F, _p(xq), _p(ids),
+              _p(expert_weights), T, top_k, _p(out), _p(ws), ws.numel(), _stream(w_gu.device))
     return out
 
 

@@ -29,6 +29,7 @@ QMM_Q6_K = 14
 QMM_OP_MMQ = 1
 QMM_OP_MOE = 2
 QMM_OP_MOE_SLOTS = 3
+QMM_OP_MOE_FFN = 4
 QMM_MMVQ_MAX_T = 8
 
 _vp, _i64, _sz, _i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
@@ -49,6 +50,7 @@ SIGNATURES = {
     "mmq_q6k_f32": (_i, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "moe_grouped_mmq": (_i, [_i, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64,
                              _vp, _vp, _sz, _vp]),
+    "moe_ffn": (_i, [_i, _vp, _i64, _i, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "moe_grouped_mmq_swiglu": (_i, [_i, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _sz,
                                     _vp]),
     "moe_grouped_mmq_routed": (_i, [_i, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64,

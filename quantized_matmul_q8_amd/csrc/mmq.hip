@@ -146,6 +146,10 @@ struct MmqParams {
   // rows [glu_f, 2 glu_f); Q8_1 output rows of glu_f / 32 blocks per slot
   uint8_t* yq;
   int glu_f;
+  // fused FFN layer: instead of Q8_1 rows, the down product's activation
+  // chunks (its nb_next super-blocks per column tile) go to xr_next
+  uint8_t* xr_next;
+  int nb_next;
 };
 
 // ----------------------------------------------------------------------------
@@ -261,6 +265,9 @@ __global__ __launch_bounds__(256) void mmq_repack_kernel(RepackParams P) {
     // 256 threads: every split-K arrival counter (dense calls only: a grouped
     // call's workspace holds its route tables there)
     if (MODE != kMoe) P.counters[kTileCntWord + threadIdx.x] = 0u;
+    // grouped: also the queue of the down product of a fused FFN layer, whose
+    // activation chunks the gate||up kernel writes (it has no repack of its own)
+    if (MODE == kMoe && threadIdx.x < kXcds) P.counters[kXcds + threadIdx.x] = 0u;
   }
   __shared__ int s_ct[MODE == kMoe ? kMoeMaxE + 1 : 1];
   if constexpr (MODE == kMoe) {
@@ -1007,6 +1014,27 @@ __device__ __forceinline__ void glu_store(const MmqParams& P, const TileRef& R, 
   if (g == 0) xs[wave * 32 + col] = s;
   __syncthreads();
   s += xs[(wave ^ 1) * 32 + col];
+  if (P.xr_next != nullptr) {
+    // the down product's chunk (column tile ctile0, super-block blk / 8),
+    // sub-block s = blk % 8, as the routed-row repack lays it out: values of
+    // half w % 2 at bytes 8k + 4g of entry (2s + w % 2, col), (beta, -beta*C),
+    // the bf16 parts of beta*S.  Padded columns come out zero (their gate||up
+    // sums are zero), as the repack writes them.
+    const int blk = R.r0 / 32, sub = blk & 7;
+    uint8_t* ch = P.xr_next + (static_cast<size_t>(R.ctile0) * P.nb_next + (blk >> 3)) * kChunkBytes;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      reinterpret_cast<uint32_t*>(ch + kChunkPay + ((2 * sub + (wave & 1)) * 32 + col) * 16 + 8 * k + 4 * g)[0] =
+          packed[k];
+    if ((wave & 1) == 0 && g == 0) {
+      const float beta = h2f(f2h_bits(d) & 0xffffu);  // the stored f16 scale
+      reinterpret_cast<float2*>(ch + kChunkFac)[sub * 32 + col] = make_float2(beta, -beta * kMagic);
+      __bf16* bmin = reinterpret_cast<__bf16*>(ch + kChunkMin);
+      split3_bf16(beta * static_cast<float>(s), bmin[col * 8 + sub], bmin[(32 + col) * 8 + sub],
+                  bmin[(64 + col) * 8 + sub]);
+    }
+    return;
+  }
   bool valid;
   const int orow = col_out_row<kMoeGlu>(P, R.tc, col, valid);
   if (valid) {
@@ -1378,10 +1406,15 @@ int moe_tile_rows(int fmt, int /*nb*/) {
 // hq != nullptr: the gate||up product (M = 2F rows) with SwiGLU -> Q8_1
 // fused into the epilogue, Q8_1 rows of F / 32 blocks into hq (Q4_K / Q5_K,
 // F % 128 == 0) instead of fp32 rows into out.
+// xr_next != nullptr (with hq): the fused FFN layer's gate||up call, writing
+// the down product's chunks (nb_next super-blocks) there instead of Q8_1 rows.
+// repack == false: the chunks in xr were written that way; the GEMM runs on
+// them with its queue counters at words 8.. (zeroed by the first repack).
 int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, const uint8_t* xq,
                    float* out, uint8_t* hq, unsigned* counters, const int32_t* counts, const int32_t* offsets,
                    const int32_t* bucket, const int32_t* ct_off, uint8_t* xr,
-                   int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st) {
+                   int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st,
+                   uint8_t* xr_next, int nb_next, bool repack) {
   RepackParams R{};
   R.xq = xq;
   R.xr = xr;
@@ -1394,8 +1427,12 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   R.top_k = top_k;
   R.rows_per_token = rows_per_token;
   R.counters = counters;  // zeroed for the GEMM (route tables reused from an earlier call leave them dirty)
-  int rc = launch_repack<kMoe>(R, nb, max_ctiles, st);
-  if (rc != QMM_OK) return rc;
+  if (repack) {
+    const int rc = launch_repack<kMoe>(R, nb, max_ctiles, st);
+    if (rc != QMM_OK) return rc;
+  } else {
+    counters += kXcds;
+  }
   MmqParams P{};
   P.w = w;
   P.xr = xr;
@@ -1417,6 +1454,8 @@ int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, con
   if (hq != nullptr) {
     if (!whole_k || (M % 256) != 0) return QMM_ERR_UNSUPPORTED;
     P.yq = hq;
+    P.xr_next = xr_next;
+    P.nb_next = nb_next;
     P.glu_f = M / 2;
     P.mt = P.glu_f / 128;
     if (fmt == QMM_Q4_K) return launch_mmq<QMM_Q4_K, 1, kMoeGlu, 1>(P, 0, st);

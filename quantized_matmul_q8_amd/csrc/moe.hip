@@ -39,7 +39,8 @@ constexpr int kMoeBM = 128;  // weight rows of the smaller grouped tile (bounds 
 int mmq_moe_launch(int fmt, const uint8_t* w, int64_t stride, int M, int nb, const uint8_t* xq,
                    float* out, uint8_t* hq, unsigned* counters, const int32_t* counts, const int32_t* offsets,
                    const int32_t* bucket, const int32_t* ct_off, uint8_t* xr,
-                   int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st);
+                   int max_ctiles, int E, int top_k, int rows_per_token, hipStream_t st,
+                   uint8_t* xr_next = nullptr, int nb_next = 0, bool repack = true);
 int64_t moe_max_ctiles(int64_t slots, int64_t E);
 int moe_tile_rows(int fmt, int nb);
 size_t moe_chunk_bytes(int64_t slots, int64_t E, int64_t K);
@@ -81,6 +82,28 @@ static MoeLayout moe_layout(void* ws, int64_t M, int64_t K, int64_t T, int64_t E
 
 size_t moe_workspace_bytes(int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k, bool weighted) {
   return moe_layout(nullptr, M, K, T, E, top_k, weighted).bytes;
+}
+
+// Fused FFN layer (moe_ffn): the down call's layout (its per-slot scratch
+// last), then the gate||up call's input chunks (K = H).  The down chunks (K =
+// F), written by the gate||up epilogue, sit where moe_layout puts a call's
+// chunks.
+struct FfnLayout {
+  MoeLayout dn;
+  uint8_t* chunks_gu;
+  size_t bytes;
+};
+static FfnLayout ffn_layout(void* ws, int64_t H, int64_t F, int64_t T, int64_t E, int64_t top_k) {
+  FfnLayout L{};
+  L.dn = moe_layout(ws, H, F, T, E, top_k, true);
+  const size_t off = align_up(L.dn.bytes, 1024);
+  L.chunks_gu = static_cast<uint8_t*>(ws) + off;
+  L.bytes = off + moe_chunk_bytes(T * top_k, E, H);
+  return L;
+}
+
+size_t moe_ffn_workspace_bytes(int64_t H, int64_t F, int64_t T, int64_t E, int64_t top_k) {
+  return ffn_layout(nullptr, H, F, T, E, top_k).bytes;
 }
 
 // Lanes of the wave holding the same expert id as this lane (v: lane
@@ -242,6 +265,27 @@ using namespace qmm;
 // One grouped call; with `routed`, the route tables already in ws (left by
 // an earlier grouped call on ws with the same ids, T, top_k and E) are used
 // instead of being prepared again.
+// Ordered weighted combine of the per-slot rows in scratch into y[T][M].
+static int combine(const float* scratch, const float* expert_weights, const int32_t* ids, int64_t E, float* y,
+                   int64_t T, int64_t top_k, int64_t M, hipStream_t st) {
+  const bool vec = (M % 4) == 0;
+  const int per_block = vec ? 1024 : 256;
+  constexpr int64_t kMaxGridY = 65535;
+  for (int64_t t0 = 0; t0 < T; t0 += kMaxGridY) {
+    const dim3 grid(static_cast<unsigned>((M + per_block - 1) / per_block),
+                    static_cast<unsigned>(std::min(kMaxGridY, T - t0)));
+    if (vec)
+      hipLaunchKernelGGL(moe_combine_kernel<true>, grid, dim3(256), 0, st, scratch, expert_weights, ids,
+                         static_cast<int>(E), y, static_cast<int>(top_k), static_cast<int>(M), static_cast<int>(t0));
+    else
+      hipLaunchKernelGGL(moe_combine_kernel<false>, grid, dim3(256), 0, st, scratch, expert_weights, ids,
+                         static_cast<int>(E), y, static_cast<int>(top_k), static_cast<int>(M), static_cast<int>(t0));
+    const int rc = launch_status();
+    if (rc != QMM_OK) return rc;
+  }
+  return QMM_OK;
+}
+
 // hq != nullptr: the fused SwiGLU call (Q8_1 rows into hq instead of fp32
 // rows into y; no routing weights).
 static int grouped_call(bool routed, int fmt, const void* w, int64_t E, int64_t M, int64_t K,
@@ -288,22 +332,7 @@ static int grouped_call(bool routed, int fmt, const void* w, int64_t E, int64_t 
                       static_cast<int>(moe_max_ctiles(T * top_k, E)), static_cast<int>(E),
                       static_cast<int>(top_k), static_cast<int>(x_rows_per_token), st);
   if (rc != QMM_OK || !expert_weights) return rc;
-  const bool vec = (M % 4) == 0;
-  const int per_block = vec ? 1024 : 256;
-  constexpr int64_t kMaxGridY = 65535;
-  for (int64_t t0 = 0; t0 < T; t0 += kMaxGridY) {
-    const dim3 grid(static_cast<unsigned>((M + per_block - 1) / per_block),
-                    static_cast<unsigned>(std::min(kMaxGridY, T - t0)));
-    if (vec)
-      hipLaunchKernelGGL(moe_combine_kernel<true>, grid, dim3(256), 0, st, L.scratch, expert_weights, ids,
-                         static_cast<int>(E), y, static_cast<int>(top_k), static_cast<int>(M), static_cast<int>(t0));
-    else
-      hipLaunchKernelGGL(moe_combine_kernel<false>, grid, dim3(256), 0, st, L.scratch, expert_weights, ids,
-                         static_cast<int>(E), y, static_cast<int>(top_k), static_cast<int>(M), static_cast<int>(t0));
-    rc = launch_status();
-    if (rc != QMM_OK) return rc;
-  }
-  return launch_status();
+  return combine(L.scratch, expert_weights, ids, E, y, T, top_k, M, st);
 }
 
 extern "C" int moe_grouped_mmq(int fmt, const void* w, int64_t E, int64_t M, int64_t K,
@@ -331,3 +360,53 @@ extern "C" int moe_grouped_mmq_routed(int fmt, const void* w, int64_t E, int64_t
                            T, top_k, y, ws, ws_bytes, stream);
 }
 
+// The routed FFN layer in one call: route preparation, the gate||up product
+// with SwiGLU -> Q8_1 in its epilogue writing the down product's activation
+// chunks directly (no Q8_1 rows, no second repack), the weighted down product
+// and the ordered combine.
+extern "C" int moe_ffn(int fmt_gu, const void* w_gu, int64_t stride_gu, int fmt_dn, const void* w_dn,
+                       int64_t stride_dn, int64_t E, int64_t H, int64_t F, const void* xq, const int32_t* ids,
+                       const float* expert_weights, int64_t T, int64_t top_k, float* y, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (fmt_gu != QMM_Q4_K && fmt_gu != QMM_Q5_K) return QMM_ERR_UNSUPPORTED;
+  if (fmt_dn != QMM_Q4_K && fmt_dn != QMM_Q5_K && fmt_dn != QMM_Q6_K) return QMM_ERR_UNSUPPORTED;
+  if (E < 1 || E > kMoeMaxE || H < kQK || (H % kQK) != 0 || H / kQK > (1 << 16) || F < kQK || (F % kQK) != 0 ||
+      2 * F > (1 << 30) || H > (1 << 30) || T < 1 || top_k < 1 || top_k > E || top_k > kMoeMaxTopK ||
+      T * top_k > (1 << 30))
+    return QMM_ERR_SHAPE;
+  const int64_t maxw = std::max(2 * F, H);
+  if (((maxw + kMoeBM - 1) / kMoeBM) * moe_max_ctiles(T * top_k, E) > (int64_t{1} << 30)) return QMM_ERR_SHAPE;
+  const auto rowb = [](int fmt, int64_t K) {
+    return (K / kQK) * (fmt == QMM_Q4_K ? kQ4Bytes : fmt == QMM_Q5_K ? kQ5Bytes : kQ6Bytes);
+  };
+  if (stride_gu < 2 * F * rowb(fmt_gu, H) || (stride_gu % 16) != 0) return QMM_ERR_SHAPE;
+  if (stride_dn < H * rowb(fmt_dn, F) || (stride_dn % (fmt_dn == QMM_Q6_K ? 2 : 16)) != 0) return QMM_ERR_SHAPE;
+  if (!w_gu || !w_dn || !xq || !ids || !expert_weights || !y || !ws) return QMM_ERR_NULL;
+  if (!aligned16(w_gu) || !aligned16(w_dn) || !aligned16(xq) || !aligned16(ids) || !aligned16(expert_weights) ||
+      !aligned16(y) || !aligned16(ws))
+    return QMM_ERR_ALIGN;
+  const FfnLayout L = ffn_layout(ws, H, F, T, E, top_k);
+  if (ws_bytes < L.bytes) return QMM_ERR_WORKSPACE;
+  hipStream_t st = to_stream(stream);
+  const int n = static_cast<int>(T * top_k);
+  const MoeLayout& D = L.dn;
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ids, n, static_cast<int>(E), D.counts,
+                     D.offsets, D.ct_off, D.bucket, D.counters);
+  int rc = launch_status();
+  if (rc != QMM_OK) return rc;
+  const int mct = static_cast<int>(moe_max_ctiles(T * top_k, E));
+  // gate||up: its own repack into chunks_gu (zeroing both queues), the
+  // SwiGLU epilogue writing the down chunks into D.chunks
+  rc = mmq_moe_launch(fmt_gu, static_cast<const uint8_t*>(w_gu), stride_gu, static_cast<int>(2 * F),
+                      static_cast<int>(H / kQK), static_cast<const uint8_t*>(xq), nullptr, D.chunks, D.counters,
+                      D.counts, D.offsets, D.bucket, D.ct_off, L.chunks_gu, mct, static_cast<int>(E),
+                      static_cast<int>(top_k), 1, st, D.chunks, static_cast<int>(F / kQK), true);
+  if (rc != QMM_OK) return rc;
+  // down on those chunks (no repack), per-slot rows into the scratch
+  rc = mmq_moe_launch(fmt_dn, static_cast<const uint8_t*>(w_dn), stride_dn, static_cast<int>(H),
+                      static_cast<int>(F / kQK), nullptr, D.scratch, nullptr, D.counters, D.counts, D.offsets,
+                      D.bucket, D.ct_off, D.chunks, mct, static_cast<int>(E), static_cast<int>(top_k), top_k, st,
+                      nullptr, 0, false);
+  if (rc != QMM_OK) return rc;
+  return combine(D.scratch, expert_weights, ids, E, y, T, top_k, H, st);
+}

@@ -5,6 +5,7 @@
 namespace qmm {
 
 size_t moe_workspace_bytes(int64_t M, int64_t K, int64_t T, int64_t E, int64_t top_k, bool weighted);
+size_t moe_ffn_workspace_bytes(int64_t H, int64_t F, int64_t T, int64_t E, int64_t top_k);
 size_t mmq_workspace_bytes(int64_t M, int64_t K, int64_t T);
 int debug_mmvq(int fmt, const void* w, const void* xq, int32_t* D, int32_t* S, int64_t M, int64_t K,
                int64_t T, hipStream_t st);
@@ -87,6 +88,7 @@ extern "C" size_t qmm_workspace_bytes(int op, int64_t M, int64_t K, int64_t T, i
   if (op == QMM_OP_MMQ) return mmq_workspace_bytes(M, K, T);
   if (op == QMM_OP_MOE) return moe_workspace_bytes(M, K, T, E, top_k, true);
   if (op == QMM_OP_MOE_SLOTS) return moe_workspace_bytes(M, K, T, E, top_k, false);
+  if (op == QMM_OP_MOE_FFN) return moe_ffn_workspace_bytes(M, K, T, E, top_k);
   return 0;
 }
 

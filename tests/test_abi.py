@@ -97,6 +97,26 @@ def test_moe_swiglu_errors():
     assert f(Q4, FAKE, 4, 256, 256, 1 << 20, FAKE, 1, FAKE, 8, 2, FAKE, FAKE, 16, NUL) == _lib.QMM_ERR_WORKSPACE
 
 
+def test_moe_ffn_errors():
+    f, Q4, Q6 = L.moe_ffn, _lib.QMM_Q4_K, _lib.QMM_Q6_K
+    big = ctypes.c_size_t(1 << 40)
+    S = 1 << 24
+    # fmt_gu, w_gu, stride_gu, fmt_dn, w_dn, stride_dn, E, H, F, xq, ids, p, T, top_k, y, ws, ws_bytes, stream
+    assert f(Q6, FAKE, S, Q4, FAKE, S, 4, 512, 256, FAKE, FAKE, FAKE, 8, 2, FAKE, FAKE, big, NUL) == \
+        _lib.QMM_ERR_UNSUPPORTED
+    assert f(Q4, FAKE, S, 9, FAKE, S, 4, 512, 256, FAKE, FAKE, FAKE, 8, 2, FAKE, FAKE, big, NUL) == \
+        _lib.QMM_ERR_UNSUPPORTED
+    assert f(Q4, FAKE, S, Q4, FAKE, S, 4, 512, 128, FAKE, FAKE, FAKE, 8, 2, FAKE, FAKE, big, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(Q4, FAKE, S, Q4, FAKE, S, 4, 500, 256, FAKE, FAKE, FAKE, 8, 2, FAKE, FAKE, big, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(Q4, FAKE, 16, Q4, FAKE, S, 4, 512, 256, FAKE, FAKE, FAKE, 8, 2, FAKE, FAKE, big, NUL) == _lib.QMM_ERR_SHAPE
+    assert f(Q4, FAKE, S, Q4, FAKE, S, 4, 512, 256, FAKE, FAKE, NUL, 8, 2, FAKE, FAKE, big, NUL) == _lib.QMM_ERR_NULL
+    assert f(Q4, FAKE, S, Q4, FAKE, S, 4, 512, 256, FAKE, FAKE, FAKE, 8, 2, MISAL, FAKE, big, NUL) == _lib.QMM_ERR_ALIGN
+    assert f(Q4, FAKE, S, Q4, FAKE, S, 4, 512, 256, FAKE, FAKE, FAKE, 8, 2, FAKE, FAKE, 64, NUL) == \
+        _lib.QMM_ERR_WORKSPACE
+    assert L.qmm_workspace_bytes(_lib.QMM_OP_MOE_FFN, 2048, 768, 512, 128, 8) > \
+        L.qmm_workspace_bytes(_lib.QMM_OP_MOE, 2048, 768, 512, 128, 8)
+
+
 def test_mmvq_pair_errors():
     f, Q4, Q6 = L.mmvq_pair, _lib.QMM_Q4_K, _lib.QMM_Q6_K
     assert f(99, FAKE, 4, FAKE, Q4, FAKE, 4, FAKE, FAKE, 256, NUL) == _lib.QMM_ERR_UNSUPPORTED

@@ -278,6 +278,39 @@ def test_fused_swiglu_matches_unfused(fmt, E, F, H, T, top_k, per_slot_rows):
     assert np.array_equal(y_f.view(np.uint32), y_u.view(np.uint32))
 
 
+# The whole routed FFN layer in one call (the gate||up epilogue writing the down
+# product's chunks itself): bit-identical to the fused SwiGLU call followed by
+# the weighted routed down call, for each down format, and at the full layer.
+@pytest.mark.parametrize("fmt_dn", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("E,F,H,T,top_k", [(16, 256, 512, 70, 4), (40, 512, 256, 5, 3)])
+def test_moe_ffn_matches_two_calls(fmt_dn, E, F, H, T, top_k):
+    g = qmm_synth.rng(E + F + T + 1)
+    gate_up = _experts("q4k", E, 2 * F, H, g)
+    down = _experts(fmt_dn, E, H, F, g)
+    xq = dev(oracle.quantize_q8_1(qmm_synth.activations(g, T, H)))
+    ids, probs = qmm_synth.router(g, T, E, top_k)
+    d_ids, d_probs = dev(ids), dev(probs)
+    say(f"moe_ffn q4k/{fmt_dn}", f"E={E} F={F} H={H} T={T} top_k={top_k}")
+    y = host(qmm.moe_ffn(qmm.QMM_Q4_K, dev(gate_up), GEN[fmt_dn][2], dev(down), xq, d_ids, d_probs))
+    ws = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k), xq.device)
+    hq = qmm.moe_grouped_swiglu(qmm.QMM_Q4_K, dev(gate_up), xq, d_ids, ws=ws)
+    y2 = host(qmm.moe_grouped_mmq(GEN[fmt_dn][2], dev(down), hq, d_ids, d_probs, ws=ws, reuse_routing=True))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+def test_moe_ffn_full_layer():
+    wl = qmm_synth.workload(4)
+    E, H, F, T, top_k = 128, 2048, 768, 512, 8
+    say("moe_ffn full layer", f"E={E} H={H} F={F} T={T} top_k={top_k}")
+    xq = qmm.q8_1_quantize(dev(wl["x"]))
+    d_ids, d_probs = dev(wl["ids"]), dev(wl["probs"])
+    gate_up, down = dev(wl["gate_up"]), dev(wl["down"])
+    y = host(qmm.moe_ffn(qmm.QMM_Q4_K, gate_up, qmm.QMM_Q4_K, down, xq, d_ids, d_probs))
+    hq = qmm.swiglu_q8_1(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, gate_up, xq, d_ids))
+    y2 = host(qmm.moe_grouped_mmq(qmm.QMM_Q4_K, down, hq, d_ids, d_probs))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
 def _near_half(v, ulps):
     """fp32 value v within `ulps` of a rounding tie n + 1/2."""
     v = np.asarray(v, np.float32)
