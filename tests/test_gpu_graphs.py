@@ -119,12 +119,14 @@ def test_routed_ffn_graph():
     y = torch.empty((T, H), dtype=torch.float32, device=DEV)
     ws = qmm.workspace(max(qmm.workspace_bytes(qmm.QMM_OP_MOE_SLOTS, 2 * F, H, T, E, top_k),
                            qmm.workspace_bytes(qmm.QMM_OP_MOE, H, F, T, E, top_k)), DEV)
-    say("graph: routed FFN (quantize, grouped gate||up, swiglu, routed down + combine; fused SwiGLU)",
+    say("graph: routed FFN (quantize, grouped gate||up, swiglu, routed down + combine; fused SwiGLU; moe_ffn)",
         f"E={E} H={H} F={F} T={T} top_k={top_k}")
 
     ws_f = qmm.workspace(ws.numel(), DEV)
     hq_f = torch.empty_like(hq)
     y_f = torch.empty_like(y)
+    ws_l = qmm.workspace(qmm.workspace_bytes(qmm.QMM_OP_MOE_FFN, H, F, T, E, top_k), DEV)
+    y_l = torch.empty_like(y)
 
     def run():
         qmm.q8_1_quantize(x, out=xq)
@@ -134,6 +136,8 @@ def test_routed_ffn_graph():
         # the same layer with the SwiGLU fused into the gate||up call
         qmm.moe_grouped_swiglu(qmm.QMM_Q4_K, gate_up, xq, ids, out=hq_f, ws=ws_f)
         qmm.moe_grouped_mmq(qmm.QMM_Q4_K, down, hq_f, ids, probs, out=y_f, ws=ws_f, reuse_routing=True)
+        # and in one call
+        qmm.moe_ffn(qmm.QMM_Q4_K, gate_up, qmm.QMM_Q4_K, down, xq, ids, probs, out=y_l, ws=ws_l)
 
     # experts relabelled: each token keeps top_k distinct experts
     relabel = torch.randperm(E, generator=torch.Generator().manual_seed(3)).to(torch.int32).to(DEV)
@@ -143,5 +147,5 @@ def test_routed_ffn_graph():
         if r >= 2:   # new routing: the replay must prepare its route tables again
             ids.copy_(relabel[ids.long()])
 
-    _check_replays(run, [gu, y, hq_f, y_f], change, "routed FFN")
-    assert torch.equal(hq, hq_f) and torch.equal(y, y_f)
+    _check_replays(run, [gu, y, hq_f, y_f, y_l], change, "routed FFN")
+    assert torch.equal(hq, hq_f) and torch.equal(y, y_f) and torch.equal(y, y_l)
